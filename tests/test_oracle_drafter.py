@@ -1,0 +1,336 @@
+"""Pins of the oracle drafter's forward against brute force, invariants the
+pages fix and special cases (no GPU)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafter_tap_amd import config, synth
+from oracle import dflash as D
+
+
+def _f32(t):
+    return synth.bf16_to_f32_numpy(t)
+
+
+def _np_weights(w):
+    out = {}
+    for k, v in w.items():
+        out[k] = [_f32(t) for t in v] if isinstance(v, list) else _f32(v)
+    return out
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = config.tiny()
+    W = _np_weights(synth.make_weights(cfg, seed=0))
+    taps = [t.numpy().astype(np.float64) for t in synth.make_taps(cfg, 64, seed=0, outliers=False)]
+    return cfg, W, taps
+
+
+def _brute_draft(cfg, W, taps, tokens, pos, valid_from):
+    """Independent scalar-loop statement of one draft block (exact fp64)."""
+    H, nq, nkv, hd, F = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn
+    eps = cfg.rms_eps
+    B = len(tokens)
+    lo = max(valid_from, pos - cfg.window, 0)
+    ctx = list(range(lo, pos))
+
+    def norm(vec, g):
+        ms = sum(x * x for x in vec) / len(vec)
+        r = 1.0 / math.sqrt(ms + eps)
+        return [g[i] * vec[i] * r for i in range(len(vec))]
+
+    def matvec(Wm, vec, r0, r1):
+        return [sum(Wm[r][c] * vec[c] for c in range(len(vec))) for r in range(r0, r1)]
+
+    def rot(vec, p):
+        half = hd // 2
+        out = list(vec)
+        for k in range(half):
+            a = p * cfg.rope_theta ** (-2.0 * k / hd)
+            z = complex(vec[k], vec[k + half]) * complex(math.cos(a), math.sin(a))
+            out[k], out[k + half] = z.real, z.imag
+        return out
+
+    # context hidden
+    cvec = []
+    for p in ctx:
+        x = []
+        for t in range(cfg.n_taps):
+            x.extend(taps[t][p][:cfg.tap_hidden])
+        cvec.append(matvec(W["fc"], x, 0, H))
+    h = [list(W["embed"][t]) for t in tokens]
+    for l in range(cfg.n_layers):
+        wqkv = W["wqkv"][l]
+        qoff, koff, voff = 0, nq * hd, (nq + nkv) * hd
+        K = [[None] * (len(ctx) + B) for _ in range(nkv)]
+        Vv = [[None] * (len(ctx) + B) for _ in range(nkv)]
+        for n, p in enumerate(ctx):
+            for g in range(nkv):
+                K[g][n] = rot(norm(matvec(wqkv, cvec[n], koff + g * hd, koff + (g + 1) * hd), W["k_norm"][l]), p)
+                Vv[g][n] = matvec(wqkv, cvec[n], voff + g * hd, voff + (g + 1) * hd)
+        a = [norm(h[i], W["ln_in"][l]) for i in range(B)]
+        Q = [[None] * B for _ in range(nq)]
+        for i in range(B):
+            for j in range(nq):
+                Q[j][i] = rot(norm(matvec(wqkv, a[i], qoff + j * hd, qoff + (j + 1) * hd), W["q_norm"][l]), pos + i)
+            for g in range(nkv):
+                K[g][len(ctx) + i] = rot(norm(matvec(wqkv, a[i], koff + g * hd, koff + (g + 1) * hd), W["k_norm"][l]), pos + i)
+                Vv[g][len(ctx) + i] = matvec(wqkv, a[i], voff + g * hd, voff + (g + 1) * hd)
+        for i in range(B):
+            o = []
+            for j in range(nq):
+                g = j // (nq // nkv)
+                s = [sum(Q[j][i][d] * K[g][t][d] for d in range(hd)) / math.sqrt(hd) for t in range(len(K[g]))]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                o.extend(sum(e[t] * Vv[g][t][d] for t in range(len(e))) / sum(e) for d in range(hd))
+            y = matvec(W["wo"][l], o, 0, H)
+            h[i] = [h[i][c] + y[c] for c in range(H)]
+            a2 = norm(h[i], W["ln_post"][l])
+            gate = matvec(W["wgu"][l], a2, 0, F)
+            up = matvec(W["wgu"][l], a2, F, 2 * F)
+            act = [gate[f] / (1 + math.exp(-gate[f])) * up[f] for f in range(F)]
+            y = matvec(W["wd"][l], act, 0, H)
+            h[i] = [h[i][c] + y[c] for c in range(H)]
+    z = [norm(h[i], W["final_norm"]) for i in range(B)]
+    return np.array(z)
+
+
+@pytest.mark.slow
+def test_draft_block_matches_scalar_brute_force():
+    # a still smaller drafter so pure-Python loops finish quickly
+    cfg = config.tiny(block=3, window=5).replace(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8,
+                                                   ffn=48, vocab=64, tap_hidden=32, mask_id=63)
+    W = {k: ([t.astype(np.float64) for t in v] if isinstance(v, list) else v.astype(np.float64))
+         for k, v in _np_weights(synth.make_weights(cfg, seed=3)).items()}
+    W["embed"] = W["embed"] * 20.0        # make the residual stream large enough to matter
+    taps = [t.numpy().astype(np.float64) for t in synth.make_taps(cfg, 12, seed=3, outliers=False)]
+    tokens = [7, 63, 63]
+    for pos, vf in ((9, 0), (9, 6), (0, 0), (3, 3)):
+        got = D.draft_block(cfg, W, taps, tokens, pos, vf, mode="exact")["z"]
+        ref = _brute_draft(cfg, W, taps, tokens, pos, vf)
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_block_is_bidirectional(tiny):
+    cfg, W, taps = tiny
+    base = [11] + [cfg.mask_id] * (cfg.block - 1)
+    z0 = D.draft_block(cfg, W, taps, base, 40, mode="exact")["z"]
+    for j in range(1, cfg.block):
+        changed = list(base)
+        changed[j] = 1234
+        z1 = D.draft_block(cfg, W, taps, changed, 40, mode="exact")["z"]
+        # every earlier row sees the later token (a causal mask would leave rows < j untouched)
+        for i in range(j):
+            assert np.max(np.abs(z1[i] - z0[i])) > 1e-6, (i, j)
+
+
+def test_sliding_window_ignores_old_rows_and_full_window_equals_full_context(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    small = cfg.replace(window=16)
+    z0 = D.draft_block(small, W, taps, tokens, 50, mode="exact")["z"]
+    pert = [t.copy() for t in taps]
+    for t in pert:
+        t[:34] = 1e3                    # rows older than pos - W = 34
+    z1 = D.draft_block(small, W, pert, tokens, 50, mode="exact")["z"]
+    np.testing.assert_array_equal(z0, z1)
+    pert[0][40] += 1.0                  # a row inside the window matters
+    z2 = D.draft_block(small, W, pert, tokens, 50, mode="exact")["z"]
+    assert np.max(np.abs(z2 - z0)) > 1e-6
+    # W >= context length: identical to the full context
+    zf = D.draft_block(cfg.replace(window=10 ** 6), W, taps, tokens, 50, mode="exact")["z"]
+    zw = D.draft_block(cfg.replace(window=50), W, taps, tokens, 50, mode="exact")["z"]
+    np.testing.assert_array_equal(zf, zw)
+    # valid_from narrows the window the same way
+    zv = D.draft_block(small, W, pert, tokens, 50, valid_from=44, mode="exact")["z"]
+    zs = D.draft_block(cfg.replace(window=6), W, pert, tokens, 50, mode="exact")["z"]
+    np.testing.assert_array_equal(zv, zs)
+
+
+def test_rope_offset_shift_invariance(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    # shifting every position (context and block) by a constant leaves outputs unchanged
+    z0 = D.draft_block(cfg, W, taps, tokens, 40, valid_from=10, mode="exact")["z"]
+    shift = 1000
+    taps_s = [np.concatenate([np.zeros((shift, t.shape[1])), t], 0) for t in taps]
+    z1 = D.draft_block(cfg, W, taps_s, tokens, 40 + shift, valid_from=10 + shift, mode="exact")["z"]
+    np.testing.assert_allclose(z1, z0, rtol=1e-9, atol=1e-9)
+
+
+def test_block_positions_must_follow_context(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    lo, pos = 20, 40
+    ref = D.draft_block(cfg, W, taps, tokens, pos, valid_from=lo, mode="exact")["z"]
+    # same context rows, but the block placed 300 positions later: outputs move at O(1)
+    taps_far = [t.copy() for t in taps]
+    far = [np.concatenate([t, np.zeros((400, t.shape[1]))], 0) for t in taps_far]
+    for t in far:
+        t[lo + 300: pos + 300] = t[lo:pos]
+    z_far = D.draft_block(cfg.replace(window=20), W, far, tokens, pos + 300, valid_from=lo + 300, mode="exact")["z"]
+    np.testing.assert_allclose(z_far, ref, rtol=1e-9, atol=1e-9)   # everything shifted: same
+    z_bad = D.draft_block(cfg, W, taps, tokens, pos + 7, valid_from=lo, mode="exact")["z"]
+    assert np.max(np.abs(z_bad - ref)) > 1e-3 * np.max(np.abs(ref))
+
+
+def test_context_length_zero_is_block_only_attention(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    out = D.draft_block(cfg, W, taps, tokens, 30, valid_from=30, want_intermediates=True, mode="exact")
+    assert out["lo"] == out["hi"] == 30
+    # with a context of garbage rows excluded by valid_from the result cannot depend on them
+    pert = [t + 5.0 for t in taps]
+    out2 = D.draft_block(cfg, W, pert, tokens, 30, valid_from=30, mode="exact")
+    np.testing.assert_array_equal(out["z"], out2["z"])
+    # one layer by hand: with no context the layer is textbook non-causal GQA
+    one = cfg.replace(n_layers=1)
+    t = torch.tensor(tokens)
+    h = torch.from_numpy(W["embed"])[t].double()
+
+    def rms(x, g):
+        return torch.from_numpy(np.asarray(g, np.float64)) * x * torch.rsqrt((x * x).mean(-1, keepdim=True) + cfg.rms_eps)
+
+    a = rms(h, W["ln_in"][0])
+    wqkv = torch.from_numpy(W["wqkv"][0]).double()
+    nq, nkv, hd, B = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block
+    q = (a @ wqkv[: nq * hd].T).view(B, nq, hd)
+    k = (a @ wqkv[nq * hd:(nq + nkv) * hd].T).view(B, nkv, hd)
+    v = (a @ wqkv[(nq + nkv) * hd:].T).view(B, nkv, hd)
+    q, k = rms(q, W["q_norm"][0]), rms(k, W["k_norm"][0])
+    ang = torch.arange(30, 30 + B, dtype=torch.float64)[:, None] * torch.from_numpy(D.rope_inv_freq(hd, cfg.rope_theta))[None]
+    cos, sin = torch.cos(ang)[:, None], torch.sin(ang)[:, None]
+
+    def rot(x):
+        x1, x2 = x[..., : hd // 2], x[..., hd // 2:]
+        return torch.cat([x1 * cos - x2 * sin, x2 * cos + x1 * sin], -1)
+
+    q, k = rot(q), rot(k)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(0, 1), k.transpose(0, 1).repeat_interleave(nq // nkv, 0),
+        v.transpose(0, 1).repeat_interleave(nq // nkv, 0))
+    h = h + o.transpose(0, 1).reshape(B, nq * hd) @ torch.from_numpy(W["wo"][0]).double().T
+    a2 = rms(h, W["ln_post"][0])
+    wgu = torch.from_numpy(W["wgu"][0]).double()
+    act = torch.nn.functional.silu(a2 @ wgu[: cfg.ffn].T) * (a2 @ wgu[cfg.ffn:].T)
+    h = h + act @ torch.from_numpy(W["wd"][0]).double().T
+    z = rms(h, W["final_norm"])
+    got = D.draft_block(one, W, taps, tokens, 30, valid_from=30, mode="exact")["z"]
+    np.testing.assert_allclose(got, z.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_duplicated_kv_weights(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    grp = cfg.n_q_heads // cfg.n_kv_heads
+    mha = cfg.replace(n_kv_heads=cfg.n_q_heads)
+    W2 = dict(W)
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    W2["wqkv"] = []
+    for w in W["wqkv"]:
+        wq, wk, wv = w[: nq * hd], w[nq * hd:(nq + nkv) * hd], w[(nq + nkv) * hd:]
+        dup = lambda m: np.repeat(m.reshape(nkv, hd, -1), grp, axis=0).reshape(nq * hd, -1)
+        W2["wqkv"].append(np.concatenate([wq, dup(wk), dup(wv)], 0))
+    z_gqa = D.draft_block(cfg, W, taps, tokens, 40, mode="exact")["z"]
+    z_mha = D.draft_block(mha, W2, taps, tokens, 40, mode="exact")["z"]
+    np.testing.assert_allclose(z_gqa, z_mha, rtol=1e-12, atol=1e-13)
+
+
+def test_fc_one_hot_column_and_linearity(tiny):
+    cfg, W, _ = tiny
+    n = 3
+    taps = [np.zeros((n, cfg.tap_hidden)) for _ in range(cfg.n_taps)]
+    taps[1][2, 17] = 1.0                     # concatenated column 256 + 17
+    c = D.ctx_hidden(cfg, W, taps, 0, n, mode="exact")
+    np.testing.assert_array_equal(c[2], W["fc"][:, cfg.tap_hidden + 17])
+    assert not np.any(c[:2])
+    rng = np.random.default_rng(9)
+    t1 = [rng.standard_normal((n, cfg.tap_hidden)) for _ in range(cfg.n_taps)]
+    t2 = [rng.standard_normal((n, cfg.tap_hidden)) for _ in range(cfg.n_taps)]
+    s = [a + 2 * b for a, b in zip(t1, t2)]
+    np.testing.assert_allclose(D.ctx_hidden(cfg, W, s, 0, n, "exact"),
+                               D.ctx_hidden(cfg, W, t1, 0, n, "exact") + 2 * D.ctx_hidden(cfg, W, t2, 0, n, "exact"),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_hc_streams_identical_equal_single_stream(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    hc = cfg.replace(hc_streams=4)
+    taps4 = [np.tile(t, (1, 4)) for t in taps]
+    z1 = D.draft_block(cfg, W, taps, tokens, 40, mode="mirror")["z"]
+    z4 = D.draft_block(hc, W, taps4, tokens, 40, mode="mirror")["z"]
+    np.testing.assert_array_equal(z1, z4)
+
+
+def test_mirror_vs_exact_drift_is_small(tiny):
+    cfg, W, taps = tiny
+    tokens = [11] + [cfg.mask_id] * (cfg.block - 1)
+    a = D.draft_block(cfg, W, taps, tokens, 40, mode="mirror")["logits"]
+    b = D.draft_block(cfg, W, taps, tokens, 40, mode="exact")["logits"]
+    drift = np.max(np.abs(a - b)) / np.max(np.abs(b))
+    assert 0 < drift < 0.05
+
+
+# ------------------------------------------------------------------ INT4 format
+
+def test_int4_pack_layout_and_unpack():
+    rng = torch.Generator().manual_seed(0)
+    N, K = 6, 256
+    w = (torch.randn(N, K, generator=rng) * 0.02).to(torch.bfloat16)
+    w[2, 64:128] = 0                       # a zero group: scale 0, q 0
+    packed, scales = synth.quantize_int4(w)
+    assert packed.shape == (N, K // 2) and packed.dtype == torch.uint8
+    assert scales.shape == (N, K // 64) and scales.dtype == torch.float16
+    deq = D.int4_unpack(packed.numpy(), scales.numpy(), K)
+    wf = w.float().numpy().astype(np.float64)
+    s = np.repeat(scales.numpy().astype(np.float64), 64, axis=1)
+    assert np.all(np.abs(deq - wf) <= s / 2 + 1e-12)
+    assert np.all(deq[2, 64:128] == 0)
+    # brute-force byte placement from the documented layout for every element
+    q = np.rint(deq / np.where(s > 0, s, 1)).astype(np.int64)
+    b = packed.numpy()
+    for n in range(N):
+        for k in range(K):
+            c, r = divmod(k, 128)
+            sidx, r2 = divmod(r, 32)
+            j, e = divmod(r2, 8)
+            word = c * 16 + 4 * j + sidx
+            nib = e // 2 if e % 2 == 0 else 4 + (e - 1) // 2
+            byte = b[n, 4 * word + nib // 2]
+            u = (int(byte) >> (4 * (nib % 2))) & 0xF
+            assert u - 8 == q[n, k]
+    # max-magnitude element of each nonzero group hits |q| = 7 (scale = max/7)
+    qg = np.abs(q).reshape(N, -1, 64).max(-1)
+    assert np.all((qg == 7) | (qg == 0))
+
+
+# ------------------------------------------------------------------ synthetic verify generator
+
+def test_geometric_accept_statistics():
+    B, n = 16, 10000
+    a = synth.geometric_accepts(n, 1, B, p=0.75, seed=0)[:, 0]
+    for i in range(1, 8):
+        p = 0.75 ** i
+        emp = np.mean(a >= i)
+        assert abs(emp - p) <= 3 * math.sqrt(p * (1 - p) / n), i
+    exp_mean = sum(0.75 ** i for i in range(1, B))
+    assert abs(a.mean() - exp_mean) < 0.08
+    assert exp_mean == pytest.approx(2.96, abs=0.01)
+    assert a.max() <= B - 1
+
+
+def test_verify_from_draft_prefix_property():
+    R, B, V = 5, 8, 50
+    g = torch.Generator().manual_seed(0)
+    d = torch.randint(0, V, (R, B - 1), generator=g, dtype=torch.int32)
+    acc = torch.tensor([0, 3, 7, 1, 5], dtype=torch.int32)
+    noise = torch.randint(0, V - 1, (R, B), generator=g, dtype=torch.int32)
+    v = synth.verify_from_draft(d, acc, V, noise)
+    for r in range(R):
+        res = D.accept(d[r].tolist(), v[r].tolist())
+        assert res["acc"] == int(acc[r])

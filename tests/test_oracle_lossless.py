@@ -1,0 +1,96 @@
+"""Losslessness of the speculative loop with the oracle drafter and the tiny
+synthetic target (no GPU): output must equal greedy decoding token for token."""
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_tap_amd import config, synth
+from oracle import dflash as D
+from oracle import target as T
+
+
+def _np(w):
+    return {k: ([synth.bf16_to_f32_numpy(t) for t in v] if isinstance(v, list) else synth.bf16_to_f32_numpy(v))
+            for k, v in w.items()}
+
+
+@pytest.fixture(scope="module")
+def setup():
+    cfg = config.tiny()
+    Wd = _np(synth.make_weights(cfg, seed=0))
+    tcfg = cfg.replace(n_layers=2)
+    Wt = _np(synth.make_weights(tcfg, seed=11))
+    Wt["embed"], Wt["lm_head"] = Wd["embed"], Wd["lm_head"]      # shared with the drafter
+    Wt["embed"] = Wt["embed"] * 30.0   # a peakier target so greedy continuations vary
+    Wd["embed"] = Wt["embed"]
+    tgt = T.TinyTarget(tcfg, Wt, n_layers=2)
+    return cfg, Wd, tgt
+
+
+def test_greedy_is_deterministic_and_batch_invariant(setup):
+    cfg, Wd, tgt = setup
+    prompt = [5, 17, 300, 4000, 12]
+    g1 = T.greedy(tgt, prompt, 20)
+    # feeding the greedy continuation as one verify block gives the same argmaxes
+    tgt.reset()
+    ids, _ = tgt.feed(prompt + g1[:-1], 0)
+    assert ids[len(prompt) - 1:] == g1
+    assert T.greedy(tgt, prompt, 20) == g1
+
+
+def test_lossless_with_oracle_drafter(setup):
+    cfg, Wd, tgt = setup
+    prompt = [5, 17, 300, 4000, 12, 99]
+    ref = T.greedy(tgt, prompt, 24)
+    res = T.speculative(tgt, T.oracle_draft_fn(cfg, Wd), prompt, 24, cfg.block, cfg.window, cfg.mask_id)
+    assert res["tokens"] == ref
+    assert len(ref) == 24
+
+
+@pytest.mark.parametrize("block", [1, 2, 8])
+def test_lossless_with_planted_drafts(setup, block):
+    """Drafts equal to the true continuation corrupted at a geometric position
+    exercise long accepts, the bonus token and budget clamping."""
+    cfg, Wd, tgt = setup
+    prompt = [7, 8, 9, 1000]
+    n_new = 37
+    ref = T.greedy(tgt, prompt, n_new + block)
+    rng = np.random.default_rng(block)
+
+    def planted(blk, pos, vf, taps):
+        start = pos - len(prompt) + 1          # index in ref of the token after blk[0]
+        d = list(ref[start:start + block - 1])
+        d += [0] * (block - 1 - len(d))
+        a = min(int(rng.geometric(0.3)) - 1, block - 1)
+        if a < block - 1:
+            d[a] = (d[a] + 1) % cfg.vocab
+        return d
+
+    res = T.speculative(tgt, planted, prompt, n_new, block, cfg.window, cfg.mask_id)
+    assert res["tokens"] == ref[:n_new]
+    if block > 1:
+        assert max(res["accepts"]) >= min(2, block - 1)
+
+
+def test_lossless_stops_at_eos(setup):
+    cfg, Wd, tgt = setup
+    prompt = [5, 17, 300, 4000, 12, 99]
+    full = T.greedy(tgt, prompt, 30)
+    eos = full[9]
+    ref = T.greedy(tgt, prompt, 30, eos_id=eos)
+    assert ref[-1] == eos and len(ref) <= 10
+
+    def planted(blk, pos, vf, taps):
+        start = pos - len(prompt) + 1
+        d = list(full[start:start + cfg.block - 1])
+        return d + [0] * (cfg.block - 1 - len(d))
+
+    res = T.speculative(tgt, planted, prompt, 30, cfg.block, cfg.window, cfg.mask_id, eos_id=eos)
+    assert res["tokens"] == ref
+
+
+def test_block_one_is_plain_greedy(setup):
+    cfg, Wd, tgt = setup
+    prompt = [3, 4]
+    ref = T.greedy(tgt, prompt, 12)
+    res = T.speculative(tgt, lambda *a: [], prompt, 12, 1, cfg.window, cfg.mask_id)
+    assert res["tokens"] == ref and all(a == 0 for a in res["accepts"])
