@@ -1,0 +1,270 @@
+"""ctypes binding of libdflash.so (entry points of include/dflash.h).
+
+Argument marshalling only: tensors are passed as device pointers
+(``data_ptr()``) and the current PyTorch stream as the HIP stream; every step of
+the round runs in the library's kernels. There is no fallback: if the library
+is missing or was built for nothing this device can run, calls fail loudly.
+
+``Drafter`` is a small convenience wrapper owning the state and workspace
+tensors of one handle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from .config import DFlashConfig
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdflash.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "dflash.h")
+
+c_int, c_void_p, c_size_t, c_float, c_ll, c_uint = (ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                     ctypes.c_float, ctypes.c_longlong, ctypes.c_uint)
+
+STATUS = {0: "DFLASH_OK", -1: "DFLASH_E_ARG", -2: "DFLASH_E_CONFIG", -3: "DFLASH_E_SHAPE",
+          -4: "DFLASH_E_CAPACITY", -5: "DFLASH_E_UNSUPPORTED", -6: "DFLASH_E_HIP",
+          -7: "DFLASH_E_DEVICE", -8: "DFLASH_E_STATE"}
+
+K_LMHEAD, K_QKV, K_O, K_GATEUP, K_DOWN, K_ATTN, K_FC, K_STAGE_KV = range(8)
+
+
+class dflash_config(ctypes.Structure):
+    _fields_ = [(n, c_int) for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
+                                      "vocab", "n_taps", "hc_streams", "tap_hidden", "block", "window",
+                                      "ring_capacity", "max_requests", "mask_id")] + \
+               [("rope_theta", c_float), ("rms_eps", c_float), ("ctx_norm", c_int), ("wfmt", c_int),
+                ("max_stage_rows", c_int)]
+
+
+PP = ctypes.POINTER(c_void_p)
+
+
+class dflash_weights(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("lm_head", c_void_p), ("fc", c_void_p), ("fc_scales", c_void_p),
+                ("ctx_norm", c_void_p), ("final_norm", c_void_p),
+                ("wqkv", PP), ("wqkv_scales", PP), ("wo", PP), ("wo_scales", PP),
+                ("wgu", PP), ("wgu_scales", PP), ("wd", PP), ("wd_scales", PP),
+                ("ln_in", PP), ("ln_post", PP), ("q_norm", PP), ("k_norm", PP)]
+
+
+class dflash_state_layout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in ("pos", "valid_from", "error", "stats", "ring_k", "ring_v", "total")]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_diffusion_drafter_tap_amd.build`"
+                           " (there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P = c_void_p
+    sig = {
+        "dflash_create": (c_int, [ctypes.POINTER(dflash_config), ctypes.POINTER(dflash_weights), ctypes.POINTER(P)]),
+        "dflash_destroy": (None, [P]),
+        "dflash_state_bytes": (c_size_t, [ctypes.POINTER(dflash_config)]),
+        "dflash_workspace_bytes": (c_size_t, [ctypes.POINTER(dflash_config)]),
+        "dflash_get_state_layout": (c_int, [ctypes.POINTER(dflash_config), ctypes.POINTER(dflash_state_layout)]),
+        "dflash_bind": (c_int, [P, P, P, P]),
+        "dflash_reset": (c_int, [P, P, c_int, c_int, c_int]),
+        "dflash_tap_stage": (c_int, [P, P, PP, c_ll, c_int, P, P, c_int]),
+        "dflash_draft_block": (c_int, [P, P, P, c_int, P, P, P, c_int]),
+        "dflash_accept": (c_int, [P, P, P, c_int, P, c_int, c_int, P, P, P, P, P]),
+        "dflash_check": (c_int, [P, P, ctypes.POINTER(c_uint)]),
+        "dflash_clear_error": (c_int, [P, P]),
+        "dflash_set_timing_events": (c_int, [P, c_int, PP, PP, c_int]),
+        "dflash_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER) -> List[str]:
+    """Names of the functions include/dflash.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return load().dflash_last_error().decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise DFlashError(fn, rc, last_error())
+
+
+def c_config(cfg: DFlashConfig) -> dflash_config:
+    c = dflash_config()
+    for name, _ in dflash_config._fields_:
+        setattr(c, name, getattr(cfg, name))
+    return c
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def state_bytes(cfg: DFlashConfig) -> int:
+    return load().dflash_state_bytes(ctypes.byref(c_config(cfg)))
+
+
+def workspace_bytes(cfg: DFlashConfig) -> int:
+    return load().dflash_workspace_bytes(ctypes.byref(c_config(cfg)))
+
+
+def state_layout(cfg: DFlashConfig) -> Dict[str, int]:
+    lay = dflash_state_layout()
+    _check("dflash_get_state_layout", load().dflash_get_state_layout(ctypes.byref(c_config(cfg)), ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n, _ in dflash_state_layout._fields_}
+
+
+class Drafter:
+    """One library handle with its own state and workspace (torch tensors on ``device``)."""
+
+    def __init__(self, cfg: DFlashConfig, weights: Dict[str, object], device="cuda"):
+        self.lib = load()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self._c_cfg = c_config(cfg)
+        self._keep = []
+        w = dflash_weights()
+
+        def arr(name):
+            if name not in weights:
+                return None
+            ptrs = (c_void_p * cfg.n_layers)(*[t.data_ptr() for t in weights[name]])
+            self._keep.append(ptrs)
+            return ctypes.cast(ptrs, PP)
+
+        for name in ("embed", "lm_head", "fc", "fc_scales", "ctx_norm", "final_norm"):
+            t = weights.get(name)
+            setattr(w, name, None if t is None else t.data_ptr())
+        for name in ("wqkv", "wo", "wgu", "wd", "ln_in", "ln_post", "q_norm", "k_norm"):
+            setattr(w, name, arr(name))
+            if name in ("wqkv", "wo", "wgu", "wd"):
+                setattr(w, name + "_scales", arr(name + "_scales"))
+        self._weights = weights
+        self._c_w = w
+        ctx = c_void_p()
+        _check("dflash_create", self.lib.dflash_create(ctypes.byref(self._c_cfg), ctypes.byref(w), ctypes.byref(ctx)))
+        self.ctx = ctx
+        self.layout = state_layout(cfg)
+        self.state = torch.empty(self.layout["total"], dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(workspace_bytes(cfg), dtype=torch.uint8, device=self.device)
+        _check("dflash_bind", self.lib.dflash_bind(ctx, self.state.data_ptr(), self.workspace.data_ptr(), _stream()))
+
+    def __del__(self):
+        ctx = getattr(self, "ctx", None)
+        if ctx is not None and ctx.value:
+            self.lib.dflash_destroy(ctx)
+            self.ctx = None
+
+    # ---------------------------------------------------------------- entry points
+    def reset(self, req: int, valid_from: int, pos: int):
+        _check("dflash_reset", self.lib.dflash_reset(self.ctx, _stream(), req, valid_from, pos))
+
+    def tap_stage(self, taps: Sequence[torch.Tensor], n_rows: int, row_stride: Optional[int] = None,
+                  req_of_row: Optional[torch.Tensor] = None, pos_of_row: Optional[torch.Tensor] = None,
+                  rows_per_req: int = 0, ptrs: Optional[Sequence[int]] = None):
+        """taps: n_taps fp32 tensors whose first row is staged row 0 (or raw
+        pointers in ``ptrs``); row_stride defaults to the tensors' row stride."""
+        if ptrs is None:
+            ptrs = [t.data_ptr() for t in taps]
+            if row_stride is None:
+                row_stride = taps[0].stride(0)
+        arr = (c_void_p * len(ptrs))(*ptrs)
+        _check("dflash_tap_stage", self.lib.dflash_tap_stage(
+            self.ctx, _stream(), ctypes.cast(arr, PP), int(row_stride), int(n_rows), _ptr(req_of_row),
+            _ptr(pos_of_row), int(rows_per_req)))
+
+    def draft_block(self, block_tokens: torch.Tensor, k: int = 1, logits: Optional[torch.Tensor] = None,
+                    ids: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None):
+        R = block_tokens.shape[0]
+        Bm1 = max(self.cfg.block - 1, 1)
+        if ids is None:
+            ids = torch.empty((R, Bm1, k), dtype=torch.int32, device=self.device)
+        _check("dflash_draft_block", self.lib.dflash_draft_block(
+            self.ctx, _stream(), block_tokens.data_ptr(), R, _ptr(logits), ids.data_ptr(), _ptr(vals), k))
+        return ids
+
+    def accept(self, draft_ids: torch.Tensor, draft_stride: int, verify_ids: torch.Tensor, eos_id: int = -1,
+               budget: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None):
+        R = verify_ids.shape[0]
+        B = self.cfg.block
+        if out is None:
+            out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
+                   "emitted": torch.empty((R, B), dtype=torch.int32, device=self.device),
+                   "n_emit": torch.empty(R, dtype=torch.int32, device=self.device),
+                   "next_tokens": torch.empty((R, B), dtype=torch.int32, device=self.device)}
+        _check("dflash_accept", self.lib.dflash_accept(
+            self.ctx, _stream(), _ptr(draft_ids), int(draft_stride), verify_ids.data_ptr(), R, int(eos_id),
+            _ptr(budget), out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
+            _ptr(out.get("next_tokens"))))
+        return out
+
+    def check(self) -> int:
+        word = c_uint(0)
+        rc = self.lib.dflash_check(self.ctx, _stream(), ctypes.byref(word))
+        if rc not in (0, -7):
+            _check("dflash_check", rc)
+        return int(word.value)
+
+    def clear_error(self):
+        _check("dflash_clear_error", self.lib.dflash_clear_error(self.ctx, _stream()))
+
+    def set_timing_events(self, kclass: int, before: Sequence, after: Sequence):
+        n = len(before)
+        b = (c_void_p * max(n, 1))(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in before])
+        a = (c_void_p * max(n, 1))(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in after])
+        self._keep.append((b, a))
+        _check("dflash_set_timing_events", self.lib.dflash_set_timing_events(
+            self.ctx, kclass, ctypes.cast(b, PP), ctypes.cast(a, PP), n))
+
+    # ---------------------------------------------------------------- state views
+    def positions(self):
+        L, R = self.layout, self.cfg.max_requests
+        pos = self.state[L["pos"]:L["pos"] + 4 * R].view(torch.int32)
+        vf = self.state[L["valid_from"]:L["valid_from"] + 4 * R].view(torch.int32)
+        return pos, vf
+
+    def stats(self) -> torch.Tensor:
+        L = self.layout
+        n = self.cfg.block + 2
+        return self.state[L["stats"]:L["stats"] + 8 * n].view(torch.int64)
+
+    def ring(self):
+        """(K [L, Rmax, nkv, C, hd], V^T [L, Rmax, nkv, hd, C]) bf16 views."""
+        c, L = self.cfg, self.layout
+        n = c.n_layers * c.max_requests * c.n_kv_heads * c.ring_capacity * c.head_dim
+        k = self.state[L["ring_k"]:L["ring_k"] + 2 * n].view(torch.bfloat16).view(
+            c.n_layers, c.max_requests, c.n_kv_heads, c.ring_capacity, c.head_dim)
+        v = self.state[L["ring_v"]:L["ring_v"] + 2 * n].view(torch.bfloat16).view(
+            c.n_layers, c.max_requests, c.n_kv_heads, c.head_dim, c.ring_capacity)
+        return k, v

@@ -1,0 +1,612 @@
+// Host side of the C ABI declared in include/dflash.h: configuration guards,
+// state/workspace layout and the per-call launch sequences. No device memory is
+// allocated here; every launch goes to the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int CU_TARGET = 512;   // workgroups wanted per weight-streaming GEMM
+constexpr int GC_DEFAULT = 128;
+
+int attn_chunk(const dflash_config& c) { return c.window <= 256 ? 64 : 128; }
+int attn_nchunks(const dflash_config& c) {
+  const int kc = attn_chunk(c);
+  return (c.window + c.block + 31 + kc - 1) / kc;
+}
+
+struct WsLayout {
+  size_t h, a, q, o, act, c32, c, partials, counters, attn_o, attn_ml, attn_cnt, cand_v, cand_i, total;
+  size_t n_counters;
+};
+
+struct GemmShape {
+  int N, K, gc, pair;
+};
+
+// Largest split-K scratch and counter count over every GEMM a call may launch.
+void gemm_scratch(const dflash_config& c, size_t* part_floats, size_t* counters) {
+  const int H = c.hidden, hd = c.head_dim;
+  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0},
+                             {H, c.n_q_heads * hd, GC_DEFAULT, 0},
+                             {c.ffn, H, GC_DEFAULT, 1},
+                             {H, c.ffn, GC_DEFAULT, 0}};
+  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0},
+                             {2 * c.n_kv_heads * hd, H, hd, 0}};
+  size_t pf = 0, cn = 0;
+  auto visit = [&](int M, const GemmShape& s) {
+    GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, CU_TARGET);
+    size_t f = gemm_partial_floats(p, s.gc);
+    if (f > pf) pf = f;
+    if (p.S > 1 && (size_t)p.groups * p.mz > cn) cn = (size_t)p.groups * p.mz;
+  };
+  for (int R = 1; R <= c.max_requests; ++R)
+    for (const auto& s : draft) visit(R * c.block, s);
+  for (int M = 1; M <= c.max_stage_rows; ++M)
+    for (const auto& s : stage) visit(M, s);
+  *part_floats = pf;
+  *counters = cn;
+}
+
+WsLayout ws_layout(const dflash_config& c) {
+  WsLayout L;
+  const size_t Mmax = (size_t)c.max_requests * c.block;
+  const size_t S = (size_t)c.max_stage_rows;
+  const size_t qw = (size_t)c.n_q_heads * c.head_dim;
+  size_t pf, cn;
+  gemm_scratch(c, &pf, &cn);
+  const size_t slots = (size_t)attn_slots(c.n_q_heads, c.n_kv_heads, c.block);
+  const size_t lrg = (size_t)c.max_requests * c.n_kv_heads;
+  const size_t nch = (size_t)attn_nchunks(c);
+  const size_t lm_groups = (c.vocab + GC_DEFAULT - 1) / GC_DEFAULT;
+  const size_t out_rows = (size_t)c.max_requests * (c.block > 1 ? c.block - 1 : 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.h = take(Mmax * c.hidden * 4);
+  L.a = take(Mmax * c.hidden * 2);
+  L.q = take(Mmax * qw * 2);
+  L.o = take(Mmax * qw * 2);
+  L.act = take(Mmax * c.ffn * 2);
+  L.c32 = take(c.ctx_norm ? S * c.hidden * 4 : 0);
+  L.c = take(S * c.hidden * 2);
+  L.partials = take(pf * 4);
+  L.counters = take((cn ? cn : 1) * 4);
+  L.n_counters = cn;
+  L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
+  L.attn_ml = take(lrg * nch * slots * 2 * 4);
+  L.attn_cnt = take(lrg * 4);
+  L.cand_v = take(lm_groups * out_rows * 16 * 4);
+  L.cand_i = take(lm_groups * out_rows * 16 * 4);
+  L.total = off;
+  return L;
+}
+
+dflash_state_layout st_layout(const dflash_config& c) {
+  dflash_state_layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.pos = take((size_t)c.max_requests * 4);
+  L.valid_from = take((size_t)c.max_requests * 4);
+  L.error = take(4);
+  L.stats = take((size_t)(c.block + 2) * 8);
+  const size_t ring = (size_t)c.n_layers * c.max_requests * c.n_kv_heads * c.ring_capacity * c.head_dim * 2;
+  L.ring_k = take(ring);
+  L.ring_v = take(ring);
+  L.total = off;
+  return L;
+}
+
+int validate_config(const dflash_config* c) {
+  if (!c) return fail(DFLASH_E_ARG, "config is NULL");
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->ffn < 1 || c->vocab < 2)
+    return fail(DFLASH_E_CONFIG, "layer/width/vocab sizes must be positive (vocab >= 2)");
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(DFLASH_E_CONFIG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
+  if (c->head_dim % 2) return fail(DFLASH_E_CONFIG, "head_dim must be even for RoPE");
+  if (c->n_taps < 1 || c->n_taps > MAX_TAPS || c->hc_streams < 1 || c->tap_hidden < 1)
+    return fail(DFLASH_E_CONFIG, "n_taps must be in [1, %d], hc_streams and tap_hidden positive", MAX_TAPS);
+  if (c->tap_hidden != c->hidden)
+    return fail(DFLASH_E_CONFIG, "tap_hidden (%d) must equal hidden (%d): the drafter shares the target's "
+                "embedding and LM head and reads its hidden rows", c->tap_hidden, c->hidden);
+  if (c->block < 1 || c->block > 64) return fail(DFLASH_E_CONFIG, "block must be in [1, 64]");
+  if (c->window < 0) return fail(DFLASH_E_CONFIG, "window must be >= 0");
+  if (c->ring_capacity < c->window + c->block || c->ring_capacity % 32)
+    return fail(DFLASH_E_CONFIG, "ring_capacity (%d) must be >= window + block (%d) and a multiple of 32",
+                c->ring_capacity, c->window + c->block);
+  if (c->max_requests < 1) return fail(DFLASH_E_CONFIG, "max_requests must be >= 1");
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DFLASH_E_CONFIG, "mask_id outside [0, vocab)");
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(DFLASH_E_CONFIG, "rope_theta > 0 and rms_eps >= 0 required");
+  if (c->max_stage_rows < 1) return fail(DFLASH_E_CONFIG, "max_stage_rows must be >= 1");
+  if (c->wfmt != DFLASH_W_BF16 && c->wfmt != DFLASH_W_INT4_G64) return fail(DFLASH_E_CONFIG, "unknown weight format %d", c->wfmt);
+  // shapes the kernels are built for
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(DFLASH_E_UNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", c->head_dim);
+  if (c->hidden % 128 || c->ffn % 128 || (c->n_q_heads * c->head_dim) % 128)
+    return fail(DFLASH_E_UNSUPPORTED, "hidden, ffn and n_q_heads*head_dim must be multiples of 128");
+  if (attn_slots(c->n_q_heads, c->n_kv_heads, c->block) > 64)
+    return fail(DFLASH_E_UNSUPPORTED, "(n_q_heads/n_kv_heads)*block = %d query rows per kv head; at most 64",
+                attn_slots(c->n_q_heads, c->n_kv_heads, c->block));
+  if (c->wfmt == DFLASH_W_INT4_G64)
+    return fail(DFLASH_E_UNSUPPORTED, "INT4 weights are not built in this library version");
+  return DFLASH_OK;
+}
+
+struct Timing {
+  std::vector<hipEvent_t> before, after;
+  unsigned long long count = 0;
+};
+
+}  // namespace
+
+struct dflash_ctx {
+  dflash_config cfg;
+  const uint16_t *embed, *lm_head, *fc, *ctx_norm, *final_norm;
+  const uint16_t* fc_s;
+  std::vector<const uint16_t*> wqkv, wo, wgu, wd, ln_in, ln_post, q_norm, k_norm;
+  std::vector<const uint16_t*> wqkv_s, wo_s, wgu_s, wd_s;
+  char* state = nullptr;
+  char* ws = nullptr;
+  dflash_state_layout sl;
+  WsLayout wl;
+  Timing timing[DFLASH_K_COUNT];
+};
+
+namespace {
+
+struct Timed {
+  dflash_ctx* ctx;
+  int k;
+  hipStream_t st;
+  bool on;
+  unsigned long long idx;
+  Timed(dflash_ctx* c, int kclass, hipStream_t s) : ctx(c), k(kclass), st(s) {
+    Timing& t = ctx->timing[k];
+    on = !t.before.empty();
+    if (on) {
+      idx = t.count % t.before.size();
+      hipEventRecord(t.before[idx], st);
+    }
+  }
+  ~Timed() {
+    if (on) {
+      Timing& t = ctx->timing[k];
+      hipEventRecord(t.after[idx], st);
+      ++t.count;
+    }
+  }
+};
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DFLASH_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+template <class T>
+T* at(char* base, size_t off) { return (T*)(base + off); }
+
+GemmArgs base_args(const dflash_ctx* c) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  const dflash_config& g = c->cfg;
+  a.nq = g.n_q_heads;
+  a.nkv = g.n_kv_heads;
+  a.hd = g.head_dim;
+  a.eps = g.rms_eps;
+  a.log2_theta = log2((double)g.rope_theta);
+  a.C = g.ring_capacity;
+  a.Rmax = g.max_requests;
+  a.pos = at<int>(c->state, c->sl.pos);
+  a.err = at<unsigned>(c->state, c->sl.error);
+  a.partials = at<float>(c->ws, c->wl.partials);
+  a.counters = at<unsigned>(c->ws, c->wl.counters);
+  a.B = g.block;
+  return a;
+}
+
+size_t ring_layer_elems(const dflash_config& g) {
+  return (size_t)g.max_requests * g.n_kv_heads * g.ring_capacity * g.head_dim;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_last_error(void) { return g_err; }
+
+size_t dflash_state_bytes(const dflash_config* cfg) {
+  if (validate_config(cfg) != DFLASH_OK) return 0;
+  return st_layout(*cfg).total;
+}
+
+size_t dflash_workspace_bytes(const dflash_config* cfg) {
+  if (validate_config(cfg) != DFLASH_OK) return 0;
+  return ws_layout(*cfg).total;
+}
+
+int dflash_get_state_layout(const dflash_config* cfg, dflash_state_layout* out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(DFLASH_E_ARG, "out is NULL");
+  *out = st_layout(*cfg);
+  return DFLASH_OK;
+}
+
+int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out) {
+  g_err[0] = 0;
+  if (!out) return fail(DFLASH_E_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!w) return fail(DFLASH_E_ARG, "weights is NULL");
+  const dflash_config& c = *cfg;
+  const bool q4 = c.wfmt == DFLASH_W_INT4_G64;
+  if (!w->embed || !w->lm_head || !w->fc || !w->final_norm)
+    return fail(DFLASH_E_ARG, "embed, lm_head, fc and final_norm are required");
+  if (c.ctx_norm && !w->ctx_norm) return fail(DFLASH_E_ARG, "ctx_norm gain required when cfg.ctx_norm = 1");
+  if (q4 && !w->fc_scales) return fail(DFLASH_E_ARG, "fc_scales required for INT4 weights");
+  const void* const* arrays[] = {w->wqkv, w->wo, w->wgu, w->wd, w->ln_in, w->ln_post, w->q_norm, w->k_norm};
+  const char* names[] = {"wqkv", "wo", "wgu", "wd", "ln_in", "ln_post", "q_norm", "k_norm"};
+  for (int i = 0; i < 8; ++i) {
+    if (!arrays[i]) return fail(DFLASH_E_ARG, "%s array is NULL", names[i]);
+    for (int l = 0; l < c.n_layers; ++l)
+      if (!arrays[i][l]) return fail(DFLASH_E_ARG, "%s[%d] is NULL", names[i], l);
+  }
+  if (q4) {
+    const void* const* sarr[] = {w->wqkv_scales, w->wo_scales, w->wgu_scales, w->wd_scales};
+    for (int i = 0; i < 4; ++i) {
+      if (!sarr[i]) return fail(DFLASH_E_ARG, "INT4 scale array %d is NULL", i);
+      for (int l = 0; l < c.n_layers; ++l)
+        if (!sarr[i][l]) return fail(DFLASH_E_ARG, "INT4 scale array %d[%d] is NULL", i, l);
+    }
+  }
+  dflash_ctx* x = new dflash_ctx;
+  x->cfg = c;
+  x->embed = (const uint16_t*)w->embed;
+  x->lm_head = (const uint16_t*)w->lm_head;
+  x->fc = (const uint16_t*)w->fc;
+  x->fc_s = (const uint16_t*)w->fc_scales;
+  x->ctx_norm = (const uint16_t*)w->ctx_norm;
+  x->final_norm = (const uint16_t*)w->final_norm;
+  for (int l = 0; l < c.n_layers; ++l) {
+    x->wqkv.push_back((const uint16_t*)w->wqkv[l]);
+    x->wo.push_back((const uint16_t*)w->wo[l]);
+    x->wgu.push_back((const uint16_t*)w->wgu[l]);
+    x->wd.push_back((const uint16_t*)w->wd[l]);
+    x->ln_in.push_back((const uint16_t*)w->ln_in[l]);
+    x->ln_post.push_back((const uint16_t*)w->ln_post[l]);
+    x->q_norm.push_back((const uint16_t*)w->q_norm[l]);
+    x->k_norm.push_back((const uint16_t*)w->k_norm[l]);
+    if (q4) {
+      x->wqkv_s.push_back((const uint16_t*)w->wqkv_scales[l]);
+      x->wo_s.push_back((const uint16_t*)w->wo_scales[l]);
+      x->wgu_s.push_back((const uint16_t*)w->wgu_scales[l]);
+      x->wd_s.push_back((const uint16_t*)w->wd_scales[l]);
+    }
+  }
+  x->sl = st_layout(c);
+  x->wl = ws_layout(c);
+  *out = x;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_ctx* ctx) { delete ctx; }
+
+int dflash_bind(dflash_ctx* ctx, void* state, void* workspace, void* stream) {
+  if (!ctx || !state || !workspace) return fail(DFLASH_E_ARG, "ctx, state and workspace are required");
+  if (((uintptr_t)state | (uintptr_t)workspace) & 255)
+    return fail(DFLASH_E_ARG, "state and workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  ctx->state = (char*)state;
+  ctx->ws = (char*)workspace;
+  hipError_t e = launch_fill_zero(state, ctx->sl.total, st);
+  if (e == hipSuccess) e = launch_fill_zero(workspace, ctx->wl.total, st);
+  if (e != hipSuccess) return hip_fail(e, "bind fill");
+  return DFLASH_OK;
+}
+
+int dflash_reset(dflash_ctx* ctx, void* stream, int req, int valid_from, int pos) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (req < 0 || req >= ctx->cfg.max_requests) return fail(DFLASH_E_SHAPE, "req %d outside [0, %d)", req, ctx->cfg.max_requests);
+  if (valid_from < 0 || valid_from > pos) return fail(DFLASH_E_ARG, "need 0 <= valid_from (%d) <= pos (%d)", valid_from, pos);
+  hipError_t e = launch_set_pos(at<int>(ctx->state, ctx->sl.pos), at<int>(ctx->state, ctx->sl.valid_from), req,
+                                valid_from, pos, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reset");
+  return DFLASH_OK;
+}
+
+int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, long long tap_row_stride,
+                     int n_rows, const int* req_of_row, const int* pos_of_row, int rows_per_req) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  const dflash_config& g = ctx->cfg;
+  if (!taps) return fail(DFLASH_E_ARG, "taps array is NULL");
+  for (int t = 0; t < g.n_taps; ++t)
+    if (!taps[t]) return fail(DFLASH_E_ARG, "taps[%d] is NULL", t);
+  if (n_rows < 1) return fail(DFLASH_E_SHAPE, "n_rows must be >= 1");
+  if (n_rows > g.max_stage_rows)
+    return fail(DFLASH_E_CAPACITY, "n_rows %d exceeds max_stage_rows %d", n_rows, g.max_stage_rows);
+  if (tap_row_stride < (long long)g.hc_streams * g.tap_hidden || tap_row_stride % 4)
+    return fail(DFLASH_E_ARG, "tap_row_stride %lld must be >= hc_streams*tap_hidden and a multiple of 4", tap_row_stride);
+  if ((!req_of_row || !pos_of_row) && rows_per_req < 1)
+    return fail(DFLASH_E_ARG, "rows_per_req must be >= 1 when req_of_row or pos_of_row is NULL");
+  if (!req_of_row && (n_rows + rows_per_req - 1) / rows_per_req > g.max_requests)
+    return fail(DFLASH_E_CAPACITY, "n_rows / rows_per_req names more than max_requests requests");
+  for (int t = 0; t < g.n_taps; ++t)
+    if ((uintptr_t)taps[t] & 15) return fail(DFLASH_E_ARG, "taps[%d] must be 16-byte aligned", t);
+  hipStream_t st = (hipStream_t)stream;
+  const int H = g.hidden, hd = g.head_dim;
+  hipError_t e;
+
+  // fc over the gathered taps
+  GemmArgs a = base_args(ctx);
+  for (int t = 0; t < g.n_taps; ++t) a.taps[t] = taps[t];
+  a.tap_stride = tap_row_stride;
+  a.n_taps = g.n_taps;
+  a.hc = g.hc_streams;
+  a.tap_hidden = g.tap_hidden;
+  a.w = ctx->fc;
+  a.M = n_rows;
+  a.N = H;
+  a.K = g.n_taps * g.tap_hidden;
+  uint16_t* c_bf = at<uint16_t>(ctx->ws, ctx->wl.c);
+  a.out = g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf;
+  a.ldo = H;
+  {
+    GemmPlan p = plan_gemm(n_rows, H, a.K, GC_DEFAULT, 0, CU_TARGET);
+    Timed tm(ctx, DFLASH_K_FC, st);
+    e = launch_gemm(a, p, X_TAPS, g.ctx_norm ? E_F32 : E_BF16, WF_BF16, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "stage fc");
+  if (g.ctx_norm) {
+    e = launch_rmsnorm(at<float>(ctx->ws, ctx->wl.c32), ctx->ctx_norm, c_bf, n_rows, H, g.rms_eps, st);
+    if (e != hipSuccess) return hip_fail(e, "stage ctx norm");
+  }
+  // per layer: K/V of the staged rows into the ring
+  const size_t rl = ring_layer_elems(g);
+  for (int l = 0; l < g.n_layers; ++l) {
+    GemmArgs b = base_args(ctx);
+    b.x = c_bf;
+    b.ldx = H;
+    b.w = ctx->wqkv[l] + (size_t)g.n_q_heads * hd * H;
+    b.M = n_rows;
+    b.N = 2 * g.n_kv_heads * hd;
+    b.K = H;
+    b.head_base = g.n_q_heads;
+    b.k_gain = ctx->k_norm[l];
+    b.q_gain = ctx->q_norm[l];
+    b.ring_k = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
+    b.ring_v = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
+    b.req_of_row = req_of_row;
+    b.pos_of_row = pos_of_row;
+    b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
+    GemmPlan p = plan_gemm(n_rows, b.N, H, hd, 0, CU_TARGET);
+    Timed tm(ctx, DFLASH_K_STAGE_KV, st);
+    e = launch_gemm(b, p, X_BF16, E_HEAD, WF_BF16, st);
+    if (e != hipSuccess) return hip_fail(e, "stage kv");
+  }
+  return DFLASH_OK;
+}
+
+int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, float* logits,
+                       int* topk_ids, float* topk_vals, int k) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  const dflash_config& g = ctx->cfg;
+  if (!block_tokens || !topk_ids) return fail(DFLASH_E_ARG, "block_tokens and topk_ids are required");
+  if (n_req < 1 || n_req > g.max_requests)
+    return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (k != 1 && k != 16) return fail(DFLASH_E_ARG, "k must be 1 or 16 (got %d)", k);
+  if (k > g.vocab) return fail(DFLASH_E_ARG, "k exceeds vocab");
+  if (g.block == 1) return DFLASH_OK;   // no mask rows: nothing to draft
+  hipStream_t st = (hipStream_t)stream;
+  const int H = g.hidden, hd = g.head_dim, B = g.block;
+  const int M = n_req * B;
+  const int qw = g.n_q_heads * hd;
+  float* h = at<float>(ctx->ws, ctx->wl.h);
+  uint16_t* act_a = at<uint16_t>(ctx->ws, ctx->wl.a);
+  uint16_t* q = at<uint16_t>(ctx->ws, ctx->wl.q);
+  uint16_t* o = at<uint16_t>(ctx->ws, ctx->wl.o);
+  uint16_t* act = at<uint16_t>(ctx->ws, ctx->wl.act);
+  unsigned* err = at<unsigned>(ctx->state, ctx->sl.error);
+  hipError_t e = launch_embed_norm(block_tokens, ctx->embed, ctx->ln_in[0], h, act_a, M, H, g.vocab, g.rms_eps, err, st);
+  if (e != hipSuccess) return hip_fail(e, "embed");
+  const size_t rl = ring_layer_elems(g);
+  for (int l = 0; l < g.n_layers; ++l) {
+    uint16_t* rk = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
+    uint16_t* rv = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
+    {  // QKV + q/k head norm + RoPE; the block's K/V go to ring slots [pos, pos+B)
+      GemmArgs a = base_args(ctx);
+      a.x = act_a;
+      a.ldx = H;
+      a.w = ctx->wqkv[l];
+      a.M = M;
+      a.N = (g.n_q_heads + 2 * g.n_kv_heads) * hd;
+      a.K = H;
+      a.head_base = 0;
+      a.q_gain = ctx->q_norm[l];
+      a.k_gain = ctx->k_norm[l];
+      a.q_out = q;
+      a.ring_k = rk;
+      a.ring_v = rv;
+      a.rows_per_req = B;
+      GemmPlan p = plan_gemm(M, a.N, H, hd, 0, CU_TARGET);
+      Timed tm(ctx, DFLASH_K_QKV, st);
+      e = launch_gemm(a, p, X_BF16, E_HEAD, WF_BF16, st);
+      if (e != hipSuccess) return hip_fail(e, "qkv");
+    }
+    {  // attention over [context window | block]
+      AttnArgs t;
+      memset(&t, 0, sizeof t);
+      t.q = q;
+      t.ring_k = rk;
+      t.ring_v = rv;
+      t.out = o;
+      t.pos = at<int>(ctx->state, ctx->sl.pos);
+      t.valid_from = at<int>(ctx->state, ctx->sl.valid_from);
+      t.B = B;
+      t.W = g.window;
+      t.C = g.ring_capacity;
+      t.nq = g.n_q_heads;
+      t.nkv = g.n_kv_heads;
+      t.hd = hd;
+      t.kc = attn_chunk(g);
+      t.n_chunks = attn_nchunks(g);
+      t.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+      t.part_o = at<float>(ctx->ws, ctx->wl.attn_o);
+      t.part_ml = at<float>(ctx->ws, ctx->wl.attn_ml);
+      t.counters = at<unsigned>(ctx->ws, ctx->wl.attn_cnt);
+      t.err = err;
+      Timed tm(ctx, DFLASH_K_ATTN, st);
+      e = launch_attention(t, n_req, st);
+      if (e != hipSuccess) return hip_fail(e, "attention");
+    }
+    {  // o projection, residual add
+      GemmArgs a = base_args(ctx);
+      a.x = o;
+      a.ldx = qw;
+      a.w = ctx->wo[l];
+      a.M = M;
+      a.N = H;
+      a.K = qw;
+      a.out = h;
+      a.ldo = H;
+      GemmPlan p = plan_gemm(M, H, qw, GC_DEFAULT, 0, CU_TARGET);
+      Timed tm(ctx, DFLASH_K_O, st);
+      e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+      if (e != hipSuccess) return hip_fail(e, "o proj");
+    }
+    e = launch_rmsnorm(h, ctx->ln_post[l], act_a, M, H, g.rms_eps, st);
+    if (e != hipSuccess) return hip_fail(e, "post norm");
+    {  // gate/up with SiLU(gate) * up
+      GemmArgs a = base_args(ctx);
+      a.x = act_a;
+      a.ldx = H;
+      a.w = ctx->wgu[l];
+      a.M = M;
+      a.N = g.ffn;
+      a.K = H;
+      a.pair_off = g.ffn;
+      a.out = act;
+      a.ldo = g.ffn;
+      GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CU_TARGET);
+      Timed tm(ctx, DFLASH_K_GATEUP, st);
+      e = launch_gemm(a, p, X_BF16, E_SILU, WF_BF16, st);
+      if (e != hipSuccess) return hip_fail(e, "gate/up");
+    }
+    {  // down projection, residual add
+      GemmArgs a = base_args(ctx);
+      a.x = act;
+      a.ldx = g.ffn;
+      a.w = ctx->wd[l];
+      a.M = M;
+      a.N = H;
+      a.K = g.ffn;
+      a.out = h;
+      a.ldo = H;
+      GemmPlan p = plan_gemm(M, H, g.ffn, GC_DEFAULT, 0, CU_TARGET);
+      Timed tm(ctx, DFLASH_K_DOWN, st);
+      e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+      if (e != hipSuccess) return hip_fail(e, "down proj");
+    }
+    const uint16_t* next_gain = l + 1 < g.n_layers ? ctx->ln_in[l + 1] : ctx->final_norm;
+    e = launch_rmsnorm(h, next_gain, act_a, M, H, g.rms_eps, st);
+    if (e != hipSuccess) return hip_fail(e, "norm");
+  }
+  {  // shared LM head with per-group top-k, then the merge
+    GemmArgs a = base_args(ctx);
+    a.x = act_a;
+    a.ldx = H;
+    a.w = ctx->lm_head;
+    a.M = M;
+    a.N = g.vocab;
+    a.K = H;
+    a.topk = k;
+    a.logits = logits;
+    a.cand_val = at<float>(ctx->ws, ctx->wl.cand_v);
+    a.cand_idx = at<int>(ctx->ws, ctx->wl.cand_i);
+    GemmPlan p = plan_gemm(M, g.vocab, H, GC_DEFAULT, 0, 0);
+    {
+      Timed tm(ctx, DFLASH_K_LMHEAD, st);
+      e = launch_gemm(a, p, X_BF16, E_TOPK, WF_BF16, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "lm head");
+    e = launch_topk_merge(a.cand_val, a.cand_idx, p.groups, n_req * (B - 1), k, topk_ids, topk_vals, st);
+    if (e != hipSuccess) return hip_fail(e, "topk merge");
+  }
+  return DFLASH_OK;
+}
+
+int dflash_accept(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride, const int* verify_ids,
+                  int n_req, int eos_id, const int* budget, int* accept_len, int* emitted, int* n_emit,
+                  int* next_tokens) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  const dflash_config& g = ctx->cfg;
+  if ((!draft_ids && g.block > 1) || !verify_ids || !accept_len || !emitted || !n_emit)
+    return fail(DFLASH_E_ARG, "draft_ids, verify_ids, accept_len, emitted and n_emit are required");
+  if (n_req < 1 || n_req > g.max_requests)
+    return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (draft_stride < 1) return fail(DFLASH_E_ARG, "draft_stride must be >= 1");
+  hipError_t e = launch_accept(draft_ids, draft_stride, verify_ids, n_req, g.block, eos_id, budget, g.mask_id,
+                               accept_len, emitted, n_emit, next_tokens, at<int>(ctx->state, ctx->sl.pos),
+                               at<unsigned long long>(ctx->state, ctx->sl.stats), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "accept");
+  return DFLASH_OK;
+}
+
+int dflash_check(dflash_ctx* ctx, void* stream, unsigned* word) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  hipStream_t st = (hipStream_t)stream;
+  unsigned w = 0;
+  hipError_t e = hipMemcpyAsync(&w, ctx->state + ctx->sl.error, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "check");
+  if (word) *word = w;
+  if (w) return fail(DFLASH_E_DEVICE, "device error word 0x%x", w);
+  return DFLASH_OK;
+}
+
+int dflash_clear_error(dflash_ctx* ctx, void* stream) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  hipError_t e = launch_fill_zero(ctx->state + ctx->sl.error, 4, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "clear error");
+  return DFLASH_OK;
+}
+
+int dflash_set_timing_events(dflash_ctx* ctx, int kclass, void* const* before, void* const* after, int n) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (kclass < 0 || kclass >= DFLASH_K_COUNT) return fail(DFLASH_E_ARG, "unknown kernel class %d", kclass);
+  if (n < 0 || (n > 0 && (!before || !after))) return fail(DFLASH_E_ARG, "bad event arrays");
+  Timing& t = ctx->timing[kclass];
+  t.before.clear();
+  t.after.clear();
+  t.count = 0;
+  for (int i = 0; i < n; ++i) {
+    t.before.push_back((hipEvent_t)before[i]);
+    t.after.push_back((hipEvent_t)after[i]);
+  }
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of the drafter round.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DEV __device__ __forceinline__
+
+// bf16 <-> fp32. The fp32 -> bf16 conversion rounds to nearest even (gfx950 has
+// a hardware conversion; the compiler emits it for this cast).
+DEV float bf2f(__bf16 v) { return (float)v; }
+DEV float bfbits2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+DEV __bf16 f2bf(float v) { return (__bf16)v; }
+DEV uint16_t f2bfbits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bfbits(lo) | ((uint32_t)f2bfbits(hi) << 16);
+}
+
+// 16-byte loads. Weights stream through once per round: non-temporal so they do
+// not evict activations, partial sums and the context ring from L2/MALL.
+DEV u32x4 ld_nt16(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+DEV u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+DEV f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// (value desc, index asc) ordering used by argmax / top-k.
+DEV bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+
+DEV void set_error(unsigned* err, unsigned bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// RoPE angle for position p and pair index d of a head of size hd, in fp64 so
+// that positions of tens of thousands keep full fp32 accuracy after the cast.
+DEV void rope_cos_sin(long long p, int d, int hd, double log2_theta, float* c, float* s) {
+  double inv = exp2(-(double)(2 * d) / (double)hd * log2_theta);
+  double a = (double)p * inv;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}

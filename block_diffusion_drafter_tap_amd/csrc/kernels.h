@@ -1,0 +1,95 @@
+// Internal interface between the host library (api.hip) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum XKind { X_BF16 = 0, X_TAPS = 1 };
+enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4, E_TOPK = 5 };
+enum WFmt { WF_BF16 = 0, WF_INT4 = 1 };
+
+constexpr int MAX_TAPS = 8;
+constexpr int GEMM_WAVES = 4;
+
+// Arguments of the skinny GEMM Y[M, N] = X[M, K] . W[N, K]^T with a fused epilogue.
+struct GemmArgs {
+  // X operand: bf16 rows (X_BF16) or fp32 tap rows reduced on the fly (X_TAPS)
+  const uint16_t* x;
+  long long ldx;
+  const float* taps[MAX_TAPS];
+  long long tap_stride;
+  int n_taps, hc, tap_hidden;
+  // W operand: bf16 [N][K] or packed INT4 [N][K/2] + fp16 scales [N][K/64]
+  const void* w;
+  const uint16_t* wscale;
+  int M, N, K;     // N counts output columns (gate/up pairs count once)
+  int ks, S;       // K per split, number of splits (grid.y)
+  int pair_off;    // W row offset of the "up" rows (E_SILU)
+  // plain epilogues
+  void* out;
+  long long ldo;
+  // split-K scratch
+  float* partials;
+  unsigned* counters;
+  // E_HEAD: per-head q/k RMSNorm + RoPE, Q to q_out, K/V to the ring
+  int head_base, nq, nkv, hd;
+  float eps;
+  double log2_theta;
+  const uint16_t* q_gain;
+  const uint16_t* k_gain;
+  uint16_t* q_out;
+  uint16_t* ring_k;   // this layer's [Rmax][nkv][C][hd]
+  uint16_t* ring_v;   // this layer's [Rmax][nkv][hd][C]
+  int C, Rmax;
+  const int* pos;         // state pos[]
+  const int* req_of_row;  // NULL -> row / rows_per_req
+  const int* pos_of_row;  // NULL -> pos[req] + row % rows_per_req
+  int rows_per_req;
+  unsigned* err;
+  // E_TOPK: rows m = r*B + i; mask rows i >= 1 produce candidates
+  int B, topk;
+  float* logits;     // NULL or [R][B-1][N]
+  float* cand_val;   // [groups][R*(B-1)][topk]
+  int* cand_idx;
+};
+
+struct GemmPlan {
+  int MT, NT, S, ks, groups, mz;
+};
+
+GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target);
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf,
+                       hipStream_t st);
+size_t gemm_partial_floats(const GemmPlan& p, int gc);
+
+// Attention over [context window | block] per (request, kv head), split over key chunks.
+struct AttnArgs {
+  const uint16_t* q;       // [R*B][nq*hd]
+  const uint16_t* ring_k;  // layer base [Rmax][nkv][C][hd]
+  const uint16_t* ring_v;  // layer base [Rmax][nkv][hd][C]
+  uint16_t* out;           // [R*B][nq*hd]
+  const int* pos;
+  const int* valid_from;
+  int B, W, C, nq, nkv, hd, kc, n_chunks;
+  float scale_log2;        // log2(e) / sqrt(hd)
+  float* part_o;           // [R*nkv][n_chunks][slots][hd]
+  float* part_ml;          // [R*nkv][n_chunks][slots][2]
+  unsigned* counters;      // [R*nkv]
+  unsigned* err;
+};
+hipError_t launch_attention(const AttnArgs& a, int R, hipStream_t st);
+int attn_slots(int nq, int nkv, int B);
+
+// Small kernels.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_embed_norm(const int* tokens, const uint16_t* embed, const uint16_t* gain,
+                             float* h, uint16_t* a, int M, int H, int V, float eps,
+                             unsigned* err, hipStream_t st);
+hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* a, int M, int H,
+                          float eps, hipStream_t st);
+hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hipStream_t st);
+hipError_t launch_topk_merge(const float* cand_val, const int* cand_idx, int groups, int rows,
+                             int k, int* ids, float* vals, hipStream_t st);
+hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B,
+                         int eos, const int* budget, int mask_id, int* accept_len,
+                         int* emitted, int* n_emit, int* next_tokens, int* pos,
+                         unsigned long long* stats, hipStream_t st);

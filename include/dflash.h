@@ -1,0 +1,245 @@
+/*
+ * dflash.h - C ABI of the MI355X (gfx950) DFlash block-diffusion drafter round.
+ *
+ * One draft round is four steps (the method of "[RFC] DFlash", ExecuTorch PR
+ * #20840, "DFlash Overview" and "Key Implementation Details", and of "feat:
+ * DFlash2 block-diffusion drafter for Qwen 3.8", Mference PR #22, "What's here"):
+ *   1. dflash_tap_stage   - gather the target's hidden rows at its tapped layers
+ *                           (optionally the per-token mean of hc hyper-connection
+ *                           streams, "dflash: the chain verify builds pipelined
+ *                           ...", mlx-serve PR #937, hc commit), concatenate,
+ *                           fc-project to the draft hidden size and write every
+ *                           draft layer's context K/V into a per-request ring.
+ *   2/3. dflash_draft_block - a masked block of B tokens through every draft
+ *                           layer in one forward (attention over [sliding context
+ *                           window | bidirectional block]), the shared LM head,
+ *                           then argmax or top-16 per mask position.
+ *   4. dflash_accept      - first-mismatch acceptance against the target's verify
+ *                           argmaxes plus the bonus token, EOS/budget clamps, and
+ *                           the context position update (rollback is implicit:
+ *                           only rows below pos are ever read).
+ *
+ * Conventions
+ *   - Every pointer argument is a DEVICE pointer unless marked "host".
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call below except dflash_check enqueues asynchronously on it and never
+ *     synchronizes, allocates or frees; callers may capture rounds in a HIP graph
+ *     (nothing in a round uses hipMemsetAsync).
+ *   - The library allocates no device memory. Weights, taps, state, workspace and
+ *     outputs belong to the caller (e.g. PyTorch tensors) and must outlive the
+ *     handle. The handle stores the config and borrowed pointers only.
+ *   - One handle = one state + one workspace; calls on one handle must be ordered
+ *     (one stream, or events between streams). Two handles never share a workspace.
+ *   - Errors: host-side validation runs before any launch and returns a negative
+ *     dflash_status; dflash_last_error() gives a message (thread-local). Values
+ *     that live on the device (tokens, positions) are checked in the kernels: a bad
+ *     value is skipped or clamped and sets a sticky bit in the device error word,
+ *     which dflash_check() returns as DFLASH_E_DEVICE.
+ *   - Layouts are row-major. Linear weights are [out, in] (torch Linear).
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_ARG = -1,         /* null/invalid argument                              */
+  DFLASH_E_CONFIG = -2,      /* inconsistent configuration (checked at create)     */
+  DFLASH_E_SHAPE = -3,       /* call shape outside what the config allows          */
+  DFLASH_E_CAPACITY = -4,    /* more rows/requests than state/workspace can hold   */
+  DFLASH_E_UNSUPPORTED = -5, /* a valid request this build does not implement      */
+  DFLASH_E_HIP = -6,         /* a HIP runtime call failed                          */
+  DFLASH_E_DEVICE = -7,      /* the device error word is non-zero (dflash_check)   */
+  DFLASH_E_STATE = -8        /* handle not bound to state/workspace                */
+} dflash_status;
+
+/* Weight format of fc and the per-layer projections (embedding and LM head are bf16). */
+typedef enum { DFLASH_W_BF16 = 0, DFLASH_W_INT4_G64 = 1 } dflash_wfmt;
+
+/* Device error word bits (sticky until dflash_bind or dflash_clear_error). */
+enum {
+  DFLASH_DEV_BAD_TOKEN = 1,      /* a block token outside [0, vocab): row 0 of embed used */
+  DFLASH_DEV_BAD_WINDOW = 2,     /* valid_from > pos: the context is treated as empty      */
+  DFLASH_DEV_BAD_ROW = 4,        /* a staged row names a request outside [0, max_requests) */
+  DFLASH_DEV_BAD_POSITION = 8    /* a negative position: the row is skipped                */
+};
+
+/*
+ * Drafter configuration (host struct, copied at create).
+ *   n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab:
+ *       Qwen3-shaped draft layers ("[RFC] DFlash" review threads: the drafter
+ *       reuses Qwen3 attention / RMSNorm / MLP / rotary embedding).
+ *   n_taps, hc_streams, tap_hidden:
+ *       tapped target layers; each tap row is hc_streams*tap_hidden fp32 values,
+ *       stream-major; fc input width = n_taps*tap_hidden. tap_hidden must equal
+ *       hidden: the drafter shares the target's embedding and LM head, and the
+ *       guard that validates the hidden size before any buffer is built is the
+ *       one the Mference PR adds (hidden_size guard commit).
+ *   block:         B, tokens per draft block (1..64); row 0 is the known token.
+ *   window:        W, context rows attended (sliding window over committed rows).
+ *   ring_capacity: C, ring slots per request and layer; C >= W + B, C % 32 == 0.
+ *   max_requests:  R_max, requests the state holds.
+ *   mask_id:       token id of the mask positions (used by dflash_accept).
+ *   rope_theta, rms_eps: RoPE base and RMSNorm epsilon.
+ *   ctx_norm:      1 = RMSNorm (gain weights.ctx_norm) after fc; 0 = none.
+ *   wfmt:          dflash_wfmt.
+ *   max_stage_rows: most rows one dflash_tap_stage call may stage (sizes workspace).
+ */
+typedef struct {
+  int n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int n_taps, hc_streams, tap_hidden;
+  int block, window, ring_capacity, max_requests, mask_id;
+  float rope_theta, rms_eps;
+  int ctx_norm;
+  int wfmt;
+  int max_stage_rows;
+} dflash_config;
+
+/*
+ * Weights: device pointers, borrowed. Per-layer fields are HOST arrays of
+ * n_layers device pointers.
+ *   embed, lm_head: bf16 [vocab, hidden] (the target's; may be the same pointer).
+ *   fc:             [hidden, n_taps*tap_hidden]
+ *   wqkv[l]:        [(n_q_heads + 2*n_kv_heads)*head_dim, hidden] = [Wq; Wk; Wv]
+ *   wo[l]:          [hidden, n_q_heads*head_dim]
+ *   wgu[l]:         [2*ffn, hidden] = [Wgate; Wup]
+ *   wd[l]:          [hidden, ffn]
+ *   For DFLASH_W_BF16 these are bf16. For DFLASH_W_INT4_G64 they are packed INT4
+ *   (uint8 [rows, in/2], `in` a multiple of 128) with fp16 scales *_scales
+ *   [rows, in/64]. Packing: per row, in 128-wide chunks c, little-endian 32-bit
+ *   word 4*j + s (j, s = 0..3) holds the values k = 128c + 32s + 8j + e, e = 0..7,
+ *   as u = q + 8 in [0, 15]; value e sits in nibble e/2 (e even) or 4 + (e-1)/2
+ *   (e odd). The weight is q * scale.
+ *   ln_in[l], ln_post[l]: bf16 [hidden]; q_norm[l], k_norm[l]: bf16 [head_dim];
+ *   final_norm: bf16 [hidden]; ctx_norm: bf16 [hidden] (read only if cfg.ctx_norm).
+ */
+typedef struct {
+  const void* embed;
+  const void* lm_head;
+  const void* fc;
+  const void* fc_scales;
+  const void* ctx_norm;
+  const void* final_norm;
+  const void* const* wqkv;
+  const void* const* wqkv_scales;
+  const void* const* wo;
+  const void* const* wo_scales;
+  const void* const* wgu;
+  const void* const* wgu_scales;
+  const void* const* wd;
+  const void* const* wd_scales;
+  const void* const* ln_in;
+  const void* const* ln_post;
+  const void* const* q_norm;
+  const void* const* k_norm;
+} dflash_weights;
+
+/* Byte offsets of the state sections (for inspection by tests and tools). */
+typedef struct {
+  size_t pos;         /* int32 [max_requests]: absolute position of block token 0  */
+  size_t valid_from;  /* int32 [max_requests]: first valid context position        */
+  size_t error;       /* uint32: device error word                                 */
+  size_t stats;       /* uint64 [block + 2]: [0] rounds, [1+i] rounds with accept  */
+                      /*   length > i (i = 0..block-1), [block+1] tokens emitted    */
+  size_t ring_k;      /* bf16 [n_layers][max_requests][n_kv_heads][C][head_dim]    */
+  size_t ring_v;      /* bf16 [n_layers][max_requests][n_kv_heads][head_dim][C]    */
+  size_t total;
+} dflash_state_layout;
+
+typedef struct dflash_ctx dflash_ctx;
+
+/* Validate `cfg` (and the non-null pointers of `w`) and make a handle. No device calls. */
+int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out);
+void dflash_destroy(dflash_ctx* ctx);
+
+/* Sizes the caller allocates (any alignment >= 256 bytes). 0 on an invalid config. */
+size_t dflash_state_bytes(const dflash_config* cfg);
+size_t dflash_workspace_bytes(const dflash_config* cfg);
+int dflash_get_state_layout(const dflash_config* cfg, dflash_state_layout* out);
+
+/* Attach state and workspace; zero-fills both on `stream` (a kernel, no memset). */
+int dflash_bind(dflash_ctx* ctx, void* state, void* workspace, void* stream);
+
+/* Continuity break / prefill start for request `req`: valid_from = `valid_from`,
+ * pos = `pos` (the Mference PR resets the drafter with realigned positions on
+ * plain-decode gaps and rewinds). Requires 0 <= valid_from <= pos. */
+int dflash_reset(dflash_ctx* ctx, void* stream, int req, int valid_from, int pos);
+
+/*
+ * Stage n_rows tap rows: x = concat_t mean_s taps[t][row, s*tap_hidden : ...]
+ * (bf16), c = fc(x) (+ ctx RMSNorm), and for every layer K = RoPE(k_norm(W_k c),
+ * position), V = W_v c written to ring slot position % C of the row's request.
+ *   taps:        HOST array [n_taps] of device pointers; taps[t] + row*tap_row_stride
+ *                is row `row` (fp32, hc_streams*tap_hidden values).
+ *   tap_row_stride: elements between rows (>= hc_streams*tap_hidden, % 4 == 0).
+ *   req_of_row:  [n_rows] int32 or NULL (then request = row / rows_per_req).
+ *   pos_of_row:  [n_rows] int32 or NULL (then position = pos[request] +
+ *                row % rows_per_req, read from the state on the device).
+ *   rows_per_req: used only where the arrays above are NULL (>= 1).
+ * The verify rows of a round are staged at [pos, pos+B) before dflash_accept;
+ * rows the accept does not commit are overwritten later and never read.
+ */
+int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps,
+                     long long tap_row_stride, int n_rows, const int* req_of_row,
+                     const int* pos_of_row, int rows_per_req);
+
+/*
+ * Draft one block per request r < n_req from block_tokens [n_req, B] (int32;
+ * token 0 known, the rest mask ids) at positions pos[r] + i, attending to the
+ * context rows [max(valid_from[r], pos[r] - W), pos[r]) and to all B block rows.
+ *   logits:    NULL or fp32 [n_req, B-1, vocab] (rows 1..B-1)
+ *   topk_ids:  int32 [n_req, B-1, k], ordered by (logit desc, id asc)
+ *   topk_vals: NULL or fp32 [n_req, B-1, k]
+ *   k:         1 (argmax) or 16.
+ * The block's own K/V are written to ring slots [pos, pos+B) (slots the next
+ * stage overwrites), so the ring must not be read there by anyone else.
+ */
+int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req,
+                       float* logits, int* topk_ids, float* topk_vals, int k);
+
+/*
+ * First-mismatch accept for requests r < n_req.
+ *   draft_ids:   element (r, j) at draft_ids[(r*(B-1) + j)*draft_stride], j < B-1
+ *                (pass topk_ids with draft_stride = k).
+ *   verify_ids:  int32 [n_req, B], the target's argmax at each verify row.
+ *   eos_id:      < 0 disables EOS truncation.
+ *   budget:      NULL or int32 [n_req]: most tokens to emit (values < 1 act as 1).
+ * Outputs: accept_len [n_req], emitted [n_req, B] (padded with -1), n_emit [n_req];
+ * next_tokens (NULL or [n_req, B]) = [last emitted, mask_id, ...]. The state's
+ * pos[r] advances by n_emit[r]; accept-profile counters are updated.
+ */
+int dflash_accept(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride,
+                  const int* verify_ids, int n_req, int eos_id, const int* budget,
+                  int* accept_len, int* emitted, int* n_emit, int* next_tokens);
+
+/* Synchronize `stream`, read the device error word into *word (host, may be NULL);
+ * returns DFLASH_E_DEVICE if it is non-zero. */
+int dflash_check(dflash_ctx* ctx, void* stream, unsigned* word);
+/* Clear the device error word (enqueued on `stream`). */
+int dflash_clear_error(dflash_ctx* ctx, void* stream);
+
+/* Kernel classes for timing. */
+enum {
+  DFLASH_K_LMHEAD = 0, DFLASH_K_QKV = 1, DFLASH_K_O = 2, DFLASH_K_GATEUP = 3,
+  DFLASH_K_DOWN = 4, DFLASH_K_ATTN = 5, DFLASH_K_FC = 6, DFLASH_K_STAGE_KV = 7,
+  DFLASH_K_COUNT = 8
+};
+/* Record caller-created hipEvents (passed as void*) around every later launch of
+ * kernel class `kclass`: launch number i uses pair i % n. n = 0 turns it off.
+ * `before`/`after` are HOST arrays of n events, borrowed until turned off. */
+int dflash_set_timing_events(dflash_ctx* ctx, int kclass, void* const* before,
+                             void* const* after, int n);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

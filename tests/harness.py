@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU parity tests: inputs for both sides, tolerance and
+top-k comparisons against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from block_diffusion_drafter_tap_amd import synth
+
+
+def host_weights(w):
+    """fp32 numpy copies (exact) of the weights the GPU reads; INT4 matrices are
+    left packed for the oracle's own unpacker."""
+    out = {}
+    for k, v in w.items():
+        if isinstance(v, list):
+            out[k] = [synth.bf16_to_f32_numpy(t) if t.dtype != torch.uint8 else t.cpu().numpy() for t in v]
+        else:
+            out[k] = synth.bf16_to_f32_numpy(v) if v.dtype != torch.uint8 else v.cpu().numpy()
+    return out
+
+
+def tol(ref: np.ndarray) -> float:
+    """|gpu - oracle| <= 1e-2 * max|oracle| + 1e-3 (bf16 in, fp32 accumulate)."""
+    return 1e-2 * float(np.max(np.abs(ref))) + 1e-3
+
+
+def assert_close(gpu, ref, what: str):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    err = float(np.max(np.abs(gpu - ref)))
+    t = tol(ref)
+    assert err <= t, f"{what}: max |gpu - oracle| = {err:.4g} > tol {t:.4g}"
+    return err
+
+
+def topk_self_consistent(gpu_logits: np.ndarray, gpu_ids: np.ndarray):
+    """GPU ids must be exactly the (value desc, index asc) order of the GPU's own logits."""
+    k = gpu_ids.shape[-1]
+    L = gpu_logits.reshape(-1, gpu_logits.shape[-1])
+    ids = gpu_ids.reshape(-1, k)
+    for r in range(L.shape[0]):
+        ref = np.lexsort((np.arange(L.shape[1]), -L[r].astype(np.float64)))[:k]
+        np.testing.assert_array_equal(ids[r], ref, err_msg=f"row {r}")
+
+
+def topk_agrees_away_from_ties(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k: int):
+    """Compare GPU ids with the oracle's at ranks whose oracle gap to the
+    neighbouring ranks exceeds delta = 1e-3 * max|row| + 1e-5. Returns the
+    number of (row, rank) pairs compared and excluded."""
+    L = oracle_logits.reshape(-1, oracle_logits.shape[-1])
+    ids = gpu_ids.reshape(-1, k)
+    compared = excluded = 0
+    for r in range(L.shape[0]):
+        order = np.lexsort((np.arange(L.shape[1]), -L[r]))[:k + 1]
+        v = L[r][order]
+        delta = 1e-3 * np.max(np.abs(L[r])) + 1e-5
+        for j in range(k):
+            lo_gap = v[j - 1] - v[j] if j > 0 else np.inf
+            hi_gap = v[j] - v[j + 1]
+            if min(lo_gap, hi_gap) > delta:
+                assert ids[r, j] == order[j], f"row {r} rank {j}: gpu {ids[r, j]} oracle {order[j]}"
+                compared += 1
+            else:
+                excluded += 1
+    return compared, excluded

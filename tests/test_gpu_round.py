@@ -1,0 +1,181 @@
+"""GPU parity of the draft round (tiny drafter) against the fp64 oracle.
+
+Everything is called through the C ABI (binding.Drafter). Inputs come from
+synth on the GPU and are copied to the host for the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafter_tap_amd import config, synth
+from oracle import dflash as D
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_tap_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def tiny_setup():
+    binding = _gpu()
+    cfg = config.tiny(max_requests=4)
+    w = synth.make_weights(cfg, seed=0, device="cuda")
+    wh = Hn.host_weights(w)
+    return binding, cfg, w, wh
+
+
+def _taps_history(cfg, n, seed):
+    taps = synth.make_taps(cfg, n, seed=seed, device="cuda", outliers=True)
+    return taps, [t.cpu().numpy().astype(np.float64) for t in taps]
+
+
+def test_single_round_parity_tiny(tiny_setup):
+    binding, cfg, w, wh = tiny_setup
+    print(f"case: tiny single round B={cfg.block} W={cfg.window} C={cfg.ring_capacity}", flush=True)
+    dr = binding.Drafter(cfg, w)
+    P = 100
+    taps, taps_h = _taps_history(cfg, P, seed=0)
+    lo = P - cfg.window
+    dr.reset(0, 0, P)
+    rows = torch.arange(lo, P, dtype=torch.int32, device="cuda")
+    dr.tap_stage([t[lo:] for t in taps], P - lo, req_of_row=torch.zeros_like(rows), pos_of_row=rows)
+    tokens = synth.block_tokens(cfg, 1, seed=0, device="cuda")
+    logits = torch.empty((1, cfg.block - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    vals = torch.empty((1, cfg.block - 1, 16), dtype=torch.float32, device="cuda")
+    ids = dr.draft_block(tokens, k=16, logits=logits, vals=vals)
+    ids1 = dr.draft_block(tokens, k=1)
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+
+    ref = D.draft_block(cfg, wh, taps_h, tokens[0].cpu().tolist(), P, 0, mode="mirror", want_intermediates=True)
+    g_logits = logits[0].cpu().numpy()
+    err = Hn.assert_close(g_logits, ref["logits"], "logits")
+    exact = D.draft_block(cfg, wh, taps_h, tokens[0].cpu().tolist(), P, 0, mode="exact")
+    print(f"logits max err {err:.3g} (mirror); oracle mirror-vs-exact drift "
+          f"{np.max(np.abs(ref['logits'] - exact['logits'])):.3g}", flush=True)
+    g_ids = ids.cpu().numpy()
+    Hn.topk_self_consistent(g_logits, g_ids[0])
+    np.testing.assert_array_equal(vals[0].cpu().numpy(), np.take_along_axis(g_logits, g_ids[0], 1))
+    np.testing.assert_array_equal(ids1.cpu().numpy()[0, :, 0], g_ids[0, :, 0])
+    comp, excl = Hn.topk_agrees_away_from_ties(ref["logits"], g_ids[0], 16)
+    print(f"top-16 ranks compared {comp}, excluded as near-ties {excl}", flush=True)
+    assert comp > 0.5 * (comp + excl)
+
+    # the ring holds the oracle's context K/V (cached == uncached)
+    rk, rv = dr.ring()
+    slots = np.arange(lo, P) % cfg.ring_capacity
+    for l in range(cfg.n_layers):
+        gk = rk[l, 0].float().cpu().numpy()[:, slots, :]                 # [nkv, n, hd]
+        gv = rv[l, 0].float().cpu().numpy()[:, :, slots].transpose(0, 2, 1)
+        Hn.assert_close(gk, ref["ctx_k"][l], f"ring K layer {l}")
+        Hn.assert_close(gv, ref["ctx_v"][l], f"ring V layer {l}")
+
+
+def test_short_context_and_reset_tiny(tiny_setup):
+    """Context shorter than the window, and context length 0 after a reset."""
+    binding, cfg, w, wh = tiny_setup
+    dr = binding.Drafter(cfg, w)
+    taps, taps_h = _taps_history(cfg, 40, seed=1)
+    tokens = synth.block_tokens(cfg, 1, seed=3, device="cuda")
+    for P, vf in ((20, 0), (37, 37), (40, 33)):
+        print(f"case: tiny pos={P} valid_from={vf}", flush=True)
+        dr.reset(0, vf, P)
+        if P > vf:
+            dr.tap_stage([t[vf:] for t in taps], P - vf, rows_per_req=P - vf,
+                         pos_of_row=torch.arange(vf, P, dtype=torch.int32, device="cuda"),
+                         req_of_row=torch.zeros(P - vf, dtype=torch.int32, device="cuda"))
+        logits = torch.empty((1, cfg.block - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+        dr.draft_block(tokens, k=1, logits=logits)
+        torch.cuda.synchronize()
+        ref = D.draft_block(cfg, wh, taps_h, tokens[0].cpu().tolist(), P, vf, mode="mirror")
+        Hn.assert_close(logits[0].cpu().numpy(), ref["logits"], f"logits pos={P} vf={vf}")
+    assert dr.check() == 0
+
+
+def test_rounds_with_accept_and_rollback_tiny(tiny_setup):
+    """Many rounds: draft -> synthetic verify -> stage verify rows -> accept.
+    Verify rows carry fresh taps every round (a rejected row's taps differ from
+    the one later committed at that position), the ring wraps, and every draft
+    must equal the oracle recomputing the context from the committed taps."""
+    binding, cfg, w, wh = tiny_setup
+    dr = binding.Drafter(cfg, w)
+    B, V = cfg.block, cfg.vocab
+    P0 = 70
+    pre, pre_h = _taps_history(cfg, P0, seed=5)
+    history = [h.copy() for h in pre_h]
+    lo = max(0, P0 - cfg.window)
+    dr.reset(0, 0, P0)
+    dr.tap_stage([t[lo:] for t in pre], P0 - lo, rows_per_req=1,
+                 pos_of_row=torch.arange(lo, P0, dtype=torch.int32, device="cuda"),
+                 req_of_row=torch.zeros(P0 - lo, dtype=torch.int32, device="cuda"))
+    tokens = synth.block_tokens(cfg, 1, seed=7, device="cuda")
+    accepts = synth.geometric_accepts(12, 1, B, p=0.75, seed=1)
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    pos = P0
+    for rnd in range(12):
+        print(f"case: tiny round {rnd} pos={pos}", flush=True)
+        logits = torch.empty((1, B - 1, V), dtype=torch.float32, device="cuda")
+        ids = dr.draft_block(tokens, k=1, logits=logits)
+        torch.cuda.synchronize()
+        ref = D.draft_block(cfg, wh, history, tokens[0].cpu().tolist(), pos, 0, mode="mirror")
+        Hn.assert_close(logits[0].cpu().numpy(), ref["logits"], f"round {rnd} logits")
+        noise = torch.randint(0, V - 1, (1, B), generator=gen, device="cuda", dtype=torch.int32)
+        acc = torch.tensor(accepts[rnd], dtype=torch.int32, device="cuda")
+        verify = synth.verify_from_draft(ids[:, :, 0].contiguous(), acc, V, noise)
+        vt = synth.make_taps(cfg, B, seed=100 + rnd, device="cuda")
+        dr.tap_stage(vt, B, rows_per_req=B)             # rows at [pos, pos + B)
+        out = dr.accept(ids, 1, verify)
+        torch.cuda.synchronize()
+        exp = D.accept(ids[0, :, 0].cpu().tolist(), verify[0].cpu().tolist())
+        assert int(out["accept_len"][0]) == exp["acc"] == int(accepts[rnd, 0])
+        n = int(out["n_emit"][0])
+        assert n == exp["n_emit"]
+        assert out["emitted"][0, :n].cpu().tolist() == exp["emitted"]
+        vt_h = [t.cpu().numpy().astype(np.float64) for t in vt]
+        history = [np.concatenate([h[:pos], v[:n]], 0) for h, v in zip(history, vt_h)]
+        pos += n
+        assert int(dr.positions()[0][0]) == pos
+        nt = out["next_tokens"][0].cpu().tolist()
+        assert nt == D.next_block(exp["emitted"], B, cfg.mask_id)
+        tokens = out["next_tokens"]
+    st = dr.stats().cpu().numpy()
+    assert st[0] == 12 and st[B + 1] == pos - P0
+    for i in range(B):
+        assert st[1 + i] == int(np.sum(accepts[:12, 0] > i))
+    assert dr.check() == 0
+
+
+def test_accept_kernel_cases(tiny_setup):
+    binding, cfg, w, wh = tiny_setup
+    dr = binding.Drafter(cfg, w)
+    B, R = cfg.block, 4
+    rng = np.random.default_rng(0)
+    for trial in range(40):
+        d = rng.integers(0, 5, (R, B - 1)).astype(np.int32)
+        v = rng.integers(0, 5, (R, B)).astype(np.int32)
+        for r in range(R):                       # plant matching prefixes
+            a = rng.integers(0, B)
+            v[r, :a] = d[r, :a] if a < B else v[r, :a]
+        eos = int(rng.integers(-1, 5)) if trial % 3 else -1
+        budget = rng.integers(-1, B + 2, R).astype(np.int32) if trial % 2 else None
+        for r in range(R):
+            dr.reset(r, 0, 1000 + r)
+        out = dr.accept(torch.from_numpy(d).cuda(), 1, torch.from_numpy(v).cuda(), eos_id=eos,
+                        budget=None if budget is None else torch.from_numpy(budget).cuda())
+        torch.cuda.synchronize()
+        pos = dr.positions()[0].cpu().numpy()
+        for r in range(R):
+            exp = D.accept(d[r].tolist(), v[r].tolist(), eos_id=eos,
+                           budget=None if budget is None else int(budget[r]))
+            n = exp["n_emit"]
+            assert int(out["accept_len"][r]) == exp["acc"]
+            assert int(out["n_emit"][r]) == n
+            em = out["emitted"][r].cpu().tolist()
+            assert em[:n] == exp["emitted"] and all(x == -1 for x in em[n:])
+            assert pos[r] == 1000 + r + n
+            assert out["next_tokens"][r].cpu().tolist() == D.next_block(exp["emitted"], B, cfg.mask_id)
