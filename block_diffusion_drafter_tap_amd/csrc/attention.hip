@@ -7,7 +7,8 @@
 // Workgroup = (key chunk, kv head, request). Its waves hold the G*B queries of
 // the kv head's query-head group, 16 per wave (one MFMA tile). Per 32-key
 // sub-tile a wave computes S^T = K Q^T (MFMA, keys x queries), runs the online
-// softmax in registers, and accumulates O^T = V^T P^T (MFMA, head_dim x queries).
+// softmax in registers, and accumulates O^T = V^T P^T (MFMA, head_dim x queries,
+// with P split into two bf16 terms).
 // The ring keeps V transposed ([hd][C]) so that both MFMA operands are 16-byte
 // loads. Keys of the two 16-row S^T tiles are permuted so that after the first
 // MFMA each lane group already holds the 8 consecutive keys the second MFMA
@@ -112,18 +113,24 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    u32x4 pb;
-    pb[0] = pack_bf16x2(p[0], p[1]);
-    pb[1] = pack_bf16x2(p[2], p[3]);
-    pb[2] = pack_bf16x2(p[4], p[5]);
-    pb[3] = pack_bf16x2(p[6], p[7]);
-    const bf16x8 pf = as_bf16x8(pb);
+    // P enters the MFMA as two bf16 terms, P = hi + lo (about 16 significant
+    // bits): a single bf16 rounding of the probabilities would move the output
+    // by far more than every other rounding of the layer together.
+    u32x4 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float h0 = bf2f(f2bf(p[2 * e])), h1 = bf2f(f2bf(p[2 * e + 1]));
+      ph[e] = pack_bf16x2(h0, h1);
+      pl[e] = pack_bf16x2(p[2 * e] - h0, p[2 * e + 1] - h1);
+    }
+    const bf16x8 pf_hi = as_bf16x8(ph), pf_lo = as_bf16x8(pl);
     const int vslot = (k0 + 8 * lg) % a.C;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
       o[t] *= alpha;
-      const uint16_t* vp = rv + (size_t)(16 * t + lr) * a.C + vslot;
-      o[t] = mfma16x16x32(as_bf16x8(ld16(vp)), pf, o[t]);
+      const bf16x8 vf8 = as_bf16x8(ld16(rv + (size_t)(16 * t + lr) * a.C + vslot));
+      o[t] = mfma16x16x32(vf8, pf_hi, o[t]);
+      o[t] = mfma16x16x32(vf8, pf_lo, o[t]);
     }
   }
   // full softmax denominator of query lr: sum over the four lane groups

@@ -46,17 +46,26 @@ def topk_self_consistent(gpu_logits: np.ndarray, gpu_ids: np.ndarray):
         np.testing.assert_array_equal(ids[r], ref, err_msg=f"row {r}")
 
 
-def topk_agrees_away_from_ties(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k: int):
-    """Compare GPU ids with the oracle's at ranks whose oracle gap to the
-    neighbouring ranks exceeds delta = 1e-3 * max|row| + 1e-5. Returns the
-    number of (row, rank) pairs compared and excluded."""
+def topk_agrees_away_from_ties(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k: int,
+                               gpu_logits: np.ndarray = None):
+    """Compare GPU ids with the oracle's at the ranks the numerics decide.
+
+    Rank j of a row is compared when the oracle's gaps to ranks j-1 and j+1
+    exceed delta = max(2 * eps_row, 1e-3 * max|row| + 1e-5), eps_row being the
+    measured max |gpu - oracle| logit error of that row: if every GPU logit is
+    within eps_row of the oracle's, two values more than 2 * eps_row apart keep
+    their order, so a mismatch there is a selection bug, not rounding. Returns
+    (compared, excluded) counts."""
     L = oracle_logits.reshape(-1, oracle_logits.shape[-1])
+    G = None if gpu_logits is None else np.asarray(gpu_logits, dtype=np.float64).reshape(L.shape)
     ids = gpu_ids.reshape(-1, k)
     compared = excluded = 0
     for r in range(L.shape[0]):
         order = np.lexsort((np.arange(L.shape[1]), -L[r]))[:k + 1]
         v = L[r][order]
         delta = 1e-3 * np.max(np.abs(L[r])) + 1e-5
+        if G is not None:
+            delta = max(delta, 2.0 * float(np.max(np.abs(G[r] - L[r]))))
         for j in range(k):
             lo_gap = v[j - 1] - v[j] if j > 0 else np.inf
             hi_gap = v[j] - v[j + 1]
