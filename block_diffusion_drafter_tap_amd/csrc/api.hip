@@ -24,17 +24,17 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int CU_TARGET = 512;   // workgroups wanted per weight-streaming GEMM
+constexpr int CU_TARGET = 256;   // workgroups (of 8 waves) wanted per weight-streaming GEMM
 constexpr int GC_DEFAULT = 128;
 
-int attn_chunk(const dflash_config& c) { return c.window <= 256 ? 64 : 128; }
+int attn_chunk(const dflash_config& c) { return c.window <= 256 ? 64 : 256; }
 int attn_nchunks(const dflash_config& c) {
   const int kc = attn_chunk(c);
   return (c.window + c.block + 31 + kc - 1) / kc;
 }
 
 struct WsLayout {
-  size_t h, a, q, o, act, c32, c, partials, counters, attn_o, attn_ml, attn_cnt, cand_v, cand_i, total;
+  size_t h, ssq, q, o, act, c32, c, partials, counters, attn_o, attn_ml, attn_cnt, cand_v, cand_i, mid_v, mid_i, total;
   size_t n_counters;
 };
 
@@ -81,7 +81,7 @@ WsLayout ws_layout(const dflash_config& c) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   L.h = take(Mmax * c.hidden * 4);
-  L.a = take(Mmax * c.hidden * 2);
+  L.ssq = take((size_t)(c.hidden / GC_DEFAULT) * Mmax * 4);
   L.q = take(Mmax * qw * 2);
   L.o = take(Mmax * qw * 2);
   L.act = take(Mmax * c.ffn * 2);
@@ -95,6 +95,9 @@ WsLayout ws_layout(const dflash_config& c) {
   L.attn_cnt = take(lrg * 4);
   L.cand_v = take(lm_groups * out_rows * 16 * 4);
   L.cand_i = take(lm_groups * out_rows * 16 * 4);
+  const size_t nblk = (lm_groups + 63) / 64;
+  L.mid_v = take(out_rows * nblk * 16 * 4);
+  L.mid_i = take(out_rows * nblk * 16 * 4);
   L.total = off;
   return L;
 }
@@ -145,6 +148,8 @@ int validate_config(const dflash_config* c) {
   if (attn_slots(c->n_q_heads, c->n_kv_heads, c->block) > 64)
     return fail(DFLASH_E_UNSUPPORTED, "(n_q_heads/n_kv_heads)*block = %d query rows per kv head; at most 64",
                 attn_slots(c->n_q_heads, c->n_kv_heads, c->block));
+  if (c->vocab > 64 * 64 * GC_DEFAULT)
+    return fail(DFLASH_E_UNSUPPORTED, "vocab %d exceeds the top-k merge capacity (%d)", c->vocab, 64 * 64 * GC_DEFAULT);
   if (c->wfmt == DFLASH_W_INT4_G64)
     return fail(DFLASH_E_UNSUPPORTED, "INT4 weights are not built in this library version");
   return DFLASH_OK;
@@ -422,21 +427,32 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
   const int M = n_req * B;
   const int qw = g.n_q_heads * hd;
   float* h = at<float>(ctx->ws, ctx->wl.h);
-  uint16_t* act_a = at<uint16_t>(ctx->ws, ctx->wl.a);
+  float* ssq = at<float>(ctx->ws, ctx->wl.ssq);
   uint16_t* q = at<uint16_t>(ctx->ws, ctx->wl.q);
   uint16_t* o = at<uint16_t>(ctx->ws, ctx->wl.o);
   uint16_t* act = at<uint16_t>(ctx->ws, ctx->wl.act);
   unsigned* err = at<unsigned>(ctx->state, ctx->sl.error);
-  hipError_t e = launch_embed_norm(block_tokens, ctx->embed, ctx->ln_in[0], h, act_a, M, H, g.vocab, g.rms_eps, err, st);
+  const int ssq_ld = g.max_requests * B;
+  const int h_blocks = H / GC_DEFAULT;
+  // every RMSNorm is applied by the GEMM that consumes it (X_NORM), from h and
+  // the per-row sums of squares its producer left in ssq
+  auto norm_input = [&](GemmArgs& a, const uint16_t* gain, int n_blocks) {
+    a.xf = h;
+    a.ldx = H;
+    a.xgain = gain;
+    a.ssq_in = ssq;
+    a.n_ssq = n_blocks;
+    a.ssq_ld = ssq_ld;
+  };
+  hipError_t e = launch_embed(block_tokens, ctx->embed, h, ssq, M, H, g.vocab, err, st);
   if (e != hipSuccess) return hip_fail(e, "embed");
   const size_t rl = ring_layer_elems(g);
   for (int l = 0; l < g.n_layers; ++l) {
     uint16_t* rk = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
     uint16_t* rv = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
-    {  // QKV + q/k head norm + RoPE; the block's K/V go to ring slots [pos, pos+B)
+    {  // RMSNorm + QKV + q/k head norm + RoPE; the block's K/V go to ring slots [pos, pos+B)
       GemmArgs a = base_args(ctx);
-      a.x = act_a;
-      a.ldx = H;
+      norm_input(a, ctx->ln_in[l], l == 0 ? 1 : h_blocks);
       a.w = ctx->wqkv[l];
       a.M = M;
       a.N = (g.n_q_heads + 2 * g.n_kv_heads) * hd;
@@ -450,7 +466,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.rows_per_req = B;
       GemmPlan p = plan_gemm(M, a.N, H, hd, 0, CU_TARGET);
       Timed tm(ctx, DFLASH_K_QKV, st);
-      e = launch_gemm(a, p, X_BF16, E_HEAD, WF_BF16, st);
+      e = launch_gemm(a, p, X_NORM, E_HEAD, WF_BF16, st);
       if (e != hipSuccess) return hip_fail(e, "qkv");
     }
     {  // attention over [context window | block]
@@ -479,7 +495,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       e = launch_attention(t, n_req, st);
       if (e != hipSuccess) return hip_fail(e, "attention");
     }
-    {  // o projection, residual add
+    {  // o projection, residual add, row sums of squares for the post-attention norm
       GemmArgs a = base_args(ctx);
       a.x = o;
       a.ldx = qw;
@@ -489,17 +505,16 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.K = qw;
       a.out = h;
       a.ldo = H;
+      a.ssq_out = ssq;
+      a.ssq_ld = ssq_ld;
       GemmPlan p = plan_gemm(M, H, qw, GC_DEFAULT, 0, CU_TARGET);
       Timed tm(ctx, DFLASH_K_O, st);
       e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
       if (e != hipSuccess) return hip_fail(e, "o proj");
     }
-    e = launch_rmsnorm(h, ctx->ln_post[l], act_a, M, H, g.rms_eps, st);
-    if (e != hipSuccess) return hip_fail(e, "post norm");
-    {  // gate/up with SiLU(gate) * up
+    {  // RMSNorm + gate/up with SiLU(gate) * up
       GemmArgs a = base_args(ctx);
-      a.x = act_a;
-      a.ldx = H;
+      norm_input(a, ctx->ln_post[l], h_blocks);
       a.w = ctx->wgu[l];
       a.M = M;
       a.N = g.ffn;
@@ -509,10 +524,10 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ldo = g.ffn;
       GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CU_TARGET);
       Timed tm(ctx, DFLASH_K_GATEUP, st);
-      e = launch_gemm(a, p, X_BF16, E_SILU, WF_BF16, st);
+      e = launch_gemm(a, p, X_NORM, E_SILU, WF_BF16, st);
       if (e != hipSuccess) return hip_fail(e, "gate/up");
     }
-    {  // down projection, residual add
+    {  // down projection, residual add, row sums of squares for the next norm
       GemmArgs a = base_args(ctx);
       a.x = act;
       a.ldx = g.ffn;
@@ -522,19 +537,17 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.K = g.ffn;
       a.out = h;
       a.ldo = H;
+      a.ssq_out = ssq;
+      a.ssq_ld = ssq_ld;
       GemmPlan p = plan_gemm(M, H, g.ffn, GC_DEFAULT, 0, CU_TARGET);
       Timed tm(ctx, DFLASH_K_DOWN, st);
       e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
       if (e != hipSuccess) return hip_fail(e, "down proj");
     }
-    const uint16_t* next_gain = l + 1 < g.n_layers ? ctx->ln_in[l + 1] : ctx->final_norm;
-    e = launch_rmsnorm(h, next_gain, act_a, M, H, g.rms_eps, st);
-    if (e != hipSuccess) return hip_fail(e, "norm");
   }
   {  // shared LM head with per-group top-k, then the merge
     GemmArgs a = base_args(ctx);
-    a.x = act_a;
-    a.ldx = H;
+    norm_input(a, ctx->final_norm, h_blocks);
     a.w = ctx->lm_head;
     a.M = M;
     a.N = g.vocab;
@@ -546,10 +559,11 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
     GemmPlan p = plan_gemm(M, g.vocab, H, GC_DEFAULT, 0, 0);
     {
       Timed tm(ctx, DFLASH_K_LMHEAD, st);
-      e = launch_gemm(a, p, X_BF16, E_TOPK, WF_BF16, st);
+      e = launch_gemm(a, p, X_NORM, E_TOPK, WF_BF16, st);
     }
     if (e != hipSuccess) return hip_fail(e, "lm head");
-    e = launch_topk_merge(a.cand_val, a.cand_idx, p.groups, n_req * (B - 1), k, topk_ids, topk_vals, st);
+    e = launch_topk_merge(a.cand_val, a.cand_idx, p.groups, n_req * (B - 1), k, at<float>(ctx->ws, ctx->wl.mid_v),
+                          at<int>(ctx->ws, ctx->wl.mid_i), topk_ids, topk_vals, st);
     if (e != hipSuccess) return hip_fail(e, "topk merge");
   }
   return DFLASH_OK;

@@ -14,8 +14,8 @@
 // MFMA each lane group already holds the 8 consecutive keys the second MFMA
 // needs as its k-values (no cross-lane shuffles between the two products).
 //
-// Chunks of one (request, kv head) write partial (max, sum, O) to scratch; the
-// last one to finish combines them in chunk order, so results do not depend on
+// Chunks of one (request, kv head) write partial (max, sum, O) to scratch and a
+// second kernel combines them in chunk order, so results do not depend on
 // scheduling.
 #include "device.h"
 #include "kernels.h"
@@ -28,8 +28,6 @@ template <int HD>
 __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   constexpr int HT = HD / 16;   // O^T tiles along head_dim
   constexpr int QS = HD / 32;   // MFMA k-steps along head_dim
-  __shared__ float s_m[64], s_l[64];
-  __shared__ int last_flag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -75,16 +73,29 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   for (int t = 0; t < HT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int k0 = kb; k0 < ke; k0 += 32) {
-    // S^T for keys k0 + 8*(rr/4) + 4*kt + rr%4 (rr = row of the tile)
-    f32x4 sc[2];
+  // K / V fragments of one 32-key sub-tile; the next sub-tile's are loaded
+  // while the current one is computed.
+  u32x4 kA[2][QS], vA[HT], kB[2][QS], vB[HT];
+  auto load = [&](int k0, u32x4 (&kf)[2][QS], u32x4 (&vf)[HT]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = k0 + 8 * (lr >> 2) + 4 * kt + (lr & 3);
       const uint16_t* kp = rk + (size_t)(key % a.C) * HD + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) kf[kt][s] = ld16(kp + 32 * s);
+    }
+    const int vslot = (k0 + 8 * lg) % a.C;
+#pragma unroll
+    for (int t = 0; t < HT; ++t) vf[t] = ld16(rv + (size_t)(16 * t + lr) * a.C + vslot);
+  };
+  auto compute = [&](int k0, const u32x4 (&kf)[2][QS], const u32x4 (&vf)[HT]) {
+    // S^T for keys k0 + 8*(rr/4) + 4*kt + rr%4 (rr = row of the tile)
+    f32x4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < QS; ++s) acc = mfma16x16x32(as_bf16x8(ld16(kp + 32 * s)), qf[s], acc);
+      for (int s = 0; s < QS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qf[s], acc);
       sc[kt] = acc;
     }
     // lane holds, for query lr, keys k0 + 8*lg + e (e = 4*kt + i)
@@ -114,8 +125,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // P enters the MFMA as two bf16 terms, P = hi + lo (about 16 significant
-    // bits): a single bf16 rounding of the probabilities would move the output
-    // by far more than every other rounding of the layer together.
+    // bits), so the probabilities are not rounded to 8 bits.
     u32x4 ph, pl;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -124,35 +134,27 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
       pl[e] = pack_bf16x2(p[2 * e] - h0, p[2 * e + 1] - h1);
     }
     const bf16x8 pf_hi = as_bf16x8(ph), pf_lo = as_bf16x8(pl);
-    const int vslot = (k0 + 8 * lg) % a.C;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
       o[t] *= alpha;
-      const bf16x8 vf8 = as_bf16x8(ld16(rv + (size_t)(16 * t + lr) * a.C + vslot));
-      o[t] = mfma16x16x32(vf8, pf_hi, o[t]);
-      o[t] = mfma16x16x32(vf8, pf_lo, o[t]);
+      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf_hi, o[t]);
+      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf_lo, o[t]);
     }
+  };
+  load(kb, kA, vA);
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    const bool more = k0 + 32 < ke;
+    if (more) load(k0 + 32, kB, vB);
+    compute(k0, kA, vA);
+    if (!more) break;
+    if (k0 + 64 < ke) load(k0 + 64, kA, vA);
+    compute(k0 + 32, kB, vB);
   }
   // full softmax denominator of query lr: sum over the four lane groups
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  // o[t][i] = O^T[hd = 16t + 4*lg + i][query lr]
-  if (n_ch == 1) {
-    if (qvalid) {
-      const float inv = 1.0f / l_run;
-      uint16_t* op = a.out + ((size_t)r * a.B + iq) * a.nq * HD + (size_t)(g * G + hq) * HD;
-#pragma unroll
-      for (int t = 0; t < HT; ++t) {
-        u32x2 v;
-        v[0] = pack_bf16x2(o[t][0] * inv, o[t][1] * inv);
-        v[1] = pack_bf16x2(o[t][2] * inv, o[t][3] * inv);
-        *(u32x2*)(op + 16 * t + 4 * lg) = v;
-      }
-    }
-    return;
-  }
-
+  // partial state of this chunk: o[t][i] = O^T[hd = 16t + 4*lg + i][query lr]
   const size_t cbase = (lrg * a.n_chunks + chunk) * (size_t)slots;
   if (qvalid) {
     float* po = a.part_o + (cbase + slot) * HD;
@@ -163,45 +165,63 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
       a.part_ml[(cbase + slot) * 2 + 1] = l_run;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counters[lrg], 1u);
-    const int last = prev == (unsigned)(n_ch - 1);
-    if (last) atomicExch(&a.counters[lrg], 0u);
-    last_flag = last;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-
-  const size_t c0 = lrg * a.n_chunks * (size_t)slots;
-  for (int s = threadIdx.x; s < slots; s += blockDim.x) {
-    float M = -INFINITY;
-    for (int c = 0; c < n_ch; ++c) M = fmaxf(M, __builtin_nontemporal_load(a.part_ml + (c0 + (size_t)c * slots + s) * 2));
-    float L = 0.f;
-    for (int c = 0; c < n_ch; ++c) {
-      const float mc = __builtin_nontemporal_load(a.part_ml + (c0 + (size_t)c * slots + s) * 2);
-      const float lc = __builtin_nontemporal_load(a.part_ml + (c0 + (size_t)c * slots + s) * 2 + 1);
-      L += exp2f(mc - M) * lc;
-    }
-    s_m[s] = M;
-    s_l[s] = 1.0f / L;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < slots * HD; e += blockDim.x) {
-    const int s = e / HD, d = e % HD;
-    const float M = s_m[s];
-    float acc = 0.f;
-    for (int c = 0; c < n_ch; ++c) {
-      const size_t cs = c0 + (size_t)c * slots + s;
-      const float mc = __builtin_nontemporal_load(a.part_ml + cs * 2);
-      acc += exp2f(mc - M) * __builtin_nontemporal_load(a.part_o + cs * HD + d);
-    }
-    const int hq2 = s / a.B, iq2 = s % a.B;
-    a.out[((size_t)r * a.B + iq2) * a.nq * HD + (size_t)(g * G + hq2) * HD + d] = f2bfbits(acc * s_l[s]);
-  }
   (void)nwaves;
+}
+
+// Combine the chunk partials of one (request, kv head): O = sum_c w_c O_c with
+// w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c, in chunk order. Each thread owns
+// four consecutive head_dim values of one query slot.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
+  const int lrg = blockIdx.x;
+  const int r = lrg / a.nkv, g = lrg % a.nkv;
+  const int G = a.nq / a.nkv, slots = G * a.B;
+  const int e = blockIdx.y * blockDim.x + threadIdx.x;   // float4 index within [slots][HD/4]
+  if (e >= slots * HD / 4) return;
+  const int s = e / (HD / 4), d4 = e % (HD / 4);
+  int pos = a.pos[r], vf = a.valid_from[r];
+  vf = vf > pos ? pos : vf;
+  int lo = pos - a.W;
+  lo = lo > vf ? lo : vf;
+  lo = lo > 0 ? lo : 0;
+  const int base = lo & ~31;
+  const int n_ch = (pos + a.B - base + a.kc - 1) / a.kc;
+  const size_t c0 = (size_t)lrg * a.n_chunks * slots;
+  const float2* ml = (const float2*)a.part_ml;
+  float M = -INFINITY;
+  for (int c0i = 0; c0i < n_ch; c0i += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0i + u < n_ch ? ml[c0 + (size_t)(c0i + u) * slots + s] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, v[u].x);
+  }
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0i = 0; c0i < n_ch; c0i += 8) {
+    float2 v[8];
+    f32x4 ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = c0i + u < n_ch;
+      const size_t cs = c0 + (size_t)(c0i + u) * slots + s;
+      v[u] = ok ? ml[cs] : make_float2(-INFINITY, 0.f);
+      ov[u] = ok ? *(const f32x4*)(a.part_o + cs * HD + 4 * d4) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wgt = exp2f(v[u].x - M);
+      L += wgt * v[u].y;
+      acc += wgt * ov[u];
+    }
+  }
+  const float inv = 1.0f / L;
+  const int hq = s / a.B, iq = s % a.B;
+  uint16_t* op = a.out + ((size_t)r * a.B + iq) * a.nq * HD + (size_t)(g * G + hq) * HD + 4 * d4;
+  u32x2 w;
+  w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)op = w;
 }
 
 }  // namespace
@@ -211,10 +231,17 @@ int attn_slots(int nq, int nkv, int B) { return (nq / nkv) * B; }
 hipError_t launch_attention(const AttnArgs& a, int R, hipStream_t st) {
   const int slots = attn_slots(a.nq, a.nkv, a.B);
   const int waves = (slots + 15) / 16;
-  if (waves > 4) return hipErrorInvalidValue;   // <= 64 query slots per kv head
+  if (waves > 4 || a.kc % 64) return hipErrorInvalidValue;   // <= 64 query slots per kv head
   const dim3 grid(a.n_chunks, a.nkv, R), block(64 * waves);
-  if (a.hd == 128) hipLaunchKernelGGL((attn_kernel<128>), grid, block, 0, st, a);
-  else if (a.hd == 64) hipLaunchKernelGGL((attn_kernel<64>), grid, block, 0, st, a);
-  else return hipErrorInvalidValue;
+  const dim3 cgrid(R * a.nkv, (slots * a.hd / 4 + 255) / 256);
+  if (a.hd == 128) {
+    hipLaunchKernelGGL((attn_kernel<128>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), cgrid, dim3(256), 0, st, a);
+  } else if (a.hd == 64) {
+    hipLaunchKernelGGL((attn_kernel<64>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), cgrid, dim3(256), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }

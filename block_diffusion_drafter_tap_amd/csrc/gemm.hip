@@ -4,41 +4,39 @@
 // (16 rows x 16 columns per instruction) so the VALU is free to issue loads.
 //
 // Work split
-//   grid.x  column groups of GC = 4 waves * NT tiles * 16 columns
-//   grid.y  K splits (S); partial sums are reduced by the last-arriving
-//           workgroup of each column group in fixed split order (deterministic)
+//   grid.x  column groups of GC = NW waves * 16 columns (one 16-row W tile per wave)
+//   grid.y  K splits (S)
 //   grid.z  row chunks of 16*MT rows
-// Each wave streams its NT weight tiles (16 rows of W each) over its K range
-// with one 128-wide K chunk of loads in flight ahead of the MFMAs; X fragments
-// come straight from L2 (X is small and shared by every workgroup).
+// The workgroup first stages its X slice [16*MT rows][K range] in LDS (for tap
+// inputs the hc-stream mean and the bf16 cast happen here, once per element);
+// then every wave streams its W tile over the K range, one 128-wide chunk of
+// loads in flight ahead of the MFMAs. Plain (cached) loads measured faster than
+// non-temporal ones for this pattern.
 //
-// MFMA operand layout used here (v_mfma_f32_16x16x32_bf16): lane l supplies
-// A[l%16][8 k-values] and B[8 k-values][l%16], the k-values of lane group
-// l/16 being k0 + 8*(l/16) + 0..7 in both operands; the result lands as
+// Split-K: each split publishes its [rows][GC] partial tile with agent-scope
+// relaxed atomic stores (coherent across the XCDs' L2s without flushing them),
+// waits for the stores to complete and bumps a per-group counter; the last
+// split to arrive sums all partials in split order (deterministic) with
+// agent-scope relaxed atomic loads and runs the epilogue. A device-scope fence
+// here would write back and invalidate L2 in every workgroup.
+//
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16): lane l supplies A[l%16][8
+// k-values] and B[8 k-values][l%16], the k-values of lane group l/16 being
+// k0 + 8*(l/16) + 0..7 in both operands; the result lands as
 // C[4*(l/16) + i][l%16], i = 0..3.
 //
-// Epilogues run on a [16*MT][GC] fp32 tile in LDS after the reduction:
+// Epilogues run on a [16*MT][GC] fp32 tile in LDS:
 //   E_BF16 / E_F32  store; E_RESID  h += Y (fp32 residual stream);
-//   E_SILU  SiLU(gate) * up -> bf16 (gate and up tiles of one workgroup pair up);
+//   E_SILU  SiLU(gate) * up -> bf16 (the first half of the waves stream gate
+//           rows, the second half the matching up rows);
 //   E_HEAD  one head per workgroup: q/k RMSNorm over head_dim, RoPE at the row's
 //           position, Q to the block buffer, K / V into the context ring;
-//   E_TOPK  LM head: per-row top-k (or argmax) of the group's columns for mask
-//           rows, written as candidates for topk_merge.
+//   E_TOPK  LM head: rows sorted in LDS (bitonic network) by (logit desc, id
+//           asc); the first k entries of each mask row become candidates.
 #include "device.h"
 #include "kernels.h"
 
 namespace {
-
-template <int NT, bool PAIR>
-DEV int tile_col(int wave, int t) {
-  if constexpr (PAIR) {
-    constexpr int HALF = NT / 2;
-    constexpr int GC = GEMM_WAVES * NT * 16;
-    return (t < HALF ? 0 : GC / 2) + wave * HALF * 16 + (t % HALF) * 16;
-  } else {
-    return wave * NT * 16 + t * 16;
-  }
-}
 
 DEV const float* tap_ptr(const GemmArgs& a, int t) {
   const float* p = a.taps[0];
@@ -48,10 +46,26 @@ DEV const float* tap_ptr(const GemmArgs& a, int t) {
   return p;
 }
 
+// 8 consecutive X values (k..k+7) of row `row` as bf16x8 (`inv`: the row's
+// 1/rms for X_NORM).
 template <int XK>
-DEV u32x4 load_x(const GemmArgs& a, int row, int k) {
-  if (XK == X_BF16) {
+DEV u32x4 load_x(const GemmArgs& a, int row, int k, float inv) {
+  if constexpr (XK == X_BF16) {
     return ld16(a.x + (size_t)row * a.ldx + k);
+  } else if constexpr (XK == X_NORM) {
+    const float* p = a.xf + (size_t)row * a.ldx + k;
+    const f32x4 h0 = *(const f32x4*)p, h1 = *(const f32x4*)(p + 4);
+    const u32x4 g = ld16(a.xgain + k);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x4 h = i ? h1 : h0;
+      r[2 * i] = pack_bf16x2(h[0] * inv * __uint_as_float(g[2 * i] << 16),
+                             h[1] * inv * __uint_as_float(g[2 * i] & 0xffff0000u));
+      r[2 * i + 1] = pack_bf16x2(h[2] * inv * __uint_as_float(g[2 * i + 1] << 16),
+                                 h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
+    }
+    return r;
   } else {
     const int t = k / a.tap_hidden;
     const int col = k - t * a.tap_hidden;
@@ -61,9 +75,9 @@ DEV u32x4 load_x(const GemmArgs& a, int row, int k) {
       s0 += *(const f32x4*)(p + (size_t)st * a.tap_hidden);
       s1 += *(const f32x4*)(p + (size_t)st * a.tap_hidden + 4);
     }
-    const float inv = 1.0f / (float)a.hc;
-    s0 *= inv;
-    s1 *= inv;
+    const float hinv = 1.0f / (float)a.hc;
+    s0 *= hinv;
+    s1 *= hinv;
     u32x4 r;
     r[0] = pack_bf16x2(s0[0], s0[1]);
     r[1] = pack_bf16x2(s0[2], s0[3]);
@@ -84,12 +98,12 @@ DEV void row_info(const GemmArgs& a, int m, int* req, long long* p) {
   *p = a.pos_of_row ? (long long)a.pos_of_row[m] : (long long)a.pos[r] + m % a.rows_per_req;
 }
 
-template <int ROWS, int GC>
+template <int GC, int NW>
 DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, int head) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hd = a.hd, half = hd / 2;
   const bool is_q = head < a.nq, is_k = !is_q && head < a.nq + a.nkv;
-  for (int r = wave; r < rows; r += GEMM_WAVES) {
+  for (int r = wave; r < rows; r += NW) {
     const int m = m0 + r;
     int req;
     long long p;
@@ -132,61 +146,79 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
   }
 }
 
-template <int ROWS, int GC>
-DEV void epi_topk(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, int group) {
-  constexpr int PER = GC / 64;  // values per lane
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// LM head selection: the group's columns of every mask row, best first.
+template <int ROWS, int GC, int NW>
+DEV void epi_topk(const GemmArgs& a, float (*tile)[GC + 1], int (*tid)[GC], int m0, int rows, int group) {
   const int n_out = (a.M / a.B) * (a.B - 1);
-  for (int r = wave; r < rows; r += GEMM_WAVES) {
-    const int m = m0 + r;
-    const int req = m / a.B, i = m % a.B;
-    if (i == 0) continue;
-    const int orow = req * (a.B - 1) + (i - 1);
-    float v[PER];
-    int id[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = lane + 64 * u;
-      id[u] = group * GC + c;
-      v[u] = id[u] < a.N ? tile[r][c] : -INFINITY;
-      if (a.logits && id[u] < a.N) a.logits[(size_t)orow * a.N + id[u]] = v[u];
+  for (int e = threadIdx.x; e < ROWS * GC; e += blockDim.x) {
+    const int r = e / GC, c = e % GC;
+    const int n = group * GC + c;
+    const bool ok = r < rows && n < a.N;
+    tid[r][c] = n;
+    if (!ok) tile[r][c] = -INFINITY;
+    if (ok && a.logits) {
+      const int m = m0 + r, i = m % a.B;
+      if (i) a.logits[(size_t)((m / a.B) * (a.B - 1) + i - 1) * a.N + n] = tile[r][c];
     }
-    unsigned live = (1u << PER) - 1u;
-    float* cv = a.cand_val + ((size_t)group * n_out + orow) * a.topk;
-    int* ci = a.cand_idx + ((size_t)group * n_out + orow) * a.topk;
-    for (int j = 0; j < a.topk; ++j) {
+  }
+  __syncthreads();
+  if (a.topk == 1) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int r = wave; r < rows; r += NW) {
+      const int m = m0 + r, i = m % a.B;
+      if (i == 0) continue;
       float bv = -INFINITY;
-      int bi = 0x7fffffff, bu = -1;
-#pragma unroll
-      for (int u = 0; u < PER; ++u)
-        if ((live >> u) & 1u)
-          if (bu < 0 || better(v[u], id[u], bv, bi)) { bv = v[u]; bi = id[u]; bu = u; }
+      int bi = 0x7fffffff;
+      for (int c = lane; c < GC; c += 64)
+        if (better(tile[r][c], tid[r][c], bv, bi)) { bv = tile[r][c]; bi = tid[r][c]; }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
-#pragma unroll
-      for (int u = 0; u < PER; ++u)
-        if (id[u] == bi) live &= ~(1u << u);
       if (lane == 0) {
-        cv[j] = bv;
-        ci[j] = bi;
+        const size_t o = (size_t)group * n_out + (m / a.B) * (a.B - 1) + i - 1;
+        a.cand_val[o] = bv;
+        a.cand_idx[o] = bi;
       }
     }
+    return;
+  }
+  // bitonic sort of every row, best first
+  for (int k = 2; k <= GC; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int p = threadIdx.x; p < ROWS * GC / 2; p += blockDim.x) {
+        const int r = p / (GC / 2), q = p % (GC / 2);
+        const int i = (q / j) * 2 * j + (q % j), l = i + j;
+        const float va = tile[r][i], vb = tile[r][l];
+        const int ia = tid[r][i], ib = tid[r][l];
+        const bool first_block = (i & k) == 0;
+        const bool swap = first_block ? better(vb, ib, va, ia) : better(va, ia, vb, ib);
+        if (swap) {
+          tile[r][i] = vb; tile[r][l] = va;
+          tid[r][i] = ib; tid[r][l] = ia;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int e = threadIdx.x; e < rows * a.topk; e += blockDim.x) {
+    const int r = e / a.topk, j = e % a.topk;
+    const int m = m0 + r, i = m % a.B;
+    if (i == 0) continue;
+    const size_t o = ((size_t)group * n_out + (m / a.B) * (a.B - 1) + i - 1) * a.topk + j;
+    a.cand_val[o] = tile[r][j];
+    a.cand_idx[o] = tid[r][j];
   }
 }
 
-template <int MT, int NT, int XK, int EPI, int WF>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
+template <int MT, int NW, int XK, int XL, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   constexpr int ROWS = MT * 16;
-  constexpr int GC = GEMM_WAVES * NT * 16;
+  constexpr int GC = NW * 16;
   constexpr bool PAIR = (EPI == E_SILU);
-  static_assert(!PAIR || NT % 2 == 0, "gate/up pairing needs an even tile count");
-  static_assert(WF == WF_BF16, "INT4 weights take the int4 kernel");
-
-  __shared__ float tile[ROWS][GC + 1];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int last_flag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -195,115 +227,176 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
   const int m0 = mz * ROWS;
   const int kbeg = split * a.ks;
   const int kend = min(a.K, kbeg + a.ks);
-  const int nchunks = (kend - kbeg) / 128;
+  const int klen = kend - kbeg;
+  const int nchunks = klen / 128;
+  const int ldl = a.ks + 8;   // LDS row pitch of the X slice (elements)
+  uint16_t* xs = (uint16_t*)smem;
 
-  const uint16_t* wrow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int row;
-    if constexpr (PAIR) {
-      constexpr int HALF = NT / 2;
-      int logical = group * (GC / 2) + wave * HALF * 16 + (t % HALF) * 16 + lr;
-      logical = min(logical, a.N - 1);
-      row = logical + (t >= HALF ? a.pair_off : 0);
-    } else {
-      row = min(group * GC + wave * NT * 16 + t * 16 + lr, a.N - 1);
-    }
-    wrow[t] = (const uint16_t*)a.w + (size_t)row * a.K + 8 * lg;
+  // this wave's W rows (16 per tile); for gate/up the first half of the waves
+  // take gate rows, the second half the up rows of the same columns
+  int wrow_i, tcol;
+  if constexpr (PAIR) {
+    constexpr int HALF = NW / 2;
+    const int logical = min(group * (GC / 2) + (wave % HALF) * 16 + lr, a.N - 1);
+    wrow_i = logical + (wave >= HALF ? a.pair_off : 0);
+    tcol = (wave >= HALF ? GC / 2 : 0) + (wave % HALF) * 16;
+  } else {
+    wrow_i = min(group * GC + wave * 16 + lr, a.N - 1);
+    tcol = wave * 16;
   }
-  int xrow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xrow[mt] = min(m0 + mt * 16 + lr, a.M - 1);
+  const uint16_t* wrow = (const uint16_t*)a.w + (size_t)wrow_i * a.K + kbeg + 8 * lg;
 
-  f32x4 acc[MT][NT];
+  // the first weight chunk is in flight while the X slice is staged
+  u32x4 wA[4], wB[4];
+  auto load_w = [&](int c, u32x4 (&w)[4]) {
+    const int k = 128 * min(c, nchunks - 1);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[mt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  // Two register stages of one 128-wide K chunk each: loads for chunk c+1 are in
-  // flight while chunk c feeds the MFMAs.
-  u32x4 wA[4][NT], wB[4][NT], xA[4][MT], xB[4][MT];
-  auto load = [&](int c, u32x4 (&w)[4][NT], u32x4 (&x)[4][MT]) {
-    const int k = kbeg + 128 * min(c, nchunks - 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) x[s][mt] = load_x<XK>(a, xrow[mt], k + 32 * s + 8 * lg);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) w[s][t] = ld_nt16(wrow[t] + k + 32 * s);
-    }
+    for (int s = 0; s < 4; ++s) w[s] = ld16(wrow + k + 32 * s);
   };
-  auto compute = [&](int c, const u32x4 (&w)[4][NT], const u32x4 (&x)[4][MT]) {
+  load_w(0, wA);
+
+  __shared__ float s_inv[ROWS];
+  if constexpr (XK == X_NORM) {
+    // 1/rms of each row from the producer's per-column-block sums of squares
+    for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
+      const int m = min(m0 + r, a.M - 1);
+      float ss = 0.f;
+      for (int b = 0; b < a.n_ssq; ++b) ss += a.ssq_in[(size_t)b * a.ssq_ld + m];
+      s_inv[r] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    }
+    __syncthreads();
+  }
+  auto row_inv = [&](int r) -> float {
+    if constexpr (XK == X_NORM) return s_inv[r];
+    return 1.0f;
+  };
+  if (XL) {
+    const int per_row = klen / 8;
+    for (int e = threadIdx.x; e < ROWS * per_row; e += blockDim.x) {
+      const int r = e / per_row, c = e % per_row;
+      *(u32x4*)(xs + r * ldl + 8 * c) = load_x<XK>(a, min(m0 + r, a.M - 1), kbeg + 8 * c, row_inv(r));
+    }
+    __syncthreads();
+  }
+  auto xfrag = [&](int mt, int kk) -> u32x4 {   // kk: offset inside the K range
+    if (XL) return *(const u32x4*)(xs + (mt * 16 + lr) * ldl + kk + 8 * lg);
+    return load_x<XK>(a, min(m0 + mt * 16 + lr, a.M - 1), kbeg + kk + 8 * lg, row_inv(mt * 16 + lr));
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int c, const u32x4 (&w)[4]) {
     const bool ok = c < nchunks;
+    const int kk = 128 * min(c, nchunks - 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 xv = ok ? x[s][mt] : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16x16x32(as_bf16x8(xv), as_bf16x8(w[s][t]), acc[mt][t]);
+        u32x4 xv = xfrag(mt, kk + 32 * s);
+        if (!ok) xv = (u32x4){0u, 0u, 0u, 0u};
+        acc[mt] = mfma16x16x32(as_bf16x8(xv), as_bf16x8(w[s]), acc[mt]);
       }
   };
-  if (nchunks > 0) {
-    load(0, wA, xA);
-    for (int c = 0; c < nchunks; c += 2) {
-      load(c + 1, wB, xB);
-      compute(c, wA, xA);
-      if (c + 2 < nchunks) load(c + 2, wA, xA);
-      compute(c + 1, wB, xB);
-    }
+  for (int c = 0; c < nchunks; c += 2) {
+    load_w(c + 1, wB);
+    compute(c, wA);
+    if (c + 2 < nchunks) load_w(c + 2, wA);
+    compute(c + 1, wB);
   }
 
+  // ---- result tile in LDS (aliases the X slice, which is dead now)
+  __syncthreads();
+  float(*tile)[GC + 1] = (float(*)[GC + 1])smem;
   const int rows = min(ROWS, a.M - m0);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = tile_col<NT, PAIR>(wave, t) + lr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tile[mt * 16 + 4 * lg + i][col] = acc[mt][t][i];
-    }
+    for (int i = 0; i < 4; ++i) tile[mt * 16 + 4 * lg + i][tcol + lr] = acc[mt][i];
   __syncthreads();
 
   if (a.S > 1) {
-    // Split-K: publish this split's tile, the last workgroup of the group sums
-    // all splits in order s = 0..S-1.
     const size_t wg = (size_t)mz * gridDim.x + group;
     float* mine = a.partials + (wg * a.S + split) * (size_t)(ROWS * GC);
-    for (int e = threadIdx.x; e < rows * GC; e += blockDim.x) mine[e] = tile[e / GC][e % GC];
-    __threadfence();
+    const int n = rows * GC;
+    for (int e = threadIdx.x; e < n; e += blockDim.x)
+      __hip_atomic_store(mine + e, tile[e / GC][e % GC], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);          // partial stores complete before the count
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(&a.counters[wg], 1u);
-      const int last = (prev == (unsigned)(a.S - 1));
-      if (last) atomicExch(&a.counters[wg], 0u);
+      const unsigned prev = __hip_atomic_fetch_add(&a.counters[wg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (unsigned)(a.S - 1);
+      if (last) __hip_atomic_store(&a.counters[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_flag = last;
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
+    // every thread owns a few tile elements and has the loads of up to 16
+    // splits of all of them in flight at once: one memory round trip per 16 splits
     const float* base = a.partials + wg * a.S * (size_t)(ROWS * GC);
-    for (int e = threadIdx.x; e < rows * GC; e += blockDim.x) {
-      float s = 0.f;
-      for (int sp = 0; sp < a.S; ++sp) s += __builtin_nontemporal_load(base + (size_t)sp * ROWS * GC + e);
-      tile[e / GC][e % GC] = s;
+    constexpr int PER = (ROWS * GC + NW * 64 - 1) / (NW * 64);
+    float sum[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sum[u] = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += 16) {
+      float v[16][PER];
+#pragma unroll
+      for (int sp = 0; sp < 16; ++sp)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int e = threadIdx.x + u * NW * 64;
+          v[sp][u] = (s0 + sp < a.S && e < n)
+                         ? __hip_atomic_load(base + (size_t)(s0 + sp) * ROWS * GC + e, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
+        }
+#pragma unroll
+      for (int sp = 0; sp < 16; ++sp)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) sum[u] += v[sp][u];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = threadIdx.x + u * NW * 64;
+      if (e < n) tile[e / GC][e % GC] = sum[u];
     }
     __syncthreads();
   }
 
   // ---- epilogue on tile[0:rows][0:GC]
-  if (EPI == E_BF16 || EPI == E_F32 || EPI == E_RESID) {
+  if constexpr (EPI == E_BF16 || EPI == E_F32) {
     for (int e = threadIdx.x; e < rows * GC; e += blockDim.x) {
       const int r = e / GC, c = e % GC;
       const int n = group * GC + c;
       if (n >= a.N) continue;
       const size_t o = (size_t)(m0 + r) * a.ldo + n;
       if (EPI == E_BF16) ((uint16_t*)a.out)[o] = f2bfbits(tile[r][c]);
-      else if (EPI == E_F32) ((float*)a.out)[o] = tile[r][c];
-      else ((float*)a.out)[o] += tile[r][c];
+      else ((float*)a.out)[o] = tile[r][c];
     }
-  } else if (EPI == E_SILU) {
+  } else if constexpr (EPI == E_RESID) {
+    // h += Y; the updated values stay in the tile for the row sums of squares
+    for (int e = threadIdx.x; e < rows * GC; e += blockDim.x) {
+      const int r = e / GC, c = e % GC;
+      const int n = group * GC + c;
+      float hv = 0.f;
+      if (n < a.N) {
+        float* hp = (float*)a.out + (size_t)(m0 + r) * a.ldo + n;
+        hv = *hp + tile[r][c];
+        *hp = hv;
+      }
+      tile[r][c] = hv;
+    }
+    if (a.ssq_out) {
+      __syncthreads();
+      for (int r = wave; r < rows; r += NW) {
+        float ss = 0.f;
+        for (int c = lane; c < GC; c += 64) ss += tile[r][c] * tile[r][c];
+        ss = wave_sum(ss);
+        if (lane == 0) a.ssq_out[(size_t)group * a.ssq_ld + m0 + r] = ss;
+      }
+    }
+  } else if constexpr (EPI == E_SILU) {
     constexpr int LC = GC / 2;
     for (int e = threadIdx.x; e < rows * LC; e += blockDim.x) {
       const int r = e / LC, c = e % LC;
@@ -313,55 +406,62 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
       const float act = g / (1.0f + expf(-g)) * u;
       ((uint16_t*)a.out)[(size_t)(m0 + r) * a.ldo + n] = f2bfbits(act);
     }
-  } else if (EPI == E_HEAD) {
-    epi_head<ROWS, GC>(a, tile, m0, rows, a.head_base + group);
-  } else if (EPI == E_TOPK) {
-    epi_topk<ROWS, GC>(a, tile, m0, rows, group);
+  } else if constexpr (EPI == E_HEAD) {
+    epi_head<GC, NW>(a, tile, m0, rows, a.head_base + group);
+  } else if constexpr (EPI == E_TOPK) {
+    int(*tid)[GC] = (int(*)[GC])(smem + sizeof(float) * ROWS * (GC + 1));
+    epi_topk<ROWS, GC, NW>(a, tile, tid, m0, rows, group);
   }
 }
 
-template <int MT, int NT, int XK, int WF>
-hipError_t launch_epi(const GemmArgs& a, dim3 grid, int epi, hipStream_t st) {
+template <int MT, int NW, int XK, int XL, int EPI>
+void launch_one(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, XK, XL, EPI>), grid, dim3(NW * 64), lds, st, a);
+}
+
+template <int MT, int NW, int XL>
+hipError_t launch_x(const GemmArgs& a, dim3 grid, size_t lds, int xk, int epi, hipStream_t st) {
+  if (xk == X_TAPS) {
+    if (epi == E_BF16) launch_one<MT, NW, X_TAPS, XL, E_BF16>(a, grid, lds, st);
+    else if (epi == E_F32) launch_one<MT, NW, X_TAPS, XL, E_F32>(a, grid, lds, st);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (xk == X_NORM) {
+    switch (epi) {
+      case E_SILU: launch_one<MT, NW, X_NORM, XL, E_SILU>(a, grid, lds, st); break;
+      case E_HEAD: launch_one<MT, NW, X_NORM, XL, E_HEAD>(a, grid, lds, st); break;
+      case E_TOPK: launch_one<MT, NW, X_NORM, XL, E_TOPK>(a, grid, lds, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (epi) {
-    case E_BF16: hipLaunchKernelGGL((gemm_kernel<MT, NT, XK, E_BF16, WF>), grid, dim3(256), 0, st, a); break;
-    case E_F32: hipLaunchKernelGGL((gemm_kernel<MT, NT, XK, E_F32, WF>), grid, dim3(256), 0, st, a); break;
-    case E_RESID:
-      if (XK != X_BF16) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_kernel<MT, NT, X_BF16, E_RESID, WF>), grid, dim3(256), 0, st, a); break;
-    case E_SILU:
-      if (XK != X_BF16 || NT % 2) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_kernel<MT, (NT % 2 ? 2 : NT), X_BF16, E_SILU, WF>), grid, dim3(256), 0, st, a); break;
-    case E_HEAD:
-      if (XK != X_BF16) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_kernel<MT, NT, X_BF16, E_HEAD, WF>), grid, dim3(256), 0, st, a); break;
-    case E_TOPK:
-      if (XK != X_BF16) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_kernel<MT, NT, X_BF16, E_TOPK, WF>), grid, dim3(256), 0, st, a); break;
+    case E_BF16: launch_one<MT, NW, X_BF16, XL, E_BF16>(a, grid, lds, st); break;
+    case E_F32: launch_one<MT, NW, X_BF16, XL, E_F32>(a, grid, lds, st); break;
+    case E_RESID: launch_one<MT, NW, X_BF16, XL, E_RESID>(a, grid, lds, st); break;
+    case E_SILU: launch_one<MT, NW, X_BF16, XL, E_SILU>(a, grid, lds, st); break;
+    case E_HEAD: launch_one<MT, NW, X_BF16, XL, E_HEAD>(a, grid, lds, st); break;
+    case E_TOPK: launch_one<MT, NW, X_BF16, XL, E_TOPK>(a, grid, lds, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int MT, int NT>
-hipError_t launch_x(const GemmArgs& a, dim3 grid, int xk, int epi, int wf, hipStream_t st) {
-  if (wf != WF_BF16) return hipErrorInvalidValue;
-  if (xk == X_TAPS) {
-    if (epi != E_BF16 && epi != E_F32) return hipErrorInvalidValue;
-    if (epi == E_BF16)
-      hipLaunchKernelGGL((gemm_kernel<MT, NT, X_TAPS, E_BF16, WF_BF16>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<MT, NT, X_TAPS, E_F32, WF_BF16>), grid, dim3(256), 0, st, a);
-    return hipGetLastError();
-  }
-  return launch_epi<MT, NT, X_BF16, WF_BF16>(a, grid, epi, st);
+template <int MT, int NW>
+hipError_t launch_xl(const GemmArgs& a, dim3 grid, size_t lds, int xl, int xk, int epi, hipStream_t st) {
+  return xl ? launch_x<MT, NW, 1>(a, grid, lds, xk, epi, st) : launch_x<MT, NW, 0>(a, grid, lds, xk, epi, st);
 }
+
+constexpr size_t XL_MAX_BYTES = 96 * 1024;
 
 }  // namespace
 
 GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target) {
   GemmPlan p;
   p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.NT = gc / (GEMM_WAVES * 16);
+  p.NT = 1;
+  p.NW = gc / 16;
   const int cols_per_group = pair ? gc / 2 : gc;
   p.groups = (N + cols_per_group - 1) / cols_per_group;
   p.mz = (M + 16 * p.MT - 1) / (16 * p.MT);
@@ -372,8 +472,14 @@ GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target) {
   S = S > kchunks ? kchunks : S;
   S = S < 1 ? 1 : S;
   const int chunks_per = (kchunks + S - 1) / S;
+  const int rows = 16 * p.MT;
+  // stage X through LDS when the slice fits; otherwise fragments come from L2
+  p.XL = (size_t)rows * (chunks_per * 128 + 8) * 2 <= XL_MAX_BYTES;
   p.ks = chunks_per * 128;
   p.S = (K + p.ks - 1) / p.ks;
+  const size_t xbytes = p.XL ? (size_t)rows * (p.ks + 8) * 2 : 0;
+  const size_t tbytes = (size_t)rows * (gc + 1) * 4 + (size_t)rows * gc * 4;   // tile + top-k ids
+  p.lds = xbytes > tbytes ? xbytes : tbytes;
   return p;
 }
 
@@ -383,21 +489,22 @@ size_t gemm_partial_floats(const GemmPlan& p, int gc) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf, hipStream_t st) {
+  if (wf != WF_BF16) return hipErrorInvalidValue;
   const dim3 grid(p.groups, p.S, p.mz);
   GemmArgs b = a;
   b.ks = p.ks;
   b.S = p.S;
-#define DISPATCH_NT(MT)                                                   \
-  switch (p.NT) {                                                         \
-    case 1: return launch_x<MT, 1>(b, grid, xk, epi, wf, st);             \
-    case 2: return launch_x<MT, 2>(b, grid, xk, epi, wf, st);             \
-    default: return hipErrorInvalidValue;                                 \
+#define DISPATCH_NW(MT)                                                         \
+  switch (p.NW) {                                                               \
+    case 4: return launch_xl<MT, 4>(b, grid, p.lds, p.XL, xk, epi, st);          \
+    case 8: return launch_xl<MT, 8>(b, grid, p.lds, p.XL, xk, epi, st);          \
+    default: return hipErrorInvalidValue;                                       \
   }
   switch (p.MT) {
-    case 1: DISPATCH_NT(1)
-    case 2: DISPATCH_NT(2)
-    case 4: DISPATCH_NT(4)
+    case 1: DISPATCH_NW(1)
+    case 2: DISPATCH_NW(2)
+    case 4: DISPATCH_NW(4)
     default: return hipErrorInvalidValue;
   }
-#undef DISPATCH_NT
+#undef DISPATCH_NW
 }

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-enum XKind { X_BF16 = 0, X_TAPS = 1 };
+enum XKind { X_BF16 = 0, X_TAPS = 1, X_NORM = 2 };
 enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4, E_TOPK = 5 };
 enum WFmt { WF_BF16 = 0, WF_INT4 = 1 };
 
@@ -12,9 +12,17 @@ constexpr int GEMM_WAVES = 4;
 
 // Arguments of the skinny GEMM Y[M, N] = X[M, K] . W[N, K]^T with a fused epilogue.
 struct GemmArgs {
-  // X operand: bf16 rows (X_BF16) or fp32 tap rows reduced on the fly (X_TAPS)
+  // X operand: bf16 rows (X_BF16), fp32 tap rows reduced on the fly (X_TAPS),
+  // or the fp32 residual normalized on the fly (X_NORM: x = h * rsqrt(ss/K + eps) * g,
+  // ss = sum over the n_ssq column blocks of ssq_in[block * ssq_ld + row])
   const uint16_t* x;
   long long ldx;
+  const float* xf;
+  const uint16_t* xgain;
+  const float* ssq_in;
+  int n_ssq;
+  int ssq_ld;
+  float* ssq_out;   // E_RESID: per-row sum of squares of the updated h, one entry per column group
   const float* taps[MAX_TAPS];
   long long tap_stride;
   int n_taps, hc, tap_hidden;
@@ -53,7 +61,8 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-  int MT, NT, S, ks, groups, mz;
+  int MT, NT, NW, XL, S, ks, groups, mz;
+  size_t lds;   // dynamic LDS bytes per workgroup
 };
 
 GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target);
@@ -81,14 +90,13 @@ int attn_slots(int nq, int nkv, int B);
 
 // Small kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
-hipError_t launch_embed_norm(const int* tokens, const uint16_t* embed, const uint16_t* gain,
-                             float* h, uint16_t* a, int M, int H, int V, float eps,
-                             unsigned* err, hipStream_t st);
+hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, float* ssq, int M, int H,
+                        int V, unsigned* err, hipStream_t st);
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* a, int M, int H,
                           float eps, hipStream_t st);
 hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hipStream_t st);
 hipError_t launch_topk_merge(const float* cand_val, const int* cand_idx, int groups, int rows,
-                             int k, int* ids, float* vals, hipStream_t st);
+                             int k, float* mid_v, int* mid_i, int* ids, float* vals, hipStream_t st);
 hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B,
                          int eos, const int* budget, int mask_id, int* accept_len,
                          int* emitted, int* n_emit, int* next_tokens, int* pos,

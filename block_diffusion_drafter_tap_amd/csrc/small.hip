@@ -23,11 +23,10 @@ DEV float block_sum(float v, float* red) {
   return t;
 }
 
-// One workgroup per row: h = E[token] (fp32), a = bf16(RMSNorm(h) * gain).
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int* tokens, const uint16_t* embed,
-                                                         const uint16_t* gain, float* h,
-                                                         uint16_t* a, int H, int V, float eps,
-                                                         unsigned* err) {
+// One workgroup per row: h = E[token] (fp32) and the row's sum of squares,
+// which the first QKV projection turns into its input RMSNorm.
+__global__ __launch_bounds__(256) void embed_kernel(const int* tokens, const uint16_t* embed, float* h,
+                                                    float* ssq, int H, int V, unsigned* err) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   int tok = tokens[m];
@@ -43,9 +42,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int* tokens, cons
     ss += v * v;
   }
   ss = block_sum(ss, red);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int k = threadIdx.x; k < H; k += blockDim.x)
-    a[(size_t)m * H + k] = f2bfbits(bfbits2f(e[k]) * inv * bfbits2f(gain[k]));
+  if (threadIdx.x == 0) ssq[m] = ss;
 }
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const uint16_t* gain,
@@ -68,63 +65,63 @@ __global__ void set_pos_kernel(int* pos, int* valid_from, int req, int vf, int p
   }
 }
 
-// Merge per-group candidate lists (each sorted best-first) into the top-k of a
-// row, ordered by (value desc, index asc). One workgroup per row; each thread
-// keeps a sorted private list over a strided subset of groups (stopping inside
-// a group at the first candidate that cannot enter its list), then the 256
-// lists are merged pairwise in shared memory.
-constexpr int KMAX = 16;
-
+// Top-k merge. Candidate lists (each sorted best first by (value desc, index
+// asc), all keys distinct) are merged pairwise in a tree held in LDS. A pair of
+// sorted lists A, B merges in one parallel step: element A[e] lands at output
+// rank e + #{B entries better than A[e]} (a binary search), likewise for B, and
+// only ranks below k are kept. One workgroup merges up to 64 lists of one row;
+// list l of row r is read at in + (l * list_stride + r * row_stride) * k.
+// Missing lists are padded with -inf entries carrying distinct ids.
 template <int K>
-__global__ __launch_bounds__(256) void topk_merge_kernel(const float* cand_val, const int* cand_idx,
-                                                         int groups, int rows, int* ids, float* vals) {
-  __shared__ float sv[256][K];
-  __shared__ int si[256][K];
-  const int row = blockIdx.x;
-  float lv[K];
-  int li[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
-  for (int gr = threadIdx.x; gr < groups; gr += blockDim.x) {
-    const float* cv = cand_val + ((size_t)gr * rows + row) * K;
-    const int* ci = cand_idx + ((size_t)gr * rows + row) * K;
-    for (int j = 0; j < K; ++j) {
-      float v = cv[j];
-      int id = ci[j];
-      if (!better(v, id, lv[K - 1], li[K - 1])) break;
-#pragma unroll
-      for (int q = 0; q < K; ++q) {
-        if (better(v, id, lv[q], li[q])) {
-          const float tv = lv[q];
-          const int ti = li[q];
-          lv[q] = v; li[q] = id;
-          v = tv; id = ti;
-        }
-      }
+__global__ __launch_bounds__(256) void topk_merge_kernel(const float* in_v, const int* in_i, int n_lists,
+                                                         long long list_stride, long long row_stride,
+                                                         float* out_v, int* out_i, long long out_row_stride) {
+  __shared__ float bv[2][64][K];
+  __shared__ int bi[2][64][K];
+  const int row = blockIdx.x, blk = blockIdx.y;
+  const int l0 = blk * 64;
+  const int nl = min(64, n_lists - l0);
+  int width = 1;
+  while (width < nl) width <<= 1;
+  for (int e = threadIdx.x; e < width * K; e += blockDim.x) {
+    const int l = e / K, j = e % K;
+    if (l < nl) {
+      const size_t o = ((size_t)(l0 + l) * list_stride + (size_t)row * row_stride) * K + j;
+      bv[0][l][j] = in_v[o];
+      bi[0][l][j] = in_i[o];
+    } else {
+      bv[0][l][j] = -INFINITY;
+      bi[0][l][j] = 0x7fffffff - e;
     }
   }
-#pragma unroll
-  for (int j = 0; j < K; ++j) { sv[threadIdx.x][j] = lv[j]; si[threadIdx.x][j] = li[j]; }
   __syncthreads();
-  for (int width = 128; width >= 1; width >>= 1) {
-    if ((int)threadIdx.x < width) {
-      const int a = threadIdx.x, b = threadIdx.x + width;
-      float ov[K];
-      int oi[K];
-      int ia = 0, ib = 0;
-      for (int j = 0; j < K; ++j) {
-        const bool ta = better(sv[a][ia], si[a][ia], sv[b][ib], si[b][ib]);
-        ov[j] = ta ? sv[a][ia] : sv[b][ib];
-        oi[j] = ta ? si[a][ia] : si[b][ib];
-        if (ta) ++ia; else ++ib;
+  int cur = 0;
+  for (; width > 1; width >>= 1) {
+    const int pairs = width / 2;
+    for (int t = threadIdx.x; t < pairs * 2 * K; t += blockDim.x) {
+      const int p = t / (2 * K), e = t % (2 * K);
+      const int own = e < K ? 2 * p : 2 * p + 1, oth = e < K ? 2 * p + 1 : 2 * p;
+      const int idx = e < K ? e : e - K;
+      const float x = bv[cur][own][idx];
+      const int xi = bi[cur][own][idx];
+      int lo = 0, hi = K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (better(bv[cur][oth][mid], bi[cur][oth][mid], x, xi)) lo = mid + 1; else hi = mid;
       }
-      for (int j = 0; j < K; ++j) { sv[a][j] = ov[j]; si[a][j] = oi[j]; }
+      const int rank = idx + lo;
+      if (rank < K) {
+        bv[cur ^ 1][p][rank] = x;
+        bi[cur ^ 1][p][rank] = xi;
+      }
     }
     __syncthreads();
+    cur ^= 1;
   }
   if ((int)threadIdx.x < K) {
-    ids[(size_t)row * K + threadIdx.x] = si[0][threadIdx.x];
-    if (vals) vals[(size_t)row * K + threadIdx.x] = sv[0][threadIdx.x];
+    const size_t o = (size_t)row * out_row_stride + (size_t)blk * K + threadIdx.x;
+    if (out_v) out_v[o] = bv[cur][0][threadIdx.x];
+    out_i[o] = bi[cur][0][threadIdx.x];
   }
 }
 
@@ -182,9 +179,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_embed_norm(const int* tokens, const uint16_t* embed, const uint16_t* gain, float* h,
-                             uint16_t* a, int M, int H, int V, float eps, unsigned* err, hipStream_t st) {
-  hipLaunchKernelGGL(embed_norm_kernel, dim3(M), dim3(256), 0, st, tokens, embed, gain, h, a, H, V, eps, err);
+hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, float* ssq, int M, int H, int V,
+                        unsigned* err, hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, embed, h, ssq, H, V, err);
   return hipGetLastError();
 }
 
@@ -200,10 +197,19 @@ hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hip
 }
 
 hipError_t launch_topk_merge(const float* cand_val, const int* cand_idx, int groups, int rows, int k,
-                             int* ids, float* vals, hipStream_t st) {
-  if (k == 1) hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(rows), dim3(256), 0, st, cand_val, cand_idx, groups, rows, ids, vals);
-  else if (k == 16) hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(rows), dim3(256), 0, st, cand_val, cand_idx, groups, rows, ids, vals);
+                             float* mid_v, int* mid_i, int* ids, float* vals, hipStream_t st) {
+  const int nblk = (groups + 63) / 64;
+  if (nblk > 64) return hipErrorInvalidValue;
+  // stage 1: blocks of 64 group lists -> one list per block; stage 2: the block lists -> top-k
+#define MERGE(KK)                                                                                        \
+  hipLaunchKernelGGL((topk_merge_kernel<KK>), dim3(rows, nblk), dim3(256), 0, st, cand_val, cand_idx,    \
+                     groups, (long long)rows, 1ll, mid_v, mid_i, (long long)nblk * KK);                   \
+  hipLaunchKernelGGL((topk_merge_kernel<KK>), dim3(rows, 1), dim3(256), 0, st, (const float*)mid_v,      \
+                     (const int*)mid_i, nblk, 1ll, (long long)nblk, vals, ids, (long long)KK);
+  if (k == 1) { MERGE(1) }
+  else if (k == 16) { MERGE(16) }
   else return hipErrorInvalidValue;
+#undef MERGE
   return hipGetLastError();
 }
 
