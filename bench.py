@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
+COPY_BYTES = 512 << 20   # calibration copy read (and written) once before warm-up
 
 WORKLOADS = {
     # name: (config builder kwargs, requests, k, description)
@@ -164,6 +165,13 @@ def main():
         dr.accept(ids, k, verify, out=out)
 
     stage_bufs = [torch.empty((R * B, row_stride), dtype=torch.float32, device=dev) for _ in range(cfg.n_taps)]
+
+    # a plain device copy of known size, so HBM byte counters of a profiled run can be
+    # scaled: counter(copy) / 2 * COPY_BYTES is what the counters report for that traffic
+    calib_src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    del calib_src, calib_dst
 
     # dominant kernel timing: HIP events around every LM-head launch in the timed region
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]

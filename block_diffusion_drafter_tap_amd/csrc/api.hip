@@ -25,35 +25,35 @@ int fail(int code, const char* fmt, ...) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int CU_TARGET = 256;   // workgroups (of 8 waves) wanted per weight-streaming GEMM
+constexpr int CU_GATEUP = 512;   // gate/up measured faster with more, shorter K splits
 constexpr int GC_DEFAULT = 128;
 
-int attn_chunk(const dflash_config& c) { return c.window <= 256 ? 64 : 256; }
 int attn_nchunks(const dflash_config& c) {
-  const int kc = attn_chunk(c);
+  const int kc = attn_chunk_keys();
   return (c.window + c.block + 31 + kc - 1) / kc;
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, c32, c, partials, counters, attn_o, attn_ml, attn_cnt, cand_v, cand_i, mid_v, mid_i, total;
+  size_t h, ssq, q, o, act, c32, c, partials, counters, attn_o, attn_ml, cand_v, cand_i, mid_v, mid_i, total;
   size_t n_counters;
 };
 
 struct GemmShape {
-  int N, K, gc, pair;
+  int N, K, gc, pair, cu;
 };
 
 // Largest split-K scratch and counter count over every GEMM a call may launch.
 void gemm_scratch(const dflash_config& c, size_t* part_floats, size_t* counters) {
   const int H = c.hidden, hd = c.head_dim;
-  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0},
-                             {H, c.n_q_heads * hd, GC_DEFAULT, 0},
-                             {c.ffn, H, GC_DEFAULT, 1},
-                             {H, c.ffn, GC_DEFAULT, 0}};
-  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0},
-                             {2 * c.n_kv_heads * hd, H, hd, 0}};
+  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, CU_TARGET},
+                             {H, c.n_q_heads * hd, GC_DEFAULT, 0, CU_TARGET},
+                             {c.ffn, H, GC_DEFAULT, 1, CU_GATEUP},
+                             {H, c.ffn, GC_DEFAULT, 0, CU_TARGET}};
+  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, CU_TARGET},
+                             {2 * c.n_kv_heads * hd, H, hd, 0, CU_TARGET}};
   size_t pf = 0, cn = 0;
   auto visit = [&](int M, const GemmShape& s) {
-    GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, CU_TARGET);
+    GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, s.cu);
     size_t f = gemm_partial_floats(p, s.gc);
     if (f > pf) pf = f;
     if (p.S > 1 && (size_t)p.groups * p.mz > cn) cn = (size_t)p.groups * p.mz;
@@ -92,7 +92,6 @@ WsLayout ws_layout(const dflash_config& c) {
   L.n_counters = cn;
   L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
   L.attn_ml = take(lrg * nch * slots * 2 * 4);
-  L.attn_cnt = take(lrg * 4);
   L.cand_v = take(lm_groups * out_rows * 16 * 4);
   L.cand_i = take(lm_groups * out_rows * 16 * 4);
   const size_t nblk = (lm_groups + 63) / 64;
@@ -145,6 +144,9 @@ int validate_config(const dflash_config* c) {
     return fail(DFLASH_E_UNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", c->head_dim);
   if (c->hidden % 128 || c->ffn % 128 || (c->n_q_heads * c->head_dim) % 128)
     return fail(DFLASH_E_UNSUPPORTED, "hidden, ffn and n_q_heads*head_dim must be multiples of 128");
+  if (c->max_requests * c->block > 64)
+    return fail(DFLASH_E_UNSUPPORTED, "max_requests * block = %d block rows; the LM-head kernel holds at most 64",
+                c->max_requests * c->block);
   if (attn_slots(c->n_q_heads, c->n_kv_heads, c->block) > 64)
     return fail(DFLASH_E_UNSUPPORTED, "(n_q_heads/n_kv_heads)*block = %d query rows per kv head; at most 64",
                 attn_slots(c->n_q_heads, c->n_kv_heads, c->block));
@@ -172,6 +174,7 @@ struct dflash_ctx {
   char* ws = nullptr;
   dflash_state_layout sl;
   WsLayout wl;
+  int n_cu = 256;   // compute units of the bound device (read at bind)
   Timing timing[DFLASH_K_COUNT];
 };
 
@@ -321,6 +324,10 @@ int dflash_bind(dflash_ctx* ctx, void* state, void* workspace, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   ctx->state = (char*)state;
   ctx->ws = (char*)workspace;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+    ctx->n_cu = ncu;
   hipError_t e = launch_fill_zero(state, ctx->sl.total, st);
   if (e == hipSuccess) e = launch_fill_zero(workspace, ctx->wl.total, st);
   if (e != hipSuccess) return hip_fail(e, "bind fill");
@@ -484,12 +491,11 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       t.nq = g.n_q_heads;
       t.nkv = g.n_kv_heads;
       t.hd = hd;
-      t.kc = attn_chunk(g);
+      t.kc = attn_chunk_keys();
       t.n_chunks = attn_nchunks(g);
       t.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
       t.part_o = at<float>(ctx->ws, ctx->wl.attn_o);
       t.part_ml = at<float>(ctx->ws, ctx->wl.attn_ml);
-      t.counters = at<unsigned>(ctx->ws, ctx->wl.attn_cnt);
       t.err = err;
       Timed tm(ctx, DFLASH_K_ATTN, st);
       e = launch_attention(t, n_req, st);
@@ -522,7 +528,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.pair_off = g.ffn;
       a.out = act;
       a.ldo = g.ffn;
-      GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CU_TARGET);
+      GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CU_GATEUP);
       Timed tm(ctx, DFLASH_K_GATEUP, st);
       e = launch_gemm(a, p, X_NORM, E_SILU, WF_BF16, st);
       if (e != hipSuccess) return hip_fail(e, "gate/up");
@@ -556,13 +562,13 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
     a.logits = logits;
     a.cand_val = at<float>(ctx->ws, ctx->wl.cand_v);
     a.cand_idx = at<int>(ctx->ws, ctx->wl.cand_i);
-    GemmPlan p = plan_gemm(M, g.vocab, H, GC_DEFAULT, 0, 0);
+    LmPlan p = plan_lmhead(M, g.vocab, H, ctx->n_cu);
     {
       Timed tm(ctx, DFLASH_K_LMHEAD, st);
-      e = launch_gemm(a, p, X_NORM, E_TOPK, WF_BF16, st);
+      e = launch_lmhead(a, p, st);
     }
     if (e != hipSuccess) return hip_fail(e, "lm head");
-    e = launch_topk_merge(a.cand_val, a.cand_idx, p.groups, n_req * (B - 1), k, at<float>(ctx->ws, ctx->wl.mid_v),
+    e = launch_topk_merge(a.cand_val, a.cand_idx, p.P, n_req * (B - 1), k, at<float>(ctx->ws, ctx->wl.mid_v),
                           at<int>(ctx->ws, ctx->wl.mid_i), topk_ids, topk_vals, st);
     if (e != hipSuccess) return hip_fail(e, "topk merge");
   }

@@ -4,188 +4,228 @@
 // block's own K/V were written to slots pos..pos+B-1 by the QKV epilogue), so a
 // query sees one contiguous position range [lo, pos+B).
 //
-// Workgroup = (key chunk, kv head, request). Its waves hold the G*B queries of
-// the kv head's query-head group, 16 per wave (one MFMA tile). Per 32-key
-// sub-tile a wave computes S^T = K Q^T (MFMA, keys x queries), runs the online
-// softmax in registers, and accumulates O^T = V^T P^T (MFMA, head_dim x queries,
-// with P split into two bf16 terms).
+// Workgroup = (key chunk of 128, kv head, request), four waves, in two phases
+// with an exact softmax inside the chunk:
+//  1. wave w takes the chunk's 32-key sub-tile w and computes S^T = K Q^T for
+//     all G*B queries of the kv head's query-head group (MFMA, keys x queries,
+//     Q staged in LDS). The chunk max of every query comes from a 4-entry LDS
+//     exchange; the wave then forms P = 2^(S - M) in registers and parks it in
+//     LDS as two bf16 terms (hi + lo keep ~16 significant bits).
+//  2. wave w owns head_dim tiles w*HD/64 ..: it accumulates O^T = V^T P^T over
+//     the four sub-tiles (MFMA, head_dim x queries) and writes its rows of the
+//     chunk partial straight from the accumulators.
+// All K/V loads of a wave are issued before the first MFMA, so a chunk's 64 KB
+// is in flight at once; no wave holds more than two head_dim tiles of O.
 // The ring keeps V transposed ([hd][C]) so that both MFMA operands are 16-byte
 // loads. Keys of the two 16-row S^T tiles are permuted so that after the first
 // MFMA each lane group already holds the 8 consecutive keys the second MFMA
 // needs as its k-values (no cross-lane shuffles between the two products).
 //
-// Chunks of one (request, kv head) write partial (max, sum, O) to scratch and a
-// second kernel combines them in chunk order, so results do not depend on
-// scheduling.
+// A second kernel combines the chunk partials in chunk order, so results do not
+// depend on scheduling. Both kernels use a 1-D grid whose workgroup id is
+// chunk * (R*nkv) + (request, head): workgroups are dealt to the 8 XCDs round
+// robin, so with R*nkv a multiple of 8 every chunk of one head lands on the
+// same XCD and the combine reads its partials from that XCD's L2.
 #include "device.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int HD_MAX = 128;
+constexpr int ATT_WAVES = 4;
+constexpr int ATT_KC = 32 * ATT_WAVES;   // keys per chunk
 
-template <int HD>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
-  constexpr int HT = HD / 16;   // O^T tiles along head_dim
-  constexpr int QS = HD / 32;   // MFMA k-steps along head_dim
+struct Range {
+  int lo, hi, base, n_ch;
+};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int chunk = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int nwaves = blockDim.x >> 6;
-  const int G = a.nq / a.nkv;
-  const int slots = G * a.B;
-
-  int pos = a.pos[r], vf = a.valid_from[r];
+// [lo, hi): keys a block query sees; chunks start at base = lo rounded down to 32.
+DEV Range key_range(const AttnArgs& a, int r, bool report) {
+  const int pos = a.pos[r];
+  int vf = a.valid_from[r];
   if (vf > pos) {
-    if (threadIdx.x == 0 && chunk == 0 && g == 0) set_error(a.err, 2u);
+    if (report) set_error(a.err, 2u);
     vf = pos;
   }
   int lo = pos - a.W;
   lo = lo > vf ? lo : vf;
   lo = lo > 0 ? lo : 0;
-  const int hi = pos + a.B;
-  const int base = lo & ~31;
-  const int n_ch = (hi - base + a.kc - 1) / a.kc;
-  if (chunk >= n_ch) return;
-  const int kb = base + chunk * a.kc;
-  const int ke = min(kb + a.kc, hi);
+  Range g;
+  g.lo = lo;
+  g.hi = pos + a.B;
+  g.base = lo & ~31;
+  g.n_ch = (g.hi - g.base + ATT_KC - 1) / ATT_KC;
+  return g;
+}
 
-  const size_t lrg = (size_t)r * a.nkv + g;
-  const uint16_t* rk = a.ring_k + lrg * (size_t)a.C * HD;
-  const uint16_t* rv = a.ring_v + lrg * (size_t)HD * a.C;
+template <int HD, int QT>
+__global__ __launch_bounds__(64 * ATT_WAVES) void attn_kernel(const AttnArgs a) {
+  constexpr int QS = HD / 32;              // MFMA k-steps along head_dim
+  constexpr int HTW = HD / 16 / ATT_WAVES; // O^T head_dim tiles per wave
+  constexpr int NSL = QT * 16;             // query slots (padded to whole tiles)
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[NSL][HD + 8];
+  __shared__ u32x4 s_p[ATT_WAVES][QT][2][64];
+  __shared__ float s_mx[ATT_WAVES][NSL], s_l[ATT_WAVES][NSL];
 
-  // this wave's 16 query slots; slot = h_local * B + i
-  const int slot = wave * 16 + lr;
-  const bool qvalid = slot < slots;
-  const int hq = qvalid ? slot / a.B : 0, iq = qvalid ? slot % a.B : 0;
-  const uint16_t* qrow = a.q + ((size_t)r * a.B + iq) * a.nq * HD + (size_t)(g * G + hq) * HD;
-  bf16x8 qf[QS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int RN = a.R * a.nkv;
+  const int lrg = blockIdx.x % RN, chunk = blockIdx.x / RN;
+  const int r = lrg / a.nkv, g = lrg % a.nkv;
+  const int G = a.nq / a.nkv;
+  const int slots = G * a.B;
+
+  const Range kr = key_range(a, r, threadIdx.x == 0 && chunk == 0 && g == 0);
+  if (chunk >= kr.n_ch) return;
+  const int kb = kr.base + chunk * ATT_KC;
+
+  const uint16_t* rk = a.ring_k + (size_t)lrg * a.C * HD;
+  const uint16_t* rv = a.ring_v + (size_t)lrg * HD * a.C;
+
+  // issue every K/V load of this wave first
+  const int k0 = kb + 32 * wave;
+  const bool live = k0 < kr.hi;
+  u32x4 kf[2][QS];
 #pragma unroll
-  for (int s = 0; s < QS; ++s) {
-    u32x4 v = ld16(qrow + 32 * s + 8 * lg);
-    if (!qvalid) v = (u32x4){0u, 0u, 0u, 0u};
-    qf[s] = as_bf16x8(v);
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = k0 + 8 * (lr >> 2) + 4 * kt + (lr & 3);
+    const uint16_t* kp = rk + (size_t)(key % a.C) * HD + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) kf[kt][s] = live ? ld16(kp + 32 * s) : (u32x4){0u, 0u, 0u, 0u};
+  }
+  u32x4 vf[ATT_WAVES][HTW];
+#pragma unroll
+  for (int sb = 0; sb < ATT_WAVES; ++sb) {
+    const int ks = kb + 32 * sb;
+    const int vslot = (ks + 8 * lg) % a.C;
+#pragma unroll
+    for (int tt = 0; tt < HTW; ++tt) {
+      const int t = wave * HTW + tt;
+      vf[sb][tt] = ks < kr.hi ? ld16(rv + (size_t)(16 * t + lr) * a.C + vslot) : (u32x4){0u, 0u, 0u, 0u};
+    }
   }
 
-  f32x4 o[HT];
-#pragma unroll
-  for (int t = 0; t < HT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // K / V fragments of one 32-key sub-tile; the next sub-tile's are loaded
-  // while the current one is computed.
-  u32x4 kA[2][QS], vA[HT], kB[2][QS], vB[HT];
-  auto load = [&](int k0, u32x4 (&kf)[2][QS], u32x4 (&vf)[HT]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = k0 + 8 * (lr >> 2) + 4 * kt + (lr & 3);
-      const uint16_t* kp = rk + (size_t)(key % a.C) * HD + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < QS; ++s) kf[kt][s] = ld16(kp + 32 * s);
+  // Q of all G*B query slots (slot = h_local * B + i); zero rows pad the last tile
+  for (int e = threadIdx.x; e < NSL * (HD / 8); e += blockDim.x) {
+    const int slot = e / (HD / 8), c = e % (HD / 8);
+    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+    if (slot < slots) {
+      const int hq = slot / a.B, iq = slot % a.B;
+      v = ld16(a.q + ((size_t)r * a.B + iq) * a.nq * HD + (size_t)(g * G + hq) * HD + 8 * c);
     }
-    const int vslot = (k0 + 8 * lg) % a.C;
+    *(u32x4*)&s_q[slot][8 * c] = v;
+  }
+  __syncthreads();
+
+  // phase 1: scores of sub-tile `wave`; lane holds, for query slot qt*16 + lr,
+  // keys k0 + 8*lg + e (e = 4*kt + i)
+  float p[QT][8];
+  const bool interior = k0 >= kr.lo && k0 + 32 <= kr.hi;
 #pragma unroll
-    for (int t = 0; t < HT; ++t) vf[t] = ld16(rv + (size_t)(16 * t + lr) * a.C + vslot);
-  };
-  auto compute = [&](int k0, const u32x4 (&kf)[2][QS], const u32x4 (&vf)[HT]) {
-    // S^T for keys k0 + 8*(rr/4) + 4*kt + rr%4 (rr = row of the tile)
-    f32x4 sc[2];
+  for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < QS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qf[s], acc);
-      sc[kt] = acc;
-    }
-    // lane holds, for query lr, keys k0 + 8*lg + e (e = 4*kt + i)
-    float p[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int s = 0; s < QS; ++s)
+        acc = mfma16x16x32(as_bf16x8(kf[kt][s]), as_bf16x8(*(const u32x4*)&s_q[qt * 16 + lr][32 * s + 8 * lg]),
+                           acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 8 * lg + 4 * kt + i;
-        const bool ok = key >= lo && key < hi;
-        const float v = ok ? sc[kt][i] * a.scale_log2 : -INFINITY;
-        p[4 * kt + i] = v;
-        mx = fmaxf(mx, v);
+        const bool ok = interior || (key >= kr.lo && key < kr.hi);
+        p[qt][4 * kt + i] = ok ? acc[i] * a.scale_log2 : -INFINITY;
       }
+    }
+    float mx = p[qt][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[qt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
+    if (lg == 0) s_mx[wave][qt * 16 + lr] = mx;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(p[e] - m_use);
-      psum += p[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // P enters the MFMA as two bf16 terms, P = hi + lo (about 16 significant
-    // bits), so the probabilities are not rounded to 8 bits.
+  for (int qt = 0; qt < QT; ++qt) {
+    const int sl = qt * 16 + lr;
+    float M = s_mx[0][sl];
+#pragma unroll
+    for (int w = 1; w < ATT_WAVES; ++w) M = fmaxf(M, s_mx[w][sl]);
+    const float m_use = M == -INFINITY ? 0.f : M;
+    float psum = 0.f;
     u32x4 ph, pl;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float h0 = bf2f(f2bf(p[2 * e])), h1 = bf2f(f2bf(p[2 * e + 1]));
+      const float p0 = exp2f(p[qt][2 * e] - m_use), p1 = exp2f(p[qt][2 * e + 1] - m_use);
+      psum += p0 + p1;
+      const float h0 = bf2f(f2bf(p0)), h1 = bf2f(f2bf(p1));
       ph[e] = pack_bf16x2(h0, h1);
-      pl[e] = pack_bf16x2(p[2 * e] - h0, p[2 * e + 1] - h1);
+      pl[e] = pack_bf16x2(p0 - h0, p1 - h1);
     }
-    const bf16x8 pf_hi = as_bf16x8(ph), pf_lo = as_bf16x8(pl);
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      o[t] *= alpha;
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf_hi, o[t]);
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf_lo, o[t]);
-    }
-  };
-  load(kb, kA, vA);
-  for (int k0 = kb; k0 < ke; k0 += 64) {
-    const bool more = k0 + 32 < ke;
-    if (more) load(k0 + 32, kB, vB);
-    compute(k0, kA, vA);
-    if (!more) break;
-    if (k0 + 64 < ke) load(k0 + 64, kA, vA);
-    compute(k0 + 32, kB, vB);
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    if (lg == 0) s_l[wave][sl] = psum;
+    s_p[wave][qt][0][lane] = ph;
+    s_p[wave][qt][1][lane] = pl;
   }
-  // full softmax denominator of query lr: sum over the four lane groups
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  __syncthreads();
 
-  // partial state of this chunk: o[t][i] = O^T[hd = 16t + 4*lg + i][query lr]
-  const size_t cbase = (lrg * a.n_chunks + chunk) * (size_t)slots;
-  if (qvalid) {
-    float* po = a.part_o + (cbase + slot) * HD;
+  // phase 2: O^T tiles of this wave's head_dim rows over the chunk's sub-tiles
+  f32x4 o[QT][HTW];
 #pragma unroll
-    for (int t = 0; t < HT; ++t) *(f32x4*)(po + 16 * t + 4 * lg) = o[t];
-    if (lg == 0) {
-      a.part_ml[(cbase + slot) * 2] = m_run;
-      a.part_ml[(cbase + slot) * 2 + 1] = l_run;
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int tt = 0; tt < HTW; ++tt) o[qt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sb = 0; sb < ATT_WAVES; ++sb) {
+    if (kb + 32 * sb >= kr.hi) break;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const bf16x8 ph = as_bf16x8(s_p[sb][qt][0][lane]), pl = as_bf16x8(s_p[sb][qt][1][lane]);
+#pragma unroll
+      for (int tt = 0; tt < HTW; ++tt) {
+        o[qt][tt] = mfma16x16x32(as_bf16x8(vf[sb][tt]), ph, o[qt][tt]);
+        o[qt][tt] = mfma16x16x32(as_bf16x8(vf[sb][tt]), pl, o[qt][tt]);
+      }
     }
   }
-  (void)nwaves;
+
+  // chunk partial: O (relative to the chunk max M), M, L
+  const size_t cbase = ((size_t)lrg * a.n_chunks + chunk) * slots;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int sl = qt * 16 + lr;
+    if (sl < slots) {
+#pragma unroll
+      for (int tt = 0; tt < HTW; ++tt)
+        *(f32x4*)(a.part_o + (cbase + sl) * HD + 16 * (wave * HTW + tt) + 4 * lg) = o[qt][tt];
+    }
+  }
+  for (int sl = threadIdx.x; sl < slots; sl += blockDim.x) {
+    float M = s_mx[0][sl], L = s_l[0][sl];
+#pragma unroll
+    for (int w = 1; w < ATT_WAVES; ++w) {
+      M = fmaxf(M, s_mx[w][sl]);
+      L += s_l[w][sl];
+    }
+    a.part_ml[(cbase + sl) * 2] = M;
+    a.part_ml[(cbase + sl) * 2 + 1] = L;
+  }
 }
 
 // Combine the chunk partials of one (request, kv head): O = sum_c w_c O_c with
 // w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c, in chunk order. Each thread owns
-// four consecutive head_dim values of one query slot.
+// four consecutive head_dim values of one query slot; workgroup id =
+// part * (R*nkv) + (request, head), the attention kernel's XCD mapping.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
-  const int lrg = blockIdx.x;
+__global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs a) {
+  const int RN = a.R * a.nkv;
+  const int lrg = blockIdx.x % RN, part = blockIdx.x / RN;
   const int r = lrg / a.nkv, g = lrg % a.nkv;
   const int G = a.nq / a.nkv, slots = G * a.B;
-  const int e = blockIdx.y * blockDim.x + threadIdx.x;   // float4 index within [slots][HD/4]
+  const int e = part * 64 + threadIdx.x;   // float4 index within [slots][HD/4]
   if (e >= slots * HD / 4) return;
   const int s = e / (HD / 4), d4 = e % (HD / 4);
-  int pos = a.pos[r], vf = a.valid_from[r];
-  vf = vf > pos ? pos : vf;
-  int lo = pos - a.W;
-  lo = lo > vf ? lo : vf;
-  lo = lo > 0 ? lo : 0;
-  const int base = lo & ~31;
-  const int n_ch = (pos + a.B - base + a.kc - 1) / a.kc;
+  const int n_ch = key_range(a, r, false).n_ch;
   const size_t c0 = (size_t)lrg * a.n_chunks * slots;
   const float2* ml = (const float2*)a.part_ml;
   float M = -INFINITY;
@@ -210,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float wgt = exp2f(v[u].x - M);
+      const float wgt = v[u].x == -INFINITY ? 0.f : exp2f(v[u].x - M);
       L += wgt * v[u].y;
       acc += wgt * ov[u];
     }
@@ -224,24 +264,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   *(u32x2*)op = w;
 }
 
+template <int HD, int QT>
+void launch_hd(const AttnArgs& a, hipStream_t st) {
+  const int RN = a.R * a.nkv;
+  const int slots = attn_slots(a.nq, a.nkv, a.B);
+  const int parts = (slots * HD / 4 + 63) / 64;
+  hipLaunchKernelGGL((attn_kernel<HD, QT>), dim3(a.n_chunks * RN), dim3(64 * ATT_WAVES), 0, st, a);
+  hipLaunchKernelGGL((attn_combine_kernel<HD>), dim3(parts * RN), dim3(64), 0, st, a);
+}
+
 }  // namespace
 
 int attn_slots(int nq, int nkv, int B) { return (nq / nkv) * B; }
+int attn_chunk_keys() { return ATT_KC; }
 
-hipError_t launch_attention(const AttnArgs& a, int R, hipStream_t st) {
+hipError_t launch_attention(const AttnArgs& args, int R, hipStream_t st) {
+  AttnArgs a = args;
+  a.R = R;
   const int slots = attn_slots(a.nq, a.nkv, a.B);
-  const int waves = (slots + 15) / 16;
-  if (waves > 4 || a.kc % 64) return hipErrorInvalidValue;   // <= 64 query slots per kv head
-  const dim3 grid(a.n_chunks, a.nkv, R), block(64 * waves);
-  const dim3 cgrid(R * a.nkv, (slots * a.hd / 4 + 255) / 256);
-  if (a.hd == 128) {
-    hipLaunchKernelGGL((attn_kernel<128>), grid, block, 0, st, a);
-    hipLaunchKernelGGL((attn_combine_kernel<128>), cgrid, dim3(256), 0, st, a);
-  } else if (a.hd == 64) {
-    hipLaunchKernelGGL((attn_kernel<64>), grid, block, 0, st, a);
-    hipLaunchKernelGGL((attn_combine_kernel<64>), cgrid, dim3(256), 0, st, a);
-  } else {
-    return hipErrorInvalidValue;
+  const int qt = (slots + 15) / 16;
+  if (qt > 4 || a.kc != ATT_KC) return hipErrorInvalidValue;   // <= 64 query slots per kv head
+#define QTS(HD)                                  \
+  switch (qt) {                                  \
+    case 1: launch_hd<HD, 1>(a, st); break;   \
+    case 2: launch_hd<HD, 2>(a, st); break;   \
+    case 3: launch_hd<HD, 3>(a, st); break;   \
+    default: launch_hd<HD, 4>(a, st); break;  \
   }
+  if (a.hd == 128) { QTS(128) }
+  else if (a.hd == 64) { QTS(64) }
+  else return hipErrorInvalidValue;
+#undef QTS
   return hipGetLastError();
 }

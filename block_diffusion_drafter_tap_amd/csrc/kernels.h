@@ -4,7 +4,7 @@
 #include <stdint.h>
 
 enum XKind { X_BF16 = 0, X_TAPS = 1, X_NORM = 2 };
-enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4, E_TOPK = 5 };
+enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4 };
 enum WFmt { WF_BF16 = 0, WF_INT4 = 1 };
 
 constexpr int MAX_TAPS = 8;
@@ -53,7 +53,7 @@ struct GemmArgs {
   const int* pos_of_row;  // NULL -> pos[req] + row % rows_per_req
   int rows_per_req;
   unsigned* err;
-  // E_TOPK: rows m = r*B + i; mask rows i >= 1 produce candidates
+  // LM head: rows m = r*B + i; mask rows i >= 1 produce candidates
   int B, topk;
   float* logits;     // NULL or [R][B-1][N]
   float* cand_val;   // [groups][R*(B-1)][topk]
@@ -70,6 +70,16 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, in
                        hipStream_t st);
 size_t gemm_partial_floats(const GemmPlan& p, int gc);
 
+// Persistent LM head with running top-k (topk 1 or 16); reads the GemmArgs
+// X_NORM fields (xf, xgain, ssq_*), w = W_lm, M, N = vocab, K, B, topk,
+// logits, cand_val, cand_idx. Candidates: [P][R*(B-1)][topk].
+struct LmPlan {
+  int MT, XL, groups, P;
+  size_t lds;
+};
+LmPlan plan_lmhead(int M, int V, int K, int n_cu);
+hipError_t launch_lmhead(const GemmArgs& a, const LmPlan& p, hipStream_t st);
+
 // Attention over [context window | block] per (request, kv head), split over key chunks.
 struct AttnArgs {
   const uint16_t* q;       // [R*B][nq*hd]
@@ -79,14 +89,15 @@ struct AttnArgs {
   const int* pos;
   const int* valid_from;
   int B, W, C, nq, nkv, hd, kc, n_chunks;
+  int R;                   // requests of this launch (set by launch_attention)
   float scale_log2;        // log2(e) / sqrt(hd)
   float* part_o;           // [R*nkv][n_chunks][slots][hd]
   float* part_ml;          // [R*nkv][n_chunks][slots][2]
-  unsigned* counters;      // [R*nkv]
   unsigned* err;
 };
 hipError_t launch_attention(const AttnArgs& a, int R, hipStream_t st);
 int attn_slots(int nq, int nkv, int B);
+int attn_chunk_keys();   // keys per attention chunk
 
 // Small kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
