@@ -34,16 +34,15 @@ int attn_nchunks(const dflash_config& c) {
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, c32, c, partials, counters, attn_o, attn_ml, cand_v, cand_i, mid_v, mid_i, total;
-  size_t n_counters;
+  size_t h, ssq, q, o, act, c32, c, partials, attn_o, attn_ml, cand_v, cand_i, mid_v, mid_i, total;
 };
 
 struct GemmShape {
   int N, K, gc, pair, cu;
 };
 
-// Largest split-K scratch and counter count over every GEMM a call may launch.
-void gemm_scratch(const dflash_config& c, size_t* part_floats, size_t* counters) {
+// Largest split-K partial buffer over every GEMM a call may launch.
+size_t gemm_scratch(const dflash_config& c) {
   const int H = c.hidden, hd = c.head_dim;
   const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, CU_TARGET},
                              {H, c.n_q_heads * hd, GC_DEFAULT, 0, CU_TARGET},
@@ -51,19 +50,17 @@ void gemm_scratch(const dflash_config& c, size_t* part_floats, size_t* counters)
                              {H, c.ffn, GC_DEFAULT, 0, CU_TARGET}};
   const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, CU_TARGET},
                              {2 * c.n_kv_heads * hd, H, hd, 0, CU_TARGET}};
-  size_t pf = 0, cn = 0;
+  size_t pf = 0;
   auto visit = [&](int M, const GemmShape& s) {
     GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, s.cu);
-    size_t f = gemm_partial_floats(p, s.gc);
+    size_t f = gemm_partial_floats(p, M, s.N, s.pair);
     if (f > pf) pf = f;
-    if (p.S > 1 && (size_t)p.groups * p.mz > cn) cn = (size_t)p.groups * p.mz;
   };
   for (int R = 1; R <= c.max_requests; ++R)
     for (const auto& s : draft) visit(R * c.block, s);
   for (int M = 1; M <= c.max_stage_rows; ++M)
     for (const auto& s : stage) visit(M, s);
-  *part_floats = pf;
-  *counters = cn;
+  return pf;
 }
 
 WsLayout ws_layout(const dflash_config& c) {
@@ -71,8 +68,7 @@ WsLayout ws_layout(const dflash_config& c) {
   const size_t Mmax = (size_t)c.max_requests * c.block;
   const size_t S = (size_t)c.max_stage_rows;
   const size_t qw = (size_t)c.n_q_heads * c.head_dim;
-  size_t pf, cn;
-  gemm_scratch(c, &pf, &cn);
+  const size_t pf = gemm_scratch(c);
   const size_t slots = (size_t)attn_slots(c.n_q_heads, c.n_kv_heads, c.block);
   const size_t lrg = (size_t)c.max_requests * c.n_kv_heads;
   const size_t nch = (size_t)attn_nchunks(c);
@@ -87,9 +83,7 @@ WsLayout ws_layout(const dflash_config& c) {
   L.act = take(Mmax * c.ffn * 2);
   L.c32 = take(c.ctx_norm ? S * c.hidden * 4 : 0);
   L.c = take(S * c.hidden * 2);
-  L.partials = take(pf * 4);
-  L.counters = take((cn ? cn : 1) * 4);
-  L.n_counters = cn;
+  L.partials = take((pf ? pf : 1) * 4);
   L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
   L.attn_ml = take(lrg * nch * slots * 2 * 4);
   L.cand_v = take(lm_groups * out_rows * 16 * 4);
@@ -224,7 +218,6 @@ GemmArgs base_args(const dflash_ctx* c) {
   a.pos = at<int>(c->state, c->sl.pos);
   a.err = at<unsigned>(c->state, c->sl.error);
   a.partials = at<float>(c->ws, c->wl.partials);
-  a.counters = at<unsigned>(c->ws, c->wl.counters);
   a.B = g.block;
   return a;
 }
@@ -385,7 +378,12 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   {
     GemmPlan p = plan_gemm(n_rows, H, a.K, GC_DEFAULT, 0, CU_TARGET);
     Timed tm(ctx, DFLASH_K_FC, st);
-    e = launch_gemm(a, p, X_TAPS, g.ctx_norm ? E_F32 : E_BF16, WF_BF16, st);
+    if (p.S > 1) {
+      e = launch_gemm(a, p, X_TAPS, E_PART, WF_BF16, st);
+      if (e == hipSuccess) e = launch_finish_store(a.partials, p.S, n_rows, H, a.out, H, !g.ctx_norm, st);
+    } else {
+      e = launch_gemm(a, p, X_TAPS, g.ctx_norm ? E_F32 : E_BF16, WF_BF16, st);
+    }
   }
   if (e != hipSuccess) return hip_fail(e, "stage fc");
   if (g.ctx_norm) {
@@ -412,7 +410,12 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
     b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
     GemmPlan p = plan_gemm(n_rows, b.N, H, hd, 0, CU_TARGET);
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
-    e = launch_gemm(b, p, X_BF16, E_HEAD, WF_BF16, st);
+    if (p.S > 1) {
+      e = launch_gemm(b, p, X_BF16, E_PART, WF_BF16, st);
+      if (e == hipSuccess) e = launch_finish_head(b, b.partials, p.S, b.N, 2 * g.n_kv_heads, st);
+    } else {
+      e = launch_gemm(b, p, X_BF16, E_HEAD, WF_BF16, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "stage kv");
   }
   return DFLASH_OK;
@@ -473,7 +476,12 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.rows_per_req = B;
       GemmPlan p = plan_gemm(M, a.N, H, hd, 0, CU_TARGET);
       Timed tm(ctx, DFLASH_K_QKV, st);
-      e = launch_gemm(a, p, X_NORM, E_HEAD, WF_BF16, st);
+      if (p.S > 1) {
+        e = launch_gemm(a, p, X_NORM, E_PART, WF_BF16, st);
+        if (e == hipSuccess) e = launch_finish_head(a, a.partials, p.S, a.N, g.n_q_heads + 2 * g.n_kv_heads, st);
+      } else {
+        e = launch_gemm(a, p, X_NORM, E_HEAD, WF_BF16, st);
+      }
       if (e != hipSuccess) return hip_fail(e, "qkv");
     }
     {  // attention over [context window | block]
@@ -515,7 +523,12 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ssq_ld = ssq_ld;
       GemmPlan p = plan_gemm(M, H, qw, GC_DEFAULT, 0, CU_TARGET);
       Timed tm(ctx, DFLASH_K_O, st);
-      e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+      if (p.S > 1) {
+        e = launch_gemm(a, p, X_BF16, E_PART, WF_BF16, st);
+        if (e == hipSuccess) e = launch_finish_resid(a.partials, p.S, M, H, h, H, ssq, ssq_ld, st);
+      } else {
+        e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+      }
       if (e != hipSuccess) return hip_fail(e, "o proj");
     }
     {  // RMSNorm + gate/up with SiLU(gate) * up
@@ -530,7 +543,12 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ldo = g.ffn;
       GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CU_GATEUP);
       Timed tm(ctx, DFLASH_K_GATEUP, st);
-      e = launch_gemm(a, p, X_NORM, E_SILU, WF_BF16, st);
+      if (p.S > 1) {
+        e = launch_gemm(a, p, X_NORM, E_PARTP, WF_BF16, st);
+        if (e == hipSuccess) e = launch_finish_silu(a.partials, p.S, M, g.ffn, act, g.ffn, st);
+      } else {
+        e = launch_gemm(a, p, X_NORM, E_SILU, WF_BF16, st);
+      }
       if (e != hipSuccess) return hip_fail(e, "gate/up");
     }
     {  // down projection, residual add, row sums of squares for the next norm
@@ -547,7 +565,12 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ssq_ld = ssq_ld;
       GemmPlan p = plan_gemm(M, H, g.ffn, GC_DEFAULT, 0, CU_TARGET);
       Timed tm(ctx, DFLASH_K_DOWN, st);
-      e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+      if (p.S > 1) {
+        e = launch_gemm(a, p, X_BF16, E_PART, WF_BF16, st);
+        if (e == hipSuccess) e = launch_finish_resid(a.partials, p.S, M, H, h, H, ssq, ssq_ld, st);
+      } else {
+        e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+      }
       if (e != hipSuccess) return hip_fail(e, "down proj");
     }
   }

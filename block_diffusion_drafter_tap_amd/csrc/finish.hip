@@ -1,0 +1,134 @@
+// Second halves of the split-K projections. The GEMM stored S partial tiles
+// P[s][m][n] (fp32); these kernels sum them in split order, so every result is
+// deterministic, and apply the projection's epilogue. Each output element's S
+// loads are independent and issued in batches of 8.
+#include "device.h"
+#include "kernels.h"
+
+namespace {
+
+// sum_s P[s * stride + off], s = 0..S-1, in order
+DEV float sum_splits(const float* P, int S, size_t stride, size_t off) {
+  float t = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s0 + u < S ? P[(size_t)(s0 + u) * stride + off] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t += v[u];
+  }
+  return t;
+}
+
+// h += Y for one row and one 128-column group; the group's sum of squares of
+// the new h goes to ssq_out[group * ssq_ld + row] (the next RMSNorm's input).
+__global__ __launch_bounds__(128) void finish_resid_kernel(const float* P, int S, int M, int N, float* h, int ldh,
+                                                           float* ssq_out, int ssq_ld) {
+  __shared__ float red[2];
+  const int grp = blockIdx.x, m = blockIdx.y;
+  const int n = grp * 128 + threadIdx.x;
+  float v = 0.f;
+  if (n < N) {
+    const float y = sum_splits(P, S, (size_t)M * N, (size_t)m * N + n);
+    float* hp = h + (size_t)m * ldh + n;
+    v = *hp + y;
+    *hp = v;
+  }
+  float ss = wave_sum(v * v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0 && ssq_out) ssq_out[(size_t)grp * ssq_ld + m] = red[0] + red[1];
+}
+
+__global__ __launch_bounds__(256) void finish_silu_kernel(const float* P, int S, int M, int N, uint16_t* act,
+                                                          int ldo) {
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const size_t stride = (size_t)M * 2 * N;
+  const float g = sum_splits(P, S, stride, (size_t)m * 2 * N + n);
+  const float u = sum_splits(P, S, stride, (size_t)m * 2 * N + N + n);
+  act[(size_t)m * ldo + n] = f2bfbits(g / (1.0f + expf(-g)) * u);
+}
+
+__global__ __launch_bounds__(256) void finish_store_kernel(const float* P, int S, int M, int N, void* out, int ldo,
+                                                           int bf16) {
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const float y = sum_splits(P, S, (size_t)M * N, (size_t)m * N + n);
+  if (bf16) ((uint16_t*)out)[(size_t)m * ldo + n] = f2bfbits(y);
+  else ((float*)out)[(size_t)m * ldo + n] = y;
+}
+
+// One wave per (row, head) of the projection: q/k heads get RMSNorm over
+// head_dim with their gain and rotate-half RoPE at the row's position; Q goes
+// to the block buffer (bf16), K to the ring at slot position % C, V (no norm)
+// to the transposed V ring. Lane d owns the rotation pair (d, d + hd/2).
+__global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, const float* P, int S, int ld,
+                                                          int n_heads) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.M * n_heads) return;
+  const int m = item / n_heads, hl = item % n_heads;
+  const int head = a.head_base + hl;
+  const int hd = a.hd, half = hd / 2;
+  const int req = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
+  long long p = -1;
+  if (req >= 0 && req < a.Rmax)
+    p = a.pos_of_row ? (long long)a.pos_of_row[m] : (long long)a.pos[req] + m % a.rows_per_req;
+  if (p < 0) {
+    if (lane == 0) set_error(a.err, req < 0 || req >= a.Rmax ? 4u : 8u);
+    return;
+  }
+  const bool on = lane < half;
+  const size_t stride = (size_t)a.M * ld, base = (size_t)m * ld + (size_t)hl * hd;
+  const float x1 = on ? sum_splits(P, S, stride, base + lane) : 0.f;
+  const float x2 = on ? sum_splits(P, S, stride, base + lane + half) : 0.f;
+  const bool is_q = head < a.nq, is_k = !is_q && head < a.nq + a.nkv;
+  if (is_q || is_k) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
+    if (!on) return;
+    const uint16_t* g = is_q ? a.q_gain : a.k_gain;
+    const float y1 = x1 * inv * bfbits2f(g[lane]);
+    const float y2 = x2 * inv * bfbits2f(g[lane + half]);
+    float c, s;
+    rope_cos_sin(p, lane, hd, a.log2_theta, &c, &s);
+    uint16_t* o = is_q ? a.q_out + (size_t)m * a.nq * hd + (size_t)head * hd
+                       : a.ring_k + (((size_t)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * hd;
+    o[lane] = f2bfbits(y1 * c - y2 * s);
+    o[lane + half] = f2bfbits(y2 * c + y1 * s);
+  } else {
+    if (!on) return;
+    uint16_t* o = a.ring_v + ((size_t)req * a.nkv + (head - a.nq - a.nkv)) * (size_t)hd * a.C + p % a.C;
+    o[(size_t)lane * a.C] = f2bfbits(x1);
+    o[(size_t)(lane + half) * a.C] = f2bfbits(x2);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_finish_resid(const float* P, int S, int M, int N, float* h, int ldh, float* ssq_out, int ssq_ld,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(finish_resid_kernel, dim3((N + 127) / 128, M), dim3(128), 0, st, P, S, M, N, h, ldh, ssq_out,
+                     ssq_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_silu(const float* P, int S, int M, int N, uint16_t* act, int ldo, hipStream_t st) {
+  hipLaunchKernelGGL(finish_silu_kernel, dim3((N + 255) / 256, M), dim3(256), 0, st, P, S, M, N, act, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_store(const float* P, int S, int M, int N, void* out, int ldo, int bf16, hipStream_t st) {
+  hipLaunchKernelGGL(finish_store_kernel, dim3((N + 255) / 256, M), dim3(256), 0, st, P, S, M, N, out, ldo, bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_head(const GemmArgs& a, const float* P, int S, int ld, int n_heads, hipStream_t st) {
+  if (a.hd > 128 || a.hd % 2) return hipErrorInvalidValue;
+  const int items = a.M * n_heads;
+  hipLaunchKernelGGL(finish_head_kernel, dim3((items + 3) / 4), dim3(256), 0, st, a, P, S, ld, n_heads);
+  return hipGetLastError();
+}

@@ -13,12 +13,12 @@
 // loads in flight ahead of the MFMAs. Plain (cached) loads measured faster than
 // non-temporal ones for this pattern.
 //
-// Split-K: each split publishes its [rows][GC] partial tile with agent-scope
-// relaxed atomic stores (coherent across the XCDs' L2s without flushing them),
-// waits for the stores to complete and bumps a per-group counter; the last
-// split to arrive sums all partials in split order (deterministic) with
-// agent-scope relaxed atomic loads and runs the epilogue. A device-scope fence
-// here would write back and invalidate L2 in every workgroup.
+// Split-K (S > 1): each split stores its partial tile straight from the MFMA
+// accumulators (E_PART, E_PARTP) and the workgroup ends; a finish kernel sums
+// the splits in split order (deterministic) and applies the epilogue. An
+// in-kernel "last split reduces" scheme was measured slower: its publish /
+// count / re-read chain is three dependent device-scope round trips at the
+// tail of every projection, while the kernel boundary costs well under 1 us.
 //
 // MFMA operand layout (v_mfma_f32_16x16x32_bf16): lane l supplies A[l%16][8
 // k-values] and B[8 k-values][l%16], the k-values of lane group l/16 being
@@ -31,6 +31,7 @@
 //           rows, the second half the matching up rows);
 //   E_HEAD  one head per workgroup: q/k RMSNorm over head_dim, RoPE at the row's
 //           position, Q to the block buffer, K / V into the context ring;
+// these need the whole K range in one workgroup (S = 1).
 //
 // The LM head has its own persistent kernel (lmhead_kernel below): each
 // workgroup stages the final-normed rows once, streams several 128-column
@@ -152,9 +153,8 @@ template <int MT, int NW, int XK, int XL, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   constexpr int ROWS = MT * 16;
   constexpr int GC = NW * 16;
-  constexpr bool PAIR = (EPI == E_SILU);
+  constexpr bool PAIR = (EPI == E_SILU || EPI == E_PARTP);
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int last_flag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -242,6 +242,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     if (c + 3 < nchunks) load_w(c + 3, wB);
   }
 
+  if constexpr (EPI == E_PART || EPI == E_PARTP) {
+    // partial tile of this split: lane holds C[4*lg + i][lr] of each row tile
+    int n;
+    bool ok;
+    if constexpr (PAIR) {
+      constexpr int HALF = NW / 2;
+      const int logical = group * (GC / 2) + (wave % HALF) * 16 + lr;
+      ok = logical < a.N;
+      n = logical + (wave >= HALF ? a.N : 0);
+    } else {
+      n = group * GC + wave * 16 + lr;
+      ok = n < a.N;
+    }
+    const int ntot = PAIR ? 2 * a.N : a.N;
+    float* dst = a.partials + (size_t)split * a.M * ntot + n;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + mt * 16 + 4 * lg + i;
+        if (ok && m < a.M) dst[(size_t)m * ntot] = acc[mt][i];
+      }
+    return;
+  }
+
   // ---- result tile in LDS (aliases the X slice, which is dead now)
   __syncthreads();
   float(*tile)[GC + 1] = (float(*)[GC + 1])smem;
@@ -251,55 +276,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) tile[mt * 16 + 4 * lg + i][tcol + lr] = acc[mt][i];
   __syncthreads();
-
-  if (a.S > 1) {
-    const size_t wg = (size_t)mz * gridDim.x + group;
-    float* mine = a.partials + (wg * a.S + split) * (size_t)(ROWS * GC);
-    const int n = rows * GC;
-    for (int e = threadIdx.x; e < n; e += blockDim.x)
-      __hip_atomic_store(mine + e, tile[e / GC][e % GC], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);          // partial stores complete before the count
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(&a.counters[wg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = prev == (unsigned)(a.S - 1);
-      if (last) __hip_atomic_store(&a.counters[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_flag = last;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    // every thread owns a few tile elements and has the loads of up to 16
-    // splits of all of them in flight at once: one memory round trip per 16 splits
-    const float* base = a.partials + wg * a.S * (size_t)(ROWS * GC);
-    constexpr int PER = (ROWS * GC + NW * 64 - 1) / (NW * 64);
-    float sum[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) sum[u] = 0.f;
-    for (int s0 = 0; s0 < a.S; s0 += 16) {
-      float v[16][PER];
-#pragma unroll
-      for (int sp = 0; sp < 16; ++sp)
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int e = threadIdx.x + u * NW * 64;
-          v[sp][u] = (s0 + sp < a.S && e < n)
-                         ? __hip_atomic_load(base + (size_t)(s0 + sp) * ROWS * GC + e, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.f;
-        }
-#pragma unroll
-      for (int sp = 0; sp < 16; ++sp)
-#pragma unroll
-        for (int u = 0; u < PER; ++u) sum[u] += v[sp][u];
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = threadIdx.x + u * NW * 64;
-      if (e < n) tile[e / GC][e % GC] = sum[u];
-    }
-    __syncthreads();
-  }
 
   // ---- epilogue on tile[0:rows][0:GC]
   if constexpr (EPI == E_BF16 || EPI == E_F32) {
@@ -358,6 +334,7 @@ hipError_t launch_x(const GemmArgs& a, dim3 grid, size_t lds, int xk, int epi, h
   if (xk == X_TAPS) {
     if (epi == E_BF16) launch_one<MT, NW, X_TAPS, XL, E_BF16>(a, grid, lds, st);
     else if (epi == E_F32) launch_one<MT, NW, X_TAPS, XL, E_F32>(a, grid, lds, st);
+    else if (epi == E_PART) launch_one<MT, NW, X_TAPS, XL, E_PART>(a, grid, lds, st);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
@@ -365,6 +342,8 @@ hipError_t launch_x(const GemmArgs& a, dim3 grid, size_t lds, int xk, int epi, h
     switch (epi) {
       case E_SILU: launch_one<MT, NW, X_NORM, XL, E_SILU>(a, grid, lds, st); break;
       case E_HEAD: launch_one<MT, NW, X_NORM, XL, E_HEAD>(a, grid, lds, st); break;
+      case E_PART: launch_one<MT, NW, X_NORM, XL, E_PART>(a, grid, lds, st); break;
+      case E_PARTP: launch_one<MT, NW, X_NORM, XL, E_PARTP>(a, grid, lds, st); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -375,6 +354,7 @@ hipError_t launch_x(const GemmArgs& a, dim3 grid, size_t lds, int xk, int epi, h
     case E_RESID: launch_one<MT, NW, X_BF16, XL, E_RESID>(a, grid, lds, st); break;
     case E_SILU: launch_one<MT, NW, X_BF16, XL, E_SILU>(a, grid, lds, st); break;
     case E_HEAD: launch_one<MT, NW, X_BF16, XL, E_HEAD>(a, grid, lds, st); break;
+    case E_PART: launch_one<MT, NW, X_BF16, XL, E_PART>(a, grid, lds, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -642,13 +622,15 @@ GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target) {
   return p;
 }
 
-size_t gemm_partial_floats(const GemmPlan& p, int gc) {
+size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair) {
   if (p.S <= 1) return 0;
-  return (size_t)p.mz * p.groups * p.S * (16 * p.MT) * gc;
+  return (size_t)p.S * M * (pair ? 2 * N : N);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf, hipStream_t st) {
   if (wf != WF_BF16) return hipErrorInvalidValue;
+  // a complete epilogue needs the whole K range in one workgroup
+  if (p.S > 1 && epi != E_PART && epi != E_PARTP) return hipErrorInvalidValue;
   const dim3 grid(p.groups, p.S, p.mz);
   GemmArgs b = a;
   b.ks = p.ks;

@@ -4,7 +4,9 @@
 #include <stdint.h>
 
 enum XKind { X_BF16 = 0, X_TAPS = 1, X_NORM = 2 };
-enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4 };
+// E_PART / E_PARTP: split-K partial tiles to partials[split][M][Ntot] (fp32), Ntot = N,
+// or 2N for a gate/up pair (gate columns first, then up); a finish kernel sums them.
+enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4, E_PART = 5, E_PARTP = 6 };
 enum WFmt { WF_BF16 = 0, WF_INT4 = 1 };
 
 constexpr int MAX_TAPS = 8;
@@ -35,9 +37,8 @@ struct GemmArgs {
   // plain epilogues
   void* out;
   long long ldo;
-  // split-K scratch
+  // split-K partial tiles (E_PART / E_PARTP)
   float* partials;
-  unsigned* counters;
   // E_HEAD: per-head q/k RMSNorm + RoPE, Q to q_out, K/V to the ring
   int head_base, nq, nkv, hd;
   float eps;
@@ -68,7 +69,7 @@ struct GemmPlan {
 GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf,
                        hipStream_t st);
-size_t gemm_partial_floats(const GemmPlan& p, int gc);
+size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
 
 // Persistent LM head with running top-k (topk 1 or 16); reads the GemmArgs
 // X_NORM fields (xf, xgain, ssq_*), w = W_lm, M, N = vocab, K, B, topk,
@@ -98,6 +99,19 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, int R, hipStream_t st);
 int attn_slots(int nq, int nkv, int B);
 int attn_chunk_keys();   // keys per attention chunk
+
+// Second halves of split-K projections: sum the S partial tiles [S][M][ld] in
+// split order, then apply the epilogue.
+//   resid: h += Y; ssq_out[g * ssq_ld + m] = sum over 128-column group g of h^2
+//   silu:  act = SiLU(gate) * up (bf16); gate at column n, up at N + n
+//   head:  q/k head RMSNorm + RoPE, Q to q_out, K/V to the ring (GemmArgs head
+//          fields), n_heads heads starting at a.head_base, rows a.M
+//   store: Y to bf16 or fp32
+hipError_t launch_finish_resid(const float* P, int S, int M, int N, float* h, int ldh, float* ssq_out, int ssq_ld,
+                               hipStream_t st);
+hipError_t launch_finish_silu(const float* P, int S, int M, int N, uint16_t* act, int ldo, hipStream_t st);
+hipError_t launch_finish_head(const GemmArgs& a, const float* P, int S, int ld, int n_heads, hipStream_t st);
+hipError_t launch_finish_store(const float* P, int S, int M, int N, void* out, int ldo, int bf16, hipStream_t st);
 
 // Small kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
