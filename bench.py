@@ -22,6 +22,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 COPY_BYTES = 512 << 20   # calibration copy read (and written) once before warm-up
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the LM-head kernel at the default workload
+LM_PROFILE = os.path.join(ROOT, "profiles", "lmhead_topk16_qwen3-4b_b16_ctx4k.md")
+LM_SOURCES = [os.path.join(ROOT, "block_diffusion_drafter_tap_amd", "csrc", f)
+              for f in ("lmhead.hip", "device.h", "kernels.h")]
+
+
+def lm_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in LM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def lm_traffic(workload: str):
+    """HBM bytes per LM-head launch measured by the committed counter summary,
+    or None when that summary is absent, covers another workload, or was taken
+    with different LM-head sources than the ones built now."""
+    if workload != "c3" or not os.path.exists(LM_PROFILE):
+        return None
+    fields = {}
+    with open(LM_PROFILE) as fh:
+        for line in fh:
+            text = line.strip().lstrip("-").strip().strip("`")
+            if text.startswith(("source_sha256:", "traffic_bytes_per_launch:")):
+                key, val = text.split(":", 1)
+                fields[key.strip()] = val.split("`")[0].strip()
+    if fields.get("source_sha256") != lm_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 WORKLOADS = {
     # name: (config builder kwargs, requests, k, description)
@@ -218,8 +253,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) fp32 taps with 0.5% x100 outlier columns, "
-                "geometric p=0.75 verify accepts)",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) fp32 taps"
+                + (" with 0.5% x100 outlier columns" if cfg.hc_streams == 1 else ", 4 hyper-connection streams")
+                + ", geometric p=0.75 verify accepts)",
         "config": {"workload": desc, "block": B, "window": W, "requests": R, "topk": k,
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": V, "hc_streams": cfg.hc_streams,
                    },
@@ -228,9 +264,9 @@ def main():
         "drafted_tokens_per_s": round(blocks_s * (B - 1), 1),
         "accepted_tokens_per_s": round(blocks_s * tau, 1),
         "tau": round(tau, 3),
-        "roofline": {"bound": "hbm", "kernel": "lm_head_topk (gemm_kernel E_TOPK)",
+        "roofline": {"bound": "hbm", "kernel": "lmhead_kernel (shared LM head + running top-k)",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": lm_traffic(args.workload),
                      "avg_launch_us": round(lm_ms * 1e3, 2), "bytes_per_launch": rb["lm_head"]},
         "cpu_baseline": None,
     }
