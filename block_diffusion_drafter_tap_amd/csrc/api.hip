@@ -29,7 +29,7 @@ constexpr int CU_GATEUP = 512;   // gate/up measured faster with more, shorter K
 constexpr int GC_DEFAULT = 128;
 
 int attn_nchunks(const dflash_config& c) {
-  const int kc = attn_chunk_keys();
+  const int kc = attn_chunk_keys(c.head_dim);
   return (c.window + c.block + 31 + kc - 1) / kc;
 }
 
@@ -51,15 +51,18 @@ size_t gemm_scratch(const dflash_config& c) {
   const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, CU_TARGET},
                              {2 * c.n_kv_heads * hd, H, hd, 0, CU_TARGET}};
   size_t pf = 0;
-  auto visit = [&](int M, const GemmShape& s) {
+  auto visit = [&](int M, const GemmShape& s, int layers) {
     GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, s.cu);
-    size_t f = gemm_partial_floats(p, M, s.N, s.pair);
+    size_t f = gemm_partial_floats(p, M, s.N, s.pair) * layers;
     if (f > pf) pf = f;
   };
+  const int batch = c.n_layers < MAX_BATCH ? c.n_layers : MAX_BATCH;
   for (int R = 1; R <= c.max_requests; ++R)
-    for (const auto& s : draft) visit(R * c.block, s);
-  for (int M = 1; M <= c.max_stage_rows; ++M)
-    for (const auto& s : stage) visit(M, s);
+    for (const auto& s : draft) visit(R * c.block, s, 1);
+  for (int M = 1; M <= c.max_stage_rows; ++M) {
+    visit(M, stage[0], 1);
+    visit(M, stage[1], batch);   // stage K/V batches up to MAX_BATCH layers
+  }
   return pf;
 }
 
@@ -392,25 +395,36 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   }
   // per layer: K/V of the staged rows into the ring
   const size_t rl = ring_layer_elems(g);
-  for (int l = 0; l < g.n_layers; ++l) {
+  GemmPlan p = plan_gemm(n_rows, 2 * g.n_kv_heads * hd, H, hd, 0, CU_TARGET);
+  // split-K (a few rows per round): up to MAX_BATCH layers share one launch of the
+  // projection and one of the head finish; S = 1 (prefill) runs one launch per layer
+  const int step = p.S > 1 ? MAX_BATCH : 1;
+  for (int l0 = 0; l0 < g.n_layers; l0 += step) {
+    const int nl = g.n_layers - l0 < step ? g.n_layers - l0 : step;
     GemmArgs b = base_args(ctx);
     b.x = c_bf;
     b.ldx = H;
-    b.w = ctx->wqkv[l] + (size_t)g.n_q_heads * hd * H;
+    b.w = ctx->wqkv[l0] + (size_t)g.n_q_heads * hd * H;
     b.M = n_rows;
     b.N = 2 * g.n_kv_heads * hd;
     b.K = H;
     b.head_base = g.n_q_heads;
-    b.k_gain = ctx->k_norm[l];
-    b.q_gain = ctx->q_norm[l];
-    b.ring_k = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
-    b.ring_v = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
+    b.k_gain = ctx->k_norm[l0];
+    b.q_gain = ctx->q_norm[l0];
+    b.ring_k = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l0 * rl;
+    b.ring_v = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l0 * rl;
     b.req_of_row = req_of_row;
     b.pos_of_row = pos_of_row;
     b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
-    GemmPlan p = plan_gemm(n_rows, b.N, H, hd, 0, CU_TARGET);
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
     if (p.S > 1) {
+      b.nb = nl;
+      for (int i = 0; i < nl; ++i) {
+        b.wb[i] = ctx->wqkv[l0 + i] + (size_t)g.n_q_heads * hd * H;
+        b.rkb[i] = at<uint16_t>(ctx->state, ctx->sl.ring_k) + (l0 + i) * rl;
+        b.rvb[i] = at<uint16_t>(ctx->state, ctx->sl.ring_v) + (l0 + i) * rl;
+        b.kgb[i] = ctx->k_norm[l0 + i];
+      }
       e = launch_gemm(b, p, X_BF16, E_PART, WF_BF16, st);
       if (e == hipSuccess) e = launch_finish_head(b, b.partials, p.S, b.N, 2 * g.n_kv_heads, st);
     } else {
@@ -499,7 +513,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       t.nq = g.n_q_heads;
       t.nkv = g.n_kv_heads;
       t.hd = hd;
-      t.kc = attn_chunk_keys();
+      t.kc = attn_chunk_keys(hd);
       t.n_chunks = attn_nchunks(g);
       t.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
       t.part_o = at<float>(ctx->ws, ctx->wl.attn_o);

@@ -4,18 +4,20 @@
 // block's own K/V were written to slots pos..pos+B-1 by the QKV epilogue), so a
 // query sees one contiguous position range [lo, pos+B).
 //
-// Workgroup = (key chunk of 128, kv head, request), four waves, in two phases
-// with an exact softmax inside the chunk:
+// Workgroup = (key chunk, kv head, request) with HD/16 waves and 32 keys per
+// wave (256-key chunks at head_dim 128), in two phases with an exact softmax
+// inside the chunk:
 //  1. wave w takes the chunk's 32-key sub-tile w and computes S^T = K Q^T for
 //     all G*B queries of the kv head's query-head group (MFMA, keys x queries,
-//     Q staged in LDS). The chunk max of every query comes from a 4-entry LDS
-//     exchange; the wave then forms P = 2^(S - M) in registers and parks it in
+//     Q staged once in LDS: the waves share it instead of each loading it).
+//     The chunk max of every query comes from an LDS exchange between the
+//     waves; the wave then forms P = 2^(S - M) in registers and parks it in
 //     LDS as two bf16 terms (hi + lo keep ~16 significant bits).
-//  2. wave w owns head_dim tiles w*HD/64 ..: it accumulates O^T = V^T P^T over
-//     the four sub-tiles (MFMA, head_dim x queries) and writes its rows of the
+//  2. wave w owns head_dim tile w: it accumulates O^T = V^T P^T over all the
+//     chunk's sub-tiles (MFMA, head_dim x queries) and writes its rows of the
 //     chunk partial straight from the accumulators.
-// All K/V loads of a wave are issued before the first MFMA, so a chunk's 64 KB
-// is in flight at once; no wave holds more than two head_dim tiles of O.
+// All K/V loads of a wave are issued before its first MFMA, so a chunk's 128 KB
+// is in flight at once, and no wave holds more than one head_dim tile of O.
 // The ring keeps V transposed ([hd][C]) so that both MFMA operands are 16-byte
 // loads. Keys of the two 16-row S^T tiles are permuted so that after the first
 // MFMA each lane group already holds the 8 consecutive keys the second MFMA
@@ -31,14 +33,12 @@
 
 namespace {
 
-constexpr int ATT_WAVES = 4;
-constexpr int ATT_KC = 32 * ATT_WAVES;   // keys per chunk
-
 struct Range {
   int lo, hi, base, n_ch;
 };
 
-// [lo, hi): keys a block query sees; chunks start at base = lo rounded down to 32.
+// [lo, hi): keys a block query sees; chunks of a.kc keys start at base = lo
+// rounded down to 32.
 DEV Range key_range(const AttnArgs& a, int r, bool report) {
   const int pos = a.pos[r];
   int vf = a.valid_from[r];
@@ -53,18 +53,23 @@ DEV Range key_range(const AttnArgs& a, int r, bool report) {
   g.lo = lo;
   g.hi = pos + a.B;
   g.base = lo & ~31;
-  g.n_ch = (g.hi - g.base + ATT_KC - 1) / ATT_KC;
+  g.n_ch = (g.hi - g.base + a.kc - 1) / a.kc;
   return g;
 }
 
-template <int HD, int QT>
-__global__ __launch_bounds__(64 * ATT_WAVES) void attn_kernel(const AttnArgs a) {
+template <int HD, int QT, int NWA>
+__global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
+  constexpr int ATT_WAVES = NWA;
+  constexpr int ATT_KC = 32 * NWA;         // keys per chunk
   constexpr int QS = HD / 32;              // MFMA k-steps along head_dim
   constexpr int HTW = HD / 16 / ATT_WAVES; // O^T head_dim tiles per wave
   constexpr int NSL = QT * 16;             // query slots (padded to whole tiles)
+  static_assert(HTW >= 1, "at most HD/16 waves");
   __shared__ __attribute__((aligned(16))) uint16_t s_q[NSL][HD + 8];
-  __shared__ u32x4 s_p[ATT_WAVES][QT][2][64];
   __shared__ float s_mx[ATT_WAVES][NSL], s_l[ATT_WAVES][NSL];
+  // P of every sub-tile (hi and lo bf16 terms), up to 64 KB: dynamic LDS
+  extern __shared__ __attribute__((aligned(16))) u32x4 s_pdyn[];
+  u32x4 (*s_p)[QT][2][64] = (u32x4 (*)[QT][2][64])s_pdyn;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -266,24 +271,26 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs a) {
 
 template <int HD, int QT>
 void launch_hd(const AttnArgs& a, hipStream_t st) {
+  constexpr int NWA = HD / 16;   // one head_dim tile of O per wave in the P.V phase
   const int RN = a.R * a.nkv;
   const int slots = attn_slots(a.nq, a.nkv, a.B);
   const int parts = (slots * HD / 4 + 63) / 64;
-  hipLaunchKernelGGL((attn_kernel<HD, QT>), dim3(a.n_chunks * RN), dim3(64 * ATT_WAVES), 0, st, a);
+  const size_t lds = (size_t)NWA * QT * 2 * 64 * sizeof(u32x4);
+  hipLaunchKernelGGL((attn_kernel<HD, QT, NWA>), dim3(a.n_chunks * RN), dim3(64 * NWA), lds, st, a);
   hipLaunchKernelGGL((attn_combine_kernel<HD>), dim3(parts * RN), dim3(64), 0, st, a);
 }
 
 }  // namespace
 
 int attn_slots(int nq, int nkv, int B) { return (nq / nkv) * B; }
-int attn_chunk_keys() { return ATT_KC; }
+int attn_chunk_keys(int hd) { return 32 * (hd / 16); }
 
 hipError_t launch_attention(const AttnArgs& args, int R, hipStream_t st) {
   AttnArgs a = args;
   a.R = R;
   const int slots = attn_slots(a.nq, a.nkv, a.B);
   const int qt = (slots + 15) / 16;
-  if (qt > 4 || a.kc != ATT_KC) return hipErrorInvalidValue;   // <= 64 query slots per kv head
+  if (qt > 4 || a.kc != attn_chunk_keys(a.hd)) return hipErrorInvalidValue;   // <= 64 query slots per kv head
 #define QTS(HD)                                  \
   switch (qt) {                                  \
     case 1: launch_hd<HD, 1>(a, st); break;   \

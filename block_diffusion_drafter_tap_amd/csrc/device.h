@@ -42,6 +42,16 @@ DEV float wave_max(float v) {
   return v;
 }
 
+// arr[i] for a block-uniform i < N, without dynamic indexing of a kernel argument
+template <class T, int N>
+DEV T pick(const T (&arr)[N], int i) {
+  T r = arr[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j)
+    if (i == j) r = arr[j];
+  return r;
+}
+
 // (value desc, index asc) ordering used by argmax / top-k.
 DEV bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 

@@ -65,12 +65,18 @@ __global__ __launch_bounds__(256) void finish_store_kernel(const float* P, int S
 // head_dim with their gain and rotate-half RoPE at the row's position; Q goes
 // to the block buffer (bf16), K to the ring at slot position % C, V (no norm)
 // to the transposed V ring. Lane d owns the rotation pair (d, d + hd/2).
-__global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, const float* P, int S, int ld,
+__global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, const float* __restrict__ P0, int S, int ld,
                                                           int n_heads) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.M * n_heads) return;
-  const int m = item / n_heads, hl = item % n_heads;
+  const int nl = a.nb > 0 ? a.nb : 1;
+  if (item >= nl * a.M * n_heads) return;
+  const int layer = item / (a.M * n_heads);
+  const int m = item % (a.M * n_heads) / n_heads, hl = item % n_heads;
+  uint16_t* ring_k = a.nb > 0 ? pick(a.rkb, layer) : a.ring_k;
+  uint16_t* ring_v = a.nb > 0 ? pick(a.rvb, layer) : a.ring_v;
+  const uint16_t* k_gain = a.nb > 0 ? pick(a.kgb, layer) : a.k_gain;
+  const float* P = P0 + (size_t)layer * S * a.M * ld;
   const int head = a.head_base + hl;
   const int hd = a.hd, half = hd / 2;
   const int req = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
@@ -90,18 +96,18 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
     if (!on) return;
-    const uint16_t* g = is_q ? a.q_gain : a.k_gain;
+    const uint16_t* g = is_q ? a.q_gain : k_gain;
     const float y1 = x1 * inv * bfbits2f(g[lane]);
     const float y2 = x2 * inv * bfbits2f(g[lane + half]);
     float c, s;
     rope_cos_sin(p, lane, hd, a.log2_theta, &c, &s);
     uint16_t* o = is_q ? a.q_out + (size_t)m * a.nq * hd + (size_t)head * hd
-                       : a.ring_k + (((size_t)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * hd;
+                       : ring_k + (((size_t)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * hd;
     o[lane] = f2bfbits(y1 * c - y2 * s);
     o[lane + half] = f2bfbits(y2 * c + y1 * s);
   } else {
     if (!on) return;
-    uint16_t* o = a.ring_v + ((size_t)req * a.nkv + (head - a.nq - a.nkv)) * (size_t)hd * a.C + p % a.C;
+    uint16_t* o = ring_v + ((size_t)req * a.nkv + (head - a.nq - a.nkv)) * (size_t)hd * a.C + p % a.C;
     o[(size_t)lane * a.C] = f2bfbits(x1);
     o[(size_t)(lane + half) * a.C] = f2bfbits(x2);
   }
@@ -128,7 +134,8 @@ hipError_t launch_finish_store(const float* P, int S, int M, int N, void* out, i
 
 hipError_t launch_finish_head(const GemmArgs& a, const float* P, int S, int ld, int n_heads, hipStream_t st) {
   if (a.hd > 128 || a.hd % 2) return hipErrorInvalidValue;
-  const int items = a.M * n_heads;
+  if (a.nb > MAX_BATCH) return hipErrorInvalidValue;
+  const int items = (a.nb > 0 ? a.nb : 1) * a.M * n_heads;
   hipLaunchKernelGGL(finish_head_kernel, dim3((items + 3) / 4), dim3(256), 0, st, a, P, S, ld, n_heads);
   return hipGetLastError();
 }

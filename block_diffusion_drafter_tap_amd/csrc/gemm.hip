@@ -155,8 +155,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int group = blockIdx.x, split = blockIdx.y, mz = blockIdx.z;
+  const int n_mz = (a.M + ROWS - 1) / ROWS;
+  const int group = blockIdx.x, split = blockIdx.y, mz = blockIdx.z % n_mz, layer = blockIdx.z / n_mz;
   const int m0 = mz * ROWS;
+  const void* wbase = a.nb > 0 ? pick(a.wb, layer) : a.w;
   const int kbeg = split * a.ks;
   const int kend = min(a.K, kbeg + a.ks);
   const int klen = kend - kbeg;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     wrow_i = min(group * GC + wave * 16 + lr, a.N - 1);
     tcol = wave * 16;
   }
-  const uint16_t* wrow = (const uint16_t*)a.w + (size_t)wrow_i * a.K + kbeg + 8 * lg;
+  const uint16_t* wrow = (const uint16_t*)wbase + (size_t)wrow_i * a.K + kbeg + 8 * lg;
 
   // Two 128-wide chunks of W loads stay in flight; the first two are issued
   // before the X slice is staged, so they stream during the staging.
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       ok = n < a.N;
     }
     const int ntot = PAIR ? 2 * a.N : a.N;
-    float* dst = a.partials + (size_t)split * a.M * ntot + n;
+    float* dst = a.partials + ((size_t)layer * a.S + split) * a.M * ntot + n;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -402,7 +404,8 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, in
   if (wf != WF_BF16) return hipErrorInvalidValue;
   // a complete epilogue needs the whole K range in one workgroup
   if (p.S > 1 && epi != E_PART && epi != E_PARTP) return hipErrorInvalidValue;
-  const dim3 grid(p.groups, p.S, p.mz);
+  if (a.nb > MAX_BATCH || (a.nb > 0 && epi != E_PART)) return hipErrorInvalidValue;
+  const dim3 grid(p.groups, p.S, p.mz * (a.nb > 0 ? a.nb : 1));
   GemmArgs b = a;
   b.ks = p.ks;
   b.S = p.S;

@@ -10,6 +10,7 @@ enum EpiKind { E_BF16 = 0, E_F32 = 1, E_RESID = 2, E_SILU = 3, E_HEAD = 4, E_PAR
 enum WFmt { WF_BF16 = 0, WF_INT4 = 1 };
 
 constexpr int MAX_TAPS = 8;
+constexpr int MAX_BATCH = 8;   // layers per batched stage K/V launch
 constexpr int GEMM_WAVES = 4;
 
 // Arguments of the skinny GEMM Y[M, N] = X[M, K] . W[N, K]^T with a fused epilogue.
@@ -39,6 +40,13 @@ struct GemmArgs {
   long long ldo;
   // split-K partial tiles (E_PART / E_PARTP)
   float* partials;
+  // layer batch (nb > 0): grid.z also runs over nb layers; layer b uses W wb[b],
+  // rings rkb[b] / rvb[b], k gain kgb[b] and partials + b * S * M * N
+  int nb;
+  const void* wb[MAX_BATCH];
+  uint16_t* rkb[MAX_BATCH];
+  uint16_t* rvb[MAX_BATCH];
+  const uint16_t* kgb[MAX_BATCH];
   // E_HEAD: per-head q/k RMSNorm + RoPE, Q to q_out, K/V to the ring
   int head_base, nq, nkv, hd;
   float eps;
@@ -98,7 +106,7 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, int R, hipStream_t st);
 int attn_slots(int nq, int nkv, int B);
-int attn_chunk_keys();   // keys per attention chunk
+int attn_chunk_keys(int hd);   // keys per attention chunk
 
 // Second halves of split-K projections: sum the S partial tiles [S][M][ld] in
 // split order, then apply the epilogue.

@@ -10,7 +10,8 @@
 //   k = 16  the first group is sorted by a bitonic network on registers and
 //           shuffles (two values per lane), later groups only insert the values
 //           that beat the current k-th entry (ballot, then a shifted insert).
-// The next group's first weight chunk is in flight during the selection.
+// Weight loads run four 128-wide chunks ahead, across group boundaries, so the
+// next group's first chunks are in flight during the selection.
 // Output: per workgroup and mask row, its k best (value, id), best first.
 
 #include "device.h"
@@ -89,7 +90,7 @@ DEV void wave_insert(float& rv, int& ri, float cv, int ci) {
   }
 }
 
-template <int MT, int XL, int KK>
+template <int MT, int XL, int KK, int D>
 __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_groups) {
   constexpr int NW = 8, GC = 128, ROWS = MT * 16, RPW = ROWS / NW;   // rows per wave
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -117,20 +118,23 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_gro
     ri[t] = 0x7fffffff - (t * 64 + lane);   // distinct placeholder ids
   }
 
+  // W chunks of 128 k-values stream D deep: chunk c of a group lives in buffer
+  // c % D (D divides the chunk count), and the last D buffers of a group are
+  // refilled with the next group's first chunks, so loads stay in flight
+  // through the top-k selection.
   int g = blockIdx.x;
-  const uint16_t* wrow;
-  auto set_group = [&](int gg) {
-    wrow = (const uint16_t*)a.w + (size_t)min(gg * GC + wave * 16 + lr, a.N - 1) * K + 8 * lg;
+  auto rowp = [&](int gg) {
+    return (const uint16_t*)a.w + (size_t)min(gg * GC + wave * 16 + lr, a.N - 1) * K + 8 * lg;
   };
-  u32x4 wA[4], wB[4];
-  auto load_w = [&](int c, u32x4 (&w)[4]) {
-    const int k = 128 * min(c, nchunks - 1);
+  u32x4 wbuf[D][4];
+  auto load_w = [&](const uint16_t* base, int c, u32x4 (&w)[4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) w[s] = ld16(wrow + k + 32 * s);
+    for (int s = 0; s < 4; ++s) w[s] = ld16(base + 128 * c + 32 * s);
   };
+  const uint16_t* wcur = rowp(min(g, n_groups - 1));
   if (g < n_groups) {
-    set_group(g);
-    load_w(0, wA);
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_w(wcur, j, wbuf[j]);
   }
   if (XL) {
     const int per_row = K / 8;
@@ -147,32 +151,27 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_gro
 
   bool first = true;
   for (; g < n_groups; g += gridDim.x) {
+    const int gnext = g + gridDim.x;
+    const bool has_next = gnext < n_groups;
+    const uint16_t* wnext = has_next ? rowp(gnext) : wcur;
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int c, const u32x4 (&w)[4]) {
-      const bool ok = c < nchunks;
-      const int kk = 128 * min(c, nchunks - 1);
+    for (int c0 = 0; c0 < nchunks; c0 += D) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int j = 0; j < D; ++j) {
+        const int c = c0 + j;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          u32x4 xv = xfrag(mt, kk + 32 * s);
-          if (!ok) xv = (u32x4){0u, 0u, 0u, 0u};
-          acc[mt] = mfma16x16x32(as_bf16x8(xv), as_bf16x8(w[s]), acc[mt]);
-        }
-    };
-    for (int c = 0; c < nchunks; c += 2) {
-      load_w(c + 1, wB);
-      compute(c, wA);
-      if (c + 2 < nchunks) load_w(c + 2, wA);
-      compute(c + 1, wB);
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), as_bf16x8(wbuf[j][s]), acc[mt]);
+        const int nc = c + D;
+        if (nc < nchunks) load_w(wcur, nc, wbuf[j]);
+        else if (has_next) load_w(wnext, nc - nchunks, wbuf[j]);
+      }
     }
-    const int gnext = g + gridDim.x;
-    if (gnext < n_groups) {   // next group's first chunk streams during the selection
-      set_group(gnext);
-      load_w(0, wA);
-    }
+    wcur = wnext;
     __syncthreads();   // every wave is done reading the previous group's tile
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -242,10 +241,19 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_gro
   }
 }
 
+template <int MT, int XL, int D>
+void launch_lm_d(const GemmArgs& a, int groups, int P, size_t lds, hipStream_t st) {
+  if (a.topk == 1) hipLaunchKernelGGL((lmhead_kernel<MT, XL, 1, D>), dim3(P), dim3(512), lds, st, a, groups);
+  else hipLaunchKernelGGL((lmhead_kernel<MT, XL, 16, D>), dim3(P), dim3(512), lds, st, a, groups);
+}
+
+// pipeline depth: the largest of 4, 2, 1 that divides the chunk count
 template <int MT, int XL>
 hipError_t launch_lm(const GemmArgs& a, int groups, int P, size_t lds, hipStream_t st) {
-  if (a.topk == 1) hipLaunchKernelGGL((lmhead_kernel<MT, XL, 1>), dim3(P), dim3(512), lds, st, a, groups);
-  else hipLaunchKernelGGL((lmhead_kernel<MT, XL, 16>), dim3(P), dim3(512), lds, st, a, groups);
+  const int nchunks = a.K / 128;
+  if (nchunks % 4 == 0) launch_lm_d<MT, XL, 4>(a, groups, P, lds, st);
+  else if (nchunks % 2 == 0) launch_lm_d<MT, XL, 2>(a, groups, P, lds, st);
+  else launch_lm_d<MT, XL, 1>(a, groups, P, lds, st);
   return hipGetLastError();
 }
 
