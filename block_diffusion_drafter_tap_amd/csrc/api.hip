@@ -24,8 +24,10 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int CU_TARGET = 256;   // workgroups (of 8 waves) wanted per weight-streaming GEMM
-constexpr int CU_GATEUP = 512;   // gate/up measured faster with more, shorter K splits
+// K chunks (of 128) per split of each projection, measured best on MI355X at the
+// qwen3-4b shape with 16 rows: about 2-4 chunks keeps a few hundred workgroups
+// streaming while the partial tiles stay small.
+constexpr int CPS_QKV = 2, CPS_O = 3, CPS_GATEUP = 4, CPS_DOWN = 3, CPS_FC = 4, CPS_STAGE_KV = 2;
 constexpr int GC_DEFAULT = 128;
 
 int attn_nchunks(const dflash_config& c) {
@@ -38,30 +40,40 @@ struct WsLayout {
 };
 
 struct GemmShape {
-  int N, K, gc, pair, cu;
+  int N, K, gc, pair, cps;
 };
+
+// Layers per stage K/V launch: split-K launches batch up to MAX_BATCH layers
+// while their partial tiles fit the budget.
+int stage_batch(const GemmPlan& p, int M, int N, int n_layers) {
+  if (p.S <= 1) return 1;
+  const long long one = (long long)gemm_partial_floats(p, M, N, 0);
+  int b = n_layers < MAX_BATCH ? n_layers : MAX_BATCH;
+  while (b > 1 && one * b > GEMM_PARTIAL_BUDGET) --b;
+  return b;
+}
 
 // Largest split-K partial buffer over every GEMM a call may launch.
 size_t gemm_scratch(const dflash_config& c) {
   const int H = c.hidden, hd = c.head_dim;
-  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, CU_TARGET},
-                             {H, c.n_q_heads * hd, GC_DEFAULT, 0, CU_TARGET},
-                             {c.ffn, H, GC_DEFAULT, 1, CU_GATEUP},
-                             {H, c.ffn, GC_DEFAULT, 0, CU_TARGET}};
-  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, CU_TARGET},
-                             {2 * c.n_kv_heads * hd, H, hd, 0, CU_TARGET}};
+  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, CPS_QKV},
+                             {H, c.n_q_heads * hd, GC_DEFAULT, 0, CPS_O},
+                             {c.ffn, H, GC_DEFAULT, 1, CPS_GATEUP},
+                             {H, c.ffn, GC_DEFAULT, 0, CPS_DOWN}};
+  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, CPS_FC},
+                             {2 * c.n_kv_heads * hd, H, hd, 0, CPS_STAGE_KV}};
   size_t pf = 0;
-  auto visit = [&](int M, const GemmShape& s, int layers) {
-    GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, s.cu);
+  auto visit = [&](int M, const GemmShape& s, bool batched) {
+    GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, s.cps);
+    const int layers = batched ? stage_batch(p, M, s.N, c.n_layers) : 1;
     size_t f = gemm_partial_floats(p, M, s.N, s.pair) * layers;
     if (f > pf) pf = f;
   };
-  const int batch = c.n_layers < MAX_BATCH ? c.n_layers : MAX_BATCH;
   for (int R = 1; R <= c.max_requests; ++R)
-    for (const auto& s : draft) visit(R * c.block, s, 1);
+    for (const auto& s : draft) visit(R * c.block, s, false);
   for (int M = 1; M <= c.max_stage_rows; ++M) {
-    visit(M, stage[0], 1);
-    visit(M, stage[1], batch);   // stage K/V batches up to MAX_BATCH layers
+    visit(M, stage[0], false);
+    visit(M, stage[1], true);
   }
   return pf;
 }
@@ -379,7 +391,7 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   a.out = g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf;
   a.ldo = H;
   {
-    GemmPlan p = plan_gemm(n_rows, H, a.K, GC_DEFAULT, 0, CU_TARGET);
+    GemmPlan p = plan_gemm(n_rows, H, a.K, GC_DEFAULT, 0, CPS_FC);
     Timed tm(ctx, DFLASH_K_FC, st);
     if (p.S > 1) {
       e = launch_gemm(a, p, X_TAPS, E_PART, WF_BF16, st);
@@ -395,10 +407,10 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   }
   // per layer: K/V of the staged rows into the ring
   const size_t rl = ring_layer_elems(g);
-  GemmPlan p = plan_gemm(n_rows, 2 * g.n_kv_heads * hd, H, hd, 0, CU_TARGET);
+  GemmPlan p = plan_gemm(n_rows, 2 * g.n_kv_heads * hd, H, hd, 0, CPS_STAGE_KV);
   // split-K (a few rows per round): up to MAX_BATCH layers share one launch of the
   // projection and one of the head finish; S = 1 (prefill) runs one launch per layer
-  const int step = p.S > 1 ? MAX_BATCH : 1;
+  const int step = stage_batch(p, n_rows, 2 * g.n_kv_heads * hd, g.n_layers);
   for (int l0 = 0; l0 < g.n_layers; l0 += step) {
     const int nl = g.n_layers - l0 < step ? g.n_layers - l0 : step;
     GemmArgs b = base_args(ctx);
@@ -418,7 +430,7 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
     b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
     if (p.S > 1) {
-      b.nb = nl;
+      b.nb = step > 1 ? nl : 0;
       for (int i = 0; i < nl; ++i) {
         b.wb[i] = ctx->wqkv[l0 + i] + (size_t)g.n_q_heads * hd * H;
         b.rkb[i] = at<uint16_t>(ctx->state, ctx->sl.ring_k) + (l0 + i) * rl;
@@ -488,7 +500,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ring_k = rk;
       a.ring_v = rv;
       a.rows_per_req = B;
-      GemmPlan p = plan_gemm(M, a.N, H, hd, 0, CU_TARGET);
+      GemmPlan p = plan_gemm(M, a.N, H, hd, 0, CPS_QKV);
       Timed tm(ctx, DFLASH_K_QKV, st);
       if (p.S > 1) {
         e = launch_gemm(a, p, X_NORM, E_PART, WF_BF16, st);
@@ -535,7 +547,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ldo = H;
       a.ssq_out = ssq;
       a.ssq_ld = ssq_ld;
-      GemmPlan p = plan_gemm(M, H, qw, GC_DEFAULT, 0, CU_TARGET);
+      GemmPlan p = plan_gemm(M, H, qw, GC_DEFAULT, 0, CPS_O);
       Timed tm(ctx, DFLASH_K_O, st);
       if (p.S > 1) {
         e = launch_gemm(a, p, X_BF16, E_PART, WF_BF16, st);
@@ -555,7 +567,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.pair_off = g.ffn;
       a.out = act;
       a.ldo = g.ffn;
-      GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CU_GATEUP);
+      GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CPS_GATEUP);
       Timed tm(ctx, DFLASH_K_GATEUP, st);
       if (p.S > 1) {
         e = launch_gemm(a, p, X_NORM, E_PARTP, WF_BF16, st);
@@ -577,7 +589,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ldo = H;
       a.ssq_out = ssq;
       a.ssq_ld = ssq_ld;
-      GemmPlan p = plan_gemm(M, H, g.ffn, GC_DEFAULT, 0, CU_TARGET);
+      GemmPlan p = plan_gemm(M, H, g.ffn, GC_DEFAULT, 0, CPS_DOWN);
       Timed tm(ctx, DFLASH_K_DOWN, st);
       if (p.S > 1) {
         e = launch_gemm(a, p, X_BF16, E_PART, WF_BF16, st);

@@ -9,8 +9,8 @@
 //   grid.z  row chunks of 16*MT rows
 // The workgroup first stages its X slice [16*MT rows][K range] in LDS (for tap
 // inputs the hc-stream mean and the bf16 cast happen here, once per element);
-// then every wave streams its W tile over the K range, two 128-wide chunks of
-// loads in flight ahead of the MFMAs. Plain (cached) loads measured faster than
+// then every wave streams its W tile over the K range, several 128-wide chunks
+// of loads in flight ahead of the MFMAs. Plain (cached) loads measured faster than
 // non-temporal ones for this pattern.
 //
 // Split-K (S > 1): each split stores its partial tile straight from the MFMA
@@ -146,7 +146,7 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
   }
 }
 
-template <int MT, int NW, int XK, int XL, int EPI>
+template <int MT, int NW, int XK, int XL, int EPI, int D>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   constexpr int ROWS = MT * 16;
   constexpr int GC = NW * 16;
@@ -180,16 +180,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   }
   const uint16_t* wrow = (const uint16_t*)wbase + (size_t)wrow_i * a.K + kbeg + 8 * lg;
 
-  // Two 128-wide chunks of W loads stay in flight; the first two are issued
-  // before the X slice is staged, so they stream during the staging.
-  u32x4 wA[4], wB[4];
+  // D 128-wide chunks of W loads stay in flight (chunk c in buffer c % D); the
+  // first D are issued before the X slice is staged, so they stream meanwhile.
+  u32x4 wbuf[D][4];
   auto load_w = [&](int c, u32x4 (&w)[4]) {
-    const int k = 128 * min(c, nchunks - 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) w[s] = ld16(wrow + k + 32 * s);
+    for (int s = 0; s < 4; ++s) w[s] = ld16(wrow + 128 * c + 32 * s);
   };
-  load_w(0, wA);
-  load_w(1, wB);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nchunks) load_w(j, wbuf[j]);
 
   __shared__ float s_inv[ROWS];
   if constexpr (XK == X_NORM) {
@@ -223,22 +223,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int c, const u32x4 (&w)[4]) {
-    const bool ok = c < nchunks;
-    const int kk = 128 * min(c, nchunks - 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        u32x4 xv = xfrag(mt, kk + 32 * s);
-        if (!ok) xv = (u32x4){0u, 0u, 0u, 0u};
-        acc[mt] = mfma16x16x32(as_bf16x8(xv), as_bf16x8(w[s]), acc[mt]);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), as_bf16x8(w[s]), acc[mt]);
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    compute(c, wA);
-    if (c + 2 < nchunks) load_w(c + 2, wA);
-    compute(c + 1, wB);
-    if (c + 3 < nchunks) load_w(c + 3, wB);
+  for (int c0 = 0; c0 < nchunks; c0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int c = c0 + j;
+      if (c < nchunks) {
+        compute(c, wbuf[j]);
+        if (c + D < nchunks) load_w(c + D, wbuf[j]);
+      }
+    }
   }
 
   if constexpr (EPI == E_PART || EPI == E_PARTP) {
@@ -323,9 +322,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   }
 }
 
+constexpr int GEMM_DEPTH = 3;   // W chunks in flight per wave (measured: 3 best or within 2%)
+
 template <int MT, int NW, int XK, int XL, int EPI>
 void launch_one(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, XK, XL, EPI>), grid, dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, XK, XL, EPI, GEMM_DEPTH>), grid, dim3(NW * 64), lds, st, a);
 }
 
 template <int MT, int NW, int XL>
@@ -369,7 +370,7 @@ constexpr size_t XL_MAX_BYTES = 96 * 1024;
 
 }  // namespace
 
-GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target) {
+GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps) {
   GemmPlan p;
   p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.NT = 1;
@@ -378,10 +379,14 @@ GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target) {
   p.groups = (N + cols_per_group - 1) / cols_per_group;
   p.mz = (M + 16 * p.MT - 1) / (16 * p.MT);
   const int kchunks = K / 128;
-  int S = 1;
+  // enough column-group x row-chunk workgroups already (prefill): no split;
+  // otherwise about cps chunks of K per split
   const long long base = (long long)p.groups * p.mz;
-  if (base < cu_target) S = (int)((cu_target + base - 1) / base);
-  S = S > kchunks ? kchunks : S;
+  int S = base >= 256 ? 1 : (kchunks + cps - 1) / cps;
+  // partial tiles stay within the workspace budget
+  const long long per_split = (long long)M * (pair ? 2 * N : N);
+  const long long cap = GEMM_PARTIAL_BUDGET / (per_split > 0 ? per_split : 1);
+  if (S > cap) S = (int)cap;
   S = S < 1 ? 1 : S;
   const int chunks_per = (kchunks + S - 1) / S;
   const int rows = 16 * p.MT;

@@ -74,7 +74,10 @@ struct GemmPlan {
   size_t lds;   // dynamic LDS bytes per workgroup
 };
 
-GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cu_target);
+// cps: target K chunks (of 128) per split when the grid needs splitting; the
+// S partial tiles of one launch never exceed GEMM_PARTIAL_BUDGET floats
+constexpr long long GEMM_PARTIAL_BUDGET = 8ll << 20;
+GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf,
                        hipStream_t st);
 size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
