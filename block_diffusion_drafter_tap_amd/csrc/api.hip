@@ -36,7 +36,7 @@ int attn_nchunks(const dflash_config& c) {
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, c32, c, partials, attn_o, attn_ml, cand_v, cand_i, mid_v, mid_i, total;
+  size_t h, ssq, q, o, act, c32, c, partials, attn_o, attn_ml, logits, gmax, total;
 };
 
 struct GemmShape {
@@ -87,7 +87,6 @@ WsLayout ws_layout(const dflash_config& c) {
   const size_t slots = (size_t)attn_slots(c.n_q_heads, c.n_kv_heads, c.block);
   const size_t lrg = (size_t)c.max_requests * c.n_kv_heads;
   const size_t nch = (size_t)attn_nchunks(c);
-  const size_t lm_groups = (c.vocab + GC_DEFAULT - 1) / GC_DEFAULT;
   const size_t out_rows = (size_t)c.max_requests * (c.block > 1 ? c.block - 1 : 1);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
@@ -101,11 +100,9 @@ WsLayout ws_layout(const dflash_config& c) {
   L.partials = take((pf ? pf : 1) * 4);
   L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
   L.attn_ml = take(lrg * nch * slots * 2 * 4);
-  L.cand_v = take(lm_groups * out_rows * 16 * 4);
-  L.cand_i = take(lm_groups * out_rows * 16 * 4);
-  const size_t nblk = (lm_groups + 63) / 64;
-  L.mid_v = take(out_rows * nblk * 16 * 4);
-  L.mid_i = take(out_rows * nblk * 16 * 4);
+  const size_t lm_rows = Mmax <= 16 ? 16 : (Mmax <= 32 ? 32 : 64 * ((Mmax + 63) / 64));
+  L.logits = take(lm_rows * c.vocab * 4);           // transposed logits when the caller passes none
+  L.gmax = take(out_rows * ((c.vocab + 15) / 16) * 4);   // per-16-column maxima of the logits
   L.total = off;
   return L;
 }
@@ -159,8 +156,8 @@ int validate_config(const dflash_config* c) {
   if (attn_slots(c->n_q_heads, c->n_kv_heads, c->block) > 64)
     return fail(DFLASH_E_UNSUPPORTED, "(n_q_heads/n_kv_heads)*block = %d query rows per kv head; at most 64",
                 attn_slots(c->n_q_heads, c->n_kv_heads, c->block));
-  if (c->vocab > 64 * 64 * GC_DEFAULT)
-    return fail(DFLASH_E_UNSUPPORTED, "vocab %d exceeds the top-k merge capacity (%d)", c->vocab, 64 * 64 * GC_DEFAULT);
+  if (c->vocab > 256 * 64 * 16)
+    return fail(DFLASH_E_UNSUPPORTED, "vocab %d exceeds the top-k selection capacity (%d)", c->vocab, 256 * 64 * 16);
   if (c->wfmt == DFLASH_W_INT4_G64)
     return fail(DFLASH_E_UNSUPPORTED, "INT4 weights are not built in this library version");
   return DFLASH_OK;
@@ -600,7 +597,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       if (e != hipSuccess) return hip_fail(e, "down proj");
     }
   }
-  {  // shared LM head with per-group top-k, then the merge
+  {  // shared LM head: mask-row logits, then per-row top-k
     GemmArgs a = base_args(ctx);
     norm_input(a, ctx->final_norm, h_blocks);
     a.w = ctx->lm_head;
@@ -608,18 +605,17 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
     a.N = g.vocab;
     a.K = H;
     a.topk = k;
-    a.logits = logits;
-    a.cand_val = at<float>(ctx->ws, ctx->wl.cand_v);
-    a.cand_idx = at<int>(ctx->ws, ctx->wl.cand_i);
-    LmPlan p = plan_lmhead(M, g.vocab, H, ctx->n_cu);
+    LmPlan p = plan_lmhead(M, B, g.vocab, H, ctx->n_cu);
+    float* lg = logits ? logits : at<float>(ctx->ws, ctx->wl.logits);
+    const int tr = logits ? 0 : 1;
+    float* gm = at<float>(ctx->ws, ctx->wl.gmax);
     {
       Timed tm(ctx, DFLASH_K_LMHEAD, st);
-      e = launch_lmhead(a, p, st);
+      e = launch_lm_logits(a, p, lg, tr, gm, st);
     }
     if (e != hipSuccess) return hip_fail(e, "lm head");
-    e = launch_topk_merge(a.cand_val, a.cand_idx, p.P, n_req * (B - 1), k, at<float>(ctx->ws, ctx->wl.mid_v),
-                          at<int>(ctx->ws, ctx->wl.mid_i), topk_ids, topk_vals, st);
-    if (e != hipSuccess) return hip_fail(e, "topk merge");
+    e = launch_lm_topk(a, p, lg, tr, gm, topk_ids, topk_vals, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k");
   }
   return DFLASH_OK;
 }

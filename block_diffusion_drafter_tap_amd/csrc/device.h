@@ -55,6 +55,40 @@ DEV T pick(const T (&arr)[N], int i) {
 // (value desc, index asc) ordering used by argmax / top-k.
 DEV bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
+// Rank-merge tree over sorted top-K lists held in LDS. Lists 0..width-1 (width a
+// power of two) live in bv/bi[0]; every entry is (value, id) with all ids
+// distinct, lists sorted best first. A pair of lists merges in one parallel
+// step: entry A[e] lands at rank e + #{entries of B better than A[e]} (binary
+// search), likewise for B, and only ranks below K are kept. Returns the buffer
+// (0 or 1) whose list 0 holds the merged result. All threads of the block call it.
+template <int K, int L>
+DEV int merge_tree(float (*bv)[L][K], int (*bi)[L][K], int width) {
+  int cur = 0;
+  for (; width > 1; width >>= 1) {
+    const int pairs = width / 2;
+    for (int t = threadIdx.x; t < pairs * 2 * K; t += blockDim.x) {
+      const int p = t / (2 * K), e = t % (2 * K);
+      const int own = e < K ? 2 * p : 2 * p + 1, oth = e < K ? 2 * p + 1 : 2 * p;
+      const int idx = e < K ? e : e - K;
+      const float x = bv[cur][own][idx];
+      const int xi = bi[cur][own][idx];
+      int lo = 0, hi = K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (better(bv[cur][oth][mid], bi[cur][oth][mid], x, xi)) lo = mid + 1; else hi = mid;
+      }
+      const int rank = idx + lo;
+      if (rank < K) {
+        bv[cur ^ 1][p][rank] = x;
+        bi[cur ^ 1][p][rank] = xi;
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  return cur;
+}
+
 DEV void set_error(unsigned* err, unsigned bit) {
   if (err) atomicOr(err, bit);
 }

@@ -193,11 +193,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 
   __shared__ float s_inv[ROWS];
   if constexpr (XK == X_NORM) {
-    // 1/rms of each row from the producer's per-column-block sums of squares
+    // 1/rms of each row from the producer's per-column-group sums of squares
+    // (summed in group order; the loads of 8 groups are in flight together)
     for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
       const int m = min(m0 + r, a.M - 1);
       float ss = 0.f;
-      for (int b = 0; b < a.n_ssq; ++b) ss += a.ssq_in[(size_t)b * a.ssq_ld + m];
+      for (int b0 = 0; b0 < a.n_ssq; b0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = a.ssq_in[(size_t)min(b0 + u, a.n_ssq - 1) * a.ssq_ld + m];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (b0 + u < a.n_ssq) ss += v[u];
+      }
       s_inv[r] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
     }
     __syncthreads();

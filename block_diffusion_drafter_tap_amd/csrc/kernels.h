@@ -62,11 +62,8 @@ struct GemmArgs {
   const int* pos_of_row;  // NULL -> pos[req] + row % rows_per_req
   int rows_per_req;
   unsigned* err;
-  // LM head: rows m = r*B + i; mask rows i >= 1 produce candidates
+  // LM head: rows m = r*B + i; mask rows i >= 1 produce logits
   int B, topk;
-  float* logits;     // NULL or [R][B-1][N]
-  float* cand_val;   // [groups][R*(B-1)][topk]
-  int* cand_idx;
 };
 
 struct GemmPlan {
@@ -82,15 +79,21 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, in
                        hipStream_t st);
 size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
 
-// Persistent LM head with running top-k (topk 1 or 16); reads the GemmArgs
-// X_NORM fields (xf, xgain, ssq_*), w = W_lm, M, N = vocab, K, B, topk,
-// logits, cand_val, cand_idx. Candidates: [P][R*(B-1)][topk].
+// LM head: persistent logits GEMM over the block rows (GemmArgs X_NORM fields
+// xf, xgain, ssq_*, w = W_lm, M = R*B, N = vocab, K, B, topk): fp32 logits to
+// the caller's logits[R*(B-1)][N] (mask rows), or transposed to a scratch
+// [N][16*MT] (all rows; coalesced), and per-16-column maxima of the mask rows to
+// gmax[R*(B-1)][ceil(N/16)]; then the exact per-row top-k to ids/vals
+// [R*(B-1)][topk] (topk <= 16).
 struct LmPlan {
   int MT, XL, groups, P;
   size_t lds;
 };
-LmPlan plan_lmhead(int M, int V, int K, int n_cu);
-hipError_t launch_lmhead(const GemmArgs& a, const LmPlan& p, hipStream_t st);
+LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu);
+hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, int transposed, float* gmax,
+                            hipStream_t st);
+hipError_t launch_lm_topk(const GemmArgs& a, const LmPlan& p, const float* logits, int transposed,
+                          const float* gmax, int* ids, float* vals, hipStream_t st);
 
 // Attention over [context window | block] per (request, kv head), split over key chunks.
 struct AttnArgs {
@@ -131,8 +134,8 @@ hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, floa
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* a, int M, int H,
                           float eps, hipStream_t st);
 hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hipStream_t st);
-hipError_t launch_topk_merge(const float* cand_val, const int* cand_idx, int groups, int rows,
-                             int k, float* mid_v, int* mid_i, int* ids, float* vals, hipStream_t st);
+hipError_t launch_topk_final(const float* list_v, const int* list_i, int n_lists, int rows, int k, int* ids,
+                             float* vals, hipStream_t st);
 hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B,
                          int eos, const int* budget, int mask_id, int* accept_len,
                          int* emitted, int* n_emit, int* next_tokens, int* pos,

@@ -1,18 +1,18 @@
-// Shared LM head with fused top-k for gfx950.
+// Shared LM head for gfx950: logits of the block's mask rows, then top-k.
 //
-// logits = W_lm z for every block row, z = RMSNorm(h; final gain) as bf16,
-// followed by per-row top-k over the vocabulary. Persistent: workgroup w
-// handles column groups w, w + P, ... of 128 vocabulary rows; the normed X is
-// staged in LDS once (or read from L2 when it does not fit). Each row belongs
-// to one wave, which keeps the row's running top-k in registers (lanes 0..k-1,
-// best first):
-//   k = 1   a wave reduction per group;
-//   k = 16  the first group is sorted by a bitonic network on registers and
-//           shuffles (two values per lane), later groups only insert the values
-//           that beat the current k-th entry (ballot, then a shifted insert).
-// Weight loads run four 128-wide chunks ahead, across group boundaries, so the
-// next group's first chunks are in flight during the selection.
-// Output: per workgroup and mask row, its k best (value, id), best first.
+// lm_logits_kernel: logits = W_lm z for every block row, z = RMSNorm(h; final
+// gain) rounded to bf16. Persistent: workgroup w streams column groups w,
+// w + P, ... of 128 vocabulary rows with 8 waves (one 16-row W tile each).
+// The normed rows are staged in LDS once (all loads of a batch in flight
+// together), W chunks of 128 k-values run D deep across group boundaries, and
+// each wave stores its fp32 tile of the mask rows straight from the MFMA
+// accumulators: there is no barrier in the streaming loop.
+//
+// The logits kernel also writes, per mask row, the max of every 16-column group.
+// topk_rows_kernel: per row, an exact radix select picks the k best groups by
+// their max, and the k best of those groups' logits are ranked directly.
+// Selecting after streaming keeps the dependent cross-lane work of a running
+// top-k out of the weight stream, where it stalled the loads.
 
 #include "device.h"
 #include "kernels.h"
@@ -39,89 +39,34 @@ DEV u32x4 norm_x8(const GemmArgs& a, int row, int k, float inv) {
   return r;
 }
 
-// Sort 128 (value, id) pairs held as lane + 64*u, u = 0, 1, best first.
-DEV void wave_sort128(float (&v)[2], int (&id)[2]) {
-  const int lane = threadIdx.x & 63;
+// bf16x8 of (h0, h1) * inv * g (g: 8 bf16 gains)
+DEV u32x4 norm8(f32x4 h0, f32x4 h1, u32x4 g, float inv) {
+  u32x4 r;
 #pragma unroll
-  for (int k = 2; k <= 128; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = lane + 64 * u;
-        float ov;
-        int oi;
-        if (j == 64) {
-          ov = v[u ^ 1];
-          oi = id[u ^ 1];
-        } else {
-          ov = __shfl_xor(v[u], j, 64);
-          oi = __shfl_xor(id[u], j, 64);
-        }
-        const bool lo = (i & j) == 0, first = (i & k) == 0;
-        const bool take_other = (lo == first) ? better(ov, oi, v[u], id[u]) : better(v[u], id[u], ov, oi);
-        if (j == 64) {
-          // both halves of the pair live in this lane: resolve once (u == 0)
-          if (u == 0 && take_other) {
-            const float tv = v[0]; const int ti = id[0];
-            v[0] = v[1]; id[0] = id[1];
-            v[1] = tv; id[1] = ti;
-          }
-        } else if (take_other) {
-          v[u] = ov;
-          id[u] = oi;
-        }
-      }
-    }
+  for (int i = 0; i < 2; ++i) {
+    const f32x4 h = i ? h1 : h0;
+    r[2 * i] = pack_bf16x2(h[0] * inv * __uint_as_float(g[2 * i] << 16),
+                           h[1] * inv * __uint_as_float(g[2 * i] & 0xffff0000u));
+    r[2 * i + 1] = pack_bf16x2(h[2] * inv * __uint_as_float(g[2 * i + 1] << 16),
+                               h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
   }
+  return r;
 }
 
-// Insert (cv, ci) into a sorted list held by lanes 0..K-1 (if it belongs).
-template <int K>
-DEV void wave_insert(float& rv, int& ri, float cv, int ci) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long ahead = __ballot(lane < K && better(rv, ri, cv, ci));
-  const int pos = __popcll(ahead);
-  const float up_v = __shfl_up(rv, 1, 64);
-  const int up_i = __shfl_up(ri, 1, 64);
-  if (pos < K && lane < K && lane >= pos) {
-    if (lane == pos) { rv = cv; ri = ci; }
-    else { rv = up_v; ri = up_i; }
-  }
-}
-
-template <int MT, int XL, int KK, int D>
-__global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_groups) {
-  constexpr int NW = 8, GC = 128, ROWS = MT * 16, RPW = ROWS / NW;   // rows per wave
+template <int MT, int XL, int D>
+__global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_groups, float* logits, int transposed,
+                                                        float* gmax) {
+  constexpr int NW = 8, GC = 128, ROWS = MT * 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ float s_inv[ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = a.K, nchunks = K / 128, ldl = K + 8;
   uint16_t* xs = (uint16_t*)smem;
-  float(*tile)[GC + 1] = (float(*)[GC + 1])(smem + (XL ? (size_t)ROWS * ldl * 2 : 0));
-  const int rows = min(ROWS, a.M);
 
-  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
-    const int m = min(r, a.M - 1);
-    float ss = 0.f;
-    for (int b = 0; b < a.n_ssq; ++b) ss += a.ssq_in[(size_t)b * a.ssq_ld + m];
-    s_inv[r] = 1.0f / sqrtf(ss / (float)K + a.eps);
-  }
-  __syncthreads();
-  // running lists: row wave + NW*t lives in lanes 0..KK-1 of rv[t], ri[t]
-  float rv[RPW];
-  int ri[RPW];
-#pragma unroll
-  for (int t = 0; t < RPW; ++t) {
-    rv[t] = -INFINITY;
-    ri[t] = 0x7fffffff - (t * 64 + lane);   // distinct placeholder ids
-  }
-
-  // W chunks of 128 k-values stream D deep: chunk c of a group lives in buffer
-  // c % D (D divides the chunk count), and the last D buffers of a group are
-  // refilled with the next group's first chunks, so loads stay in flight
-  // through the top-k selection.
+  // W chunks stream D deep: chunk c of a group lives in buffer c % D (D divides
+  // the chunk count); the last D buffers of a group are refilled with the next
+  // group's first chunks
   int g = blockIdx.x;
   auto rowp = [&](int gg) {
     return (const uint16_t*)a.w + (size_t)min(gg * GC + wave * 16 + lr, a.N - 1) * K + 8 * lg;
@@ -136,11 +81,44 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_gro
 #pragma unroll
     for (int j = 0; j < D; ++j) load_w(wcur, j, wbuf[j]);
   }
+
+  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
+    const int m = min(r, a.M - 1);
+    float ss = 0.f;
+    for (int b0 = 0; b0 < a.n_ssq; b0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.ssq_in[(size_t)min(b0 + u, a.n_ssq - 1) * a.ssq_ld + m];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < a.n_ssq) ss += v[u];
+    }
+    s_inv[r] = 1.0f / sqrtf(ss / (float)K + a.eps);
+  }
+  __syncthreads();
   if (XL) {
-    const int per_row = K / 8;
-    for (int e = threadIdx.x; e < ROWS * per_row; e += blockDim.x) {
-      const int r = e / per_row, c = e % per_row;
-      *(u32x4*)(xs + r * ldl + 8 * c) = norm_x8(a, min(r, a.M - 1), 8 * c, s_inv[r]);
+    // 8 vectors of a thread in flight per batch
+    const int per_row = K / 8, total = ROWS * per_row;
+    for (int e0 = threadIdx.x; e0 < total; e0 += 8 * blockDim.x) {
+      f32x4 h0[8], h1[8];
+      u32x4 gg[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(e0 + u * (int)blockDim.x, total - 1);
+        const int r = e / per_row, c = e % per_row;
+        const float* p = a.xf + (size_t)min(r, a.M - 1) * a.ldx + 8 * c;
+        h0[u] = *(const f32x4*)p;
+        h1[u] = *(const f32x4*)(p + 4);
+        gg[u] = ld16(a.xgain + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * (int)blockDim.x;
+        if (e < total) {
+          const int r = e / per_row, c = e % per_row;
+          *(u32x4*)(xs + r * ldl + 8 * c) = norm8(h0[u], h1[u], gg[u], s_inv[r]);
+        }
+      }
     }
     __syncthreads();
   }
@@ -149,7 +127,6 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_gro
     return norm_x8(a, min(mt * 16 + lr, a.M - 1), k + 8 * lg, s_inv[mt * 16 + lr]);
   };
 
-  bool first = true;
   for (; g < n_groups; g += gridDim.x) {
     const int gnext = g + gridDim.x;
     const bool has_next = gnext < n_groups;
@@ -172,94 +149,294 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const GemmArgs a, int n_gro
       }
     }
     wcur = wnext;
-    __syncthreads();   // every wave is done reading the previous group's tile
+    // Logits: the caller's layout [R*(B-1)][N] (mask rows only), or the
+    // transposed scratch layout [N][16*MT] (every row), where a wave's 16
+    // columns x 16 rows of a tile are one contiguous 1 KB store.
+    // The 16 lanes of a lane group also reduce their row's max over the wave's
+    // 16 columns (one entry per 16-column group, for the top-k filter).
+    const int n = g * GC + wave * 16 + lr;
+    const int ng = (a.N + 15) / 16, grp16 = g * (GC / 16) + wave;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+      if (transposed && n < a.N) *(f32x4*)(logits + (size_t)n * ROWS + mt * 16 + 4 * lg) = acc[mt];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tile[mt * 16 + 4 * lg + i][wave * 16 + lr] = acc[mt][i];
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < RPW; ++t) {
-      const int r = wave + NW * t;
-      float v[2];
-      int id[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = lane + 64 * u, n = g * GC + c;
-        id[u] = n;
-        const bool ok = r < rows && n < a.N;
-        v[u] = ok ? tile[r][c] : -INFINITY;
-        if (ok && a.logits) {
-          const int i = r % a.B;
-          if (i) a.logits[(size_t)((r / a.B) * (a.B - 1) + i - 1) * a.N + n] = v[u];
-        }
-      }
-      if constexpr (KK == 1) {
-        float bv = v[0];
-        int bi = id[0];
-        if (better(v[1], id[1], bv, bi)) { bv = v[1]; bi = id[1]; }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const float ov = __shfl_xor(bv, o, 64);
-          const int oi = __shfl_xor(bi, o, 64);
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        if (better(bv, bi, rv[t], ri[t])) { rv[t] = bv; ri[t] = bi; }
-      } else if (first) {
-        wave_sort128(v, id);
-        rv[t] = v[0];   // lanes 0..15 hold the group's 16 best
-        ri[t] = id[0];
-      } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float thv = __shfl(rv[t], KK - 1, 64);
-          int thi = __shfl(ri[t], KK - 1, 64);
-          unsigned long long mask = __ballot(better(v[u], id[u], thv, thi));
-          while (mask) {
-            const int b = __builtin_ctzll(mask);
-            mask &= mask - 1;
-            const float cv = __shfl(v[u], b, 64);
-            const int ci = __shfl(id[u], b, 64);
-            if (!better(cv, ci, thv, thi)) continue;   // threshold rose meanwhile
-            wave_insert<KK>(rv[t], ri[t], cv, ci);
-            thv = __shfl(rv[t], KK - 1, 64);
-            thi = __shfl(ri[t], KK - 1, 64);
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * lg + i;
+        const int bi = m % a.B;
+        const bool row_ok = m < a.M && bi != 0;
+        const size_t orow = (size_t)((m / a.B) * (a.B - 1) + bi - 1);
+        if (!transposed && row_ok && n < a.N) logits[orow * a.N + n] = acc[mt][i];
+        float v = n < a.N ? acc[mt][i] : -INFINITY;
+        v = fmaxf(v, __shfl_xor(v, 1, 64));
+        v = fmaxf(v, __shfl_xor(v, 2, 64));
+        v = fmaxf(v, __shfl_xor(v, 4, 64));
+        v = fmaxf(v, __shfl_xor(v, 8, 64));
+        if (row_ok && lr == 0 && grp16 < ng) gmax[orow * ng + grp16] = v;
       }
     }
-    first = false;
   }
-  const int n_out = (a.M / a.B) * (a.B - 1);
+}
+
+// Order-preserving key of an fp32 value (larger value -> larger key; -0 maps to
+// +0; NaN ordered above +inf, never produced by the logits).
+DEV unsigned fkey(float v) {
+  unsigned u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;   // -0 and +0 compare equal (ties go by index)
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exact top-k (k <= 16) by (key desc, index asc) over the block's values: thread t
+// holds the PER keys of indices [t*PER, t*PER + cnt) (contiguous, in index
+// order). Radix select on 8-bit digits finds the k-th key P; every key above P is
+// taken, and of the keys equal to P the lowest indices fill the rest. Writes the k
+// selected (key, index) pairs to sel_key/sel_idx (unordered). 256 threads.
+template <int PER>
+DEV void block_select(const unsigned (&key)[PER], int cnt, int base_idx, int k, unsigned* sel_key, int* sel_idx,
+                      unsigned* hist, int* scratch) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  unsigned prefix = 0, pmask = 0;
+  int need = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[t] = 0;
+    __syncthreads();
 #pragma unroll
-  for (int t = 0; t < RPW; ++t) {
-    const int r = wave + NW * t, i = r % a.B;
-    if (r >= rows || i == 0 || lane >= KK) continue;
-    const size_t o = ((size_t)blockIdx.x * n_out + (r / a.B) * (a.B - 1) + i - 1) * KK + lane;
-    a.cand_val[o] = rv[t];
-    a.cand_idx[o] = ri[t];
+    for (int j = 0; j < PER; ++j)
+      if (j < cnt && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l; an inclusive scan over lanes counts
+      // the keys at or above each lane's lowest digit
+      unsigned c[4], s4 = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        s4 += c[q];
+      }
+      unsigned incl = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned up = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += up;
+      }
+      const unsigned long long hit = __ballot(incl >= (unsigned)need);
+      const int L = (int)__builtin_ctzll(hit);   // first lane reaching need (exists: need <= count)
+      if (lane == L) {
+        unsigned above = incl - s4;
+        int d = 255 - 4 * lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (above + c[q] >= (unsigned)need) { d = 255 - 4 * lane - q; break; }
+          above += c[q];
+        }
+        scratch[0] = d;
+        scratch[1] = (int)above;
+      }
+    }
+    __syncthreads();
+    const int d = scratch[0];
+    need -= scratch[1];
+    prefix |= (unsigned)d << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  // keys above P: k - need of them, any order
+  if (t == 0) scratch[2] = 0;
+  int eq = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) eq += (j < cnt && key[j] == prefix) ? 1 : 0;
+  // exclusive scan of the per-thread counts of keys equal to P (index order)
+  int incl = eq;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += up;
+  }
+  if (lane == 63) scratch[4 + wave] = incl;
+  __syncthreads();
+  int before = incl - eq;
+  for (int w = 0; w < wave; ++w) before += scratch[4 + w];
+  const int n_above = k - need;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (j >= cnt) continue;
+    if (key[j] > prefix) {
+      const int slot = atomicAdd(&scratch[2], 1);
+      sel_key[slot] = key[j];
+      sel_idx[slot] = base_idx + j;
+    } else if (key[j] == prefix) {
+      if (before < need) {
+        sel_key[n_above + before] = key[j];
+        sel_idx[n_above + before] = base_idx + j;
+      }
+      ++before;
+    }
+  }
+  __syncthreads();
+}
+
+// Within one wave: the k-th largest (1 <= k <= number of valid entries) of up
+// to 256 keys, four per lane (entry lane + 64q). Bitwise radix select with
+// ballots: at each bit, the keys that match the decided high bits and have the
+// bit set are counted; if they are enough the k-th largest has the bit set,
+// else they all rank above it.
+DEV unsigned wave_kth_largest(const unsigned (&key)[4], const bool (&valid)[4], int k) {
+  unsigned prefix = 0;
+  int need = k;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned cand = prefix | (1u << bit);
+    const unsigned hi = ~((1u << bit) - 1u);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += __popcll(__ballot(valid[q] && (key[q] & hi) == cand));
+    if (cnt >= need) prefix = cand;
+    else need -= cnt;
+  }
+  return prefix;
+}
+
+// Per mask row: T = the k-th best per-thread maximum of the 16-column group
+// maxima (a wave radix select); every group reaching T is a candidate, a
+// superset of the k best groups, since at least k groups reach T. A top-k logit
+// always lies in a top-k group under (max desc, group asc), because groups are
+// contiguous index ranges. The candidates' logits (at most 512; otherwise the
+// exact top-k groups from a block radix select) are ranked by counting. Output
+// sorted by (value desc, index asc). The row's group maxima are staged in
+// dynamic LDS.
+// logits element (row r, column n): caller layout logits[r * N + n], or the
+// transposed scratch logits[n * cs + srow], srow = req*B + i for r = req*(B-1) + i - 1.
+template <int PER>
+__global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ logits, long long cs, int B,
+                                                        int transposed, const float* __restrict__ gmax, int N, int k,
+                                                        int* ids, float* vals) {
+  extern __shared__ __attribute__((aligned(16))) float s_g[];   // [ng]
+  __shared__ unsigned hist[256];
+  __shared__ int scratch[8];
+  __shared__ unsigned sel_key[16];
+  __shared__ int sel_idx[16];
+  __shared__ unsigned cand_k[256];
+  __shared__ int cand_i[256];
+  __shared__ unsigned s_tmax[256];
+  __shared__ __attribute__((aligned(16))) unsigned cb_k[512];
+  __shared__ __attribute__((aligned(16))) int cb_i[512];
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int ng = (N + 15) / 16;
+  const float* gm = gmax + (size_t)row * ng;
+  if (t == 0) scratch[3] = 0;
+  // thread t owns groups t + 256*j: coalesced loads, all in flight together
+  float gv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) gv[j] = gm[min(t + 256 * j, ng - 1)];
+  unsigned key[PER];
+  unsigned tmax = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    key[j] = t + 256 * j < ng ? fkey(gv[j]) : 0u;
+    tmax = key[j] > tmax ? key[j] : tmax;
+  }
+  s_tmax[t] = tmax;
+  __syncthreads();
+  const int kg = min(k, ng);   // fewer groups than k: all of them
+  // T = the kg-th best per-thread maximum: at least kg groups reach it, so every
+  // top-kg group does
+  if (wave == 0) {
+    unsigned q4[4];
+    bool v4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      q4[q] = s_tmax[lane + 64 * q];
+      v4[q] = true;
+    }
+    const unsigned T = wave_kth_largest(q4, v4, kg);
+    if (lane == 0) scratch[2] = (int)T;
+  }
+  __syncthreads();
+  const unsigned T = (unsigned)scratch[2];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (t + 256 * j < ng && key[j] >= T) {
+      const int slot = atomicAdd(&scratch[3], 1);
+      if (slot < 256) {
+        cand_k[slot] = key[j];
+        cand_i[slot] = t + 256 * j;
+      }
+    }
+  }
+  __syncthreads();
+  const int n_cand = scratch[3];
+  // candidate groups: all groups reaching T when their logits fit (a superset
+  // of the top-kg groups), else exactly the top-kg groups (radix select)
+  int n_groups_c;
+  const int* gsel;
+  if (n_cand * 16 <= 512) {
+    n_groups_c = n_cand;
+    gsel = cand_i;
+  } else {
+    // ties defeat the filter: exact radix select over contiguous group ranges
+    // (thread t owns groups [t*PER, t*PER + cnt)), staged through LDS
+    for (int j0 = t; j0 < ng; j0 += 256) s_g[j0] = gm[j0];
+    __syncthreads();
+    const int g0 = t * PER;
+    const int cnt = max(0, min(PER, ng - g0));
+    unsigned kc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) kc[j] = j < cnt ? fkey(s_g[min(g0 + j, ng - 1)]) : 0u;
+    block_select<PER>(kc, cnt, g0, kg, sel_key, sel_idx, hist, scratch);
+    n_groups_c = kg;
+    gsel = sel_idx;
+  }
+  // stage B: the logits of the candidate groups, ranked by counting
+  const int nc = 16 * n_groups_c;
+  const size_t srow = transposed ? (size_t)(row / (B - 1) * B + row % (B - 1) + 1) : (size_t)row;
+  for (int e = t; e < nc; e += 256) {
+    const int n = 16 * gsel[e / 16] + (e % 16);
+    const int nn = min(n, N - 1);
+    const float v = transposed ? logits[(size_t)nn * cs + srow] : logits[srow * N + nn];
+    cb_k[e] = n < N ? fkey(v) : 0u;
+    cb_i[e] = n < N ? n : 0x7fffffff - e;
+  }
+  const int ncp = (nc + 3) & ~3;
+  for (int e = nc + t; e < ncp; e += 256) {   // pad to whole 16-byte reads
+    cb_k[e] = 0u;
+    cb_i[e] = 0x7fffffff - e;
+  }
+  __syncthreads();
+  const u32x4* k4 = (const u32x4*)cb_k;
+  const u32x4* i4 = (const u32x4*)cb_i;
+  for (int e = t; e < nc; e += 256) {
+    const unsigned kk = cb_k[e];
+    const int ii = cb_i[e];
+    int rank = 0;
+    for (int j4 = 0; j4 < ncp / 4; ++j4) {
+      const u32x4 qk = k4[j4], qi = i4[j4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rank += (qk[q] > kk || (qk[q] == kk && (int)qi[q] < ii)) ? 1 : 0;
+    }
+    if (rank < k) {
+      ids[(size_t)row * k + rank] = ii;
+      if (vals) {
+        const unsigned u = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;   // inverse of fkey
+        vals[(size_t)row * k + rank] = __uint_as_float(u);
+      }
+    }
   }
 }
 
-template <int MT, int XL, int D>
-void launch_lm_d(const GemmArgs& a, int groups, int P, size_t lds, hipStream_t st) {
-  if (a.topk == 1) hipLaunchKernelGGL((lmhead_kernel<MT, XL, 1, D>), dim3(P), dim3(512), lds, st, a, groups);
-  else hipLaunchKernelGGL((lmhead_kernel<MT, XL, 16, D>), dim3(P), dim3(512), lds, st, a, groups);
-}
-
-// pipeline depth: the largest of 4, 2, 1 that divides the chunk count
 template <int MT, int XL>
-hipError_t launch_lm(const GemmArgs& a, int groups, int P, size_t lds, hipStream_t st) {
+hipError_t launch_lm(const GemmArgs& a, int groups, int P, size_t lds, float* logits, int tr, float* gmax,
+                     hipStream_t st) {
   const int nchunks = a.K / 128;
-  if (nchunks % 4 == 0) launch_lm_d<MT, XL, 4>(a, groups, P, lds, st);
-  else if (nchunks % 2 == 0) launch_lm_d<MT, XL, 2>(a, groups, P, lds, st);
-  else launch_lm_d<MT, XL, 1>(a, groups, P, lds, st);
+  if (nchunks % 4 == 0)
+    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+  else if (nchunks % 2 == 0)
+    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 2>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+  else
+    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 1>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
   return hipGetLastError();
 }
 
 }  // namespace
 
-LmPlan plan_lmhead(int M, int V, int K, int n_cu) {
+LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   LmPlan p;
   p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.groups = (V + 127) / 128;
@@ -268,18 +445,38 @@ LmPlan plan_lmhead(int M, int V, int K, int n_cu) {
   const int rows = 16 * p.MT;
   const size_t xbytes = (size_t)rows * (K + 8) * 2;
   p.XL = xbytes <= LM_XL_MAX_BYTES;
-  p.lds = (p.XL ? xbytes : 0) + (size_t)rows * 129 * 4;
+  p.lds = p.XL ? xbytes : 0;
   return p;
 }
 
-hipError_t launch_lmhead(const GemmArgs& a, const LmPlan& p, hipStream_t st) {
-  if (a.topk != 1 && a.topk != 16) return hipErrorInvalidValue;
-#define LM(MT) return p.XL ? launch_lm<MT, 1>(a, p.groups, p.P, p.lds, st) : launch_lm<MT, 0>(a, p.groups, p.P, p.lds, st);
+hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, int transposed, float* gmax,
+                            hipStream_t st) {
+  if (a.B < 2) return hipErrorInvalidValue;
+  hipError_t e;
+#define LM(MT) e = p.XL ? launch_lm<MT, 1>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) : launch_lm<MT, 0>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st);
   switch (p.MT) {
-    case 1: LM(1)
-    case 2: LM(2)
-    case 4: LM(4)
+    case 1: LM(1) break;
+    case 2: LM(2) break;
+    case 4: LM(4) break;
     default: return hipErrorInvalidValue;
   }
 #undef LM
+  return e;
+}
+
+hipError_t launch_lm_topk(const GemmArgs& a, const LmPlan& p, const float* logits, int transposed,
+                          const float* gmax, int* ids, float* vals, hipStream_t st) {
+  if (a.topk < 1 || a.topk > 16 || a.B < 2) return hipErrorInvalidValue;
+  const int rows = (a.M / a.B) * (a.B - 1);
+  const int ng = (a.N + 15) / 16;
+  if (ng > 256 * 64) return hipErrorInvalidValue;   // at most 64 groups per thread
+  const long long cs = 16ll * p.MT;   // transposed scratch: [N][16*MT]
+  const size_t lds = (size_t)ng * sizeof(float);
+#define TK(PER) hipLaunchKernelGGL((topk_rows_kernel<PER>), dim3(rows), dim3(256), lds, st, logits, cs, a.B, transposed, gmax, a.N, a.topk, ids, vals)
+  if (ng <= 256 * 8) TK(8);
+  else if (ng <= 256 * 16) TK(16);
+  else if (ng <= 256 * 40) TK(40);
+  else TK(64);
+#undef TK
+  return hipGetLastError();
 }

@@ -1,5 +1,6 @@
 // Latency-bound kernels of the drafter round: state fill, embedding gather with
-// the first RMSNorm, RMSNorm, position set, top-k merge and first-mismatch accept.
+// the first RMSNorm, RMSNorm, position set, the final top-k merge and
+// first-mismatch accept.
 #include "device.h"
 #include "kernels.h"
 
@@ -65,12 +66,9 @@ __global__ void set_pos_kernel(int* pos, int* valid_from, int req, int vf, int p
   }
 }
 
-// Top-k merge. Candidate lists (each sorted best first by (value desc, index
-// asc), all keys distinct) are merged pairwise in a tree held in LDS. A pair of
-// sorted lists A, B merges in one parallel step: element A[e] lands at output
-// rank e + #{B entries better than A[e]} (a binary search), likewise for B, and
-// only ranks below k are kept. One workgroup merges up to 64 lists of one row;
-// list l of row r is read at in + (l * list_stride + r * row_stride) * k.
+// Top-k merge of up to 64 candidate lists of one row per workgroup (sorted best
+// first by (value desc, index asc), all keys distinct) with the rank-merge tree.
+// List l of row r is read at in + (l * list_stride + r * row_stride) * K.
 // Missing lists are padded with -inf entries carrying distinct ids.
 template <int K>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const float* in_v, const int* in_i, int n_lists,
@@ -95,29 +93,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* in_v, cons
     }
   }
   __syncthreads();
-  int cur = 0;
-  for (; width > 1; width >>= 1) {
-    const int pairs = width / 2;
-    for (int t = threadIdx.x; t < pairs * 2 * K; t += blockDim.x) {
-      const int p = t / (2 * K), e = t % (2 * K);
-      const int own = e < K ? 2 * p : 2 * p + 1, oth = e < K ? 2 * p + 1 : 2 * p;
-      const int idx = e < K ? e : e - K;
-      const float x = bv[cur][own][idx];
-      const int xi = bi[cur][own][idx];
-      int lo = 0, hi = K;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (better(bv[cur][oth][mid], bi[cur][oth][mid], x, xi)) lo = mid + 1; else hi = mid;
-      }
-      const int rank = idx + lo;
-      if (rank < K) {
-        bv[cur ^ 1][p][rank] = x;
-        bi[cur ^ 1][p][rank] = xi;
-      }
-    }
-    __syncthreads();
-    cur ^= 1;
-  }
+  const int cur = merge_tree<K, 64>(bv, bi, width);
   if ((int)threadIdx.x < K) {
     const size_t o = (size_t)row * out_row_stride + (size_t)blk * K + threadIdx.x;
     if (out_v) out_v[o] = bv[cur][0][threadIdx.x];
@@ -196,20 +172,18 @@ hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hip
   return hipGetLastError();
 }
 
-hipError_t launch_topk_merge(const float* cand_val, const int* cand_idx, int groups, int rows, int k,
-                             float* mid_v, int* mid_i, int* ids, float* vals, hipStream_t st) {
-  const int nblk = (groups + 63) / 64;
-  if (nblk > 64) return hipErrorInvalidValue;
-  // stage 1: blocks of 64 group lists -> one list per block; stage 2: the block lists -> top-k
-#define MERGE(KK)                                                                                        \
-  hipLaunchKernelGGL((topk_merge_kernel<KK>), dim3(rows, nblk), dim3(256), 0, st, cand_val, cand_idx,    \
-                     groups, (long long)rows, 1ll, mid_v, mid_i, (long long)nblk * KK);                   \
-  hipLaunchKernelGGL((topk_merge_kernel<KK>), dim3(rows, 1), dim3(256), 0, st, (const float*)mid_v,      \
-                     (const int*)mid_i, nblk, 1ll, (long long)nblk, vals, ids, (long long)KK);
-  if (k == 1) { MERGE(1) }
-  else if (k == 16) { MERGE(16) }
-  else return hipErrorInvalidValue;
-#undef MERGE
+hipError_t launch_topk_final(const float* list_v, const int* list_i, int n_lists, int rows, int k, int* ids,
+                             float* vals, hipStream_t st) {
+  if (n_lists > 64) return hipErrorInvalidValue;
+  // lists [rows][n_lists][k] -> ids/vals [rows][k]
+  if (k == 1)
+    hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(rows, 1), dim3(256), 0, st, list_v, list_i, n_lists, 1ll,
+                       (long long)n_lists, vals, ids, 1ll);
+  else if (k == 16)
+    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(rows, 1), dim3(256), 0, st, list_v, list_i, n_lists, 1ll,
+                       (long long)n_lists, vals, ids, 16ll);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -179,3 +179,35 @@ def test_accept_kernel_cases(tiny_setup):
             assert em[:n] == exp["emitted"] and all(x == -1 for x in em[n:])
             assert pos[r] == 1000 + r + n
             assert out["next_tokens"][r].cpu().tolist() == D.next_block(exp["emitted"], B, cfg.mask_id)
+
+
+def test_topk_exact_ties_tiny(tiny_setup):
+    """Massive exact ties in the logits: the LM head's rows repeat with period 37,
+    so every logit value occurs ~110 times. Top-16 and argmax must still be the
+    (value desc, index asc) order of the GPU's own logits, bit-exact."""
+    binding, cfg, w, wh = tiny_setup
+    print("case: tiny top-k with repeated LM-head rows", flush=True)
+    w2 = dict(w)
+    period = 37
+    base = w["lm_head"][:period]
+    w2["lm_head"] = base.repeat((cfg.vocab + period - 1) // period, 1)[:cfg.vocab].contiguous()
+    dr = binding.Drafter(cfg, w2)
+    P = 40
+    taps, _ = _taps_history(cfg, P, seed=5)
+    dr.reset(0, 0, P)
+    rows = torch.arange(0, P, dtype=torch.int32, device="cuda")
+    dr.tap_stage([t[:P] for t in taps], P, req_of_row=torch.zeros_like(rows), pos_of_row=rows)
+    tokens = synth.block_tokens(cfg, 1, seed=3, device="cuda")
+    logits = torch.empty((1, cfg.block - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    vals = torch.empty((1, cfg.block - 1, 16), dtype=torch.float32, device="cuda")
+    ids = dr.draft_block(tokens, k=16, logits=logits, vals=vals)
+    ids1 = dr.draft_block(tokens, k=1)
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    g_logits = logits[0].cpu().numpy()
+    g_ids = ids.cpu().numpy()[0]
+    # ties really are there: the best value repeats in every row
+    assert all(np.sum(g_logits[r] == g_logits[r].max()) > 16 for r in range(g_logits.shape[0]))
+    Hn.topk_self_consistent(g_logits, g_ids)
+    np.testing.assert_array_equal(vals[0].cpu().numpy(), np.take_along_axis(g_logits, g_ids, 1))
+    np.testing.assert_array_equal(ids1.cpu().numpy()[0, :, 0], g_ids[:, 0])
