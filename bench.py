@@ -59,15 +59,20 @@ def lm_traffic(workload: str):
 
 
 WORKLOADS = {
-    # name: (config builder kwargs, requests, k, description)
-    "c3": (dict(block=16, window=4096), 1, 16,
+    # name: (config builder, builder kwargs, requests, k, description)
+    "c3": ("qwen3_4b", dict(block=16, window=4096), 1, 16,
            "qwen3-4b-shaped drafter (5 layers, hidden 2560, 32/8 heads x 128, ffn 9728, vocab 151936, 5 taps), "
            "block 16, context window 4096 rows staged from a 16384-row tap buffer, top-16, 1 request"),
-    "c3b8": (dict(block=8, window=4096), 1, 16,
+    "c3b8": ("qwen3_4b", dict(block=8, window=4096), 1, 16,
              "qwen3-4b-shaped drafter, block 8, context window 4096, top-16, 1 request"),
-    "c2": (dict(block=16, window=1024), 1, 1,
+    "c2": ("qwen3_4b", dict(block=16, window=1024), 1, 1,
            "qwen3-4b-shaped drafter, block 16, context 1024 rows, argmax, 1 request"),
-    "c5": (dict(block=8, window=4096, max_requests=8, hc_streams=4), 8, 1,
+    "c4": ("qwen3_8b_int4", dict(block=8, window=2048), 1, 1,
+           "qwen3-8b-shaped drafter with INT4 g64 projections (5 layers, hidden 4096, 32/8 heads x 128, "
+           "ffn 12288, bf16 LM head vocab 151936), block 8, context 2048, argmax, 1 request"),
+    "c4b6": ("qwen3_8b_int4", dict(block=6, window=2048), 1, 1,
+             "qwen3-8b-shaped drafter with INT4 g64 projections, block 6, context 2048, argmax, 1 request"),
+    "c5": ("qwen3_4b", dict(block=8, window=4096, max_requests=8, hc_streams=4), 8, 1,
            "qwen3-4b-shaped drafter fed by 4 hyper-connection streams per tap, block 8, "
            "8 requests with their own 4096-row contexts, argmax"),
 }
@@ -77,9 +82,14 @@ def round_bytes(cfg, R: int, k: int) -> dict:
     """Algorithmic HBM bytes of one round: every weight once, each request's
     context K/V window read once per layer, new ring rows written, taps read,
     embeddings gathered, ids written."""
+    from block_diffusion_drafter_tap_amd import config
+
     H, hd, L = cfg.hidden, cfg.head_dim, cfg.n_layers
-    layer_w = (cfg.qkv_rows * H + H * cfg.n_q_heads * hd + 2 * cfg.ffn * H + H * cfg.ffn) * 2 + 4 * H * 2 + 2 * hd * 2
-    fc = H * cfg.tap_width * 2
+    # bytes per projection weight: bf16, or a nibble plus an fp16 scale per 64
+    wb = 0.5 + 2.0 / 64 if cfg.wfmt == config.WFMT_INT4_G64 else 2
+    layer_w = int((cfg.qkv_rows * H + H * cfg.n_q_heads * hd + 2 * cfg.ffn * H + H * cfg.ffn) * wb) \
+        + 4 * H * 2 + 2 * hd * 2
+    fc = int(H * cfg.tap_width * wb)
     lm = cfg.vocab * H * 2
     keys = cfg.window + cfg.block
     ring_read = R * L * 2 * cfg.n_kv_heads * keys * hd * 2
@@ -97,13 +107,16 @@ def cpu_baseline(cfg, w, taps_hist, tokens, pos, valid_from, budget_s: float = 1
     sample: whole draft rounds of request 0 at the benchmark's shapes, repeated
     until `budget_s` of CPU time has passed (at least one)."""
     import numpy as np
+    import torch
     from threadpoolctl import threadpool_info
 
     from oracle import dflash as D
     from block_diffusion_drafter_tap_amd import synth
 
-    wh = {kk: ([synth.bf16_to_f32_numpy(t) for t in v] if isinstance(v, list) else synth.bf16_to_f32_numpy(v))
-          for kk, v in w.items()}
+    def host(t):
+        return t.cpu().numpy() if t.dtype == torch.uint8 else synth.bf16_to_f32_numpy(t)
+
+    wh = D.dequantize({kk: ([host(t) for t in v] if isinstance(v, list) else host(v)) for kk, v in w.items()})
     n, t0 = 0, time.perf_counter()
     while True:
         D.draft_block(cfg, wh, taps_hist, tokens, pos, valid_from, mode="mirror")
@@ -114,7 +127,7 @@ def cpu_baseline(cfg, w, taps_hist, tokens, pos, valid_from, budget_s: float = 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {"value": n / el, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} full draft round(s) of one request (uncached context recompute of the "
-                      f"{cfg.window}-row window, 5 layers, LM head + top-k) in {el:.1f} s"}
+                      f"{cfg.window}-row window, {cfg.n_layers} layers, LM head + top-k) in {el:.1f} s"}
 
 
 def main():
@@ -128,7 +141,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the draft round shards by request with no exchange, see DESIGN.md", file=sys.stderr)
+              "the draft round shards by request with no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -136,8 +149,8 @@ def main():
 
     from block_diffusion_drafter_tap_amd import binding, config, synth
 
-    kw, R, k, desc = WORKLOADS[args.workload]
-    cfg = config.qwen3_4b(max_stage_rows=4096, **kw)
+    builder, kw, R, k, desc = WORKLOADS[args.workload]
+    cfg = getattr(config, builder)(max_stage_rows=kw["window"], **kw)
     B, V, W = cfg.block, cfg.vocab, cfg.window
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -258,7 +271,7 @@ def main():
                 + ", geometric p=0.75 verify accepts)",
         "config": {"workload": desc, "block": B, "window": W, "requests": R, "topk": k,
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": V, "hc_streams": cfg.hc_streams,
-                   },
+                   "weights": "int4_g64" if cfg.wfmt == config.WFMT_INT4_G64 else "bf16"},
         "achieved_gbps": round(rb["total"] / (ms_step / 1e3) / 1e9, 1),
         "round_bytes": rb["total"],
         "drafted_tokens_per_s": round(blocks_s * (B - 1), 1),

@@ -27,8 +27,26 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // K chunks (of 128) per split of each projection, measured best on MI355X at the
 // qwen3-4b shape with 16 rows: about 2-4 chunks keeps a few hundred workgroups
 // streaming while the partial tiles stay small.
-constexpr int CPS_QKV = 2, CPS_O = 3, CPS_GATEUP = 4, CPS_DOWN = 3, CPS_FC = 4, CPS_STAGE_KV = 2;
+enum Proj { P_QKV, P_O, P_GATEUP, P_DOWN, P_FC, P_STAGE_KV };
+constexpr int CPS_BF16[] = {2, 3, 4, 3, 4, 2};
+// INT4 chunks carry a quarter of the bytes; measured best at the qwen3-8b
+// shape with 8 rows (hidden 4096, ffn 12288)
+constexpr int CPS_INT4[] = {6, 2, 8, 4, 4, 2};
 constexpr int GC_DEFAULT = 128;
+
+int wf_of(const dflash_config& c) { return c.wfmt == DFLASH_W_INT4_G64 ? WF_INT4 : WF_BF16; }
+GemmPlan plan_for(const dflash_config& c, int M, int N, int K, int gc, int pair, Proj pj) {
+  const int cps = c.wfmt == DFLASH_W_INT4_G64 ? CPS_INT4[pj] : CPS_BF16[pj];
+  return plan_gemm(M, N, K, gc, pair, cps, wf_of(c));
+}
+
+// Rows [row, ...) of a projection matrix [N][K]: bf16 rows of K elements, or
+// packed INT4 rows of K/2 bytes with fp16 scale rows of K/64.
+const void* w_rows(const dflash_config& c, const uint16_t* w, size_t row, int K) {
+  if (c.wfmt == DFLASH_W_INT4_G64) return (const uint8_t*)w + row * (size_t)(K / 2);
+  return w + row * (size_t)K;
+}
+const uint16_t* s_rows(const uint16_t* s, size_t row, int K) { return s ? s + row * (size_t)(K / 64) : nullptr; }
 
 int attn_nchunks(const dflash_config& c) {
   const int kc = attn_chunk_keys(c.head_dim);
@@ -40,7 +58,8 @@ struct WsLayout {
 };
 
 struct GemmShape {
-  int N, K, gc, pair, cps;
+  int N, K, gc, pair;
+  Proj pj;
 };
 
 // Layers per stage K/V launch: split-K launches batch up to MAX_BATCH layers
@@ -56,15 +75,15 @@ int stage_batch(const GemmPlan& p, int M, int N, int n_layers) {
 // Largest split-K partial buffer over every GEMM a call may launch.
 size_t gemm_scratch(const dflash_config& c) {
   const int H = c.hidden, hd = c.head_dim;
-  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, CPS_QKV},
-                             {H, c.n_q_heads * hd, GC_DEFAULT, 0, CPS_O},
-                             {c.ffn, H, GC_DEFAULT, 1, CPS_GATEUP},
-                             {H, c.ffn, GC_DEFAULT, 0, CPS_DOWN}};
-  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, CPS_FC},
-                             {2 * c.n_kv_heads * hd, H, hd, 0, CPS_STAGE_KV}};
+  const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, P_QKV},
+                             {H, c.n_q_heads * hd, GC_DEFAULT, 0, P_O},
+                             {c.ffn, H, GC_DEFAULT, 1, P_GATEUP},
+                             {H, c.ffn, GC_DEFAULT, 0, P_DOWN}};
+  const GemmShape stage[] = {{H, c.n_taps * c.tap_hidden, GC_DEFAULT, 0, P_FC},
+                             {2 * c.n_kv_heads * hd, H, hd, 0, P_STAGE_KV}};
   size_t pf = 0;
   auto visit = [&](int M, const GemmShape& s, bool batched) {
-    GemmPlan p = plan_gemm(M, s.N, s.K, s.gc, s.pair, s.cps);
+    GemmPlan p = plan_for(c, M, s.N, s.K, s.gc, s.pair, s.pj);
     const int layers = batched ? stage_batch(p, M, s.N, c.n_layers) : 1;
     size_t f = gemm_partial_floats(p, M, s.N, s.pair) * layers;
     if (f > pf) pf = f;
@@ -158,8 +177,6 @@ int validate_config(const dflash_config* c) {
                 attn_slots(c->n_q_heads, c->n_kv_heads, c->block));
   if (c->vocab > 256 * 64 * 16)
     return fail(DFLASH_E_UNSUPPORTED, "vocab %d exceeds the top-k selection capacity (%d)", c->vocab, 256 * 64 * 16);
-  if (c->wfmt == DFLASH_W_INT4_G64)
-    return fail(DFLASH_E_UNSUPPORTED, "INT4 weights are not built in this library version");
   return DFLASH_OK;
 }
 
@@ -182,6 +199,8 @@ struct dflash_ctx {
   WsLayout wl;
   int n_cu = 256;   // compute units of the bound device (read at bind)
   Timing timing[DFLASH_K_COUNT];
+  // INT4 scales of layer l's matrix (NULL for bf16 weights)
+  static const uint16_t* sc(const std::vector<const uint16_t*>& v, int l) { return v.empty() ? nullptr : v[l]; }
 };
 
 namespace {
@@ -381,20 +400,22 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   a.hc = g.hc_streams;
   a.tap_hidden = g.tap_hidden;
   a.w = ctx->fc;
+  a.wscale = ctx->fc_s;
   a.M = n_rows;
   a.N = H;
   a.K = g.n_taps * g.tap_hidden;
+  const int wf = wf_of(g);
   uint16_t* c_bf = at<uint16_t>(ctx->ws, ctx->wl.c);
   a.out = g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf;
   a.ldo = H;
   {
-    GemmPlan p = plan_gemm(n_rows, H, a.K, GC_DEFAULT, 0, CPS_FC);
+    GemmPlan p = plan_for(g, n_rows, H, a.K, GC_DEFAULT, 0, P_FC);
     Timed tm(ctx, DFLASH_K_FC, st);
     if (p.S > 1) {
-      e = launch_gemm(a, p, X_TAPS, E_PART, WF_BF16, st);
+      e = launch_gemm(a, p, X_TAPS, E_PART, wf, st);
       if (e == hipSuccess) e = launch_finish_store(a.partials, p.S, n_rows, H, a.out, H, !g.ctx_norm, st);
     } else {
-      e = launch_gemm(a, p, X_TAPS, g.ctx_norm ? E_F32 : E_BF16, WF_BF16, st);
+      e = launch_gemm(a, p, X_TAPS, g.ctx_norm ? E_F32 : E_BF16, wf, st);
     }
   }
   if (e != hipSuccess) return hip_fail(e, "stage fc");
@@ -404,7 +425,8 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   }
   // per layer: K/V of the staged rows into the ring
   const size_t rl = ring_layer_elems(g);
-  GemmPlan p = plan_gemm(n_rows, 2 * g.n_kv_heads * hd, H, hd, 0, CPS_STAGE_KV);
+  GemmPlan p = plan_for(g, n_rows, 2 * g.n_kv_heads * hd, H, hd, 0, P_STAGE_KV);
+  const size_t kv_row0 = (size_t)g.n_q_heads * hd;   // the K and V rows of the fused QKV matrix
   // split-K (a few rows per round): up to MAX_BATCH layers share one launch of the
   // projection and one of the head finish; S = 1 (prefill) runs one launch per layer
   const int step = stage_batch(p, n_rows, 2 * g.n_kv_heads * hd, g.n_layers);
@@ -413,7 +435,8 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
     GemmArgs b = base_args(ctx);
     b.x = c_bf;
     b.ldx = H;
-    b.w = ctx->wqkv[l0] + (size_t)g.n_q_heads * hd * H;
+    b.w = w_rows(g, ctx->wqkv[l0], kv_row0, H);
+    b.wscale = s_rows(dflash_ctx::sc(ctx->wqkv_s, l0), kv_row0, H);
     b.M = n_rows;
     b.N = 2 * g.n_kv_heads * hd;
     b.K = H;
@@ -429,15 +452,16 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
     if (p.S > 1) {
       b.nb = step > 1 ? nl : 0;
       for (int i = 0; i < nl; ++i) {
-        b.wb[i] = ctx->wqkv[l0 + i] + (size_t)g.n_q_heads * hd * H;
+        b.wb[i] = w_rows(g, ctx->wqkv[l0 + i], kv_row0, H);
+        b.wsb[i] = s_rows(dflash_ctx::sc(ctx->wqkv_s, l0 + i), kv_row0, H);
         b.rkb[i] = at<uint16_t>(ctx->state, ctx->sl.ring_k) + (l0 + i) * rl;
         b.rvb[i] = at<uint16_t>(ctx->state, ctx->sl.ring_v) + (l0 + i) * rl;
         b.kgb[i] = ctx->k_norm[l0 + i];
       }
-      e = launch_gemm(b, p, X_BF16, E_PART, WF_BF16, st);
+      e = launch_gemm(b, p, X_BF16, E_PART, wf, st);
       if (e == hipSuccess) e = launch_finish_head(b, b.partials, p.S, b.N, 2 * g.n_kv_heads, st);
     } else {
-      e = launch_gemm(b, p, X_BF16, E_HEAD, WF_BF16, st);
+      e = launch_gemm(b, p, X_BF16, E_HEAD, wf, st);
     }
     if (e != hipSuccess) return hip_fail(e, "stage kv");
   }
@@ -467,6 +491,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
   unsigned* err = at<unsigned>(ctx->state, ctx->sl.error);
   const int ssq_ld = g.max_requests * B;
   const int h_blocks = H / GC_DEFAULT;
+  const int wf = wf_of(g);
   // every RMSNorm is applied by the GEMM that consumes it (X_NORM), from h and
   // the per-row sums of squares its producer left in ssq
   auto norm_input = [&](GemmArgs& a, const uint16_t* gain, int n_blocks) {
@@ -487,6 +512,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       GemmArgs a = base_args(ctx);
       norm_input(a, ctx->ln_in[l], l == 0 ? 1 : h_blocks);
       a.w = ctx->wqkv[l];
+      a.wscale = dflash_ctx::sc(ctx->wqkv_s, l);
       a.M = M;
       a.N = (g.n_q_heads + 2 * g.n_kv_heads) * hd;
       a.K = H;
@@ -497,13 +523,13 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ring_k = rk;
       a.ring_v = rv;
       a.rows_per_req = B;
-      GemmPlan p = plan_gemm(M, a.N, H, hd, 0, CPS_QKV);
+      GemmPlan p = plan_for(g, M, a.N, H, hd, 0, P_QKV);
       Timed tm(ctx, DFLASH_K_QKV, st);
       if (p.S > 1) {
-        e = launch_gemm(a, p, X_NORM, E_PART, WF_BF16, st);
+        e = launch_gemm(a, p, X_NORM, E_PART, wf, st);
         if (e == hipSuccess) e = launch_finish_head(a, a.partials, p.S, a.N, g.n_q_heads + 2 * g.n_kv_heads, st);
       } else {
-        e = launch_gemm(a, p, X_NORM, E_HEAD, WF_BF16, st);
+        e = launch_gemm(a, p, X_NORM, E_HEAD, wf, st);
       }
       if (e != hipSuccess) return hip_fail(e, "qkv");
     }
@@ -537,6 +563,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.x = o;
       a.ldx = qw;
       a.w = ctx->wo[l];
+      a.wscale = dflash_ctx::sc(ctx->wo_s, l);
       a.M = M;
       a.N = H;
       a.K = qw;
@@ -544,13 +571,13 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ldo = H;
       a.ssq_out = ssq;
       a.ssq_ld = ssq_ld;
-      GemmPlan p = plan_gemm(M, H, qw, GC_DEFAULT, 0, CPS_O);
+      GemmPlan p = plan_for(g, M, H, qw, GC_DEFAULT, 0, P_O);
       Timed tm(ctx, DFLASH_K_O, st);
       if (p.S > 1) {
-        e = launch_gemm(a, p, X_BF16, E_PART, WF_BF16, st);
+        e = launch_gemm(a, p, X_BF16, E_PART, wf, st);
         if (e == hipSuccess) e = launch_finish_resid(a.partials, p.S, M, H, h, H, ssq, ssq_ld, st);
       } else {
-        e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+        e = launch_gemm(a, p, X_BF16, E_RESID, wf, st);
       }
       if (e != hipSuccess) return hip_fail(e, "o proj");
     }
@@ -558,19 +585,20 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       GemmArgs a = base_args(ctx);
       norm_input(a, ctx->ln_post[l], h_blocks);
       a.w = ctx->wgu[l];
+      a.wscale = dflash_ctx::sc(ctx->wgu_s, l);
       a.M = M;
       a.N = g.ffn;
       a.K = H;
       a.pair_off = g.ffn;
       a.out = act;
       a.ldo = g.ffn;
-      GemmPlan p = plan_gemm(M, g.ffn, H, GC_DEFAULT, 1, CPS_GATEUP);
+      GemmPlan p = plan_for(g, M, g.ffn, H, GC_DEFAULT, 1, P_GATEUP);
       Timed tm(ctx, DFLASH_K_GATEUP, st);
       if (p.S > 1) {
-        e = launch_gemm(a, p, X_NORM, E_PARTP, WF_BF16, st);
+        e = launch_gemm(a, p, X_NORM, E_PARTP, wf, st);
         if (e == hipSuccess) e = launch_finish_silu(a.partials, p.S, M, g.ffn, act, g.ffn, st);
       } else {
-        e = launch_gemm(a, p, X_NORM, E_SILU, WF_BF16, st);
+        e = launch_gemm(a, p, X_NORM, E_SILU, wf, st);
       }
       if (e != hipSuccess) return hip_fail(e, "gate/up");
     }
@@ -579,6 +607,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.x = act;
       a.ldx = g.ffn;
       a.w = ctx->wd[l];
+      a.wscale = dflash_ctx::sc(ctx->wd_s, l);
       a.M = M;
       a.N = H;
       a.K = g.ffn;
@@ -586,13 +615,13 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
       a.ldo = H;
       a.ssq_out = ssq;
       a.ssq_ld = ssq_ld;
-      GemmPlan p = plan_gemm(M, H, g.ffn, GC_DEFAULT, 0, CPS_DOWN);
+      GemmPlan p = plan_for(g, M, H, g.ffn, GC_DEFAULT, 0, P_DOWN);
       Timed tm(ctx, DFLASH_K_DOWN, st);
       if (p.S > 1) {
-        e = launch_gemm(a, p, X_BF16, E_PART, WF_BF16, st);
+        e = launch_gemm(a, p, X_BF16, E_PART, wf, st);
         if (e == hipSuccess) e = launch_finish_resid(a.partials, p.S, M, H, h, H, ssq, ssq_ld, st);
       } else {
-        e = launch_gemm(a, p, X_BF16, E_RESID, WF_BF16, st);
+        e = launch_gemm(a, p, X_BF16, E_RESID, wf, st);
       }
       if (e != hipSuccess) return hip_fail(e, "down proj");
     }

@@ -25,6 +25,17 @@
 // k0 + 8*(l/16) + 0..7 in both operands; the result lands as
 // C[4*(l/16) + i][l%16], i = 0..3.
 //
+// INT4 weights (symmetric, groups of 64 along K, fp16 scales): in the 128-wide
+// chunk c of a row, 32-bit word 4*j + s of the packed row holds the eight values
+// k = 128c + 32s + 8j + e (e = 0..7) as u = q + 8, value e in nibble e/2 (even
+// e) or 4 + (e-1)/2 (odd e). Lane group lg therefore gets all its k-values of
+// the chunk's four MFMA steps with one 16-byte load (words 4lg..4lg+3), and the
+// nibble pair (e, e+1) of a word w becomes the bf16 pair (128 + u_e, 128 + u_e+1)
+// in two ops: ((w >> 2e) & 0x000F000F) | 0x43004300 (0x4300 is bf16 128.0, whose
+// ulp is 1). The MFMAs of one 64-group accumulate t = sum x * (u + 128) from
+// zero; with xs = sum x over the group (row sums of the bf16 X values, computed
+// once while X is staged) the group adds s * (t - 136 * xs) = s * sum x * q.
+//
 // Epilogues run on a [16*MT][GC] fp32 tile in LDS:
 //   E_BF16 / E_F32  store; E_RESID  h += Y (fp32 residual stream);
 //   E_SILU  SiLU(gate) * up -> bf16 (the first half of the waves stream gate
@@ -146,11 +157,29 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
   }
 }
 
-template <int MT, int NW, int XK, int XL, int EPI, int D>
+// (128 + u_e, 128 + u_e+1) for the nibble pairs of one packed word (see above)
+DEV u32x4 int4_biased_bf16(uint32_t w) {
+  u32x4 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r[t] = ((w >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+DEV float half_bits_to_float(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+
+// Per-row sums over 64-wide K groups of the bf16 X values, [klen/64][ROWS] floats
+// after the X slice (or at the start of LDS when X is not staged).
+template <int ROWS>
+DEV size_t xsum_offset(int XL, int ks) {
+  return XL ? (((size_t)ROWS * (ks + 8) * 2 + 15) & ~(size_t)15) : 0;
+}
+
+template <int MT, int NW, int XK, int XL, int EPI, int D, int WF>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   constexpr int ROWS = MT * 16;
   constexpr int GC = NW * 16;
   constexpr bool PAIR = (EPI == E_SILU || EPI == E_PARTP);
+  constexpr bool Q4 = WF == WF_INT4;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -179,17 +208,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     tcol = wave * 16;
   }
   const uint16_t* wrow = (const uint16_t*)wbase + (size_t)wrow_i * a.K + kbeg + 8 * lg;
+  const uint8_t* qrow = (const uint8_t*)wbase + (size_t)wrow_i * (a.K / 2) + kbeg / 2 + 16 * lg;
+  const uint16_t* srow = nullptr;
+  if constexpr (Q4) srow = (a.nb > 0 ? pick(a.wsb, layer) : a.wscale) + (size_t)wrow_i * (a.K / 64) + kbeg / 64;
 
   // D 128-wide chunks of W loads stay in flight (chunk c in buffer c % D); the
   // first D are issued before the X slice is staged, so they stream meanwhile.
-  u32x4 wbuf[D][4];
-  auto load_w = [&](int c, u32x4 (&w)[4]) {
+  // bf16: four 16-byte loads per chunk; INT4: one 16-byte load of packed words
+  // plus the chunk's two fp16 group scales.
+  u32x4 wbuf[D][Q4 ? 1 : 4];
+  uint32_t sbuf[D];
+  auto load_w = [&](int c, int j) {
+    if constexpr (Q4) {
+      wbuf[j][0] = ld16(qrow + 64 * c);
+      sbuf[j] = *(const uint32_t*)(srow + 2 * c);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) w[s] = ld16(wrow + 128 * c + 32 * s);
+      for (int s = 0; s < 4; ++s) wbuf[j][s] = ld16(wrow + 128 * c + 32 * s);
+    }
   };
+  // Loads are never behind a branch (a chunk past the end re-reads the last
+  // one): the compiler then counts outstanding loads exactly and waits only for
+  // the buffer it needs, instead of draining every load at each branch.
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (j < nchunks) load_w(j, wbuf[j]);
+    if (j < nchunks) load_w(j, j);
 
   __shared__ float s_inv[ROWS];
   if constexpr (XK == X_NORM) {
@@ -214,11 +257,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     if constexpr (XK == X_NORM) return s_inv[r];
     return 1.0f;
   };
-  if (XL) {
+  float* xsum = (float*)(smem + xsum_offset<ROWS>(XL, a.ks));
+  if (XL || Q4) {
+    // one pass over the X slice: stage it (XL) and, for INT4, sum each row's
+    // bf16 values per 64-group (8 lanes hold the 8 pieces of one group: the
+    // per-row count klen/8 is a multiple of 16, so groups never straddle rows
+    // and all 8 lanes of a group are active together)
     const int per_row = klen / 8;
     for (int e = threadIdx.x; e < ROWS * per_row; e += blockDim.x) {
       const int r = e / per_row, c = e % per_row;
-      *(u32x4*)(xs + r * ldl + 8 * c) = load_x<XK>(a, min(m0 + r, a.M - 1), kbeg + 8 * c, row_inv(r));
+      const u32x4 v = load_x<XK>(a, min(m0 + r, a.M - 1), kbeg + 8 * c, row_inv(r));
+      if (XL) *(u32x4*)(xs + r * ldl + 8 * c) = v;
+      if constexpr (Q4) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t += __uint_as_float(v[i] << 16) + __uint_as_float(v[i] & 0xffff0000u);
+        t += __shfl_xor(t, 1, 64);
+        t += __shfl_xor(t, 2, 64);
+        t += __shfl_xor(t, 4, 64);
+        if ((c & 7) == 0) xsum[(c >> 3) * ROWS + r] = t;
+      }
     }
     __syncthreads();
   }
@@ -230,20 +288,42 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int c, const u32x4 (&w)[4]) {
+  auto compute = [&](int c, int j) {
+    if constexpr (Q4) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int gi = 0; gi < 2; ++gi) {
+        const float sc = half_bits_to_float(gi ? sbuf[j] >> 16 : sbuf[j] & 0xffffu);
+        f32x4 t[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), as_bf16x8(w[s]), acc[mt]);
+        for (int mt = 0; mt < MT; ++mt) t[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 2 * gi; s < 2 * gi + 2; ++s) {
+          const bf16x8 b = as_bf16x8(int4_biased_bf16(wbuf[j][0][s]));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) t[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), b, t[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4 xg = *(const f32x4*)(xsum + (2 * c + gi) * ROWS + mt * 16 + 4 * lg);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sc, fmaf(-136.0f, xg[i], t[mt][i]), acc[mt][i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), as_bf16x8(wbuf[j][s]), acc[mt]);
+    }
   };
   for (int c0 = 0; c0 < nchunks; c0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int c = c0 + j;
       if (c < nchunks) {
-        compute(c, wbuf[j]);
-        if (c + D < nchunks) load_w(c + D, wbuf[j]);
+        compute(c, j);
+        if (c + D < nchunks) load_w(c + D, j);
       }
     }
   }
@@ -330,55 +410,63 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   }
 }
 
-constexpr int GEMM_DEPTH = 3;   // W chunks in flight per wave (measured: 3 best or within 2%)
+constexpr int GEMM_DEPTH = 3;      // bf16 W chunks in flight per wave (measured: 3 best or within 2%)
+constexpr int GEMM_DEPTH_Q4 = 8;   // INT4 chunks are a quarter of the bytes
+// with X fragments read from L2 (no LDS slice) the deeper INT4 pipeline spills
+constexpr int GEMM_DEPTH_Q4_NOXL = 4;
 
 template <int MT, int NW, int XK, int XL, int EPI>
-void launch_one(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, XK, XL, EPI, GEMM_DEPTH>), grid, dim3(NW * 64), lds, st, a);
+void launch_one(const GemmArgs& a, dim3 grid, size_t lds, int wf, hipStream_t st) {
+  constexpr int DQ = XL ? GEMM_DEPTH_Q4 : GEMM_DEPTH_Q4_NOXL;
+  if (wf == WF_INT4)
+    hipLaunchKernelGGL((gemm_kernel<MT, NW, XK, XL, EPI, DQ, WF_INT4>), grid, dim3(NW * 64), lds, st, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<MT, NW, XK, XL, EPI, GEMM_DEPTH, WF_BF16>), grid, dim3(NW * 64), lds, st, a);
 }
 
 template <int MT, int NW, int XL>
-hipError_t launch_x(const GemmArgs& a, dim3 grid, size_t lds, int xk, int epi, hipStream_t st) {
+hipError_t launch_x(const GemmArgs& a, dim3 grid, size_t lds, int xk, int epi, int wf, hipStream_t st) {
   if (xk == X_TAPS) {
-    if (epi == E_BF16) launch_one<MT, NW, X_TAPS, XL, E_BF16>(a, grid, lds, st);
-    else if (epi == E_F32) launch_one<MT, NW, X_TAPS, XL, E_F32>(a, grid, lds, st);
-    else if (epi == E_PART) launch_one<MT, NW, X_TAPS, XL, E_PART>(a, grid, lds, st);
+    if (epi == E_BF16) launch_one<MT, NW, X_TAPS, XL, E_BF16>(a, grid, lds, wf, st);
+    else if (epi == E_F32) launch_one<MT, NW, X_TAPS, XL, E_F32>(a, grid, lds, wf, st);
+    else if (epi == E_PART) launch_one<MT, NW, X_TAPS, XL, E_PART>(a, grid, lds, wf, st);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
   if (xk == X_NORM) {
     switch (epi) {
-      case E_SILU: launch_one<MT, NW, X_NORM, XL, E_SILU>(a, grid, lds, st); break;
-      case E_HEAD: launch_one<MT, NW, X_NORM, XL, E_HEAD>(a, grid, lds, st); break;
-      case E_PART: launch_one<MT, NW, X_NORM, XL, E_PART>(a, grid, lds, st); break;
-      case E_PARTP: launch_one<MT, NW, X_NORM, XL, E_PARTP>(a, grid, lds, st); break;
+      case E_SILU: launch_one<MT, NW, X_NORM, XL, E_SILU>(a, grid, lds, wf, st); break;
+      case E_HEAD: launch_one<MT, NW, X_NORM, XL, E_HEAD>(a, grid, lds, wf, st); break;
+      case E_PART: launch_one<MT, NW, X_NORM, XL, E_PART>(a, grid, lds, wf, st); break;
+      case E_PARTP: launch_one<MT, NW, X_NORM, XL, E_PARTP>(a, grid, lds, wf, st); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (epi) {
-    case E_BF16: launch_one<MT, NW, X_BF16, XL, E_BF16>(a, grid, lds, st); break;
-    case E_F32: launch_one<MT, NW, X_BF16, XL, E_F32>(a, grid, lds, st); break;
-    case E_RESID: launch_one<MT, NW, X_BF16, XL, E_RESID>(a, grid, lds, st); break;
-    case E_SILU: launch_one<MT, NW, X_BF16, XL, E_SILU>(a, grid, lds, st); break;
-    case E_HEAD: launch_one<MT, NW, X_BF16, XL, E_HEAD>(a, grid, lds, st); break;
-    case E_PART: launch_one<MT, NW, X_BF16, XL, E_PART>(a, grid, lds, st); break;
+    case E_BF16: launch_one<MT, NW, X_BF16, XL, E_BF16>(a, grid, lds, wf, st); break;
+    case E_F32: launch_one<MT, NW, X_BF16, XL, E_F32>(a, grid, lds, wf, st); break;
+    case E_RESID: launch_one<MT, NW, X_BF16, XL, E_RESID>(a, grid, lds, wf, st); break;
+    case E_SILU: launch_one<MT, NW, X_BF16, XL, E_SILU>(a, grid, lds, wf, st); break;
+    case E_HEAD: launch_one<MT, NW, X_BF16, XL, E_HEAD>(a, grid, lds, wf, st); break;
+    case E_PART: launch_one<MT, NW, X_BF16, XL, E_PART>(a, grid, lds, wf, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int MT, int NW>
-hipError_t launch_xl(const GemmArgs& a, dim3 grid, size_t lds, int xl, int xk, int epi, hipStream_t st) {
-  return xl ? launch_x<MT, NW, 1>(a, grid, lds, xk, epi, st) : launch_x<MT, NW, 0>(a, grid, lds, xk, epi, st);
+hipError_t launch_xl(const GemmArgs& a, dim3 grid, size_t lds, int xl, int xk, int epi, int wf, hipStream_t st) {
+  return xl ? launch_x<MT, NW, 1>(a, grid, lds, xk, epi, wf, st) : launch_x<MT, NW, 0>(a, grid, lds, xk, epi, wf, st);
 }
 
 constexpr size_t XL_MAX_BYTES = 96 * 1024;
+constexpr size_t GEMM_LDS_MAX = 160 * 1024;   // LDS per workgroup on gfx950
 
 
 }  // namespace
 
-GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps) {
+GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps, int wf) {
   GemmPlan p;
   p.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.NT = 1;
@@ -398,11 +486,14 @@ GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps) {
   S = S < 1 ? 1 : S;
   const int chunks_per = (kchunks + S - 1) / S;
   const int rows = 16 * p.MT;
-  // stage X through LDS when the slice fits; otherwise fragments come from L2
-  p.XL = (size_t)rows * (chunks_per * 128 + 8) * 2 <= XL_MAX_BYTES;
   p.ks = chunks_per * 128;
   p.S = (K + p.ks - 1) / p.ks;
-  const size_t xbytes = p.XL ? (size_t)rows * (p.ks + 8) * 2 : 0;
+  // INT4: per-row sums of X over each 64-group of the K range
+  const size_t sbytes = wf == WF_INT4 ? (size_t)rows * (p.ks / 64) * 4 : 0;
+  const size_t xl_bytes = (((size_t)rows * (p.ks + 8) * 2 + 15) & ~(size_t)15) + sbytes;
+  // stage X through LDS when the slice fits; otherwise fragments come from L2
+  p.XL = xl_bytes <= XL_MAX_BYTES;
+  const size_t xbytes = p.XL ? xl_bytes : sbytes;
   const size_t tbytes = (size_t)rows * (gc + 1) * 4;   // result tile
   p.lds = xbytes > tbytes ? xbytes : tbytes;
   return p;
@@ -414,7 +505,9 @@ size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf, hipStream_t st) {
-  if (wf != WF_BF16) return hipErrorInvalidValue;
+  if (wf != WF_BF16 && wf != WF_INT4) return hipErrorInvalidValue;
+  if (wf == WF_INT4 && (a.K % 128 || (a.nb > 0 ? !a.wsb[0] : !a.wscale))) return hipErrorInvalidValue;
+  if (p.lds > GEMM_LDS_MAX) return hipErrorInvalidValue;
   // a complete epilogue needs the whole K range in one workgroup
   if (p.S > 1 && epi != E_PART && epi != E_PARTP) return hipErrorInvalidValue;
   if (a.nb > MAX_BATCH || (a.nb > 0 && epi != E_PART)) return hipErrorInvalidValue;
@@ -424,8 +517,8 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, in
   b.S = p.S;
 #define DISPATCH_NW(MT)                                                         \
   switch (p.NW) {                                                               \
-    case 4: return launch_xl<MT, 4>(b, grid, p.lds, p.XL, xk, epi, st);          \
-    case 8: return launch_xl<MT, 8>(b, grid, p.lds, p.XL, xk, epi, st);          \
+    case 4: return launch_xl<MT, 4>(b, grid, p.lds, p.XL, xk, epi, wf, st);      \
+    case 8: return launch_xl<MT, 8>(b, grid, p.lds, p.XL, xk, epi, wf, st);      \
     default: return hipErrorInvalidValue;                                       \
   }
   switch (p.MT) {

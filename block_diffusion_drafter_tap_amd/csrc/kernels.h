@@ -44,6 +44,7 @@ struct GemmArgs {
   // rings rkb[b] / rvb[b], k gain kgb[b] and partials + b * S * M * N
   int nb;
   const void* wb[MAX_BATCH];
+  const uint16_t* wsb[MAX_BATCH];   // INT4 scales of layer b
   uint16_t* rkb[MAX_BATCH];
   uint16_t* rvb[MAX_BATCH];
   const uint16_t* kgb[MAX_BATCH];
@@ -72,9 +73,10 @@ struct GemmPlan {
 };
 
 // cps: target K chunks (of 128) per split when the grid needs splitting; the
-// S partial tiles of one launch never exceed GEMM_PARTIAL_BUDGET floats
+// S partial tiles of one launch never exceed GEMM_PARTIAL_BUDGET floats.
+// wf: weight format (INT4 adds per-group row sums of X to the LDS budget).
 constexpr long long GEMM_PARTIAL_BUDGET = 8ll << 20;
-GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps);
+GemmPlan plan_gemm(int M, int N, int K, int gc, int pair, int cps, int wf);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, int wf,
                        hipStream_t st);
 size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);

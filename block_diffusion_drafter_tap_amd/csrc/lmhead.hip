@@ -19,7 +19,9 @@
 
 namespace {
 
-constexpr size_t LM_XL_MAX_BYTES = 96 * 1024;   // stage the normed rows in LDS up to this size
+// stage the normed rows in LDS up to this size (one persistent workgroup per
+// CU, so nearly all of the 160 KB of a gfx950 CU)
+constexpr size_t LM_XL_MAX_BYTES = 159 * 1024;
 
 // 8 consecutive values (k..k+7) of row `row` of the final RMSNorm as bf16x8:
 // z = h * inv * g, h the fp32 residual stream, inv the row's 1/rms.

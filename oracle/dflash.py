@@ -384,3 +384,25 @@ def int4_unpack(packed, scales, K: int) -> np.ndarray:
                     q[:, 128 * c + 32 * s + 8 * j + e] = u.astype(np.float64) - 8.0
     sc = np.asarray(scales, dtype=np.float16).astype(np.float64)
     return q * np.repeat(sc, 64, axis=1)
+
+
+def dequantize(W) -> Dict[str, object]:
+    """The weights an INT4-projection drafter computes with.
+
+    Every projection that comes with ``<name>_scales`` (fc, wqkv, wo, wgu, wd)
+    is replaced by its exact values q*s from ``int4_unpack``; embed, LM head and
+    norm gains pass through unchanged (the INT4 workload keeps the LM head in
+    bf16; [P1] quantizes the drafter's projections at load, "What's here"). The
+    round itself is then the same definition as for bf16 weights.
+    """
+    out = dict(W)
+    for name in ("fc", "wqkv", "wo", "wgu", "wd"):
+        key = name + "_scales"
+        if out.get(key) is None:
+            continue
+        if isinstance(W[name], list):
+            out[name] = [int4_unpack(p, s, 2 * np.asarray(p).shape[1]) for p, s in zip(W[name], W[key])]
+        else:
+            out[name] = int4_unpack(W[name], W[key], 2 * np.asarray(W[name]).shape[1])
+        del out[key]
+    return out

@@ -334,3 +334,23 @@ def test_verify_from_draft_prefix_property():
     for r in range(R):
         res = D.accept(d[r].tolist(), v[r].tolist())
         assert res["acc"] == int(acc[r])
+
+
+def test_dequantize_replaces_every_packed_projection():
+    cfg = config.tiny(wfmt=config.WFMT_INT4_G64)
+    w = synth.make_weights(cfg, seed=1, device="cpu")
+    wh = {k: ([t.float().numpy() if t.dtype != torch.uint8 else t.numpy() for t in v] if isinstance(v, list)
+              else (v.float().numpy() if v.dtype != torch.uint8 else v.numpy())) for k, v in w.items()}
+    dq = D.dequantize(wh)
+    assert not any(k.endswith("_scales") for k in dq)
+    assert dq["fc"].shape == (cfg.hidden, cfg.n_taps * cfg.tap_hidden)
+    for name in ("wqkv", "wo", "wgu", "wd"):
+        for l in range(cfg.n_layers):
+            p = wh[name][l]
+            ref = D.int4_unpack(p, wh[name + "_scales"][l], 2 * p.shape[1])
+            np.testing.assert_array_equal(dq[name][l], ref)
+            # every value is q * s with |q| <= 8: within 8 scales of zero, on the scale grid
+            s = np.repeat(wh[name + "_scales"][l].astype(np.float64), 64, axis=1)
+            q = dq[name][l] / np.where(s > 0, s, 1)
+            assert np.all(q == np.rint(q)) and np.all(np.abs(q) <= 8)
+    np.testing.assert_array_equal(dq["lm_head"], wh["lm_head"])
