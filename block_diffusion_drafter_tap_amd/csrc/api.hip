@@ -48,13 +48,21 @@ const void* w_rows(const dflash_config& c, const uint16_t* w, size_t row, int K)
 }
 const uint16_t* s_rows(const uint16_t* s, size_t row, int K) { return s ? s + row * (size_t)(K / 64) : nullptr; }
 
+// Staging calls of at least this many rows (bf16 weights) take the prefill
+// path: tap gather, then tiled GEMMs for fc and each layer's context K/V.
+constexpr int PREFILL_MIN_ROWS = 256;
+bool prefill_enabled(const dflash_config& c) {
+  return c.wfmt == DFLASH_W_BF16 && c.max_stage_rows >= PREFILL_MIN_ROWS &&
+         tile_bn(PREFILL_MIN_ROWS, c.hidden, 256) != 0 && tile_bn(PREFILL_MIN_ROWS, 2 * c.n_kv_heads * c.head_dim, 256) != 0;
+}
+
 int attn_nchunks(const dflash_config& c) {
   const int kc = attn_chunk_keys(c.head_dim);
   return (c.window + c.block + 31 + kc - 1) / kc;
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, c32, c, partials, attn_o, attn_ml, logits, gmax, total;
+  size_t h, ssq, q, o, act, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, total;
 };
 
 struct GemmShape {
@@ -94,6 +102,11 @@ size_t gemm_scratch(const dflash_config& c) {
     visit(M, stage[0], false);
     visit(M, stage[1], true);
   }
+  // prefill: one layer's context K/V projection in fp32 before the head finish
+  if (prefill_enabled(c)) {
+    const size_t kv = (size_t)c.max_stage_rows * 2 * c.n_kv_heads * hd;
+    if (kv > pf) pf = kv;
+  }
   return pf;
 }
 
@@ -116,6 +129,7 @@ WsLayout ws_layout(const dflash_config& c) {
   L.act = take(Mmax * c.ffn * 2);
   L.c32 = take(c.ctx_norm ? S * c.hidden * 4 : 0);
   L.c = take(S * c.hidden * 2);
+  L.xg = take(prefill_enabled(c) ? S * c.n_taps * c.tap_hidden * 2 : 0);   // gathered tap rows (prefill)
   L.partials = take((pf ? pf : 1) * 4);
   L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
   L.attn_ml = take(lrg * nch * slots * 2 * 4);
@@ -257,6 +271,65 @@ size_t ring_layer_elems(const dflash_config& g) {
   return (size_t)g.max_requests * g.n_kv_heads * g.ring_capacity * g.head_dim;
 }
 
+// Many staged rows at once: gather the taps once as bf16, then fc and every
+// layer's context K/V as tiled GEMMs (the K/V in fp32, then the head finish:
+// k RMSNorm, RoPE at each row's position, K and V into the ring).
+int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, long long tap_row_stride, int n_rows,
+                  const int* req_of_row, const int* pos_of_row, int rows_per_req) {
+  const dflash_config& g = ctx->cfg;
+  const int H = g.hidden, hd = g.head_dim, TW = g.n_taps * g.tap_hidden;
+  const int nkv_w = 2 * g.n_kv_heads * hd;
+  hipError_t e;
+  uint16_t* xg = at<uint16_t>(ctx->ws, ctx->wl.xg);
+  uint16_t* c_bf = at<uint16_t>(ctx->ws, ctx->wl.c);
+  {
+    Timed tm(ctx, DFLASH_K_FC, st);
+    TapGather tg;
+    memset(&tg, 0, sizeof tg);
+    for (int t = 0; t < g.n_taps; ++t) tg.taps[t] = taps[t];
+    tg.tap_stride = tap_row_stride;
+    tg.n_taps = g.n_taps;
+    tg.hc = g.hc_streams;
+    tg.tap_hidden = g.tap_hidden;
+    tg.out = xg;
+    e = launch_tap_gather(tg, n_rows, st);
+    if (e == hipSuccess) {
+      TileArgs ta{xg, TW, ctx->fc, n_rows, H, TW,
+                  g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf, H};
+      e = launch_gemm_tile(ta, tile_bn(n_rows, H, ctx->n_cu), !g.ctx_norm, st);
+    }
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill fc");
+  if (g.ctx_norm) {
+    e = launch_rmsnorm(at<float>(ctx->ws, ctx->wl.c32), ctx->ctx_norm, c_bf, n_rows, H, g.rms_eps, st);
+    if (e != hipSuccess) return hip_fail(e, "prefill ctx norm");
+  }
+  const size_t rl = ring_layer_elems(g);
+  float* kv = at<float>(ctx->ws, ctx->wl.partials);
+  for (int l = 0; l < g.n_layers; ++l) {
+    Timed tm(ctx, DFLASH_K_STAGE_KV, st);
+    TileArgs ta{c_bf, H, ctx->wqkv[l] + (size_t)g.n_q_heads * hd * H, n_rows, nkv_w, H, kv, nkv_w};
+    e = launch_gemm_tile(ta, tile_bn(n_rows, nkv_w, ctx->n_cu), 0, st);
+    if (e == hipSuccess) {
+      GemmArgs b = base_args(ctx);
+      b.M = n_rows;
+      b.N = nkv_w;
+      b.K = H;
+      b.head_base = g.n_q_heads;
+      b.k_gain = ctx->k_norm[l];
+      b.q_gain = ctx->q_norm[l];
+      b.ring_k = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
+      b.ring_v = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
+      b.req_of_row = req_of_row;
+      b.pos_of_row = pos_of_row;
+      b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
+      e = launch_finish_head(b, kv, 1, nkv_w, 2 * g.n_kv_heads, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill kv");
+  }
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +464,8 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   hipStream_t st = (hipStream_t)stream;
   const int H = g.hidden, hd = g.head_dim;
   hipError_t e;
+  if (n_rows >= PREFILL_MIN_ROWS && prefill_enabled(g))
+    return stage_prefill(ctx, st, taps, tap_row_stride, n_rows, req_of_row, pos_of_row, rows_per_req);
 
   // fc over the gathered taps
   GemmArgs a = base_args(ctx);

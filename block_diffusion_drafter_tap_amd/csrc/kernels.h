@@ -129,6 +129,27 @@ hipError_t launch_finish_silu(const float* P, int S, int M, int N, uint16_t* act
 hipError_t launch_finish_head(const GemmArgs& a, const float* P, int S, int ld, int n_heads, hipStream_t st);
 hipError_t launch_finish_store(const float* P, int S, int M, int N, void* out, int ldo, int bf16, hipStream_t st);
 
+// Prefill staging (many rows, bf16 weights): the gathered tap rows as bf16, and
+// a tiled GEMM Y[M][N] = X[M][K] . W[N][K]^T (K a multiple of 64, N of the
+// column tile bn in {64, 128}; fp32 or bf16 out, row pitch ldo).
+struct TapGather {
+  const float* taps[MAX_TAPS];
+  long long tap_stride;
+  int n_taps, hc, tap_hidden;
+  uint16_t* out;   // [M][n_taps * tap_hidden]
+};
+struct TileArgs {
+  const uint16_t* x;
+  long long ldx;
+  const uint16_t* w;
+  int M, N, K;
+  void* out;
+  long long ldo;
+};
+hipError_t launch_tap_gather(const TapGather& g, int M, hipStream_t st);
+int tile_bn(int M, int N, int n_cu);   // 0: N fits neither tile
+hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t st);
+
 // Small kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, float* ssq, int M, int H,
