@@ -52,8 +52,9 @@ const uint16_t* s_rows(const uint16_t* s, size_t row, int K) { return s ? s + ro
 // path: tap gather, then tiled GEMMs for fc and each layer's context K/V.
 constexpr int PREFILL_MIN_ROWS = 256;
 bool prefill_enabled(const dflash_config& c) {
-  return c.wfmt == DFLASH_W_BF16 && c.max_stage_rows >= PREFILL_MIN_ROWS &&
-         tile_bn(PREFILL_MIN_ROWS, c.hidden, 256) != 0 && tile_bn(PREFILL_MIN_ROWS, 2 * c.n_kv_heads * c.head_dim, 256) != 0;
+  // fc in 64- or 128-column tiles; context K/V in 128-column tiles of whole heads
+  return c.wfmt == DFLASH_W_BF16 && c.max_stage_rows >= PREFILL_MIN_ROWS && tile_bn(PREFILL_MIN_ROWS, c.hidden, 256) != 0 &&
+         (c.n_kv_heads * c.head_dim) % 128 == 0 && 128 % c.head_dim == 0;
 }
 
 int attn_nchunks(const dflash_config& c) {
@@ -101,11 +102,6 @@ size_t gemm_scratch(const dflash_config& c) {
   for (int M = 1; M <= c.max_stage_rows; ++M) {
     visit(M, stage[0], false);
     visit(M, stage[1], true);
-  }
-  // prefill: one layer's context K/V projection in fp32 before the head finish
-  if (prefill_enabled(c)) {
-    const size_t kv = (size_t)c.max_stage_rows * 2 * c.n_kv_heads * hd;
-    if (kv > pf) pf = kv;
   }
   return pf;
 }
@@ -272,8 +268,8 @@ size_t ring_layer_elems(const dflash_config& g) {
 }
 
 // Many staged rows at once: gather the taps once as bf16, then fc and every
-// layer's context K/V as tiled GEMMs (the K/V in fp32, then the head finish:
-// k RMSNorm, RoPE at each row's position, K and V into the ring).
+// layer's context K/V as tiled GEMMs (the K/V tiles end in the head epilogue:
+// k RMSNorm, RoPE at each row's position, K and V into the rings).
 int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, long long tap_row_stride, int n_rows,
                   const int* req_of_row, const int* pos_of_row, int rows_per_req) {
   const dflash_config& g = ctx->cfg;
@@ -305,26 +301,18 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     if (e != hipSuccess) return hip_fail(e, "prefill ctx norm");
   }
   const size_t rl = ring_layer_elems(g);
-  float* kv = at<float>(ctx->ws, ctx->wl.partials);
   for (int l = 0; l < g.n_layers; ++l) {
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
-    TileArgs ta{c_bf, H, ctx->wqkv[l] + (size_t)g.n_q_heads * hd * H, n_rows, nkv_w, H, kv, nkv_w};
-    e = launch_gemm_tile(ta, tile_bn(n_rows, nkv_w, ctx->n_cu), 0, st);
-    if (e == hipSuccess) {
-      GemmArgs b = base_args(ctx);
-      b.M = n_rows;
-      b.N = nkv_w;
-      b.K = H;
-      b.head_base = g.n_q_heads;
-      b.k_gain = ctx->k_norm[l];
-      b.q_gain = ctx->q_norm[l];
-      b.ring_k = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
-      b.ring_v = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
-      b.req_of_row = req_of_row;
-      b.pos_of_row = pos_of_row;
-      b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
-      e = launch_finish_head(b, kv, 1, nkv_w, 2 * g.n_kv_heads, st);
-    }
+    TileArgs ta{c_bf, H, ctx->wqkv[l] + (size_t)g.n_q_heads * hd * H, n_rows, nkv_w, H, nullptr, 0};
+    GemmArgs b = base_args(ctx);
+    b.M = n_rows;
+    b.k_gain = ctx->k_norm[l];
+    b.ring_k = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
+    b.ring_v = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
+    b.req_of_row = req_of_row;
+    b.pos_of_row = pos_of_row;
+    b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
+    e = launch_gemm_tile_heads(ta, b, st);
     if (e != hipSuccess) return hip_fail(e, "prefill kv");
   }
   return DFLASH_OK;

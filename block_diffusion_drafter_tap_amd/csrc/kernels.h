@@ -149,6 +149,9 @@ struct TileArgs {
 hipError_t launch_tap_gather(const TapGather& g, int M, hipStream_t st);
 int tile_bn(int M, int N, int n_cu);   // 0: N fits neither tile
 hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t st);
+// Context K/V projection (N = 2 * nkv * hd, 128-column tiles of whole heads)
+// straight into the rings: GemmArgs head fields as for the head finish.
+hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStream_t st);
 
 // Small kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);

@@ -10,10 +10,12 @@
 //                      64 x BN/2 per wave, MFMA 16x16x32 bf16); K in stages of 64
 //                      double-buffered through LDS (rows padded by 8 elements so
 //                      the 16 rows of a fragment read fall in different banks),
-//                      each stage's global loads issued one stage ahead. Tiles
+//                      each stage's global loads issued two stages ahead. Tiles
 //                      are numbered row-major and dealt out XCD-major (workgroup
 //                      i runs on XCD i % 8), so the tiles resident on one XCD
 //                      share X rows in its L2.
+#include <string.h>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -47,14 +49,31 @@ __global__ __launch_bounds__(256) void tap_gather_kernel(const TapGather g) {
   *(u32x4*)(g.out + (size_t)m * g.n_taps * g.tap_hidden + e) = r;
 }
 
-template <int BN, int OUT_BF16>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a) {
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_HEADS = 2 };
+
+// Row -> (request, absolute position) of a staged row; p < 0 flags a bad row.
+DEV void staged_row(const GemmArgs& h, int m, int* req, long long* p) {
+  const int r = h.req_of_row ? h.req_of_row[m] : m / h.rows_per_req;
+  *req = r;
+  *p = (r < 0 || r >= h.Rmax) ? -1
+       : (h.pos_of_row ? (long long)h.pos_of_row[m] : (long long)h.pos[r] + m % h.rows_per_req);
+}
+
+// OUT_HEADS: the tile's columns are whole context K heads (k RMSNorm over the
+// head, RoPE at the row's position, rows into the K ring) or V heads (into the
+// transposed V ring, 64 consecutive rows of one dimension per wave store).
+template <int BN, int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
   constexpr int WN = BN / 2;        // columns per wave
   constexpr int NJ = WN / 16;       // 16-column MFMA tiles per wave
   constexpr int XP = PF_BM * PF_BK / 8 / 256;   // 16-byte X pieces per thread per stage
   constexpr int WP = BN * PF_BK / 8 / 256;      // W pieces
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][PF_BM][PF_LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][PF_LDK];
+  constexpr int XS_BYTES = 2 * PF_BM * PF_LDK * 2, WS_BYTES = 2 * BN * PF_LDK * 2;
+  constexpr int TILE_BYTES = OUT == OUT_HEADS ? PF_BM * (BN + 1) * 4 : 0;
+  constexpr int SMEM = XS_BYTES + WS_BYTES > TILE_BYTES ? XS_BYTES + WS_BYTES : TILE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  auto xs = (uint16_t(*)[PF_BM][PF_LDK])smem;
+  auto ws = (uint16_t(*)[BN][PF_LDK])(smem + XS_BYTES);
 
   const int mt = (a.M + PF_BM - 1) / PF_BM, nt = a.N / BN, tiles = mt * nt;
   const int per_xcd = (tiles + 7) / 8;
@@ -67,30 +86,32 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int nst = a.K / PF_BK;
 
-  u32x4 xr[XP], wr[WP];
-  auto load = [&](int s) {
+  // two register sets: stage s + 2 is loaded while stage s computes and is
+  // stored to LDS after stage s + 1 computes (two stages of latency cover)
+  u32x4 xr[2][XP], wr[2][WP];
+  auto load = [&](int s, int q) {
     const int k0 = s * PF_BK;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + i * 256, row = p / 8, seg = p % 8;
-      xr[i] = ld16(a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + k0 + 8 * seg);
+      xr[q][i] = ld16(a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + k0 + 8 * seg);
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
       const int p = tid + i * 256, row = p / 8, seg = p % 8;
-      wr[i] = ld16(a.w + (size_t)(n0 + row) * a.K + k0 + 8 * seg);
+      wr[q][i] = ld16(a.w + (size_t)(n0 + row) * a.K + k0 + 8 * seg);
     }
   };
-  auto store = [&](int b) {
+  auto store = [&](int b, int q) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + i * 256;
-      *(u32x4*)&xs[b][p / 8][8 * (p % 8)] = xr[i];
+      *(u32x4*)&xs[b][p / 8][8 * (p % 8)] = xr[q][i];
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
       const int p = tid + i * 256;
-      *(u32x4*)&ws[b][p / 8][8 * (p % 8)] = wr[i];
+      *(u32x4*)&ws[b][p / 8][8 * (p % 8)] = wr[q][i];
     }
   };
 
@@ -100,12 +121,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  store(0);
-  if (nst > 1) load(1);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int b = s & 1;
+  auto compute = [&](int b) {
 #pragma unroll
     for (int kk = 0; kk < PF_BK; kk += 32) {
       u32x4 af[4], bf[NJ];
@@ -118,33 +134,102 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
     }
-    if (s + 1 < nst) store(b ^ 1);
-    if (s + 2 < nst) load(s + 2);
-    __syncthreads();
+  };
+  // stage s lives in LDS buffer s & 1 and register set s & 1; the stage count
+  // is even (K a multiple of 128). No load sits behind a branch (the last two
+  // steps re-read the last stage), so each store waits only for its own set.
+  load(0, 0);
+  load(1, 1);
+  store(0, 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < nst; s0 += 2) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      load(min(s0 + q + 2, nst - 1), q);
+      compute(q);
+      store(q ^ 1, q ^ 1);
+      __syncthreads();
+    }
   }
 
   // lane holds C[4*lg + r][lr] of each 16 x 16 tile
+  if constexpr (OUT != OUT_HEADS) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + 16 * i + 4 * lg + r;
-      if (m >= a.M) continue;
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 64 + 16 * i + 4 * lg + r;
+        if (m >= a.M) continue;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + wn * WN + 16 * j + lr;
-        if (OUT_BF16) ((uint16_t*)a.out)[(size_t)m * a.ldo + n] = f2bfbits(acc[i][j][r]);
-        else ((float*)a.out)[(size_t)m * a.ldo + n] = acc[i][j][r];
+        for (int j = 0; j < NJ; ++j) {
+          const int n = n0 + wn * WN + 16 * j + lr;
+          if (OUT == OUT_BF16) ((uint16_t*)a.out)[(size_t)m * a.ldo + n] = f2bfbits(acc[i][j][r]);
+          else ((float*)a.out)[(size_t)m * a.ldo + n] = acc[i][j][r];
+        }
+      }
+  } else {
+    // the stage buffers are free after the loop's last barrier
+    __shared__ int s_req[PF_BM], s_pos[PF_BM];
+    auto tile = (float(*)[BN + 1])smem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) tile[wm * 64 + 16 * i + 4 * lg + r][wn * WN + 16 * j + lr] = acc[i][j][r];
+    const int rows = min(PF_BM, a.M - m0);
+    for (int r = tid; r < rows; r += 256) {
+      int req;
+      long long p;
+      staged_row(h, m0 + r, &req, &p);
+      if (p < 0) set_error(h.err, req < 0 || req >= h.Rmax ? 4u : 8u);
+      s_req[r] = req;
+      s_pos[r] = p < 0 ? -1 : (int)p;
+    }
+    __syncthreads();
+    const int hd = h.hd, half = hd / 2, nh = BN / hd;
+    if (n0 < h.nkv * hd) {
+      // K heads: one wave per (row, head), lane d < hd/2 owns the pair (d, d + hd/2)
+      const bool on = lane < half;
+      const float g1 = on ? bfbits2f(h.k_gain[lane]) : 0.f, g2 = on ? bfbits2f(h.k_gain[lane + half]) : 0.f;
+      const double freq = rope_freq(on ? lane : 0, hd, h.log2_theta);
+      for (int it = wave; it < rows * nh; it += 4) {
+        const int r = it / nh, hh = it % nh;
+        const int p = s_pos[r];
+        if (p < 0) continue;
+        const float x1 = on ? tile[r][hh * hd + lane] : 0.f;
+        const float x2 = on ? tile[r][hh * hd + lane + half] : 0.f;
+        const float ss = wave_sum(x1 * x1 + x2 * x2);
+        const float inv = 1.0f / sqrtf(ss / (float)hd + h.eps);
+        if (!on) continue;
+        const float y1 = x1 * inv * g1, y2 = x2 * inv * g2;
+        float c, sn;
+        rope_cs(p, freq, &c, &sn);
+        uint16_t* o = h.ring_k + (((size_t)s_req[r] * h.nkv + n0 / hd + hh) * h.C + p % h.C) * hd;
+        o[lane] = f2bfbits(y1 * c - y2 * sn);
+        o[lane + half] = f2bfbits(y2 * c + y1 * sn);
+      }
+    } else {
+      // V heads: one wave per (dimension, 64-row half); lane = row
+      for (int it = wave; it < nh * hd * 2; it += 4) {
+        const int hh = it / (2 * hd), d = (it / 2) % hd, r = (it & 1) * 64 + lane;
+        if (r >= rows) continue;
+        const int p = s_pos[r];
+        if (p < 0) continue;
+        const int gv = (n0 - h.nkv * hd) / hd + hh;
+        h.ring_v[(((size_t)s_req[r] * h.nkv + gv) * hd + d) * h.C + p % h.C] = f2bfbits(tile[r][hh * hd + d]);
       }
     }
+  }
 }
 
 template <int BN>
-hipError_t launch_tile(const TileArgs& a, int out_bf16, hipStream_t st) {
+hipError_t launch_tile(const TileArgs& a, const GemmArgs& h, int out, hipStream_t st) {
   const int tiles = ((a.M + PF_BM - 1) / PF_BM) * (a.N / BN);
   const dim3 grid(8 * ((tiles + 7) / 8));
-  if (out_bf16) hipLaunchKernelGGL((gemm_tile_kernel<BN, 1>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((gemm_tile_kernel<BN, 0>), grid, dim3(256), 0, st, a);
+  if (out == OUT_BF16) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_BF16>), grid, dim3(256), 0, st, a, h);
+  else if (out == OUT_F32) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_F32>), grid, dim3(256), 0, st, a, h);
+  else hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_HEADS>), grid, dim3(256), 0, st, a, h);
   return hipGetLastError();
 }
 
@@ -169,6 +254,17 @@ int tile_bn(int M, int N, int n_cu) {
 }
 
 hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t st) {
-  if (a.M < 1 || a.K % PF_BK || (bn != 64 && bn != 128) || a.N % bn) return hipErrorInvalidValue;
-  return bn == 128 ? launch_tile<128>(a, out_bf16, st) : launch_tile<64>(a, out_bf16, st);
+  if (a.M < 1 || a.K % (2 * PF_BK) || (bn != 64 && bn != 128) || a.N % bn) return hipErrorInvalidValue;
+  GemmArgs none;
+  memset(&none, 0, sizeof none);
+  const int out = out_bf16 ? OUT_BF16 : OUT_F32;
+  return bn == 128 ? launch_tile<128>(a, none, out, st) : launch_tile<64>(a, none, out, st);
+}
+
+hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStream_t st) {
+  // whole heads per tile: 128 columns (1 head of 128 or 2 of 64)
+  if (a.M < 1 || a.K % (2 * PF_BK) || h.hd < 2 || h.hd > 128 || h.hd % 2 || 128 % h.hd || a.N != 2 * h.nkv * h.hd ||
+      (h.nkv * h.hd) % 128)
+    return hipErrorInvalidValue;
+  return launch_tile<128>(a, h, OUT_HEADS, st);
 }
