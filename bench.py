@@ -24,7 +24,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure (no sparsity)
 COPY_BYTES = 512 << 20   # calibration copy read (and written) once before warm-up
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the LM-head kernel at the default workload
-LM_PROFILE = os.path.join(ROOT, "profiles", "lmhead_topk16_qwen3-4b_b16_ctx4k.md")
+LM_PROFILE = os.path.join(ROOT, "profiles", "lm_logits_qwen3-4b_b16_ctx4k.md")
 LM_SOURCES = [os.path.join(ROOT, "block_diffusion_drafter_tap_amd", "csrc", f)
               for f in ("lmhead.hip", "device.h", "kernels.h")]
 
@@ -300,7 +300,7 @@ def main():
         "drafted_tokens_per_s": round(blocks_s * (B - 1), 1),
         "accepted_tokens_per_s": round(blocks_s * tau, 1),
         "tau": round(tau, 3),
-        "roofline": {"bound": "hbm", "kernel": "lmhead_kernel (shared LM head + running top-k)",
+        "roofline": {"bound": "hbm", "kernel": "lm_logits_kernel (shared LM head logits + 16-column maxima)",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": lm_traffic(args.workload),
                      "avg_launch_us": round(lm_ms * 1e3, 2), "bytes_per_launch": rb["lm_head"]},
