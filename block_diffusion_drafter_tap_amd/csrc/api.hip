@@ -63,7 +63,7 @@ int attn_nchunks(const dflash_config& c) {
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, total;
+  size_t h, ssq, q, o, act, z, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, total;
 };
 
 struct GemmShape {
@@ -123,6 +123,7 @@ WsLayout ws_layout(const dflash_config& c) {
   L.q = take(Mmax * qw * 2);
   L.o = take(Mmax * qw * 2);
   L.act = take(Mmax * c.ffn * 2);
+  L.z = take(Mmax * c.hidden * 2);   // final-normed rows (LM head without LDS staging)
   L.c32 = take(c.ctx_norm ? S * c.hidden * 4 : 0);
   L.c = take(S * c.hidden * 2);
   L.xg = take(prefill_enabled(c) ? S * c.n_taps * c.tap_hidden * 2 : 0);   // gathered tap rows (prefill)
@@ -698,6 +699,14 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
     a.K = H;
     a.topk = k;
     LmPlan p = plan_lmhead(M, B, g.vocab, H, ctx->n_cu);
+    if (!p.XL) {
+      // more rows than LDS holds: the final RMSNorm once into bf16 rows, read
+      // from L2 by the head
+      uint16_t* z = at<uint16_t>(ctx->ws, ctx->wl.z);
+      e = launch_lm_norm_rows(a, z, st);
+      if (e != hipSuccess) return hip_fail(e, "final norm");
+      a.x = z;
+    }
     float* lg = logits ? logits : at<float>(ctx->ws, ctx->wl.logits);
     const int tr = logits ? 0 : 1;
     float* gm = at<float>(ctx->ws, ctx->wl.gmax);

@@ -82,7 +82,9 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, in
 size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
 
 // LM head: persistent logits GEMM over the block rows (GemmArgs X_NORM fields
-// xf, xgain, ssq_*, w = W_lm, M = R*B, N = vocab, K, B, topk): fp32 logits to
+// xf, xgain, ssq_*, w = W_lm, M = R*B, N = vocab, K, B, topk; when the plan does
+// not stage the rows in LDS (XL = 0), x / ldx instead hold the final-normed rows
+// as bf16, written by the caller beforehand): fp32 logits to
 // the caller's logits[R*(B-1)][N] (mask rows), or transposed to a scratch
 // [N][16*MT] (all rows; coalesced), and per-16-column maxima of the mask rows to
 // gmax[R*(B-1)][ceil(N/16)]; then the exact per-row top-k to ids/vals
@@ -92,6 +94,9 @@ struct LmPlan {
   size_t lds;
 };
 LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu);
+// the final-normed rows as bf16 z[M][K] (for plans with XL = 0), from the same
+// X_NORM fields, with the LDS staging's arithmetic
+hipError_t launch_lm_norm_rows(const GemmArgs& a, uint16_t* z, hipStream_t st);
 hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, int transposed, float* gmax,
                             hipStream_t st);
 hipError_t launch_lm_topk(const GemmArgs& a, const LmPlan& p, const float* logits, int transposed,

@@ -23,24 +23,6 @@ namespace {
 // CU, so nearly all of the 160 KB of a gfx950 CU)
 constexpr size_t LM_XL_MAX_BYTES = 159 * 1024;
 
-// 8 consecutive values (k..k+7) of row `row` of the final RMSNorm as bf16x8:
-// z = h * inv * g, h the fp32 residual stream, inv the row's 1/rms.
-DEV u32x4 norm_x8(const GemmArgs& a, int row, int k, float inv) {
-  const float* p = a.xf + (size_t)row * a.ldx + k;
-  const f32x4 h0 = *(const f32x4*)p, h1 = *(const f32x4*)(p + 4);
-  const u32x4 g = ld16(a.xgain + k);
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const f32x4 h = i ? h1 : h0;
-    r[2 * i] = pack_bf16x2(h[0] * inv * __uint_as_float(g[2 * i] << 16),
-                           h[1] * inv * __uint_as_float(g[2 * i] & 0xffff0000u));
-    r[2 * i + 1] = pack_bf16x2(h[2] * inv * __uint_as_float(g[2 * i + 1] << 16),
-                               h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
-  }
-  return r;
-}
-
 // bf16x8 of (h0, h1) * inv * g (g: 8 bf16 gains)
 DEV u32x4 norm8(f32x4 h0, f32x4 h1, u32x4 g, float inv) {
   u32x4 r;
@@ -53,6 +35,27 @@ DEV u32x4 norm8(f32x4 h0, f32x4 h1, u32x4 g, float inv) {
                                h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
   }
   return r;
+}
+
+// The final-normed rows as bf16 for the path that does not stage them in LDS,
+// with the staging's arithmetic (sums of squares added in column-group order,
+// the same normalize-and-round per 8 values), so a row's logits do not depend
+// on how many rows share the launch.
+__global__ __launch_bounds__(256) void lm_norm_rows_kernel(const GemmArgs a, uint16_t* z) {
+  __shared__ float s_inv;
+  const int m = blockIdx.x;
+  if (threadIdx.x == 0) {
+    float ss = 0.f;
+    for (int g = 0; g < a.n_ssq; ++g) ss += a.ssq_in[(size_t)g * a.ssq_ld + m];
+    s_inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  for (int c = threadIdx.x; c < a.K / 8; c += blockDim.x) {
+    const float* p = a.xf + (size_t)m * a.ldx + 8 * c;
+    *(u32x4*)(z + (size_t)m * a.K + 8 * c) =
+        norm8(*(const f32x4*)p, *(const f32x4*)(p + 4), ld16(a.xgain + 8 * c), inv);
+  }
 }
 
 template <int MT, int XL, int D>
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     for (int j = 0; j < D; ++j) load_w(wcur, j, wbuf[j]);
   }
 
-  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
+  for (int r = threadIdx.x; r < (XL ? ROWS : 0); r += blockDim.x) {
     const int m = min(r, a.M - 1);
     float ss = 0.f;
     for (int b0 = 0; b0 < a.n_ssq; b0 += 8) {
@@ -126,7 +129,8 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
   }
   auto xfrag = [&](int mt, int k) -> u32x4 {
     if (XL) return *(const u32x4*)(xs + (mt * 16 + lr) * ldl + k + 8 * lg);
-    return norm_x8(a, min(mt * 16 + lr, a.M - 1), k + 8 * lg, s_inv[mt * 16 + lr]);
+    // rows too many for LDS: the normed rows were written as bf16 (a.x) beforehand
+    return ld16(a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + k + 8 * lg);
   };
 
   for (; g < n_groups; g += gridDim.x) {
@@ -449,6 +453,12 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   p.XL = xbytes <= LM_XL_MAX_BYTES;
   p.lds = p.XL ? xbytes : 0;
   return p;
+}
+
+hipError_t launch_lm_norm_rows(const GemmArgs& a, uint16_t* z, hipStream_t st) {
+  if (a.K % 8 || a.M < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lm_norm_rows_kernel, dim3(a.M), dim3(256), 0, st, a, z);
+  return hipGetLastError();
 }
 
 hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, int transposed, float* gmax,
