@@ -4,9 +4,12 @@
 // block's own K/V were written to slots pos..pos+B-1 by the QKV epilogue), so a
 // query sees one contiguous position range [lo, pos+B).
 //
-// Workgroup = (key chunk, kv head, request) with HD/16 waves and 32 keys per
-// wave (256-key chunks at head_dim 128), in two phases with an exact softmax
-// inside the chunk:
+// Workgroup = (key chunk, kv head, request, query-slot part) with HD/16 waves
+// and 32 keys per wave (256-key chunks at head_dim 128). The G*B query slots of
+// a kv head are split over `hs` workgroups when there would otherwise be fewer
+// than 256 workgroups (each then stages only its slots' Q and P in LDS; the
+// chunk's K/V are read by each part, from L2 after the first). Two phases with
+// an exact softmax inside the chunk:
 //  1. wave w takes the chunk's 32-key sub-tile w and computes S^T = K Q^T for
 //     all G*B queries of the kv head's query-head group (MFMA, keys x queries,
 //     Q staged once in LDS: the waves share it instead of each loading it).
@@ -25,9 +28,10 @@
 //
 // A second kernel combines the chunk partials in chunk order, so results do not
 // depend on scheduling. Both kernels use a 1-D grid whose workgroup id is
-// chunk * (R*nkv) + (request, head): workgroups are dealt to the 8 XCDs round
-// robin, so with R*nkv a multiple of 8 every chunk of one head lands on the
-// same XCD and the combine reads its partials from that XCD's L2.
+// (chunk * hs + part) * (R*nkv) + (request, head): workgroups are dealt to the 8
+// XCDs round robin, so with R*nkv a multiple of 8 every chunk and part of one
+// head lands on the same XCD, and the combine reads its partials from that
+// XCD's L2.
 #include "device.h"
 #include "kernels.h"
 
@@ -74,10 +78,13 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int RN = a.R * a.nkv;
-  const int lrg = blockIdx.x % RN, chunk = blockIdx.x / RN;
+  const int lrg = blockIdx.x % RN, rest = blockIdx.x / RN;
+  const int hs = rest % a.hs, chunk = rest / a.hs;
   const int r = lrg / a.nkv, g = lrg % a.nkv;
   const int G = a.nq / a.nkv;
   const int slots = G * a.B;
+  const int s0 = hs * NSL;                 // this workgroup's first query slot
+  const int nsl = min(NSL, slots - s0);    // its query slots
 
   const Range kr = key_range(a, r, threadIdx.x == 0 && chunk == 0 && g == 0);
   if (chunk >= kr.n_ch) return;
@@ -109,15 +116,16 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
     }
   }
 
-  // Q of all G*B query slots (slot = h_local * B + i); zero rows pad the last tile
+  // Q of this workgroup's query slots (slot = h_local * B + i); zero rows pad the last tile
   for (int e = threadIdx.x; e < NSL * (HD / 8); e += blockDim.x) {
-    const int slot = e / (HD / 8), c = e % (HD / 8);
+    const int ls = e / (HD / 8), c = e % (HD / 8);
     u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-    if (slot < slots) {
+    if (ls < nsl) {
+      const int slot = s0 + ls;
       const int hq = slot / a.B, iq = slot % a.B;
       v = ld16(a.q + ((size_t)r * a.B + iq) * a.nq * HD + (size_t)(g * G + hq) * HD + 8 * c);
     }
-    *(u32x4*)&s_q[slot][8 * c] = v;
+    *(u32x4*)&s_q[ls][8 * c] = v;
   }
   __syncthreads();
 
@@ -195,17 +203,17 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
   }
 
   // chunk partial: O (relative to the chunk max M), M, L
-  const size_t cbase = ((size_t)lrg * a.n_chunks + chunk) * slots;
+  const size_t cbase = ((size_t)lrg * a.n_chunks + chunk) * slots + s0;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int sl = qt * 16 + lr;
-    if (sl < slots) {
+    if (sl < nsl) {
 #pragma unroll
       for (int tt = 0; tt < HTW; ++tt)
         *(f32x4*)(a.part_o + (cbase + sl) * HD + 16 * (wave * HTW + tt) + 4 * lg) = o[qt][tt];
     }
   }
-  for (int sl = threadIdx.x; sl < slots; sl += blockDim.x) {
+  for (int sl = threadIdx.x; sl < nsl; sl += blockDim.x) {
     float M = s_mx[0][sl], L = s_l[0][sl];
 #pragma unroll
     for (int w = 1; w < ATT_WAVES; ++w) {
@@ -220,7 +228,8 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
 // Combine the chunk partials of one (request, kv head): O = sum_c w_c O_c with
 // w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c, in chunk order. Each thread owns
 // four consecutive head_dim values of one query slot; workgroup id =
-// part * (R*nkv) + (request, head), the attention kernel's XCD mapping.
+// part * (R*nkv) + (request, head), so each head's combine runs on the XCD that
+// ran its chunks.
 template <int HD>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs a) {
   const int RN = a.R * a.nkv;
@@ -276,7 +285,7 @@ void launch_hd(const AttnArgs& a, hipStream_t st) {
   const int slots = attn_slots(a.nq, a.nkv, a.B);
   const int parts = (slots * HD / 4 + 63) / 64;
   const size_t lds = (size_t)NWA * QT * 2 * 64 * sizeof(u32x4);
-  hipLaunchKernelGGL((attn_kernel<HD, QT, NWA>), dim3(a.n_chunks * RN), dim3(64 * NWA), lds, st, a);
+  hipLaunchKernelGGL((attn_kernel<HD, QT, NWA>), dim3(a.n_chunks * a.hs * RN), dim3(64 * NWA), lds, st, a);
   hipLaunchKernelGGL((attn_combine_kernel<HD>), dim3(parts * RN), dim3(64), 0, st, a);
 }
 
@@ -289,7 +298,15 @@ hipError_t launch_attention(const AttnArgs& args, int R, hipStream_t st) {
   AttnArgs a = args;
   a.R = R;
   const int slots = attn_slots(a.nq, a.nkv, a.B);
-  const int qt = (slots + 15) / 16;
+  const int qt_all = (slots + 15) / 16;
+  // query-slot split: few (chunk, kv head) workgroups leave CUs idle and every
+  // wave reads all of a workgroup's Q and P from LDS, so split the query tiles
+  // over up to qt_all workgroups until there are at least 256 (measured: 512 is slower)
+  int hs = 1;
+  while (hs < qt_all && (long long)a.n_chunks * R * a.nkv * hs < 256) hs *= 2;
+  if (hs > qt_all) hs = qt_all;
+  a.hs = hs;
+  const int qt = (qt_all + hs - 1) / hs;
   if (qt > 4 || a.kc != attn_chunk_keys(a.hd)) return hipErrorInvalidValue;   // <= 64 query slots per kv head
 #define QTS(HD)                                  \
   switch (qt) {                                  \

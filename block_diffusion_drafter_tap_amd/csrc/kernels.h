@@ -112,6 +112,7 @@ struct AttnArgs {
   const int* valid_from;
   int B, W, C, nq, nkv, hd, kc, n_chunks;
   int R;                   // requests of this launch (set by launch_attention)
+  int hs;                  // query-slot parts per (chunk, kv head) (set by launch_attention)
   float scale_log2;        // log2(e) / sqrt(hd)
   float* part_o;           // [R*nkv][n_chunks][slots][hd]
   float* part_ml;          // [R*nkv][n_chunks][slots][2]
