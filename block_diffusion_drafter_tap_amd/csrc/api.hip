@@ -699,9 +699,9 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
     a.K = H;
     a.topk = k;
     LmPlan p = plan_lmhead(M, B, g.vocab, H, ctx->n_cu);
-    if (!p.XL) {
-      // more rows than LDS holds: the final RMSNorm once into bf16 rows, read
-      // from L2 by the head
+    if (p.XL != 1) {
+      // more rows than LDS holds: the final RMSNorm once into bf16 rows, which
+      // the head streams through LDS windows (or reads from L2)
       uint16_t* z = at<uint16_t>(ctx->ws, ctx->wl.z);
       e = launch_lm_norm_rows(a, z, st);
       if (e != hipSuccess) return hip_fail(e, "final norm");

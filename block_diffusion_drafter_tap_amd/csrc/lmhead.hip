@@ -87,7 +87,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     for (int j = 0; j < D; ++j) load_w(wcur, j, wbuf[j]);
   }
 
-  for (int r = threadIdx.x; r < (XL ? ROWS : 0); r += blockDim.x) {
+  for (int r = threadIdx.x; r < (XL == 1 ? ROWS : 0); r += blockDim.x) {
     const int m = min(r, a.M - 1);
     float ss = 0.f;
     for (int b0 = 0; b0 < a.n_ssq; b0 += 8) {
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     s_inv[r] = 1.0f / sqrtf(ss / (float)K + a.eps);
   }
   __syncthreads();
-  if (XL) {
+  if (XL == 1) {
     // 8 vectors of a thread in flight per batch
     const int per_row = K / 8, total = ROWS * per_row;
     for (int e0 = threadIdx.x; e0 < total; e0 += 8 * blockDim.x) {
@@ -127,10 +127,41 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     }
     __syncthreads();
   }
-  auto xfrag = [&](int mt, int k) -> u32x4 {
-    if (XL) return *(const u32x4*)(xs + (mt * 16 + lr) * ldl + k + 8 * lg);
-    // rows too many for LDS: the normed rows were written as bf16 (a.x) beforehand
-    return ld16(a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + k + 8 * lg);
+  // XL == 2: the normed bf16 rows (a.x, written beforehand) pass through LDS in
+  // windows of D chunks, double-buffered: the 8 waves share one copy, the next
+  // window's loads are in flight while the current one is used, and one barrier
+  // per window separates them (D divides the chunk count)
+  constexpr int WK = 128 * D, WLD = WK + 8;
+  constexpr int WPT = XL == 2 ? ROWS * WK / 8 / 512 : 1;   // 16-byte pieces per thread per window
+  static_assert(XL != 2 || (WPT >= 1 && ROWS * WK / 8 == WPT * 512), "a window is whole pieces of every thread");
+  const int nwin = nchunks / D;
+  u32x4 xr[WPT];
+  auto wload = [&](int w) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int p = threadIdx.x + i * 512, r = p / (WK / 8), c = p % (WK / 8);
+      xr[i] = ld16(a.x + (size_t)min(r, a.M - 1) * a.ldx + w * WK + 8 * c);
+    }
+  };
+  auto wstore = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int p = threadIdx.x + i * 512, r = p / (WK / 8), c = p % (WK / 8);
+      *(u32x4*)(xs + ((size_t)b * ROWS + r) * WLD + 8 * c) = xr[i];
+    }
+  };
+  int wb = 0;   // LDS buffer of the current window
+  if constexpr (XL == 2) {
+    wload(0);
+    wstore(0);
+    __syncthreads();
+  }
+  // kk: offset inside the K range; kl: offset inside the current window
+  auto xfrag = [&](int mt, int kk, int kl) -> u32x4 {
+    if constexpr (XL == 1) return *(const u32x4*)(xs + (mt * 16 + lr) * ldl + kk + 8 * lg);
+    if constexpr (XL == 2) return *(const u32x4*)(xs + ((size_t)wb * ROWS + mt * 16 + lr) * WLD + kl + 8 * lg);
+    // rows too many for LDS and K not a multiple of the window: straight from L2
+    return ld16(a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + kk + 8 * lg);
   };
 
   for (; g < n_groups; g += gridDim.x) {
@@ -141,6 +172,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < nchunks; c0 += D) {
+      if constexpr (XL == 2) wload((c0 / D + 1) % nwin);   // the next window (window 0 of the next group at the end)
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         const int c = c0 + j;
@@ -148,10 +180,16 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
         for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), as_bf16x8(wbuf[j][s]), acc[mt]);
+            acc[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s, 128 * j + 32 * s)), as_bf16x8(wbuf[j][s]),
+                                   acc[mt]);
         const int nc = c + D;
         if (nc < nchunks) load_w(wcur, nc, wbuf[j]);
         else if (has_next) load_w(wnext, nc - nchunks, wbuf[j]);
+      }
+      if constexpr (XL == 2) {
+        wstore(wb ^ 1);
+        __syncthreads();
+        wb ^= 1;
       }
     }
     wcur = wnext;
@@ -431,12 +469,17 @@ template <int MT, int XL>
 hipError_t launch_lm(const GemmArgs& a, int groups, int P, size_t lds, float* logits, int tr, float* gmax,
                      hipStream_t st) {
   const int nchunks = a.K / 128;
-  if (nchunks % 4 == 0)
+  if constexpr (XL == 2) {   // windows of 4 chunks
+    if (nchunks % 4) return hipErrorInvalidValue;
     hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
-  else if (nchunks % 2 == 0)
-    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 2>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
-  else
-    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 1>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+  } else {
+    if (nchunks % 4 == 0)
+      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+    else if (nchunks % 2 == 0)
+      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 2>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+    else
+      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 1>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+  }
   return hipGetLastError();
 }
 
@@ -449,9 +492,10 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   const int per = (p.groups + n_cu - 1) / n_cu;
   p.P = (p.groups + per - 1) / per;
   const int rows = 16 * p.MT;
-  const size_t xbytes = (size_t)rows * (K + 8) * 2;
-  p.XL = xbytes <= LM_XL_MAX_BYTES;
-  p.lds = p.XL ? xbytes : 0;
+  const size_t xbytes = (size_t)rows * (K + 8) * 2;            // the whole normed rows
+  const size_t wbytes = (size_t)2 * rows * (4 * 128 + 8) * 2;  // two windows of 4 chunks
+  p.XL = xbytes <= LM_XL_MAX_BYTES ? 1 : (K % 512 == 0 && wbytes <= LM_XL_MAX_BYTES ? 2 : 0);
+  p.lds = p.XL == 1 ? xbytes : (p.XL == 2 ? wbytes : 0);
   return p;
 }
 
@@ -465,7 +509,10 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
                             hipStream_t st) {
   if (a.B < 2) return hipErrorInvalidValue;
   hipError_t e;
-#define LM(MT) e = p.XL ? launch_lm<MT, 1>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) : launch_lm<MT, 0>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st);
+#define LM(MT)                                                                              \
+  e = p.XL == 1   ? launch_lm<MT, 1>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) \
+      : p.XL == 2 ? launch_lm<MT, 2>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) \
+                  : launch_lm<MT, 0>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st);
   switch (p.MT) {
     case 1: LM(1) break;
     case 2: LM(2) break;
