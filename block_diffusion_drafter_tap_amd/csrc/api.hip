@@ -48,12 +48,12 @@ const void* w_rows(const dflash_config& c, const uint16_t* w, size_t row, int K)
 }
 const uint16_t* s_rows(const uint16_t* s, size_t row, int K) { return s ? s + row * (size_t)(K / 64) : nullptr; }
 
-// Staging calls of at least this many rows (bf16 weights) take the prefill
-// path: tap gather, then tiled GEMMs for fc and each layer's context K/V.
+// Staging calls of at least this many rows take the prefill path: tap gather,
+// then tiled GEMMs for fc and each layer's context K/V.
 constexpr int PREFILL_MIN_ROWS = 256;
 bool prefill_enabled(const dflash_config& c) {
   // fc in 64- or 128-column tiles; context K/V in 128-column tiles of whole heads
-  return c.wfmt == DFLASH_W_BF16 && c.max_stage_rows >= PREFILL_MIN_ROWS && tile_bn(PREFILL_MIN_ROWS, c.hidden, 256) != 0 &&
+  return c.max_stage_rows >= PREFILL_MIN_ROWS && tile_bn(PREFILL_MIN_ROWS, c.hidden, 256) != 0 &&
          (c.n_kv_heads * c.head_dim) % 128 == 0 && 128 % c.head_dim == 0;
 }
 
@@ -292,7 +292,7 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     e = launch_tap_gather(tg, n_rows, st);
     if (e == hipSuccess) {
       TileArgs ta{xg, TW, ctx->fc, n_rows, H, TW,
-                  g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf, H};
+                  g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf, H, ctx->fc_s};
       e = launch_gemm_tile(ta, tile_bn(n_rows, H, ctx->n_cu), !g.ctx_norm, st);
     }
   }
@@ -304,7 +304,9 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
   const size_t rl = ring_layer_elems(g);
   for (int l = 0; l < g.n_layers; ++l) {
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
-    TileArgs ta{c_bf, H, ctx->wqkv[l] + (size_t)g.n_q_heads * hd * H, n_rows, nkv_w, H, nullptr, 0};
+    const size_t kv_row0 = (size_t)g.n_q_heads * hd;   // the K and V rows of the fused QKV matrix
+    TileArgs ta{c_bf, H, w_rows(g, ctx->wqkv[l], kv_row0, H), n_rows, nkv_w, H, nullptr, 0,
+                s_rows(dflash_ctx::sc(ctx->wqkv_s, l), kv_row0, H)};
     GemmArgs b = base_args(ctx);
     b.M = n_rows;
     b.k_gain = ctx->k_norm[l];

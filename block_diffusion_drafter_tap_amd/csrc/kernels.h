@@ -147,10 +147,11 @@ struct TapGather {
 struct TileArgs {
   const uint16_t* x;
   long long ldx;
-  const uint16_t* w;
+  const void* w;             // bf16 [N][K], or packed INT4 [N][K/2] when wscale is set
   int M, N, K;
   void* out;
   long long ldo;
+  const uint16_t* wscale;    // INT4 fp16 group scales [N][K/64], or NULL for bf16 weights
 };
 hipError_t launch_tap_gather(const TapGather& g, int M, hipStream_t st);
 int tile_bn(int M, int N, int n_cu);   // 0: N fits neither tile

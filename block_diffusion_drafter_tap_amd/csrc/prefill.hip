@@ -1,7 +1,6 @@
 // Prefill staging: many context rows at once (a request's whole window), where
 // fc and the per-layer K/V projections are dense contractions (thousands of
-// rows) rather than weight streams. bf16 weights only; INT4 weights stage
-// through the split-K path.
+// rows) rather than weight streams. bf16 or INT4 (g64) weights.
 //
 //   tap_gather_kernel  X[m][t*H + j] = bf16(mean over the hc streams of tap t)
 //                      (the same arithmetic as the skinny GEMM's tap staging)
@@ -62,18 +61,28 @@ DEV void staged_row(const GemmArgs& h, int m, int* req, long long* p) {
 // OUT_HEADS: the tile's columns are whole context K heads (k RMSNorm over the
 // head, RoPE at the row's position, rows into the K ring) or V heads (into the
 // transposed V ring, 64 consecutive rows of one dimension per wave store).
-template <int BN, int OUT>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
+// INT4 weights (Q4): a K stage of 64 is one quantization group. Its packed words
+// are unpacked into the LDS W tile as bf16 (128 + u) pairs (one and-or per pair;
+// bf16's ulp at 128 is 1), the group scale of every W row goes to LDS, and the X
+// staging also leaves each row's sum of the stage's bf16 values. The stage's
+// MFMAs accumulate t = sum x * (u + 128) from zero and the stage adds
+// s * (t - 136 * sum x) = s * sum x * q.
+template <int BN, int OUT, int Q4>
+__global__ __launch_bounds__(256, Q4 ? 1 : 2)   // INT4 holds per-group accumulators too: one workgroup per CU
+void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
   constexpr int WN = BN / 2;        // columns per wave
   constexpr int NJ = WN / 16;       // 16-column MFMA tiles per wave
   constexpr int XP = PF_BM * PF_BK / 8 / 256;   // 16-byte X pieces per thread per stage
-  constexpr int WP = BN * PF_BK / 8 / 256;      // W pieces
+  constexpr int WP = Q4 ? 1 : BN * PF_BK / 8 / 256;   // W pieces (bf16)
+  constexpr int TPR = 256 / BN;     // INT4: threads per W row, each with 4 / TPR of its word pairs
+  constexpr int JPT = 4 / TPR;
   constexpr int XS_BYTES = 2 * PF_BM * PF_LDK * 2, WS_BYTES = 2 * BN * PF_LDK * 2;
   constexpr int TILE_BYTES = OUT == OUT_HEADS ? PF_BM * (BN + 1) * 4 : 0;
   constexpr int SMEM = XS_BYTES + WS_BYTES > TILE_BYTES ? XS_BYTES + WS_BYTES : TILE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   auto xs = (uint16_t(*)[PF_BM][PF_LDK])smem;
   auto ws = (uint16_t(*)[BN][PF_LDK])(smem + XS_BYTES);
+  __shared__ float s_xsum[Q4 ? 2 : 1][Q4 ? PF_BM : 1], s_sc[Q4 ? 2 : 1][Q4 ? BN : 1];
 
   const int mt = (a.M + PF_BM - 1) / PF_BM, nt = a.N / BN, tiles = mt * nt;
   const int per_xcd = (tiles + 7) / 8;
@@ -89,6 +98,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, con
   // two register sets: stage s + 2 is loaded while stage s computes and is
   // stored to LDS after stage s + 1 computes (two stages of latency cover)
   u32x4 xr[2][XP], wr[2][WP];
+  u32x2 qr[2][JPT];   // INT4: the stage's two words of each word pair j of this thread's row
+  uint32_t sr[2];     // INT4: the row's fp16 group scale
+  const int wrow = tid / TPR, jt = (tid % TPR) * JPT;
   auto load = [&](int s, int q) {
     const int k0 = s * PF_BK;
 #pragma unroll
@@ -96,10 +108,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, con
       const int p = tid + i * 256, row = p / 8, seg = p % 8;
       xr[q][i] = ld16(a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + k0 + 8 * seg);
     }
+    if constexpr (Q4) {
+      // 128-wide chunk s/2, half s%2: words 4j + 2(s%2) and 4j + 2(s%2) + 1 hold
+      // the stage's k-values 32i + 8j + e (i = 0, 1)
+      const uint8_t* rp = (const uint8_t*)a.w + (size_t)(n0 + wrow) * (a.K / 2) + (s / 2) * 64 + (s % 2) * 8;
 #pragma unroll
-    for (int i = 0; i < WP; ++i) {
-      const int p = tid + i * 256, row = p / 8, seg = p % 8;
-      wr[q][i] = ld16(a.w + (size_t)(n0 + row) * a.K + k0 + 8 * seg);
+      for (int jj = 0; jj < JPT; ++jj) qr[q][jj] = *(const u32x2*)(rp + 16 * (jt + jj));
+      sr[q] = a.wscale[(size_t)(n0 + wrow) * (a.K / 64) + s];
+    } else {
+#pragma unroll
+      for (int i = 0; i < WP; ++i) {
+        const int p = tid + i * 256, row = p / 8, seg = p % 8;
+        wr[q][i] = ld16((const uint16_t*)a.w + (size_t)(n0 + row) * a.K + k0 + 8 * seg);
+      }
     }
   };
   auto store = [&](int b, int q) {
@@ -107,11 +128,35 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, con
     for (int i = 0; i < XP; ++i) {
       const int p = tid + i * 256;
       *(u32x4*)&xs[b][p / 8][8 * (p % 8)] = xr[q][i];
-    }
+      if constexpr (Q4) {
+        // the row's 8 pieces sit on 8 consecutive lanes
+        float t = 0.f;
 #pragma unroll
-    for (int i = 0; i < WP; ++i) {
-      const int p = tid + i * 256;
-      *(u32x4*)&ws[b][p / 8][8 * (p % 8)] = wr[q][i];
+        for (int u = 0; u < 4; ++u) t += __uint_as_float(xr[q][i][u] << 16) + __uint_as_float(xr[q][i][u] & 0xffff0000u);
+        t += __shfl_xor(t, 1, 64);
+        t += __shfl_xor(t, 2, 64);
+        t += __shfl_xor(t, 4, 64);
+        if (p % 8 == 0) s_xsum[b][p / 8] = t;
+      }
+    }
+    if constexpr (Q4) {
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t w = qr[q][jj][i];
+          u32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = ((w >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+          *(u32x4*)&ws[b][wrow][32 * i + 8 * (jt + jj)] = v;
+        }
+      if (tid % TPR == 0) s_sc[b][wrow] = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[q]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WP; ++i) {
+        const int p = tid + i * 256;
+        *(u32x4*)&ws[b][p / 8][8 * (p % 8)] = wr[q][i];
+      }
     }
   };
 
@@ -122,6 +167,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, con
     for (int j = 0; j < NJ; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int b) {
+    f32x4 t[Q4 ? 4 : 1][Q4 ? NJ : 1];
+    if constexpr (Q4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) t[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int kk = 0; kk < PF_BK; kk += 32) {
       u32x4 af[4], bf[NJ];
@@ -132,7 +184,22 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, con
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+        for (int j = 0; j < NJ; ++j) {
+          if constexpr (Q4) t[i][j] = mfma16x16x32(as_bf16x8(af[i]), as_bf16x8(bf[j]), t[i][j]);
+          else acc[i][j] = mfma16x16x32(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+        }
+    }
+    if constexpr (Q4) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float sc = s_sc[b][wn * WN + 16 * j + lr];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 xg = *(const f32x4*)&s_xsum[b][wm * 64 + 16 * i + 4 * lg];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, fmaf(-136.0f, xg[r], t[i][j][r]), acc[i][j][r]);
+        }
+      }
     }
   };
   // stage s lives in LDS buffer s & 1 and register set s & 1; the stage count
@@ -223,14 +290,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(const TileArgs a, con
   }
 }
 
-template <int BN>
-hipError_t launch_tile(const TileArgs& a, const GemmArgs& h, int out, hipStream_t st) {
+template <int BN, int Q4>
+hipError_t launch_tile_q(const TileArgs& a, const GemmArgs& h, int out, hipStream_t st) {
   const int tiles = ((a.M + PF_BM - 1) / PF_BM) * (a.N / BN);
   const dim3 grid(8 * ((tiles + 7) / 8));
-  if (out == OUT_BF16) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_BF16>), grid, dim3(256), 0, st, a, h);
-  else if (out == OUT_F32) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_F32>), grid, dim3(256), 0, st, a, h);
-  else hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_HEADS>), grid, dim3(256), 0, st, a, h);
+  if (out == OUT_BF16) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_BF16, Q4>), grid, dim3(256), 0, st, a, h);
+  else if (out == OUT_F32) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_F32, Q4>), grid, dim3(256), 0, st, a, h);
+  else hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_HEADS, Q4>), grid, dim3(256), 0, st, a, h);
   return hipGetLastError();
+}
+
+template <int BN>
+hipError_t launch_tile(const TileArgs& a, const GemmArgs& h, int out, hipStream_t st) {
+  if (a.wscale) return launch_tile_q<BN, 1>(a, h, out, st);
+  return launch_tile_q<BN, 0>(a, h, out, st);
 }
 
 }  // namespace

@@ -1,8 +1,8 @@
 """GPU parity of prefill staging: a staging call of at least 256 rows takes the
 tap-gather + tiled-GEMM path. Checked against the oracle (ring K/V and a draft
 round) on the tiny drafter with ragged row tiles, one and four hyper-connection
-streams, with and without the context RMSNorm; and against the same rows staged
-by the split-K path in chunks below the threshold."""
+streams, with and without the context RMSNorm, bf16 and INT4 weights; and
+against the same rows staged by the split-K path in chunks below the threshold."""
 import numpy as np
 import pytest
 import torch
@@ -21,14 +21,15 @@ def _gpu():
     return binding
 
 
-@pytest.mark.parametrize("hc,ctx_norm", [(1, 0), (4, 0), (1, 1)])
-def test_prefill_tiny_vs_oracle(hc, ctx_norm):
+@pytest.mark.parametrize("hc,ctx_norm,wfmt", [(1, 0, config.WFMT_BF16), (4, 0, config.WFMT_BF16),
+                                               (1, 1, config.WFMT_BF16), (1, 0, config.WFMT_INT4_G64)])
+def test_prefill_tiny_vs_oracle(hc, ctx_norm, wfmt):
     binding = _gpu()
     W, P = 300, 340
-    cfg = config.tiny(window=W, max_stage_rows=600, hc_streams=hc, ctx_norm=ctx_norm)
-    print(f"case: tiny prefill hc={hc} ctx_norm={ctx_norm} rows={W}", flush=True)
+    cfg = config.tiny(window=W, max_stage_rows=600, hc_streams=hc, ctx_norm=ctx_norm, wfmt=wfmt)
+    print(f"case: tiny prefill hc={hc} ctx_norm={ctx_norm} wfmt={wfmt} rows={W}", flush=True)
     w = synth.make_weights(cfg, seed=3, device="cuda")
-    wh = Hn.host_weights(w)
+    wh = D.dequantize(Hn.host_weights(w))
     taps = synth.make_taps(cfg, P, seed=4, device="cuda", outliers=(hc == 1))
     hist = [t.cpu().numpy() for t in taps]
     dr = binding.Drafter(cfg, w)
