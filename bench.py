@@ -137,9 +137,24 @@ def cpu_baseline(cfg, w, taps_hist, tokens, pos, valid_from, budget_s: float = 1
         if el >= budget_s or n >= 8:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    # one more round on a single BLAS thread when a round is short enough
+    one = None
+    if el / n <= 5.0:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            t1 = time.perf_counter()
+            D.draft_block(cfg, wh, taps_hist, tokens, pos, valid_from, mode="mirror")
+            one = round(1.0 / (time.perf_counter() - t1), 4)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": n / el, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} full draft round(s) of one request (uncached context recompute of the "
-                      f"{cfg.window}-row window, {cfg.n_layers} layers, LM head + top-k) in {el:.1f} s"}
+                      f"{cfg.window}-row window, {cfg.n_layers} layers, LM head + top-k) in {el:.1f} s",
+            "value_1_thread": one, "cpu_model": model}
 
 
 def main():
@@ -270,11 +285,66 @@ def main():
     if word != 0:
         raise SystemExit(f"device error word 0x{word:x}")
     lm_ms = float(np.mean([b.elapsed_time(a) for b, a in zip(ev_b, ev_a)]))
+    st = dr.stats().cpu().numpy()   # accept profile of the warm-up + timed rounds
+
+    # per-round distribution: a second pass of the same rounds with an event
+    # between consecutive rounds (kept out of the headline loop above)
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    for j, i in enumerate(range(args.warmup, n_rounds)):
+        rev[j].record()
+        one_round(i)
+    rev[-1].record()
+    torch.cuda.synchronize()
+    per_round = np.array([rev[j].elapsed_time(rev[j + 1]) for j in range(args.steps)])
+
+    # the same round captured once into a HIP graph and replayed: launch cost
+    # vs plain launches (the replays restage the same verify rows)
+    graph = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_round(args.warmup)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_round(args.warmup)
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        word = dr.check()
+        if word != 0:
+            raise SystemExit(f"device error word 0x{word:x} after graph replays")
+        graph = {"ms_per_step": round(gms, 4), "value": round(R / (gms / 1e3), 2), "replays": args.steps}
+        del g
+    except RuntimeError as exc:   # capture unsupported here: report why, keep the plain result
+        graph = {"error": str(exc)[:200]}
+
+    # HBM read reference: a plain streaming-read kernel of this library over 1 GiB
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    sink = torch.empty(1024, dtype=torch.int32, device=dev)
+    binding.stream_read(src, sink)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record()
+    for _ in range(10):
+        binding.stream_read(src, sink)
+    r1.record()
+    torch.cuda.synchronize()
+    read_gbps = 10 * src.numel() * 4 / (r0.elapsed_time(r1) / 1e3) / 1e9
+    del src, sink
 
     ms_step = ms / args.steps
     blocks_s = R * args.steps / (ms / 1e3)
     rb = round_bytes(cfg, R, k)
-    st = dr.stats().cpu().numpy()
     tau = float(st[B + 1] / max(st[0], 1))
     lm_gbps = rb["lm_head"] / (lm_ms / 1e3) / 1e9
     result = {
@@ -306,6 +376,11 @@ def main():
                      "avg_launch_us": round(lm_ms * 1e3, 2), "bytes_per_launch": rb["lm_head"]},
         "cpu_baseline": None,
         "prefill": prefill_report(cfg, W, prefill_ms),
+        "round_ms": {"p10": round(float(np.percentile(per_round, 10)), 4),
+                     "p50": round(float(np.percentile(per_round, 50)), 4),
+                     "p90": round(float(np.percentile(per_round, 90)), 4)},
+        "graph": graph,
+        "hbm_read_reference_gbps": round(read_gbps, 1),
     }
     if not args.no_cpu_baseline:
         import numpy as np  # noqa: F811

@@ -89,6 +89,7 @@ def load(path: str = LIB_PATH):
         "dflash_check": (c_int, [P, P, ctypes.POINTER(c_uint)]),
         "dflash_clear_error": (c_int, [P, P]),
         "dflash_set_timing_events": (c_int, [P, c_int, PP, PP, c_int]),
+        "dflash_stream_read": (c_int, [P, c_size_t, P, P]),
         "dflash_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -105,6 +106,13 @@ def header_functions(path: str = HEADER) -> List[str]:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor):
+    """One streaming read of `src` (the HBM read reference), on the current stream."""
+    lib = load()
+    _check("dflash_stream_read", lib.dflash_stream_read(src.data_ptr(), src.numel() * src.element_size(),
+                                                        sink.data_ptr(), _stream()))
 
 
 def last_error() -> str:

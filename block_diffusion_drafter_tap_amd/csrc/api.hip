@@ -762,6 +762,14 @@ int dflash_clear_error(dflash_ctx* ctx, void* stream) {
   return DFLASH_OK;
 }
 
+int dflash_stream_read(const void* src, size_t bytes, unsigned* sink, void* stream) {
+  if (!src || !sink) return fail(DFLASH_E_ARG, "src and sink are required");
+  if (bytes % 16 || ((uintptr_t)src & 15)) return fail(DFLASH_E_ARG, "src must be 16-byte aligned and bytes a multiple of 16");
+  hipError_t e = launch_stream_read(src, bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "stream read");
+  return DFLASH_OK;
+}
+
 int dflash_set_timing_events(dflash_ctx* ctx, int kclass, void* const* before, void* const* after, int n) {
   if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
   if (kclass < 0 || kclass >= DFLASH_K_COUNT) return fail(DFLASH_E_ARG, "unknown kernel class %d", kclass);

@@ -161,6 +161,8 @@ hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t
 hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStream_t st);
 
 // Small kernels.
+constexpr int STREAM_READ_BLOCKS = 1024;
+hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* sink, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, float* ssq, int M, int H,
                         int V, unsigned* err, hipStream_t st);

@@ -12,6 +12,31 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
     p[i] = 0u;
 }
 
+// Streaming read of `n16` 16-byte vectors (the HBM read reference of the
+// measurements): 1024 workgroups x 256 threads, eight independent 16-byte
+// loads per thread in flight, an XOR of everything read per workgroup into
+// sink[blockIdx.x] so that no load is dead.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* src, size_t n16, unsigned* sink) {
+  __shared__ unsigned red[4];
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u];
+  }
+  for (; i < n16; i += stride) x ^= src[i];
+  unsigned v = x[0] ^ x[1] ^ x[2] ^ x[3];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v ^= __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 // Block-wide sum over 256 threads.
 DEV float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -152,6 +177,12 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   size_t blocks = (words + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t*)p, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* sink, hipStream_t st) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(STREAM_READ_BLOCKS), dim3(256), 0, st, (const u32x4*)src, bytes / 16,
+                     sink);
   return hipGetLastError();
 }
 

@@ -236,6 +236,14 @@ enum {
 int dflash_set_timing_events(dflash_ctx* ctx, int kclass, void* const* before,
                              void* const* after, int n);
 
+/* Measurement reference, not part of the round: read `bytes` (a multiple of 16)
+ * of device memory at `src` (16-byte aligned) once with a plain streaming-read
+ * kernel of this library, enqueued on `stream`; its duration against `bytes` is
+ * the HBM read rate the round's kernels are compared with beside the vendor
+ * peak. `sink`: device uint32[1024] that receives an XOR of what each
+ * workgroup read (contents meaningless; it keeps the loads live). */
+int dflash_stream_read(const void* src, size_t bytes, unsigned* sink, void* stream);
+
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* dflash_last_error(void);
 
