@@ -85,7 +85,9 @@ def load(path: str = LIB_PATH):
         "dflash_reset": (c_int, [P, P, c_int, c_int, c_int]),
         "dflash_tap_stage": (c_int, [P, P, PP, c_ll, c_int, P, P, c_int]),
         "dflash_draft_block": (c_int, [P, P, P, c_int, P, P, P, c_int]),
+        "dflash_draft_block_n": (c_int, [P, P, P, c_int, c_int, P, P, P, c_int]),
         "dflash_accept": (c_int, [P, P, P, c_int, P, c_int, c_int, P, P, P, P, P]),
+        "dflash_accept_n": (c_int, [P, P, P, c_int, P, c_int, c_int, c_int, P, P, P, P, P]),
         "dflash_check": (c_int, [P, P, ctypes.POINTER(c_uint)]),
         "dflash_clear_error": (c_int, [P, P]),
         "dflash_set_timing_events": (c_int, [P, c_int, PP, PP, c_int]),
@@ -222,6 +224,16 @@ class Drafter:
             self.ctx, _stream(), block_tokens.data_ptr(), R, _ptr(logits), ids.data_ptr(), _ptr(vals), k))
         return ids
 
+    def draft_block_n(self, block_tokens: torch.Tensor, k: int = 1, logits: Optional[torch.Tensor] = None,
+                      ids: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None):
+        """draft_block with the block length of this call = block_tokens.shape[1]."""
+        R, b = block_tokens.shape
+        if ids is None:
+            ids = torch.empty((R, max(b - 1, 1), k), dtype=torch.int32, device=self.device)
+        _check("dflash_draft_block_n", self.lib.dflash_draft_block_n(
+            self.ctx, _stream(), block_tokens.data_ptr(), R, int(b), _ptr(logits), ids.data_ptr(), _ptr(vals), k))
+        return ids
+
     def accept(self, draft_ids: torch.Tensor, draft_stride: int, verify_ids: torch.Tensor, eos_id: int = -1,
                budget: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None):
         R = verify_ids.shape[0]
@@ -235,6 +247,20 @@ class Drafter:
             self.ctx, _stream(), _ptr(draft_ids), int(draft_stride), verify_ids.data_ptr(), R, int(eos_id),
             _ptr(budget), out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
             _ptr(out.get("next_tokens"))))
+        return out
+
+    def accept_n(self, draft_ids: Optional[torch.Tensor], draft_stride: int, verify_ids: torch.Tensor,
+                 eos_id: int = -1, budget: Optional[torch.Tensor] = None):
+        """accept for a round of block length verify_ids.shape[1]."""
+        R, b = verify_ids.shape
+        out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
+               "emitted": torch.empty((R, b), dtype=torch.int32, device=self.device),
+               "n_emit": torch.empty(R, dtype=torch.int32, device=self.device),
+               "next_tokens": torch.empty((R, b), dtype=torch.int32, device=self.device)}
+        _check("dflash_accept_n", self.lib.dflash_accept_n(
+            self.ctx, _stream(), _ptr(draft_ids), int(draft_stride), verify_ids.data_ptr(), R, int(b), int(eos_id),
+            _ptr(budget), out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
+            out["next_tokens"].data_ptr()))
         return out
 
     def check(self) -> int:

@@ -537,16 +537,24 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
 int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, float* logits,
                        int* topk_ids, float* topk_vals, int k) {
   if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  return dflash_draft_block_n(ctx, stream, block_tokens, n_req, ctx->cfg.block, logits, topk_ids, topk_vals, k);
+}
+
+int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, int block_len,
+                         float* logits, int* topk_ids, float* topk_vals, int k) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
   if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
   const dflash_config& g = ctx->cfg;
   if (!block_tokens || !topk_ids) return fail(DFLASH_E_ARG, "block_tokens and topk_ids are required");
   if (n_req < 1 || n_req > g.max_requests)
     return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (block_len < 1 || block_len > g.block)
+    return fail(DFLASH_E_SHAPE, "block_len %d outside [1, %d]", block_len, g.block);
   if (k != 1 && k != 16) return fail(DFLASH_E_ARG, "k must be 1 or 16 (got %d)", k);
   if (k > g.vocab) return fail(DFLASH_E_ARG, "k exceeds vocab");
-  if (g.block == 1) return DFLASH_OK;   // no mask rows: nothing to draft
+  if (block_len == 1) return DFLASH_OK;   // no mask rows: nothing to draft
   hipStream_t st = (hipStream_t)stream;
-  const int H = g.hidden, hd = g.head_dim, B = g.block;
+  const int H = g.hidden, hd = g.head_dim, B = block_len;
   const int M = n_req * B;
   const int qw = g.n_q_heads * hd;
   float* h = at<float>(ctx->ws, ctx->wl.h);
@@ -555,7 +563,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
   uint16_t* o = at<uint16_t>(ctx->ws, ctx->wl.o);
   uint16_t* act = at<uint16_t>(ctx->ws, ctx->wl.act);
   unsigned* err = at<unsigned>(ctx->state, ctx->sl.error);
-  const int ssq_ld = g.max_requests * B;
+  const int ssq_ld = g.max_requests * g.block;   // row pitch of the ssq buffer
   const int h_blocks = H / GC_DEFAULT;
   const int wf = wf_of(g);
   // every RMSNorm is applied by the GEMM that consumes it (X_NORM), from h and
@@ -699,6 +707,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
     a.M = M;
     a.N = g.vocab;
     a.K = H;
+    a.B = B;   // this call's block length
     a.topk = k;
     LmPlan p = plan_lmhead(M, B, g.vocab, H, ctx->n_cu);
     if (p.XL != 1) {
@@ -727,15 +736,25 @@ int dflash_accept(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft
                   int n_req, int eos_id, const int* budget, int* accept_len, int* emitted, int* n_emit,
                   int* next_tokens) {
   if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  return dflash_accept_n(ctx, stream, draft_ids, draft_stride, verify_ids, n_req, ctx->cfg.block, eos_id, budget,
+                         accept_len, emitted, n_emit, next_tokens);
+}
+
+int dflash_accept_n(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride, const int* verify_ids,
+                    int n_req, int block_len, int eos_id, const int* budget, int* accept_len, int* emitted,
+                    int* n_emit, int* next_tokens) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
   if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
   const dflash_config& g = ctx->cfg;
-  if ((!draft_ids && g.block > 1) || !verify_ids || !accept_len || !emitted || !n_emit)
+  if (block_len < 1 || block_len > g.block)
+    return fail(DFLASH_E_SHAPE, "block_len %d outside [1, %d]", block_len, g.block);
+  if ((!draft_ids && block_len > 1) || !verify_ids || !accept_len || !emitted || !n_emit)
     return fail(DFLASH_E_ARG, "draft_ids, verify_ids, accept_len, emitted and n_emit are required");
   if (n_req < 1 || n_req > g.max_requests)
     return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
   if (draft_stride < 1) return fail(DFLASH_E_ARG, "draft_stride must be >= 1");
-  hipError_t e = launch_accept(draft_ids, draft_stride, verify_ids, n_req, g.block, eos_id, budget, g.mask_id,
-                               accept_len, emitted, n_emit, next_tokens, at<int>(ctx->state, ctx->sl.pos),
+  hipError_t e = launch_accept(draft_ids, draft_stride, verify_ids, n_req, block_len, g.block, eos_id, budget,
+                               g.mask_id, accept_len, emitted, n_emit, next_tokens, at<int>(ctx->state, ctx->sl.pos),
                                at<unsigned long long>(ctx->state, ctx->sl.stats), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "accept");
   return DFLASH_OK;

@@ -171,7 +171,7 @@ hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* a, int
 hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hipStream_t st);
 hipError_t launch_topk_final(const float* list_v, const int* list_i, int n_lists, int rows, int k, int* ids,
                              float* vals, hipStream_t st);
-hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B,
+hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B, int stats_b,
                          int eos, const int* budget, int mask_id, int* accept_len,
                          int* emitted, int* n_emit, int* next_tokens, int* pos,
                          unsigned long long* stats, hipStream_t st);

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* in_v, cons
 // lanes j < B-1 whose draft differs from the verify id gives the accept length
 // as the index of its lowest set bit.
 __global__ __launch_bounds__(64) void accept_kernel(const int* draft, int draft_stride,
-                                                    const int* verify, int B, int eos,
+                                                    const int* verify, int B, int stats_b, int eos,
                                                     const int* budget, int mask_id,
                                                     int* accept_len, int* emitted, int* n_emit,
                                                     int* next_tokens, int* pos,
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64) void accept_kernel(const int* draft, int draft_
     pos[r] += n;
     if (stats) {
       atomicAdd(&stats[0], 1ull);
-      atomicAdd(&stats[B + 1], (unsigned long long)n);
+      atomicAdd(&stats[stats_b + 1], (unsigned long long)n);   // slots laid out for the configured block
     }
   }
   if (stats && j < acc) atomicAdd(&stats[1 + j], 1ull);
@@ -218,10 +218,10 @@ hipError_t launch_topk_final(const float* list_v, const int* list_i, int n_lists
   return hipGetLastError();
 }
 
-hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B, int eos,
+hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B, int stats_b, int eos,
                          const int* budget, int mask_id, int* accept_len, int* emitted, int* n_emit,
                          int* next_tokens, int* pos, unsigned long long* stats, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(R), dim3(64), 0, st, draft, draft_stride, verify, B, eos,
+  hipLaunchKernelGGL(accept_kernel, dim3(R), dim3(64), 0, st, draft, draft_stride, verify, B, stats_b, eos,
                      budget, mask_id, accept_len, emitted, n_emit, next_tokens, pos, stats);
   return hipGetLastError();
 }

@@ -204,6 +204,18 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
                        float* logits, int* topk_ids, float* topk_vals, int k);
 
 /*
+ * dflash_draft_block with a per-call block length b = block_len in [1, cfg.block]
+ * in place of cfg.block: every shape above uses b (block_tokens [n_req, b], b-1
+ * drafted rows). For the shrunk last rounds of a generation: the block length
+ * of a round is min(block size, tokens still to generate, sequence capacity
+ * left) ("[RFC] DFlash", ExecuTorch PR #20840: the review item on a dynamic
+ * block length and the author's reply). b = 1 drafts nothing (a target-only
+ * step).
+ */
+int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req,
+                         int block_len, float* logits, int* topk_ids, float* topk_vals, int k);
+
+/*
  * First-mismatch accept for requests r < n_req.
  *   draft_ids:   element (r, j) at draft_ids[(r*(B-1) + j)*draft_stride], j < B-1
  *                (pass topk_ids with draft_stride = k).
@@ -217,6 +229,17 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, i
 int dflash_accept(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride,
                   const int* verify_ids, int n_req, int eos_id, const int* budget,
                   int* accept_len, int* emitted, int* n_emit, int* next_tokens);
+
+/*
+ * dflash_accept for a round drafted with block length b = block_len in
+ * [1, cfg.block] (dflash_draft_block_n): draft_ids hold b-1 drafts per request,
+ * verify_ids [n_req, b], emitted and next_tokens [n_req, b]. b = 1 emits the
+ * target's token verify_ids[r][0]. The accept-profile counters keep the layout
+ * of the configured block.
+ */
+int dflash_accept_n(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride,
+                    const int* verify_ids, int n_req, int block_len, int eos_id, const int* budget,
+                    int* accept_len, int* emitted, int* n_emit, int* next_tokens);
 
 /* Synchronize `stream`, read the device error word into *word (host, may be NULL);
  * returns DFLASH_E_DEVICE if it is non-zero. */

@@ -347,6 +347,20 @@ def next_block(emitted: List[int], block: int, mask_id: int) -> List[int]:
     return [int(emitted[-1])] + [int(mask_id)] * (block - 1)
 
 
+def block_len(block_size: int, max_new: int, n_generated: int, max_seq: int, position: int) -> int:
+    """Block length of the next round: the configured block, shrunk so that a
+    round can neither emit past the generation budget nor run past the sequence
+    capacity ("[RFC] DFlash": the review item asking for a dynamic block length
+    and the author's reply, which bounds it by 1 <= block_len <= block size).
+
+      block_len = min(block_size, max_new - n_generated, max_seq - position)
+
+    A value below 1 means no round is left; 1 is a target-only step (no draft
+    rows: the accept emits the target's token).
+    """
+    return min(int(block_size), int(max_new) - int(n_generated), int(max_seq) - int(position))
+
+
 def tokens_per_round(profile: Sequence[float]) -> float:
     """Mean tokens per round from a per-draft-position accept profile.
 

@@ -111,25 +111,33 @@ DraftFn = Callable[[List[int], int, int, List[np.ndarray]], Sequence[int]]
 
 
 def speculative(target: TinyTarget, draft_fn: DraftFn, prompt: Sequence[int], n_new: int,
-                block: int, window: int, mask_id: int, eos_id: int = -1) -> Dict[str, object]:
+                block: int, window: int, mask_id: int, eos_id: int = -1, dynamic: bool = False,
+                max_seq: Optional[int] = None) -> Dict[str, object]:
     """DFlash draft/verify loop ([P3] "Phase 3": draft a block, verify it with the
     target, accept to the first mismatch plus the target's token, roll the cache
     back; [P1]: verify stages the tap rows the drafter reads next).
 
     ``draft_fn(block_tokens, pos, valid_from, taps_by_position)`` returns B-1
     draft ids; taps_by_position[t] holds the committed tap rows [0, pos) of tapped
-    layer t. Returns the emitted tokens and per-round accept lengths.
+    layer t. With ``dynamic`` each round's block length is ``D.block_len`` of the
+    remaining budget and of the sequence capacity ``max_seq`` (positions fed to
+    the target stay below it); a length of 1 is a target-only step. Returns the
+    emitted tokens, per-round accept lengths and block lengths.
     """
     target.reset()
     ids, taps = target.feed(prompt, 0)
     committed = [t.copy() for t in taps]
     pos = len(prompt)
     out = [ids[-1]]
-    accepts = []
+    accepts, blocks = [], []
+    cap = max_seq if max_seq is not None else pos + n_new + block
     while len(out) < n_new and out[-1] != eos_id:
-        blk = D.next_block(out, block, mask_id)
-        draft = [int(t) for t in draft_fn(blk, pos, 0, committed)]
-        assert len(draft) == block - 1
+        b = D.block_len(block, n_new, len(out), cap, pos) if dynamic else block
+        if b < 1:
+            break
+        blk = D.next_block(out, b, mask_id)
+        draft = [int(t) for t in draft_fn(blk, pos, 0, committed)] if b > 1 else []
+        assert len(draft) == b - 1
         verify, vtaps = target.feed([blk[0]] + draft, pos)
         res = D.accept(draft, verify, eos_id=eos_id, budget=n_new - len(out))
         n = res["n_emit"]
@@ -138,7 +146,8 @@ def speculative(target: TinyTarget, draft_fn: DraftFn, prompt: Sequence[int], n_
         pos += n
         out.extend(res["emitted"])
         accepts.append(res["acc"])
-    return {"tokens": out, "accepts": accepts}
+        blocks.append(b)
+    return {"tokens": out, "accepts": accepts, "blocks": blocks}
 
 
 def oracle_draft_fn(cfg, W, mode: str = "mirror") -> DraftFn:

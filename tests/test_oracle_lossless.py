@@ -94,3 +94,35 @@ def test_block_one_is_plain_greedy(setup):
     ref = T.greedy(tgt, prompt, 12)
     res = T.speculative(tgt, lambda *a: [], prompt, 12, 1, cfg.window, cfg.mask_id)
     assert res["tokens"] == ref and all(a == 0 for a in res["accepts"])
+
+
+def test_block_len_cases():
+    # the configured block while budget and capacity are large
+    assert D.block_len(8, 100, 10, 1000, 50) == 8
+    # the budget binds: 3 tokens left -> a block of 3 (2 drafts + the target's token)
+    assert D.block_len(8, 100, 97, 1000, 50) == 3
+    # the sequence capacity binds
+    assert D.block_len(8, 100, 10, 55, 50) == 5
+    # one token left: a target-only step
+    assert D.block_len(16, 24, 23, 1000, 7) == 1
+    # nothing left
+    assert D.block_len(8, 24, 24, 1000, 7) <= 0 and D.block_len(8, 100, 10, 50, 50) <= 0
+
+
+@pytest.mark.parametrize("max_seq_extra", [None, 19])
+def test_lossless_with_dynamic_block_len(setup, max_seq_extra):
+    """Rounds shrink at the end of the budget (and of the sequence capacity):
+    the output is still the target's greedy decoding, ends exactly at the budget
+    (or where the capacity stops it), and no round runs past either bound."""
+    cfg, Wd, tgt = setup
+    prompt = [5, 17, 300, 4000, 12, 99]
+    n_new = 23
+    max_seq = None if max_seq_extra is None else len(prompt) + max_seq_extra
+    res = T.speculative(tgt, T.oracle_draft_fn(cfg, Wd), prompt, n_new, cfg.block, cfg.window, cfg.mask_id,
+                        dynamic=True, max_seq=max_seq)
+    n_expect = n_new if max_seq is None else min(n_new, max_seq - len(prompt) + 1)
+    assert res["tokens"] == T.greedy(tgt, prompt, n_expect)
+    assert all(1 <= b <= cfg.block for b in res["blocks"])
+    fed = len(prompt) + len(res["tokens"]) - 1   # positions fed to the target: all but the last token
+    assert max_seq is None or fed <= max_seq
+    assert res["blocks"][-1] < cfg.block    # the last round was shrunk
