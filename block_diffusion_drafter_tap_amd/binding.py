@@ -92,6 +92,10 @@ def load(path: str = LIB_PATH):
         "dflash_clear_error": (c_int, [P, P]),
         "dflash_set_timing_events": (c_int, [P, c_int, PP, PP, c_int]),
         "dflash_stream_read": (c_int, [P, c_size_t, P, P]),
+        "dflash_create_target": (c_int, [ctypes.POINTER(dflash_config), ctypes.POINTER(dflash_weights),
+                                         ctypes.POINTER(P)]),
+        "dflash_verify_block": (c_int, [P, P, P, c_int, c_int, P, c_int, PP, c_ll, P, P]),
+        "dflash_advance": (c_int, [P, P, P, c_int]),
         "dflash_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -158,8 +162,9 @@ def state_layout(cfg: DFlashConfig) -> Dict[str, int]:
 class Drafter:
     """One library handle with its own state and workspace (torch tensors on ``device``)."""
 
-    def __init__(self, cfg: DFlashConfig, weights: Dict[str, object], device="cuda"):
+    def __init__(self, cfg: DFlashConfig, weights: Dict[str, object], device="cuda", target: bool = False):
         self.lib = load()
+        self.target = target
         self.cfg = cfg
         self.device = torch.device(device)
         self._c_cfg = c_config(cfg)
@@ -183,7 +188,9 @@ class Drafter:
         self._weights = weights
         self._c_w = w
         ctx = c_void_p()
-        _check("dflash_create", self.lib.dflash_create(ctypes.byref(self._c_cfg), ctypes.byref(w), ctypes.byref(ctx)))
+        create = self.lib.dflash_create_target if target else self.lib.dflash_create
+        _check("dflash_create_target" if target else "dflash_create",
+               create(ctypes.byref(self._c_cfg), ctypes.byref(w), ctypes.byref(ctx)))
         self.ctx = ctx
         self.layout = state_layout(cfg)
         self.state = torch.empty(self.layout["total"], dtype=torch.uint8, device=self.device)
@@ -262,6 +269,24 @@ class Drafter:
             _ptr(budget), out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
             out["next_tokens"].data_ptr()))
         return out
+
+    def verify_block(self, block_tokens: torch.Tensor, tap_layers: Sequence[int] = (),
+                     tap_out: Sequence[torch.Tensor] = (), logits: Optional[torch.Tensor] = None):
+        """Verify pass of a target handle: argmax ids [R, b]; the residual rows after
+        the tapped layers are written into tap_out (fp32 [R*b, >= hidden])."""
+        R, b = block_tokens.shape
+        ids = torch.empty((R, b), dtype=torch.int32, device=self.device)
+        n = len(tap_layers)
+        layers = (ctypes.c_int * max(n, 1))(*tap_layers)
+        outs = (c_void_p * max(n, 1))(*[t.data_ptr() for t in tap_out])
+        ld = tap_out[0].stride(0) if n else 0
+        _check("dflash_verify_block", self.lib.dflash_verify_block(
+            self.ctx, _stream(), block_tokens.data_ptr(), R, int(b), ctypes.cast(layers, c_void_p) if n else None, n,
+            ctypes.cast(outs, PP) if n else None, int(ld), _ptr(logits), ids.data_ptr()))
+        return ids
+
+    def advance(self, n_emit: torch.Tensor):
+        _check("dflash_advance", self.lib.dflash_advance(self.ctx, _stream(), n_emit.data_ptr(), n_emit.numel()))
 
     def check(self) -> int:
         word = c_uint(0)

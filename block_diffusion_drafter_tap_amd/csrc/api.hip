@@ -115,7 +115,7 @@ WsLayout ws_layout(const dflash_config& c) {
   const size_t slots = (size_t)attn_slots(c.n_q_heads, c.n_kv_heads, c.block);
   const size_t lrg = (size_t)c.max_requests * c.n_kv_heads;
   const size_t nch = (size_t)attn_nchunks(c);
-  const size_t out_rows = (size_t)c.max_requests * (c.block > 1 ? c.block - 1 : 1);
+  const size_t out_rows = Mmax;   // LM-head output rows: the mask rows of a draft, every row of a verify pass
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   L.h = take(Mmax * c.hidden * 4);
@@ -208,6 +208,7 @@ struct dflash_ctx {
   char* ws = nullptr;
   dflash_state_layout sl;
   WsLayout wl;
+  bool target = false;   // a causal target (dflash_create_target): verify passes only
   int n_cu = 256;   // compute units of the bound device (read at bind)
   Timing timing[DFLASH_K_COUNT];
   // INT4 scales of layer l's matrix (NULL for bf16 weights)
@@ -321,6 +322,10 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
   return DFLASH_OK;
 }
 
+int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int n_req, int block_len, int causal,
+                  const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld, int first_row,
+                  float* logits, int* topk_ids, float* topk_vals, int k);
+
 }  // namespace
 
 extern "C" {
@@ -345,7 +350,7 @@ int dflash_get_state_layout(const dflash_config* cfg, dflash_state_layout* out) 
   return DFLASH_OK;
 }
 
-int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out) {
+static int create_impl(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out, bool target) {
   g_err[0] = 0;
   if (!out) return fail(DFLASH_E_ARG, "out is NULL");
   *out = nullptr;
@@ -354,10 +359,11 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_ctx*
   if (!w) return fail(DFLASH_E_ARG, "weights is NULL");
   const dflash_config& c = *cfg;
   const bool q4 = c.wfmt == DFLASH_W_INT4_G64;
-  if (!w->embed || !w->lm_head || !w->fc || !w->final_norm)
-    return fail(DFLASH_E_ARG, "embed, lm_head, fc and final_norm are required");
-  if (c.ctx_norm && !w->ctx_norm) return fail(DFLASH_E_ARG, "ctx_norm gain required when cfg.ctx_norm = 1");
-  if (q4 && !w->fc_scales) return fail(DFLASH_E_ARG, "fc_scales required for INT4 weights");
+  if (!w->embed || !w->lm_head || (!target && !w->fc) || !w->final_norm)
+    return fail(DFLASH_E_ARG, target ? "embed, lm_head and final_norm are required"
+                                     : "embed, lm_head, fc and final_norm are required");
+  if (!target && c.ctx_norm && !w->ctx_norm) return fail(DFLASH_E_ARG, "ctx_norm gain required when cfg.ctx_norm = 1");
+  if (!target && q4 && !w->fc_scales) return fail(DFLASH_E_ARG, "fc_scales required for INT4 weights");
   const void* const* arrays[] = {w->wqkv, w->wo, w->wgu, w->wd, w->ln_in, w->ln_post, w->q_norm, w->k_norm};
   const char* names[] = {"wqkv", "wo", "wgu", "wd", "ln_in", "ln_post", "q_norm", "k_norm"};
   for (int i = 0; i < 8; ++i) {
@@ -399,8 +405,17 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_ctx*
   }
   x->sl = st_layout(c);
   x->wl = ws_layout(c);
+  x->target = target;
   *out = x;
   return DFLASH_OK;
+}
+
+int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out) {
+  return create_impl(cfg, w, out, false);
+}
+
+int dflash_create_target(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out) {
+  return create_impl(cfg, w, out, true);
 }
 
 void dflash_destroy(dflash_ctx* ctx) { delete ctx; }
@@ -544,6 +559,7 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
                          float* logits, int* topk_ids, float* topk_vals, int k) {
   if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
   if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (ctx->target) return fail(DFLASH_E_STATE, "a target handle runs verify passes, not drafts");
   const dflash_config& g = ctx->cfg;
   if (!block_tokens || !topk_ids) return fail(DFLASH_E_ARG, "block_tokens and topk_ids are required");
   if (n_req < 1 || n_req > g.max_requests)
@@ -553,7 +569,57 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
   if (k != 1 && k != 16) return fail(DFLASH_E_ARG, "k must be 1 or 16 (got %d)", k);
   if (k > g.vocab) return fail(DFLASH_E_ARG, "k exceeds vocab");
   if (block_len == 1) return DFLASH_OK;   // no mask rows: nothing to draft
-  hipStream_t st = (hipStream_t)stream;
+  return forward_block(ctx, (hipStream_t)stream, block_tokens, n_req, block_len, 0, nullptr, 0, nullptr, 0, 1, logits,
+                       topk_ids, topk_vals, k);
+}
+
+int dflash_verify_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, int block_len,
+                        const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld, float* logits,
+                        int* ids) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (!ctx->target) return fail(DFLASH_E_STATE, "verify passes need a target handle (dflash_create_target)");
+  const dflash_config& g = ctx->cfg;
+  if (!block_tokens || !ids) return fail(DFLASH_E_ARG, "block_tokens and ids are required");
+  if (n_req < 1 || n_req > g.max_requests)
+    return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (block_len < 1 || block_len > g.block)
+    return fail(DFLASH_E_SHAPE, "block_len %d outside [1, %d]", block_len, g.block);
+  if (n_tap_out < 0 || n_tap_out > MAX_TAPS || (n_tap_out > 0 && (!tap_layers || !tap_out)))
+    return fail(DFLASH_E_ARG, "n_tap_out must be in [0, %d] with tap_layers and tap_out given", MAX_TAPS);
+  for (int t = 0; t < n_tap_out; ++t) {
+    if (tap_layers[t] < 0 || tap_layers[t] >= g.n_layers)
+      return fail(DFLASH_E_ARG, "tap_layers[%d] = %d outside [0, %d)", t, tap_layers[t], g.n_layers);
+    if (!tap_out[t] || ((uintptr_t)tap_out[t] & 15)) return fail(DFLASH_E_ARG, "tap_out[%d] must be 16-byte aligned", t);
+  }
+  if (n_tap_out > 0 && (tap_ld < g.hidden || tap_ld % 4)) return fail(DFLASH_E_ARG, "tap_ld must be >= hidden, % 4 == 0");
+  return forward_block(ctx, (hipStream_t)stream, block_tokens, n_req, block_len, 1, tap_layers, n_tap_out, tap_out,
+                       tap_ld, 0, logits, ids, nullptr, 1);
+}
+
+int dflash_advance(dflash_ctx* ctx, void* stream, const int* n_emit, int n_req) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (!n_emit) return fail(DFLASH_E_ARG, "n_emit is required");
+  if (n_req < 1 || n_req > ctx->cfg.max_requests)
+    return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, ctx->cfg.max_requests);
+  hipError_t e = launch_advance(at<int>(ctx->state, ctx->sl.pos), n_emit, n_req, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "advance");
+  return DFLASH_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// One block forward of every request r < n_req at positions pos[r] + i: the
+// drafter's masked block (bidirectional, the mask rows' top-k) or a causal
+// target's verify pass (block row i sees rows <= i, argmax of every row, the
+// residual rows after the tapped layers copied out).
+int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int n_req, int block_len, int causal,
+                  const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld, int first_row,
+                  float* logits, int* topk_ids, float* topk_vals, int k) {
+  const dflash_config& g = ctx->cfg;
   const int H = g.hidden, hd = g.head_dim, B = block_len;
   const int M = n_req * B;
   const int qw = g.n_q_heads * hd;
@@ -628,6 +694,7 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
       t.part_o = at<float>(ctx->ws, ctx->wl.attn_o);
       t.part_ml = at<float>(ctx->ws, ctx->wl.attn_ml);
       t.err = err;
+      t.causal = causal;
       Timed tm(ctx, DFLASH_K_ATTN, st);
       e = launch_attention(t, n_req, st);
       if (e != hipSuccess) return hip_fail(e, "attention");
@@ -699,6 +766,11 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
       }
       if (e != hipSuccess) return hip_fail(e, "down proj");
     }
+    for (int t = 0; t < n_tap_out; ++t)   // the residual after this layer, for the drafter's taps
+      if (tap_layers[t] == l) {
+        e = launch_copy_rows(h, M, H, tap_out[t], tap_ld, st);
+        if (e != hipSuccess) return hip_fail(e, "tap copy");
+      }
   }
   {  // shared LM head: mask-row logits, then per-row top-k
     GemmArgs a = base_args(ctx);
@@ -708,6 +780,7 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
     a.N = g.vocab;
     a.K = H;
     a.B = B;   // this call's block length
+    a.lm_first_row = first_row;
     a.topk = k;
     LmPlan p = plan_lmhead(M, B, g.vocab, H, ctx->n_cu);
     if (p.XL != 1) {
@@ -731,6 +804,10 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
   }
   return DFLASH_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int dflash_accept(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride, const int* verify_ids,
                   int n_req, int eos_id, const int* budget, int* accept_len, int* emitted, int* n_emit,

@@ -1,6 +1,7 @@
 // Block attention for gfx950: every block query attends to the context window
 // [lo, pos) and to all B block rows [pos, pos+B), with no mask inside (the block
-// is bidirectional). Keys and values of both live in the per-request ring (the
+// is bidirectional; a causal target's verify pass sets `causal`, and block row i
+// then sees block rows j <= i only). Keys and values of both live in the per-request ring (the
 // block's own K/V were written to slots pos..pos+B-1 by the QKV epilogue), so a
 // query sees one contiguous position range [lo, pos+B).
 //
@@ -38,7 +39,7 @@
 namespace {
 
 struct Range {
-  int lo, hi, base, n_ch;
+  int lo, hi, base, n_ch, pos;
 };
 
 // [lo, hi): keys a block query sees; chunks of a.kc keys start at base = lo
@@ -54,6 +55,7 @@ DEV Range key_range(const AttnArgs& a, int r, bool report) {
   lo = lo > vf ? lo : vf;
   lo = lo > 0 ? lo : 0;
   Range g;
+  g.pos = pos;
   g.lo = lo;
   g.hi = pos + a.B;
   g.base = lo & ~31;
@@ -132,9 +134,12 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
   // phase 1: scores of sub-tile `wave`; lane holds, for query slot qt*16 + lr,
   // keys k0 + 8*lg + e (e = 4*kt + i)
   float p[QT][8];
-  const bool interior = k0 >= kr.lo && k0 + 32 <= kr.hi;
+  // no per-key mask needed: the sub-tile lies inside the window (and, for a
+  // causal pass, before the block)
+  const bool interior = k0 >= kr.lo && k0 + 32 <= (a.causal ? kr.pos : kr.hi);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
+    const int iq = (s0 + qt * 16 + lr) % a.B;   // block row of this lane's query slot
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 8 * lg + 4 * kt + i;
-        const bool ok = interior || (key >= kr.lo && key < kr.hi);
+        const bool ok = interior || (key >= kr.lo && key < kr.hi && (!a.causal || key <= kr.pos + iq));
         p[qt][4 * kt + i] = ok ? acc[i] * a.scale_log2 : -INFINITY;
       }
     }

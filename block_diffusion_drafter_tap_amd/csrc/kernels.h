@@ -63,8 +63,9 @@ struct GemmArgs {
   const int* pos_of_row;  // NULL -> pos[req] + row % rows_per_req
   int rows_per_req;
   unsigned* err;
-  // LM head: rows m = r*B + i; mask rows i >= 1 produce logits
-  int B, topk;
+  // LM head: rows m = r*B + i; rows i >= lm_first_row produce logits (1: the
+  // mask rows of a draft; 0: every row of a verify pass)
+  int B, topk, lm_first_row;
 };
 
 struct GemmPlan {
@@ -111,6 +112,7 @@ struct AttnArgs {
   const int* pos;
   const int* valid_from;
   int B, W, C, nq, nkv, hd, kc, n_chunks;
+  int causal;              // 1: block query i sees block keys j <= i only (a target verify pass)
   int R;                   // requests of this launch (set by launch_attention)
   int hs;                  // query-slot parts per (chunk, kv head) (set by launch_attention)
   float scale_log2;        // log2(e) / sqrt(hd)
@@ -159,6 +161,11 @@ hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t
 // Context K/V projection (N = 2 * nkv * hd, 128-column tiles of whole heads)
 // straight into the rings: GemmArgs head fields as for the head finish.
 hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStream_t st);
+
+// Verify pass of a causal target: copy the residual rows h [M][H] of a tapped
+// layer to a tap buffer with row pitch ld; add n_emit to the positions.
+hipError_t launch_copy_rows(const float* h, int M, int H, float* dst, long long ld, hipStream_t st);
+hipError_t launch_advance(int* pos, const int* n_emit, int n_req, hipStream_t st);
 
 // Small kernels.
 constexpr int STREAM_READ_BLOCKS = 1024;

@@ -206,9 +206,9 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + 4 * lg + i;
-        const int bi = m % a.B;
-        const bool row_ok = m < a.M && bi != 0;
-        const size_t orow = (size_t)((m / a.B) * (a.B - 1) + bi - 1);
+        const int bi = m % a.B, r0 = a.lm_first_row;
+        const bool row_ok = m < a.M && bi >= r0;
+        const size_t orow = (size_t)((m / a.B) * (a.B - r0) + bi - r0);
         if (!transposed && row_ok && n < a.N) logits[orow * a.N + n] = acc[mt][i];
         float v = n < a.N ? acc[mt][i] : -INFINITY;
         v = fmaxf(v, __shfl_xor(v, 1, 64));
@@ -347,9 +347,11 @@ DEV unsigned wave_kth_largest(const unsigned (&key)[4], const bool (&valid)[4], 
 // sorted by (value desc, index asc). The row's group maxima are staged in
 // dynamic LDS.
 // logits element (row r, column n): caller layout logits[r * N + n], or the
-// transposed scratch logits[n * cs + srow], srow = req*B + i for r = req*(B-1) + i - 1.
+// transposed scratch logits[n * cs + srow], srow = req*B + i for r = req*(B-r0) + i - r0
+// (output rows are the block rows i >= r0: the mask rows for drafts, r0 = 1;
+// every row for a verify pass, r0 = 0).
 template <int PER>
-__global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ logits, long long cs, int B,
+__global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ logits, long long cs, int B, int r0,
                                                         int transposed, const float* __restrict__ gmax, int N, int k,
                                                         int* ids, float* vals) {
   extern __shared__ __attribute__((aligned(16))) float s_g[];   // [ng]
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
   }
   // stage B: the logits of the candidate groups, ranked by counting
   const int nc = 16 * n_groups_c;
-  const size_t srow = transposed ? (size_t)(row / (B - 1) * B + row % (B - 1) + 1) : (size_t)row;
+  const size_t srow = transposed ? (size_t)(row / (B - r0) * B + row % (B - r0) + r0) : (size_t)row;
   for (int e = t; e < nc; e += 256) {
     const int n = 16 * gsel[e / 16] + (e % 16);
     const int nn = min(n, N - 1);
@@ -507,7 +509,7 @@ hipError_t launch_lm_norm_rows(const GemmArgs& a, uint16_t* z, hipStream_t st) {
 
 hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, int transposed, float* gmax,
                             hipStream_t st) {
-  if (a.B < 2) return hipErrorInvalidValue;
+  if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
   hipError_t e;
 #define LM(MT)                                                                              \
   e = p.XL == 1   ? launch_lm<MT, 1>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) \
@@ -525,13 +527,14 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
 
 hipError_t launch_lm_topk(const GemmArgs& a, const LmPlan& p, const float* logits, int transposed,
                           const float* gmax, int* ids, float* vals, hipStream_t st) {
-  if (a.topk < 1 || a.topk > 16 || a.B < 2) return hipErrorInvalidValue;
-  const int rows = (a.M / a.B) * (a.B - 1);
+  const int r0 = a.lm_first_row;
+  if (a.topk < 1 || a.topk > 16 || r0 < 0 || r0 > 1 || a.B < r0 + 1) return hipErrorInvalidValue;
+  const int rows = (a.M / a.B) * (a.B - r0);
   const int ng = (a.N + 15) / 16;
   if (ng > 256 * 64) return hipErrorInvalidValue;   // at most 64 groups per thread
   const long long cs = 16ll * p.MT;   // transposed scratch: [N][16*MT]
   const size_t lds = (size_t)ng * sizeof(float);
-#define TK(PER) hipLaunchKernelGGL((topk_rows_kernel<PER>), dim3(rows), dim3(256), lds, st, logits, cs, a.B, transposed, gmax, a.N, a.topk, ids, vals)
+#define TK(PER) hipLaunchKernelGGL((topk_rows_kernel<PER>), dim3(rows), dim3(256), lds, st, logits, cs, a.B, r0, transposed, gmax, a.N, a.topk, ids, vals)
   if (ng <= 256 * 8) TK(8);
   else if (ng <= 256 * 16) TK(16);
   else if (ng <= 256 * 40) TK(40);

@@ -186,6 +186,28 @@ hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* sink, hip
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void copy_rows_kernel(const float* h, int H, float* dst, long long ld) {
+  const int m = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c < H) *(f32x4*)(dst + (size_t)m * ld + c) = *(const f32x4*)(h + (size_t)m * H + c);
+}
+
+__global__ void advance_kernel(int* pos, const int* n_emit, int n_req) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < n_req) pos[r] += n_emit[r];
+}
+
+hipError_t launch_copy_rows(const float* h, int M, int H, float* dst, long long ld, hipStream_t st) {
+  if (H % 4 || ld % 4 || M < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3((H / 4 + 255) / 256, M), dim3(256), 0, st, h, H, dst, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance(int* pos, const int* n_emit, int n_req, hipStream_t st) {
+  hipLaunchKernelGGL(advance_kernel, dim3((n_req + 63) / 64), dim3(64), 0, st, pos, n_emit, n_req);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, float* ssq, int M, int H, int V,
                         unsigned* err, hipStream_t st) {
   hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, embed, h, ssq, H, V, err);

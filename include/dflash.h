@@ -241,6 +241,45 @@ int dflash_accept_n(dflash_ctx* ctx, void* stream, const int* draft_ids, int dra
                     const int* verify_ids, int n_req, int block_len, int eos_id, const int* budget,
                     int* accept_len, int* emitted, int* n_emit, int* next_tokens);
 
+/*
+ * Causal target (the verify side of the loop). A target handle is created from
+ * the same config and weight structs (fc, fc_scales and ctx_norm are not used):
+ * a Qwen3-shaped causal decoder whose own per-layer K/V live in the ring of its
+ * state, at slot position mod ring_capacity, over the window of the config.
+ * The verify pass runs the B rows of the round (the last emitted token and the
+ * drafts) through every layer with block row i attending to the window and to
+ * block rows j <= i, writes the block's K/V to ring slots [pos, pos+B), returns
+ * the argmax (lowest id on ties) of every row, and copies the residual rows
+ * after the tapped layers, which are the drafter's taps ("[RFC] DFlash",
+ * ExecuTorch PR #20840, "Key Implementation Details": the target returns its
+ * selected layers' hidden rows with the verify logits; "feat: DFlash2", Mference
+ * PR #22, the commit on verify staging tap rows for the drafter). Rows the
+ * accept does not commit are overwritten by the next pass (rollback is moving
+ * pos: dflash_advance adds the accept's n_emit, dflash_reset restarts).
+ */
+int dflash_create_target(const dflash_config* cfg, const dflash_weights* w, dflash_ctx** out);
+
+/*
+ * Verify pass of a target handle for requests r < n_req at positions pos[r] + i,
+ * i < b = block_len in [1, cfg.block].
+ *   block_tokens: int32 [n_req, b].
+ *   tap_layers:   NULL or HOST int[n_tap_out], layer indices in [0, n_layers):
+ *                 tap t receives the residual after layer tap_layers[t].
+ *   tap_out:      NULL or HOST array of n_tap_out device pointers, each fp32
+ *                 [n_req * b] rows of pitch tap_ld (>= hidden, % 4 == 0),
+ *                 16-byte aligned; row r*b + i is block row i of request r.
+ *   logits:       NULL or fp32 [n_req, b, vocab].
+ *   ids:          int32 [n_req, b], argmax of every row.
+ */
+int dflash_verify_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, int block_len,
+                        const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld,
+                        float* logits, int* ids);
+
+/* pos[r] += n_emit[r] for r < n_req (n_emit: device int32 [n_req], e.g. the
+ * drafter's dflash_accept output), enqueued on `stream`: commits a target's
+ * accepted rows. */
+int dflash_advance(dflash_ctx* ctx, void* stream, const int* n_emit, int n_req);
+
 /* Synchronize `stream`, read the device error word into *word (host, may be NULL);
  * returns DFLASH_E_DEVICE if it is non-zero. */
 int dflash_check(dflash_ctx* ctx, void* stream, unsigned* word);

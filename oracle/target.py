@@ -30,9 +30,14 @@ class TinyTarget:
     (wqkv, wo, wgu, wd, ln_in, ln_post, q_norm, k_norm), plus embed, lm_head and
     final_norm. ``cfg`` supplies the widths (the drafter's config)."""
 
-    def __init__(self, cfg, weights: Dict[str, object], n_layers: int = 2):
+    def __init__(self, cfg, weights: Dict[str, object], n_layers: int = 2, mode: str = "exact"):
+        """``mode``: "exact" (fp64 throughout) or "mirror" (values rounded to bf16
+        at the drafter's cast points: normed rows feeding products, Q/K after
+        head norm + RoPE, V and the cached K/V, attention output, SiLU.up, the
+        final normed row)."""
         self.cfg = cfg
         self.n_layers = n_layers
+        self.rnd = D._rnd(mode)
         f = D._f64
         self.W = {
             "embed": f(weights["embed"]), "lm_head": f(weights["lm_head"]),
@@ -56,39 +61,43 @@ class TinyTarget:
         cfg, W = self.cfg, self.W
         nq, nkv, hd, eps = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps
         assert position == self.length
+        rnd = self.rnd
         h = W["embed"][int(token)].copy()
         taps = []
         for l in range(self.n_layers):
-            a = D.rmsnorm(h, W["ln_in"][l], eps)
+            a = rnd(D.rmsnorm(h, W["ln_in"][l], eps))
             wq, wk, wv = D._split_qkv(cfg, W["wqkv"][l])
             q = D.rmsnorm((wq @ a).reshape(nq, hd), W["q_norm"][l], eps)
             k = D.rmsnorm((wk @ a).reshape(nkv, hd), W["k_norm"][l], eps)
-            v = (wv @ a).reshape(nkv, hd)
+            v = rnd((wv @ a).reshape(nkv, hd))
             pos = np.array([position])
-            q = D.rope(q[:, None, :], pos, cfg.rope_theta)       # [nq, 1, hd]
-            k = D.rope(k[:, None, :], pos, cfg.rope_theta)[:, 0]
+            q = rnd(D.rope(q[:, None, :], pos, cfg.rope_theta))       # [nq, 1, hd]
+            k = rnd(D.rope(k[:, None, :], pos, cfg.rope_theta)[:, 0])
             self.k[l] = np.concatenate([self.k[l], k[None]], 0)
             self.v[l] = np.concatenate([self.v[l], v[None]], 0)
-            o = D.attention(q, self.k[l].transpose(1, 0, 2), self.v[l].transpose(1, 0, 2))
+            o = rnd(D.attention(q, self.k[l].transpose(1, 0, 2), self.v[l].transpose(1, 0, 2)))
             h = h + W["wo"][l] @ o.reshape(nq * hd)
-            a2 = D.rmsnorm(h, W["ln_post"][l], eps)
+            a2 = rnd(D.rmsnorm(h, W["ln_post"][l], eps))
             g = W["wgu"][l][: cfg.ffn] @ a2
             u = W["wgu"][l][cfg.ffn:] @ a2
-            h = h + W["wd"][l] @ (D.silu(g) * u)
+            h = h + W["wd"][l] @ rnd(D.silu(g) * u)
             taps.append(h.copy())
-        logits = W["lm_head"] @ D.rmsnorm(h, W["final_norm"], eps)
+        logits = W["lm_head"] @ rnd(D.rmsnorm(h, W["final_norm"], eps))
         return logits, taps
 
-    def feed(self, tokens: Sequence[int], start: int):
+    def feed(self, tokens: Sequence[int], start: int, want_logits: bool = False):
         """Rows for tokens at positions start.. (causal, one at a time).
-        Returns (argmax ids [n], taps [n_layers][n, H] as float32)."""
-        ids, taps = [], [[] for _ in range(self.n_layers)]
+        Returns (argmax ids [n], taps [n_layers][n, H] as float32), plus the
+        fp64 logits [n, V] when ``want_logits``."""
+        ids, taps, lg = [], [[] for _ in range(self.n_layers)], []
         for i, t in enumerate(tokens):
             logits, tr = self._row(t, start + i)
             ids.append(int(D.topk(logits, 1)[0][0, 0]))
+            lg.append(logits)
             for l in range(self.n_layers):
                 taps[l].append(tr[l])
-        return ids, [np.asarray(t, dtype=np.float32).reshape(len(tokens), -1) for t in taps]
+        out = (ids, [np.asarray(t, dtype=np.float32).reshape(len(tokens), -1) for t in taps])
+        return out + (np.asarray(lg),) if want_logits else out
 
     def truncate(self, n: int):
         """Keep the first n cached rows (rollback after a verify pass)."""

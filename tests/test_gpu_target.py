@@ -1,0 +1,165 @@
+"""GPU verify passes of a causal target (dflash_create_target,
+dflash_verify_block, dflash_advance) on the tiny 2-layer target:
+  - parity with the oracle target in mirror mode: logits, argmax away from
+    ties and the tapped residual rows, for prompt chunks of 8, 8 and 5 rows;
+  - batch invariance: a block of 8 rows in one pass equals 8 one-row passes,
+    bit for bit (ids and taps);
+  - the whole loop on the GPU (target verify -> its taps staged into the
+    drafter -> drafter accept -> target advance) equals the GPU target's own
+    greedy decoding token for token."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafter_tap_amd import config, synth
+from oracle import dflash as D
+from oracle import target as T
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(w):
+    return {k: ([synth.bf16_to_f32_numpy(t) for t in v] if isinstance(v, list) else synth.bf16_to_f32_numpy(v))
+            for k, v in w.items()}
+
+
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_tap_amd import binding
+    dcfg = config.tiny(window=64)
+    tcfg = config.tiny(window=128).replace(n_layers=2)
+    wd = synth.make_weights(dcfg, seed=0, device="cuda")
+    wt = synth.make_weights(tcfg, seed=11, device="cuda")
+    # a peakier target so greedy continuations vary; drafter and target share embedding and head
+    emb = (wd["embed"].float() * 30.0).to(torch.bfloat16)
+    wt["embed"], wt["lm_head"] = emb, wd["lm_head"]
+    wd["embed"] = emb
+    return binding, dcfg, tcfg, wd, wt
+
+
+def _feed(tg, toks, tap_layers, n_rows=None):
+    """One verify pass of `toks` (list) on target handle tg: (ids, taps, logits)."""
+    b = len(toks)
+    H = tg.cfg.hidden
+    taps = [torch.empty((b, H), dtype=torch.float32, device="cuda") for _ in tap_layers]
+    logits = torch.empty((1, b, tg.cfg.vocab), dtype=torch.float32, device="cuda")
+    ids = tg.verify_block(torch.tensor([toks], dtype=torch.int32, device="cuda"), tap_layers, taps, logits)
+    return ids, taps, logits
+
+
+def test_verify_vs_oracle_target_tiny():
+    binding, dcfg, tcfg, wd, wt = _setup()
+    print("case: tiny target verify vs mirror oracle target", flush=True)
+    tg = binding.Drafter(tcfg, wt, target=True)
+    tg.reset(0, 0, 0)
+    ref = T.TinyTarget(tcfg, _np(wt), n_layers=2, mode="mirror")
+    prompt = [5, 17, 300, 4000, 12, 99, 7, 8, 1, 2, 3, 4, 55, 66, 77, 88, 9, 10, 11, 12, 13]
+    pos = 0
+    for n in (8, 8, 5):
+        chunk = prompt[pos:pos + n]
+        ids, taps, logits = _feed(tg, chunk, [0, 1])
+        torch.cuda.synchronize()
+        assert tg.check() == 0
+        ids_o, taps_o, lg_o = ref.feed(chunk, pos, want_logits=True)
+        g = logits[0].cpu().numpy()
+        el = Hn.assert_close(g, lg_o, f"logits rows {pos}..")
+        comp, excl = Hn.topk_agrees_away_from_ties(lg_o, ids.cpu().numpy().reshape(-1, 1), 1, gpu_logits=g)
+        for l in range(2):
+            Hn.assert_close(taps[l].cpu().numpy(), taps_o[l], f"tap layer {l} rows {pos}..")
+        print(f"rows {pos}..{pos + n - 1}: logits err {el:.3g}, argmax compared {comp}, near-ties {excl}", flush=True)
+        tg.advance(torch.tensor([n], dtype=torch.int32, device="cuda"))
+        pos += n
+    assert int(tg.positions()[0][0]) == pos
+
+
+def test_verify_batch_invariance_tiny():
+    binding, dcfg, tcfg, wd, wt = _setup()
+    print("case: tiny target, one 8-row pass vs 8 one-row passes", flush=True)
+    prompt = [5, 17, 300, 4000, 12, 99, 7, 8, 1, 2]
+    nxt = [44, 45, 46, 47, 48, 49, 50, 51]
+    out = []
+    for mode in ("block", "rows"):
+        tg = binding.Drafter(tcfg, wt, target=True)
+        tg.reset(0, 0, 0)
+        _feed(tg, prompt[:8], [0, 1])
+        tg.advance(torch.tensor([8], dtype=torch.int32, device="cuda"))
+        _feed(tg, prompt[8:], [0, 1])
+        tg.advance(torch.tensor([2], dtype=torch.int32, device="cuda"))
+        if mode == "block":
+            ids, taps, _ = _feed(tg, nxt, [0, 1])
+            out.append((ids.cpu().numpy().reshape(-1), [t.cpu().numpy() for t in taps]))
+        else:
+            ids_all, taps_all = [], [[], []]
+            for t in nxt:
+                ids, taps, _ = _feed(tg, [t], [0, 1])
+                tg.advance(torch.tensor([1], dtype=torch.int32, device="cuda"))
+                ids_all.append(int(ids[0, 0]))
+                for l in range(2):
+                    taps_all[l].append(taps[l].cpu().numpy()[0])
+            out.append((np.array(ids_all), [np.stack(t) for t in taps_all]))
+        torch.cuda.synchronize()
+        assert tg.check() == 0
+    np.testing.assert_array_equal(out[0][0], out[1][0])
+    for l in range(2):
+        np.testing.assert_array_equal(out[0][1][l], out[1][1][l])
+
+
+def test_full_gpu_loop_lossless_tiny():
+    binding, dcfg, tcfg, wd, wt = _setup()
+    print("case: GPU drafter + GPU target loop vs GPU target greedy", flush=True)
+    prompt = [5, 17, 300, 4000, 12, 99, 7, 8, 1, 2, 3]
+    n_new = 36
+    B = dcfg.block
+
+    def prefill(tg, dr):
+        pos = 0
+        last_ids = None
+        while pos < len(prompt):
+            chunk = prompt[pos:pos + B]
+            ids, taps, _ = _feed(tg, chunk, [0, 1])
+            tg.advance(torch.tensor([len(chunk)], dtype=torch.int32, device="cuda"))
+            if dr is not None:
+                rows = torch.arange(pos, pos + len(chunk), dtype=torch.int32, device="cuda")
+                dr.tap_stage(taps, len(chunk), req_of_row=torch.zeros_like(rows), pos_of_row=rows)
+            pos += len(chunk)
+            last_ids = ids
+        return [int(last_ids[0, -1])], pos
+
+    # reference: the GPU target's greedy decoding, one row per pass
+    tg = binding.Drafter(tcfg, wt, target=True)
+    tg.reset(0, 0, 0)
+    ref, pos = prefill(tg, None)
+    while len(ref) < n_new:
+        ids, _, _ = _feed(tg, [ref[-1]], [0, 1])
+        tg.advance(torch.tensor([1], dtype=torch.int32, device="cuda"))
+        ref.append(int(ids[0, 0]))
+
+    # speculative loop, all on the GPU
+    tg = binding.Drafter(tcfg, wt, target=True)
+    dr = binding.Drafter(dcfg, wd)
+    tg.reset(0, 0, 0)
+    dr.reset(0, 0, len(prompt))
+    out, pos = prefill(tg, dr)
+    rounds = 0
+    while len(out) < n_new:
+        blk = D.next_block(out, B, dcfg.mask_id)
+        d_ids = dr.draft_block(torch.tensor([blk], dtype=torch.int32, device="cuda"), k=1)
+        vtok = torch.cat([torch.tensor([blk[0]], dtype=torch.int32, device="cuda"), d_ids[0, :, 0]]).view(1, B)
+        H = tcfg.hidden
+        taps = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+        v_ids = tg.verify_block(vtok, [0, 1], taps)
+        dr.tap_stage(taps, B, rows_per_req=B)
+        budget = torch.tensor([n_new - len(out)], dtype=torch.int32, device="cuda")
+        res = dr.accept(d_ids, 1, v_ids, budget=budget)
+        tg.advance(res["n_emit"])
+        n = int(res["n_emit"][0])
+        out.extend(res["emitted"][0, :n].cpu().tolist())
+        pos += n
+        rounds += 1
+        assert int(dr.positions()[0][0]) == pos and int(tg.positions()[0][0]) == pos
+    torch.cuda.synchronize()
+    assert dr.check() == 0 and tg.check() == 0
+    assert out == ref, (out, ref)
+    print(f"lossless over {rounds} rounds, {len(out)} tokens", flush=True)

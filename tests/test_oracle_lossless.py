@@ -126,3 +126,20 @@ def test_lossless_with_dynamic_block_len(setup, max_seq_extra):
     fed = len(prompt) + len(res["tokens"]) - 1   # positions fed to the target: all but the last token
     assert max_seq is None or fed <= max_seq
     assert res["blocks"][-1] < cfg.block    # the last round was shrunk
+
+
+def test_target_mirror_mode_drift_is_small(setup):
+    """The mirror target (bf16 at the drafter's cast points) stays close to the
+    exact one and agrees on the argmax of every row of a short feed."""
+    cfg, Wd, tgt = setup
+    Wt = {k: getattr(tgt, "W")[k] for k in tgt.W}
+    mir = T.TinyTarget(tgt.cfg, Wt, n_layers=2, mode="mirror")
+    toks = [5, 17, 300, 4000, 12, 99, 7, 8]
+    tgt.reset()
+    ids_e, taps_e, lg_e = tgt.feed(toks, 0, want_logits=True)
+    ids_m, taps_m, lg_m = mir.feed(toks, 0, want_logits=True)
+    drift = np.max(np.abs(lg_m - lg_e)) / np.max(np.abs(lg_e))
+    assert 0 < drift < 0.05
+    assert ids_m == ids_e
+    for a, b in zip(taps_e, taps_m):
+        assert np.max(np.abs(a - b)) <= 0.05 * np.max(np.abs(a))
