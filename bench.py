@@ -103,6 +103,51 @@ def round_bytes(cfg, R: int, k: int) -> dict:
             "ring_read": ring_read}
 
 
+def verify_report(cfg, dev, n_layers: int = 36, steps: int = 20) -> dict:
+    """One causal verify pass of a target with the drafter's layer shape at
+    Qwen3-4B depth (36 layers): the block's B rows at context W, every row's
+    argmax, the residual rows after 5 evenly spaced layers copied out as the
+    drafter's taps. The target's ring is zeroed (the pass reads W context rows
+    whatever they hold, so the timing is that of real contents)."""
+    import torch
+    from block_diffusion_drafter_tap_amd import binding, synth
+
+    B, W, H, hd = cfg.block, cfg.window, cfg.hidden, cfg.head_dim
+    tcfg = cfg.replace(n_layers=n_layers, max_requests=1)
+    w = synth.make_weights(tcfg, seed=7, device=dev)
+    tg = binding.Drafter(tcfg, w, target=True)
+    tg.state.zero_()
+    tg.reset(0, 0, W)
+    T = cfg.n_taps
+    tap_layers = [1 + i * (n_layers - 3) // (T - 1) for i in range(T)] if T > 1 else [n_layers - 1]
+    taps = [torch.empty((B, H), dtype=torch.float32, device=dev) for _ in tap_layers]
+    tokens = synth.block_tokens(tcfg, 1, seed=3, device=dev)
+    for _ in range(3):
+        tg.verify_block(tokens, tap_layers, taps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        tg.verify_block(tokens, tap_layers, taps)
+    e1.record()
+    torch.cuda.synchronize()
+    word = tg.check()
+    if word != 0:
+        raise SystemExit(f"device error word 0x{word:x} in the verify pass")
+    ms = e0.elapsed_time(e1) / steps
+    layer_w = (tcfg.qkv_rows * H + H * tcfg.n_q_heads * hd + 3 * tcfg.ffn * H) * 2 + 4 * H * 2 + 2 * hd * 2
+    kv = n_layers * 2 * tcfg.n_kv_heads * hd * 2
+    nbytes = (n_layers * layer_w + tcfg.vocab * H * 2 + kv * (W + B) + kv * B + len(tap_layers) * B * H * 4
+              + B * H * 2 + B * 4)
+    gbps = nbytes / (ms / 1e3) / 1e9
+    del tg, w
+    torch.cuda.empty_cache()
+    return {"target": f"{n_layers} layers of the drafter's shape (hidden {H}, {tcfg.n_q_heads}/{tcfg.n_kv_heads} "
+                      f"heads x {hd}, ffn {tcfg.ffn}), vocab {tcfg.vocab}, causal",
+            "rows": B, "context": W, "tap_layers": tap_layers, "ms": round(ms, 4), "bytes": int(nbytes),
+            "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def prefill_report(cfg, rows: int, ms: float) -> dict:
     """Prefill staging of one request's window (fc over the gathered taps, then
     every layer's context K/V into the ring): a dense contraction, reported
@@ -165,6 +210,7 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-verify", action="store_true", help="skip the target verify-pass measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -220,13 +266,16 @@ def main():
     keep = (j < torch.from_numpy(acc).to(dev).view(n_rounds, R, 1))          # [rounds, R, B]
     g = torch.Generator(device=dev).manual_seed(2)
     noise1 = torch.randint(0, V - 1, (n_rounds, R, B), generator=g, device=dev, dtype=torch.int32) + 1
+    # per-round offsets of the verify ids: 0 where the target agrees with the draft
+    # (j < a), else 1 + noise in [1, V-1], so (draft + offset) mod V differs there
+    delta = torch.where(keep, torch.zeros_like(noise1), noise1)[:, :, :B - 1].contiguous()
 
     tokens = synth.block_tokens(cfg, R, seed=0, device=dev)
     ids = torch.empty((R, B - 1, k), dtype=torch.int32, device=dev)
     vals = torch.empty((R, B - 1, k), dtype=torch.float32, device=dev)
-    ext = torch.zeros((R, B), dtype=torch.int32, device=dev)
-    tmp = torch.empty((R, B), dtype=torch.int32, device=dev)
-    verify = torch.empty((R, B), dtype=torch.int32, device=dev)
+    # the last verify id (the bonus token after a full accept) is a fixed token
+    verify = torch.ones((R, B), dtype=torch.int32, device=dev)
+    vview = verify[:, :B - 1]
     out = {"accept_len": torch.empty(R, dtype=torch.int32, device=dev),
            "emitted": torch.empty((R, B), dtype=torch.int32, device=dev),
            "n_emit": torch.empty(R, dtype=torch.int32, device=dev),
@@ -235,10 +284,8 @@ def main():
 
     def one_round(i: int):
         dr.draft_block(tokens, k=k, ids=ids, vals=vals)
-        ext[:, :B - 1].copy_(ids[:, :, 0])
-        torch.add(ext, noise1[i], out=tmp)
-        torch.remainder(tmp, V, out=tmp)
-        torch.where(keep[i], ext, tmp, out=verify)
+        torch.add(ids[:, :, 0], delta[i], out=vview)
+        vview.remainder_(V)
         off = (i * B) % (pool_rows - B)
         if R == 1:
             ptrs = [pool_cat[t][0, off:].data_ptr() for t in range(cfg.n_taps)]
@@ -328,6 +375,25 @@ def main():
     except RuntimeError as exc:   # capture unsupported here: report why, keep the plain result
         graph = {"error": str(exc)[:200]}
 
+    # per-call block length: the draft forward alone at shorter blocks of this handle
+    draft_ms_by_block = {}
+    for b in sorted({B, B // 2, 4, 2}, reverse=True):
+        if 1 < b <= B:
+            tk = tokens[:, :b].contiguous()
+            idb = torch.empty((R, b - 1, k), dtype=torch.int32, device=dev)
+            for _ in range(3):
+                dr.draft_block_n(tk, k=k, ids=idb)
+            b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            b0.record()
+            for _ in range(20):
+                dr.draft_block_n(tk, k=k, ids=idb)
+            b1.record()
+            torch.cuda.synchronize()
+            draft_ms_by_block[str(b)] = round(b0.elapsed_time(b1) / 20, 4)
+    if dr.check() != 0:
+        raise SystemExit("device error word set by the block-length sweep")
+
     # HBM read reference: a plain streaming-read kernel of this library over 1 GiB
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     sink = torch.empty(1024, dtype=torch.int32, device=dev)
@@ -381,7 +447,11 @@ def main():
                      "p90": round(float(np.percentile(per_round, 90)), 4)},
         "graph": graph,
         "hbm_read_reference_gbps": round(read_gbps, 1),
+        "draft_ms_by_block": draft_ms_by_block,
+        "verify": None,
     }
+    if not args.no_verify and R == 1 and cfg.wfmt == config.WFMT_BF16:
+        result["verify"] = verify_report(cfg, dev)
     if not args.no_cpu_baseline:
         import numpy as np  # noqa: F811
         taps_h = [hist[0][t].cpu().numpy() for t in range(cfg.n_taps)]

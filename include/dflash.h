@@ -247,8 +247,9 @@ int dflash_accept_n(dflash_ctx* ctx, void* stream, const int* draft_ids, int dra
  * a Qwen3-shaped causal decoder whose own per-layer K/V live in the ring of its
  * state, at slot position mod ring_capacity, over the window of the config.
  * The verify pass runs the B rows of the round (the last emitted token and the
- * drafts) through every layer with block row i attending to the window and to
- * block rows j <= i, writes the block's K/V to ring slots [pos, pos+B), returns
+ * drafts) through every layer with block row i attending to ring rows
+ * [max(valid_from, pos - window), pos) and to block rows j <= i (a target with
+ * full attention sets window >= its longest sequence), writes the block's K/V to ring slots [pos, pos+B), returns
  * the argmax (lowest id on ties) of every row, and copies the residual rows
  * after the tapped layers, which are the drafter's taps ("[RFC] DFlash",
  * ExecuTorch PR #20840, "Key Implementation Details": the target returns its

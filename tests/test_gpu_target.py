@@ -6,7 +6,8 @@ dflash_verify_block, dflash_advance) on the tiny 2-layer target:
     bit for bit (ids and taps);
   - the whole loop on the GPU (target verify -> its taps staged into the
     drafter -> drafter accept -> target advance) equals the GPU target's own
-    greedy decoding token for token."""
+    greedy decoding token for token, with the drafter's drafts and with planted
+    drafts that are accepted up to a seeded place."""
 import numpy as np
 import pytest
 import torch
@@ -106,12 +107,19 @@ def test_verify_batch_invariance_tiny():
         np.testing.assert_array_equal(out[0][1][l], out[1][1][l])
 
 
-def test_full_gpu_loop_lossless_tiny():
+@pytest.mark.parametrize("drafts", ["drafter", "planted"])
+def test_full_gpu_loop_lossless_tiny(drafts):
+    """drafts="drafter": the GPU drafter's top-1 (random weights: mostly
+    rejected). drafts="planted": the target's own continuation with one wrong
+    token at a seeded place per round (or none), so rounds accept 0..B-1 drafts
+    plus the target's token and the target rolls back the rest of its block."""
     binding, dcfg, tcfg, wd, wt = _setup()
-    print("case: GPU drafter + GPU target loop vs GPU target greedy", flush=True)
+    print(f"case: GPU {drafts} drafts + GPU target loop vs GPU target greedy", flush=True)
     prompt = [5, 17, 300, 4000, 12, 99, 7, 8, 1, 2, 3]
     n_new = 36
     B = dcfg.block
+    V = dcfg.vocab
+    rng = np.random.default_rng(21)
 
     def prefill(tg, dr):
         pos = 0
@@ -131,7 +139,7 @@ def test_full_gpu_loop_lossless_tiny():
     tg = binding.Drafter(tcfg, wt, target=True)
     tg.reset(0, 0, 0)
     ref, pos = prefill(tg, None)
-    while len(ref) < n_new:
+    while len(ref) < n_new + B:
         ids, _, _ = _feed(tg, [ref[-1]], [0, 1])
         tg.advance(torch.tensor([1], dtype=torch.int32, device="cuda"))
         ref.append(int(ids[0, 0]))
@@ -143,9 +151,17 @@ def test_full_gpu_loop_lossless_tiny():
     dr.reset(0, 0, len(prompt))
     out, pos = prefill(tg, dr)
     rounds = 0
+    accepts = []
     while len(out) < n_new:
         blk = D.next_block(out, B, dcfg.mask_id)
         d_ids = dr.draft_block(torch.tensor([blk], dtype=torch.int32, device="cuda"), k=1)
+        if drafts == "planted":
+            plant = list(ref[len(out):len(out) + B - 1])
+            j = int(rng.integers(0, B))            # j == B - 1: every draft right
+            if j < B - 1:
+                plant[j] = (plant[j] + 1) % V
+            d_ids = torch.tensor(plant, dtype=torch.int32, device="cuda").view(1, B - 1, 1)
+            accepts.append(j)
         vtok = torch.cat([torch.tensor([blk[0]], dtype=torch.int32, device="cuda"), d_ids[0, :, 0]]).view(1, B)
         H = tcfg.hidden
         taps = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -161,5 +177,7 @@ def test_full_gpu_loop_lossless_tiny():
         assert int(dr.positions()[0][0]) == pos and int(tg.positions()[0][0]) == pos
     torch.cuda.synchronize()
     assert dr.check() == 0 and tg.check() == 0
-    assert out == ref, (out, ref)
+    assert out == ref[:n_new], (out, ref[:n_new])
+    if drafts == "planted":
+        assert max(accepts) >= 3
     print(f"lossless over {rounds} rounds, {len(out)} tokens", flush=True)
