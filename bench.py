@@ -211,6 +211,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-verify", action="store_true", help="skip the target verify-pass measurement")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the draft-forward block-length sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -377,7 +378,7 @@ def main():
 
     # per-call block length: the draft forward alone at shorter blocks of this handle
     draft_ms_by_block = {}
-    for b in sorted({B, B // 2, 4, 2}, reverse=True):
+    for b in ([] if args.no_sweep else sorted({B, B // 2, 4, 2}, reverse=True)):
         if 1 < b <= B:
             tk = tokens[:, :b].contiguous()
             idb = torch.empty((R, b - 1, k), dtype=torch.int32, device=dev)
