@@ -99,6 +99,39 @@ class TinyTarget:
         out = (ids, [np.asarray(t, dtype=np.float32).reshape(len(tokens), -1) for t in taps])
         return out + (np.asarray(lg),) if want_logits else out
 
+    def prefill(self, tokens: Sequence[int]):
+        """Append the cache rows of a prompt without logits or taps. The same
+        per-row arithmetic as ``_row`` (cast points included), with the rows'
+        projections done as one matrix product per weight and the causal
+        attention of row i over cache rows [0, start + i]. Equal to feeding the
+        tokens one at a time up to fp64 summation order; pinned against ``feed``."""
+        cfg, W = self.cfg, self.W
+        nq, nkv, hd, eps, F = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.ffn
+        rnd = self.rnd
+        start, n = self.length, len(tokens)
+        pos = np.arange(start, start + n)
+        h = W["embed"][np.asarray(tokens, dtype=np.int64)].copy()            # [n, H]
+        for l in range(self.n_layers):
+            a = rnd(D.rmsnorm(h, W["ln_in"][l], eps))
+            wq, wk, wv = D._split_qkv(cfg, W["wqkv"][l])
+            q = D.rmsnorm((a @ wq.T).reshape(n, nq, hd), W["q_norm"][l], eps)
+            k = D.rmsnorm((a @ wk.T).reshape(n, nkv, hd), W["k_norm"][l], eps)
+            v = rnd((a @ wv.T).reshape(n, nkv, hd))
+            q = rnd(D.rope(q.transpose(1, 0, 2), pos, cfg.rope_theta))        # [nq, n, hd]
+            k = rnd(D.rope(k.transpose(1, 0, 2), pos, cfg.rope_theta))        # [nkv, n, hd]
+            self.k[l] = np.concatenate([self.k[l], k.transpose(1, 0, 2)], 0)
+            self.v[l] = np.concatenate([self.v[l], v], 0)
+            kc, vc = self.k[l].transpose(1, 0, 2), self.v[l].transpose(1, 0, 2)
+            o = np.empty((n, nq, hd))
+            for i in range(n):
+                hi = start + i + 1
+                o[i] = D.attention(q[:, i:i + 1, :], kc[:, :hi], vc[:, :hi])[0]
+            h = h + rnd(o).reshape(n, nq * hd) @ W["wo"][l].T
+            a2 = rnd(D.rmsnorm(h, W["ln_post"][l], eps))
+            g = a2 @ W["wgu"][l][:F].T
+            u = a2 @ W["wgu"][l][F:].T
+            h = h + rnd(D.silu(g) * u) @ W["wd"][l].T
+
     def truncate(self, n: int):
         """Keep the first n cached rows (rollback after a verify pass)."""
         self.k = [k[:n] for k in self.k]

@@ -181,3 +181,44 @@ def test_full_gpu_loop_lossless_tiny(drafts):
     if drafts == "planted":
         assert max(accepts) >= 3
     print(f"lossless over {rounds} rounds, {len(out)} tokens", flush=True)
+
+
+def test_verify_fullsize_vs_oracle_target():
+    """Verify pass at the qwen3-4b layer shape (hidden 2560, 32/8 heads x 128, ffn
+    9728, vocab 151936; 4 layers, window 4096): a 300-row prompt fed in 16-row
+    passes puts the 16-row block in the second 256-key chunk; its logits,
+    argmaxes (away from ties) and the taps after layers 1 and 3 are compared with
+    the mirror oracle target, which takes the prompt through its batched prefix
+    routine."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_tap_amd import binding
+    tcfg = config.qwen3_4b(block=16, window=4096, max_stage_rows=16).replace(n_layers=4)
+    B, V, H = tcfg.block, tcfg.vocab, tcfg.hidden
+    print("case: qwen3-4b-shaped 4-layer target, prompt 300, verify block 16", flush=True)
+    wt = synth.make_weights(tcfg, seed=21, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(22)
+    P = 300
+    toks = torch.randint(0, V - 1, (P + B,), generator=g, device="cuda", dtype=torch.int32)
+    prompt, blk = toks[:P].cpu().tolist(), toks[P:].cpu().tolist()
+    tg = binding.Drafter(tcfg, wt, target=True)
+    tg.reset(0, 0, 0)
+    for r0 in range(0, P, B):
+        n = min(B, P - r0)
+        _feed(tg, prompt[r0:r0 + n], [])
+        tg.advance(torch.tensor([n], dtype=torch.int32, device="cuda"))
+    ids, taps, logits = _feed(tg, blk, [1, 3])
+    torch.cuda.synchronize()
+    assert tg.check() == 0
+    assert int(tg.positions()[0][0]) == P
+    ref = T.TinyTarget(tcfg, _np(wt), n_layers=4, mode="mirror")
+    ref.prefill(prompt)
+    ids_o, taps_o, lg_o = ref.feed(blk, P, want_logits=True)
+    gl = logits[0].cpu().numpy()
+    el = Hn.assert_close(gl, lg_o, "verify logits")
+    comp, excl = Hn.topk_agrees_away_from_ties(lg_o, ids.cpu().numpy().reshape(-1, 1), 1, gpu_logits=gl)
+    Hn.topk_self_consistent(gl, ids.cpu().numpy().reshape(-1, 1))
+    et = [Hn.assert_close(taps[i].cpu().numpy(), taps_o[l], f"tap after layer {l}") for i, l in enumerate((1, 3))]
+    print(f"logits err {el:.3g}, tap errs {et[0]:.3g} {et[1]:.3g}, argmax compared {comp}, near-ties {excl}",
+          flush=True)
+    assert comp >= 4

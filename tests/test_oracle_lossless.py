@@ -143,3 +143,28 @@ def test_target_mirror_mode_drift_is_small(setup):
     assert ids_m == ids_e
     for a, b in zip(taps_e, taps_m):
         assert np.max(np.abs(a - b)) <= 0.05 * np.max(np.abs(a))
+
+
+@pytest.mark.parametrize("mode", ["exact", "mirror"])
+def test_target_prefill_equals_feed(setup, mode):
+    """The batched prefix routine leaves the same cache as feeding the prompt row
+    by row: the rows fed afterwards get the same logits and taps."""
+    cfg, Wd, tgt = setup
+    Wt = {k: tgt.W[k] for k in tgt.W}
+    a = T.TinyTarget(tgt.cfg, Wt, n_layers=2, mode=mode)
+    b = T.TinyTarget(tgt.cfg, Wt, n_layers=2, mode=mode)
+    prompt = [5, 17, 300, 4000, 12, 99, 7, 8, 1, 2, 3, 4, 5]
+    nxt = [44, 45, 46]
+    a.feed(prompt, 0)
+    _, ta, la = a.feed(nxt, len(prompt), want_logits=True)
+    b.prefill(prompt[:6])
+    b.prefill(prompt[6:])
+    assert b.length == len(prompt)
+    _, tb, lb = b.feed(nxt, len(prompt), want_logits=True)
+    # exact: fp64 summation order only; mirror: a bf16 rounding may flip at a tie
+    tol = 1e-10 if mode == "exact" else 1e-3
+    assert np.max(np.abs(la - lb)) <= tol * np.max(np.abs(la))
+    for x, y in zip(ta, tb):
+        assert np.max(np.abs(x - y)) <= max(tol, 1e-6) * np.max(np.abs(x))
+    for l in range(2):
+        assert np.max(np.abs(a.k[l] - b.k[l])) <= tol * np.max(np.abs(a.k[l]))
