@@ -10,9 +10,10 @@
 //                      double-buffered through LDS (rows padded by 8 elements so
 //                      the 16 rows of a fragment read fall in different banks),
 //                      each stage's global loads issued two stages ahead. Tiles
-//                      are numbered row-major and dealt out XCD-major (workgroup
-//                      i runs on XCD i % 8), so the tiles resident on one XCD
-//                      share X rows in its L2.
+//                      are numbered in groups of 8 row blocks, column-major
+//                      inside a group, and dealt out XCD-major (workgroup i runs
+//                      on XCD i % 8): the tiles resident on one XCD form an
+//                      8 x 8 block that shares X rows and W columns in its L2.
 #include <string.h>
 
 #include "device.h"
@@ -20,7 +21,7 @@
 
 namespace {
 
-constexpr int PF_BM = 128, PF_BK = 64, PF_LDK = PF_BK + 8;
+constexpr int PF_BM = 128, PF_BK = 64, PF_LDK = PF_BK + 8, PF_GM = 8;
 
 __global__ __launch_bounds__(256) void tap_gather_kernel(const TapGather g) {
   const int m = blockIdx.y;
@@ -86,9 +87,15 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
 
   const int mt = (a.M + PF_BM - 1) / PF_BM, nt = a.N / BN, tiles = mt * nt;
   const int per_xcd = (tiles + 7) / 8;
-  const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (tile >= tiles) return;
-  const int m0 = (tile / nt) * PF_BM, n0 = (tile % nt) * BN;
+  const int seq = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (seq >= tiles) return;
+  // the tile sequence runs through groups of PF_GM row blocks, column-major inside
+  // a group: the 64 tiles resident on one XCD span 8 row blocks x 8 column blocks,
+  // so each X row block and each W column block is re-read from that XCD's L2
+  const int grp = seq / (PF_GM * nt), first = grp * PF_GM;
+  const int gm = min(PF_GM, mt - first);
+  const int r = seq - grp * PF_GM * nt;
+  const int m0 = (first + r % gm) * PF_BM, n0 = (r / gm) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
