@@ -222,3 +222,49 @@ def test_verify_fullsize_vs_oracle_target():
     print(f"logits err {el:.3g}, tap errs {et[0]:.3g} {et[1]:.3g}, argmax compared {comp}, near-ties {excl}",
           flush=True)
     assert comp >= 4
+
+
+def test_verify_multi_request_invariance_tiny():
+    """Three requests in one target handle, each from its own start position
+    (valid_from = pos = 5r) with its own tokens, advancing by different amounts:
+    every verify pass of the 3-request call equals the same pass of a
+    single-request handle bit for bit (ids, taps, logits)."""
+    binding, dcfg, tcfg, wd, wt = _setup()
+    R, b = 3, 8
+    tcfg3 = tcfg.replace(max_requests=R)
+    print("case: tiny target, 3 requests in one call vs single-request handles", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(31)
+    V, H = tcfg.vocab, tcfg.hidden
+    n_pass = 5
+    toks = torch.randint(0, V - 1, (n_pass, R, b), generator=g, device="cuda", dtype=torch.int32)
+    adv = torch.tensor([[8, 8, 8], [8, 8, 8], [3, 8, 1], [5, 2, 8], [1, 1, 1]], dtype=torch.int32, device="cuda")
+
+    def run(handle, reqs):
+        handle_out = []
+        for p in range(n_pass):
+            n = len(reqs)
+            taps = [torch.empty((n * b, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+            logits = torch.empty((n, b, V), dtype=torch.float32, device="cuda")
+            ids = handle.verify_block(toks[p, reqs].contiguous(), [0, 1], taps, logits)
+            handle.advance(adv[p, reqs].contiguous())
+            handle_out.append((ids.cpu().numpy(), [t.cpu().numpy().reshape(n, b, H) for t in taps],
+                               logits.cpu().numpy()))
+        torch.cuda.synchronize()
+        assert handle.check() == 0
+        return handle_out
+
+    multi = binding.Drafter(tcfg3, wt, target=True)
+    for r in range(R):
+        multi.reset(r, 5 * r, 5 * r)
+    out_m = run(multi, list(range(R)))
+    pos_m = multi.positions()[0].cpu().numpy()
+    for r in range(R):
+        single = binding.Drafter(tcfg, wt, target=True)
+        single.reset(0, 5 * r, 5 * r)
+        out_s = run(single, [r])
+        assert int(single.positions()[0][0]) == int(pos_m[r]) == 5 * r + int(adv[:, r].sum())
+        for p in range(n_pass):
+            np.testing.assert_array_equal(out_m[p][0][r], out_s[p][0][0], err_msg=f"ids pass {p} req {r}")
+            for l in range(2):
+                np.testing.assert_array_equal(out_m[p][1][l][r], out_s[p][1][l][0], err_msg=f"taps pass {p} req {r}")
+            np.testing.assert_array_equal(out_m[p][2][r], out_s[p][2][0], err_msg=f"logits pass {p} req {r}")
