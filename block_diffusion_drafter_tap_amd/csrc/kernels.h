@@ -168,7 +168,7 @@ hipError_t launch_copy_rows(const float* h, int M, int H, float* dst, long long 
 hipError_t launch_advance(int* pos, const int* n_emit, int n_req, hipStream_t st);
 
 // Small kernels.
-constexpr int STREAM_READ_BLOCKS = 1024;
+constexpr int STREAM_READ_BLOCKS = 256;
 hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* sink, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, float* ssq, int M, int H,

@@ -362,8 +362,9 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
   __shared__ unsigned cand_k[256];
   __shared__ int cand_i[256];
   __shared__ unsigned s_tmax[256];
-  __shared__ __attribute__((aligned(16))) unsigned cb_k[512];
-  __shared__ __attribute__((aligned(16))) int cb_i[512];
+  // candidate logits as (key << 32 | ~index): one unsigned compare orders them
+  // by (value desc, index asc)
+  __shared__ __attribute__((aligned(16))) unsigned long long cb[512];
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ng = (N + 15) / 16;
   const float* gm = gmax + (size_t)row * ng;
@@ -437,33 +438,48 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
     const int n = 16 * gsel[e / 16] + (e % 16);
     const int nn = min(n, N - 1);
     const float v = transposed ? logits[(size_t)nn * cs + srow] : logits[srow * N + nn];
-    cb_k[e] = n < N ? fkey(v) : 0u;
-    cb_i[e] = n < N ? n : 0x7fffffff - e;
+    // past the vocabulary: key 0 (below every logit's key), distinct per slot
+    cb[e] = n < N ? ((unsigned long long)fkey(v) << 32) | (unsigned)~n : (unsigned long long)e;
   }
-  const int ncp = (nc + 3) & ~3;
-  for (int e = nc + t; e < ncp; e += 256) {   // pad to whole 16-byte reads
-    cb_k[e] = 0u;
-    cb_i[e] = 0x7fffffff - e;
-  }
+  // pad to whole steps of 8 entries (four 16-byte reads) with entries that rank
+  // below every logit
+  const int ncp = (nc + 7) & ~7;
+  for (int e = nc + t; e < ncp; e += 256) cb[e] = (unsigned long long)e;
   __syncthreads();
-  const u32x4* k4 = (const u32x4*)cb_k;
-  const u32x4* i4 = (const u32x4*)cb_i;
-  for (int e = t; e < nc; e += 256) {
-    const unsigned kk = cb_k[e];
-    const int ii = cb_i[e];
-    int rank = 0;
-    for (int j4 = 0; j4 < ncp / 4; ++j4) {
-      const u32x4 qk = k4[j4], qi = i4[j4];
+  // rank = number of entries with a larger combined key. Thread t ranks entries
+  // t and t + 256 in one branch-free pass over the list, four 16-byte reads
+  // (eight entries) per step so that the LDS reads overlap.
+  if (t < nc) {
+    const u32x4* c4 = (const u32x4*)cb;
+    const unsigned long long ca = cb[t];
+    const bool two = t + 256 < nc;
+    const unsigned long long cbv = two ? cb[t + 256] : ~0ull;
+    int ra = 0, rb = 0;
+    for (int j = 0; j < ncp / 2; j += 4) {
+      u32x4 q[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) rank += (qk[q] > kk || (qk[q] == kk && (int)qi[q] < ii)) ? 1 : 0;
+      for (int u = 0; u < 4; ++u) q[u] = c4[j + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned long long c = ((unsigned long long)q[u][2 * h + 1] << 32) | q[u][2 * h];
+          ra += c > ca ? 1 : 0;
+          rb += c > cbv ? 1 : 0;
+        }
     }
-    if (rank < k) {
-      ids[(size_t)row * k + rank] = ii;
-      if (vals) {
-        const unsigned u = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;   // inverse of fkey
-        vals[(size_t)row * k + rank] = __uint_as_float(u);
+    auto put = [&](unsigned long long c, int rank) {
+      if (rank < k) {
+        ids[(size_t)row * k + rank] = (int)~(unsigned)c;
+        if (vals) {
+          const unsigned kk = (unsigned)(c >> 32);
+          const unsigned u = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;   // inverse of fkey
+          vals[(size_t)row * k + rank] = __uint_as_float(u);
+        }
       }
-    }
+    };
+    put(ca, ra);
+    if (two) put(cbv, rb);
   }
 }
 

@@ -13,9 +13,11 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
 }
 
 // Streaming read of `n16` 16-byte vectors (the HBM read reference of the
-// measurements): 1024 workgroups x 256 threads, eight independent 16-byte
-// loads per thread in flight, an XOR of everything read per workgroup into
-// sink[blockIdx.x] so that no load is dead.
+// measurements): 256 workgroups x 256 threads, eight independent nontemporal
+// 16-byte loads per thread in flight (the fastest plain read measured on
+// MI355X over the shapes tried: grids of 256-4096 workgroups, 256 or 512
+// threads, 4 or 8 loads in flight, temporal or nontemporal), an XOR of
+// everything read per workgroup into sink[blockIdx.x] so that no load is dead.
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* src, size_t n16, unsigned* sink) {
   __shared__ unsigned red[4];
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* src, size
   for (; i + 7 * stride < n16; i += 8 * stride) {
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < 8; ++u) v[u] = ld_nt16(src + i + u * stride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) x ^= v[u];
   }

@@ -301,10 +301,11 @@ int dflash_set_timing_events(dflash_ctx* ctx, int kclass, void* const* before,
 
 /* Measurement reference, not part of the round: read `bytes` (a multiple of 16)
  * of device memory at `src` (16-byte aligned) once with a plain streaming-read
- * kernel of this library, enqueued on `stream`; its duration against `bytes` is
+ * kernel of this library (256 workgroups, eight nontemporal 16-byte loads in
+ * flight per thread), enqueued on `stream`; its duration against `bytes` is
  * the HBM read rate the round's kernels are compared with beside the vendor
- * peak. `sink`: device uint32[1024] that receives an XOR of what each
- * workgroup read (contents meaningless; it keeps the loads live). */
+ * peak. `sink`: device uint32[1024] (the first 256 are written) that receives
+ * an XOR of what each workgroup read (contents meaningless; it keeps the loads live). */
 int dflash_stream_read(const void* src, size_t bytes, unsigned* sink, void* stream);
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
