@@ -231,12 +231,14 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
 }
 
 // Combine the chunk partials of one (request, kv head): O = sum_c w_c O_c with
-// w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c, in chunk order. Each thread owns
+// w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c, in chunk order (up to 24 chunks
+// from one batch of loads, more in batches of 8, with the same sums). Each thread owns
 // four consecutive head_dim values of one query slot; workgroup id =
 // part * (R*nkv) + (request, head), so each head's combine runs on the XCD that
 // ran its chunks.
 template <int HD>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs a) {
+  constexpr int CB = 24;   // chunks combined from one batch of loads
   const int RN = a.R * a.nkv;
   const int lrg = blockIdx.x % RN, part = blockIdx.x / RN;
   const int r = lrg / a.nkv, g = lrg % a.nkv;
@@ -248,30 +250,62 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs a) {
   const size_t c0 = (size_t)lrg * a.n_chunks * slots;
   const float2* ml = (const float2*)a.part_ml;
   float M = -INFINITY;
-  for (int c0i = 0; c0i < n_ch; c0i += 8) {
-    float2 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = c0i + u < n_ch ? ml[c0 + (size_t)(c0i + u) * slots + s] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) M = fmaxf(M, v[u].x);
-  }
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0i = 0; c0i < n_ch; c0i += 8) {
-    float2 v[8];
-    f32x4 ov[8];
+  if (n_ch <= CB) {
+    // every chunk's loads in one batch: one L2 round trip. The sums run in chunk
+    // order over n_ch rounded up to 8 terms (zero-weight padding), the same
+    // sequence as the batched loop below.
+    float2 v[CB];
+    f32x4 ov[CB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool ok = c0i + u < n_ch;
-      const size_t cs = c0 + (size_t)(c0i + u) * slots + s;
-      v[u] = ok ? ml[cs] : make_float2(-INFINITY, 0.f);
-      ov[u] = ok ? *(const f32x4*)(a.part_o + cs * HD + 4 * d4) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < CB; ++u) {   // a chunk index past the end re-reads the last chunk
+      const size_t cs = c0 + (size_t)min(u, n_ch - 1) * slots + s;
+      v[u] = ml[cs];
+      ov[u] = *(const f32x4*)(a.part_o + cs * HD + 4 * d4);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wgt = v[u].x == -INFINITY ? 0.f : exp2f(v[u].x - M);
-      L += wgt * v[u].y;
-      acc += wgt * ov[u];
+    for (int u = 0; u < CB; ++u)
+      if (u >= n_ch) {
+        v[u] = make_float2(-INFINITY, 0.f);
+        ov[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) M = fmaxf(M, v[u].x);
+    const int terms = (n_ch + 7) & ~7;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (u < terms) {
+        const float wgt = v[u].x == -INFINITY ? 0.f : exp2f(v[u].x - M);
+        L += wgt * v[u].y;
+        acc += wgt * ov[u];
+      }
+    }
+  } else {
+    for (int c0i = 0; c0i < n_ch; c0i += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = c0i + u < n_ch ? ml[c0 + (size_t)(c0i + u) * slots + s] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) M = fmaxf(M, v[u].x);
+    }
+    for (int c0i = 0; c0i < n_ch; c0i += 8) {
+      float2 v[8];
+      f32x4 ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = c0i + u < n_ch;
+        const size_t cs = c0 + (size_t)(c0i + u) * slots + s;
+        v[u] = ok ? ml[cs] : make_float2(-INFINITY, 0.f);
+        ov[u] = ok ? *(const f32x4*)(a.part_o + cs * HD + 4 * d4) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = v[u].x == -INFINITY ? 0.f : exp2f(v[u].x - M);
+        L += wgt * v[u].y;
+        acc += wgt * ov[u];
+      }
     }
   }
   const float inv = 1.0f / L;

@@ -7,8 +7,24 @@
 
 namespace {
 
-// sum_s P[s * stride + off], s = 0..S-1, in order
+// sum_s P[s * stride + off], s = 0..S-1, in order, padded with +0 terms to a
+// multiple of 8 (the padding is part of the fixed addition sequence). Up to 32
+// splits, every load is issued before the first add: one L2 round trip.
+template <int N>
+DEV float sum_splits_n(const float* P, int S, size_t stride, size_t off) {
+  float v[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) v[u] = u < S ? P[(size_t)u * stride + off] : 0.f;
+  float t = 0.f;
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if (u < ((S + 7) & ~7)) t += v[u];
+  return t;
+}
 DEV float sum_splits(const float* P, int S, size_t stride, size_t off) {
+  if (S <= 8) return sum_splits_n<8>(P, S, stride, off);
+  if (S <= 16) return sum_splits_n<16>(P, S, stride, off);
+  if (S <= 32) return sum_splits_n<32>(P, S, stride, off);
   float t = 0.f;
   for (int s0 = 0; s0 < S; s0 += 8) {
     float v[8];
@@ -79,6 +95,13 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
   const float* P = P0 + (size_t)layer * S * a.M * ld;
   const int head = a.head_base + hl;
   const int hd = a.hd, half = hd / 2;
+  // the partial sums do not depend on the row's position: their loads go out
+  // first, together with the position lookups
+  const bool on = lane < half;
+  const size_t stride = (size_t)a.M * ld, base = (size_t)m * ld + (size_t)hl * hd;
+  const float s1 = sum_splits(P, S, stride, base + (on ? lane : 0));
+  const float s2 = sum_splits(P, S, stride, base + (on ? lane + half : 0));
+  const float x1 = on ? s1 : 0.f, x2 = on ? s2 : 0.f;
   const int req = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
   long long p = -1;
   if (req >= 0 && req < a.Rmax)
@@ -87,10 +110,6 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
     if (lane == 0) set_error(a.err, req < 0 || req >= a.Rmax ? 4u : 8u);
     return;
   }
-  const bool on = lane < half;
-  const size_t stride = (size_t)a.M * ld, base = (size_t)m * ld + (size_t)hl * hd;
-  const float x1 = on ? sum_splits(P, S, stride, base + lane) : 0.f;
-  const float x2 = on ? sum_splits(P, S, stride, base + lane + half) : 0.f;
   const bool is_q = head < a.nq, is_k = !is_q && head < a.nq + a.nkv;
   if (is_q || is_k) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
