@@ -5,14 +5,17 @@
 // w + P, ... of 128 vocabulary rows with 8 waves (one 16-row W tile each).
 // The normed rows are staged in LDS once (all loads of a batch in flight
 // together), W chunks of 128 k-values run D deep across group boundaries, and
-// each wave stores its fp32 tile of the mask rows straight from the MFMA
-// accumulators: there is no barrier in the streaming loop.
+// there is no barrier in the streaming loop. Each wave's fp32 tiles wait in LDS
+// and are stored after its last weight load has been issued (as many groups as
+// the LDS left over holds).
 //
 // The logits kernel also writes, per mask row, the max of every 16-column group.
 // topk_rows_kernel: per row, an exact radix select picks the k best groups by
 // their max, and the k best of those groups' logits are ranked directly.
 // Selecting after streaming keeps the dependent cross-lane work of a running
 // top-k out of the weight stream, where it stalled the loads.
+
+#include <algorithm>
 
 #include "device.h"
 #include "kernels.h"
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void lm_norm_rows_kernel(const GemmArgs a, uin
 
 template <int MT, int XL, int D>
 __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_groups, float* logits, int transposed,
-                                                        float* gmax) {
+                                                        float* gmax, int nslots, int defer_off) {
   constexpr int NW = 8, GC = 128, ROWS = MT * 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ float s_inv[ROWS];
@@ -68,6 +71,8 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
   const int lr = lane & 15, lg = lane >> 4;
   const int K = a.K, nchunks = K / 128, ldl = K + 8;
   uint16_t* xs = (uint16_t*)smem;
+  // accumulator fragments of this workgroup's first nslots groups, [slot][wave][mt][lane]
+  f32x4* dslot = (f32x4*)(smem + defer_off);
 
   // W chunks stream D deep: chunk c of a group lives in buffer c % D (D divides
   // the chunk count); the last D buffers of a group are refilled with the next
@@ -164,6 +169,34 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     return ld16(a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + kk + 8 * lg);
   };
 
+  // Logits: the caller's layout [R*(B-1)][N] (mask rows only), or the
+  // transposed scratch layout [N][16*MT] (every row), where a wave's 16
+  // columns x 16 rows of a tile are one contiguous 1 KB store.
+  // The 16 lanes of a lane group also reduce their row's max over the wave's
+  // 16 columns (one entry per 16-column group, for the top-k filter).
+  auto epilogue = [&](int gg, const f32x4 (&ac)[MT]) {
+    const int n = gg * GC + wave * 16 + lr;
+    const int ng = (a.N + 15) / 16, grp16 = gg * (GC / 16) + wave;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (transposed && n < a.N) *(f32x4*)(logits + (size_t)n * ROWS + mt * 16 + 4 * lg) = ac[mt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * lg + i;
+        const int bi = m % a.B, r0 = a.lm_first_row;
+        const bool row_ok = m < a.M && bi >= r0;
+        const size_t orow = (size_t)((m / a.B) * (a.B - r0) + bi - r0);
+        if (!transposed && row_ok && n < a.N) logits[orow * a.N + n] = ac[mt][i];
+        float v = n < a.N ? ac[mt][i] : -INFINITY;
+        v = fmaxf(v, __shfl_xor(v, 1, 64));
+        v = fmaxf(v, __shfl_xor(v, 2, 64));
+        v = fmaxf(v, __shfl_xor(v, 4, 64));
+        v = fmaxf(v, __shfl_xor(v, 8, 64));
+        if (row_ok && lr == 0 && grp16 < ng) gmax[orow * ng + grp16] = v;
+      }
+    }
+  };
+
   for (; g < n_groups; g += gridDim.x) {
     const int gnext = g + gridDim.x;
     const bool has_next = gnext < n_groups;
@@ -193,31 +226,25 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
       }
     }
     wcur = wnext;
-    // Logits: the caller's layout [R*(B-1)][N] (mask rows only), or the
-    // transposed scratch layout [N][16*MT] (every row), where a wave's 16
-    // columns x 16 rows of a tile are one contiguous 1 KB store.
-    // The 16 lanes of a lane group also reduce their row's max over the wave's
-    // 16 columns (one entry per 16-column group, for the top-k filter).
-    const int n = g * GC + wave * 16 + lr;
-    const int ng = (a.N + 15) / 16, grp16 = g * (GC / 16) + wave;
+    // A store here would hold up the next group's weight loads: vector loads and
+    // stores share one in-order counter, so every later load wait would include
+    // the store's write acknowledgement. The first nslots groups therefore park
+    // their fragments in LDS, and their epilogues run after the last load.
+    const int gi = (g - (int)blockIdx.x) / (int)gridDim.x;
+    if (gi < nslots) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (transposed && n < a.N) *(f32x4*)(logits + (size_t)n * ROWS + mt * 16 + 4 * lg) = acc[mt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + 4 * lg + i;
-        const int bi = m % a.B, r0 = a.lm_first_row;
-        const bool row_ok = m < a.M && bi >= r0;
-        const size_t orow = (size_t)((m / a.B) * (a.B - r0) + bi - r0);
-        if (!transposed && row_ok && n < a.N) logits[orow * a.N + n] = acc[mt][i];
-        float v = n < a.N ? acc[mt][i] : -INFINITY;
-        v = fmaxf(v, __shfl_xor(v, 1, 64));
-        v = fmaxf(v, __shfl_xor(v, 2, 64));
-        v = fmaxf(v, __shfl_xor(v, 4, 64));
-        v = fmaxf(v, __shfl_xor(v, 8, 64));
-        if (row_ok && lr == 0 && grp16 < ng) gmax[orow * ng + grp16] = v;
-      }
+      for (int mt = 0; mt < MT; ++mt) dslot[((size_t)(gi * NW + wave) * MT + mt) * 64 + lane] = acc[mt];
+    } else {
+      epilogue(g, acc);
     }
+  }
+  for (int gi = 0; gi < nslots; ++gi) {
+    const int gg = (int)blockIdx.x + gi * (int)gridDim.x;
+    if (gg >= n_groups) break;
+    f32x4 ac[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ac[mt] = dslot[((size_t)(gi * NW + wave) * MT + mt) * 64 + lane];
+    epilogue(gg, ac);
   }
 }
 
@@ -484,19 +511,24 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
 }
 
 template <int MT, int XL>
-hipError_t launch_lm(const GemmArgs& a, int groups, int P, size_t lds, float* logits, int tr, float* gmax,
-                     hipStream_t st) {
+hipError_t launch_lm(const GemmArgs& a, const LmPlan& p, float* logits, int tr, float* gmax, hipStream_t st) {
+  const int groups = p.groups, P = p.P, ns = p.slots, doff = p.defer_off;
+  const size_t lds = p.lds;
   const int nchunks = a.K / 128;
   if constexpr (XL == 2) {   // windows of 4 chunks
     if (nchunks % 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+    hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax, ns,
+                         doff);
   } else {
     if (nchunks % 4 == 0)
-      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 4>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax, ns,
+                         doff);
     else if (nchunks % 2 == 0)
-      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 2>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 2>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax, ns,
+                         doff);
     else
-      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 1>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax);
+      hipLaunchKernelGGL((lm_logits_kernel<MT, XL, 1>), dim3(P), dim3(512), lds, st, a, groups, logits, tr, gmax, ns,
+                         doff);
   }
   return hipGetLastError();
 }
@@ -514,6 +546,12 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   const size_t wbytes = (size_t)2 * rows * (4 * 128 + 8) * 2;  // two windows of 4 chunks
   p.XL = xbytes <= LM_XL_MAX_BYTES ? 1 : (K % 512 == 0 && wbytes <= LM_XL_MAX_BYTES ? 2 : 0);
   p.lds = p.XL == 1 ? xbytes : (p.XL == 2 ? wbytes : 0);
+  // LDS left over holds the deferred accumulator fragments (8 waves x MT x 1 KB per group)
+  p.defer_off = (int)((p.lds + 15) & ~(size_t)15);
+  const size_t slot_bytes = (size_t)8 * p.MT * 64 * 16;
+  const size_t room = LM_XL_MAX_BYTES > (size_t)p.defer_off ? LM_XL_MAX_BYTES - p.defer_off : 0;
+  p.slots = (int)std::min<size_t>((size_t)per, room / slot_bytes);
+  if (p.slots > 0) p.lds = p.defer_off + p.slots * slot_bytes;
   return p;
 }
 
@@ -528,9 +566,9 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
   if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
   hipError_t e;
 #define LM(MT)                                                                              \
-  e = p.XL == 1   ? launch_lm<MT, 1>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) \
-      : p.XL == 2 ? launch_lm<MT, 2>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st) \
-                  : launch_lm<MT, 0>(a, p.groups, p.P, p.lds, logits, transposed, gmax, st);
+  e = p.XL == 1   ? launch_lm<MT, 1>(a, p, logits, transposed, gmax, st) \
+      : p.XL == 2 ? launch_lm<MT, 2>(a, p, logits, transposed, gmax, st) \
+                  : launch_lm<MT, 0>(a, p, logits, transposed, gmax, st);
   switch (p.MT) {
     case 1: LM(1) break;
     case 2: LM(2) break;
