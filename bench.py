@@ -135,6 +135,30 @@ def verify_report(cfg, dev, n_layers: int = 36, steps: int = 20) -> dict:
     if word != 0:
         raise SystemExit(f"device error word 0x{word:x} in the verify pass")
     ms = e0.elapsed_time(e1) / steps
+    # the same pass replayed from a HIP graph: its ~430 dependent launches no
+    # longer wait on the host, whose launch rate differs between machines
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            tg.verify_block(tokens, tap_layers, taps)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            tg.verify_block(tokens, tap_layers, taps)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+        del g
+    except RuntimeError:
+        graph_ms = None
     layer_w = (tcfg.qkv_rows * H + H * tcfg.n_q_heads * hd + 3 * tcfg.ffn * H) * 2 + 4 * H * 2 + 2 * hd * 2
     kv = n_layers * 2 * tcfg.n_kv_heads * hd * 2
     nbytes = (n_layers * layer_w + tcfg.vocab * H * 2 + kv * (W + B) + kv * B + len(tap_layers) * B * H * 4
@@ -145,7 +169,9 @@ def verify_report(cfg, dev, n_layers: int = 36, steps: int = 20) -> dict:
     return {"target": f"{n_layers} layers of the drafter's shape (hidden {H}, {tcfg.n_q_heads}/{tcfg.n_kv_heads} "
                       f"heads x {hd}, ffn {tcfg.ffn}), vocab {tcfg.vocab}, causal",
             "rows": B, "context": W, "tap_layers": tap_layers, "ms": round(ms, 4), "bytes": int(nbytes),
-            "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "graph_ms": None if graph_ms is None else round(graph_ms, 4),
+            "graph_frac": None if graph_ms is None else round(nbytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def prefill_report(cfg, rows: int, ms: float) -> dict:
