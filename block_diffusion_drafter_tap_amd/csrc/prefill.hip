@@ -323,12 +323,14 @@ hipError_t launch_tap_gather(const TapGather& g, int M, hipStream_t st) {
 }
 
 int tile_bn(int M, int N, int n_cu) {
-  // the column tile that leaves the fewest idle slots in the last round of
-  // workgroups (2 per CU); 128 when equal
+  // the column tile with the shorter estimated time over rounds of workgroups
+  // (2 per CU); 128 when equal. A 128-wide tile takes about 1.2x the time of a
+  // 64-wide one (measured at fc 4096 x 2560 x 12800: 0.93 -> 0.84 ms for the
+  // prefill stage with 128), since both are bound by operand reads from L2.
   const int mt = (M + PF_BM - 1) / PF_BM, slots = 2 * n_cu;
   if (N % 128) return N % 64 ? 0 : 64;
   const long long t128 = (long long)mt * (N / 128), t64 = (long long)mt * (N / 64);
-  const double c128 = (double)((t128 + slots - 1) / slots) * 2.0;   // a 128-wide tile costs two 64-wide ones
+  const double c128 = (double)((t128 + slots - 1) / slots) * 1.25;
   const double c64 = (double)((t64 + slots - 1) / slots);
   return c64 < c128 ? 64 : 128;
 }
