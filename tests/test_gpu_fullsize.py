@@ -107,3 +107,46 @@ def test_qwen3_4b_context1024_argmax(big):
     _check_round(cfg, wh, [t.cpu().numpy() for t in taps], tokens[0].cpu().tolist(), P, 0, logits[0], ids[0],
                  "ctx1024")
     assert dr.check() == 0
+
+
+def test_hc_eight_requests_window4096_batched():
+    """The 8-request workload at its full size, in the launch configuration bench.py
+    times: qwen3-4b-shaped drafter fed by 4 hyper-connection streams per tap,
+    block 8, every request staging its own 4096-row context window, then one
+    batched draft (argmax). Requests 0 and 7 (different start positions, hence
+    different chunk alignments) are compared with the oracle's uncached
+    recompute of their own windows."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_tap_amd import binding
+    R, W = 8, 4096
+    cfg = config.qwen3_4b(block=8, window=W, max_requests=R, hc_streams=4, max_stage_rows=W)
+    B, V = cfg.block, cfg.vocab
+    print("case: qwen3-4b hc=4, block 8, 8 requests x 4096-row windows, argmax", flush=True)
+    w = synth.make_weights(cfg, seed=0, device="cuda")
+    dr = binding.Drafter(cfg, w)
+    starts = [W + 37 * r for r in range(R)]
+    keep = {}
+    for r in range(R):
+        taps = synth.make_taps(cfg, W, seed=20, device="cuda", stream=r, outliers=False)
+        ps = torch.arange(starts[r] - W, starts[r], dtype=torch.int32, device="cuda")
+        dr.reset(r, starts[r] - W, starts[r])
+        dr.tap_stage(taps, W, req_of_row=torch.full_like(ps, r), pos_of_row=ps)
+        if r in (0, R - 1):
+            keep[r] = [t.cpu().numpy() for t in taps]
+        del taps
+    tokens = synth.block_tokens(cfg, R, seed=21, device="cuda")
+    logits = torch.empty((R, B - 1, V), dtype=torch.float32, device="cuda")
+    ids = dr.draft_block(tokens, k=1, logits=logits)
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    wh = Hn.host_weights(w)
+    for r, th in keep.items():
+        # the oracle indexes taps by absolute position: rows before the window are never read
+        taps_h = [np.concatenate([np.zeros((starts[r] - W, t.shape[1])), t.astype(np.float64)], 0) for t in th]
+        ref = D.draft_block(cfg, wh, taps_h, tokens[r].cpu().tolist(), starts[r], starts[r] - W, mode="mirror")
+        g = logits[r].cpu().numpy()
+        err = Hn.assert_close(g, ref["logits"], f"request {r} logits")
+        comp, excl = Hn.topk_agrees_away_from_ties(ref["logits"], ids[r].cpu().numpy(), 1, gpu_logits=g)
+        print(f"request {r}: logits max err {err:.3g}; argmax compared {comp}, near-ties excluded {excl}", flush=True)
+        assert comp > 0
