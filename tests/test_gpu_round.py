@@ -211,3 +211,66 @@ def test_topk_exact_ties_tiny(tiny_setup):
     Hn.topk_self_consistent(g_logits, g_ids)
     np.testing.assert_array_equal(vals[0].cpu().numpy(), np.take_along_axis(g_logits, g_ids, 1))
     np.testing.assert_array_equal(ids1.cpu().numpy()[0, :, 0], g_ids[:, 0])
+
+
+def test_empty_and_oversized_calls_refused_before_any_launch(tiny_setup):
+    """Host validation on a bound handle: a staging call of 0 rows or of more rows
+    than the workspace holds, a draft of 0 or too many requests, a block length of
+    0 or above the configured block, k outside {1, 16}, and an accept of 0 or too
+    many requests are each refused with their status before anything is enqueued:
+    positions, the ring and the device error word are unchanged afterwards, and
+    the handle still drafts."""
+    binding, cfg, w, _ = tiny_setup
+    E_ARG, E_SHAPE, E_CAPACITY = -1, -3, -4
+    dr = binding.Drafter(cfg, w)
+    P, B = 20, cfg.block
+    taps = synth.make_taps(cfg, P, seed=5, device="cuda")
+    dr.reset(0, 0, P)
+    dr.tap_stage(taps, P, req_of_row=torch.zeros(P, dtype=torch.int32, device="cuda"),
+                 pos_of_row=torch.arange(P, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    pos0 = [t.clone() for t in dr.positions()]
+    ring0 = [t.clone() for t in dr.ring()]
+    tokens = synth.block_tokens(cfg, cfg.max_requests + 1, seed=6, device="cuda")
+    ids = torch.empty((cfg.max_requests + 1, B, 16), dtype=torch.int32, device="cuda")
+    verify = torch.ones((cfg.max_requests + 1, B), dtype=torch.int32, device="cuda")
+
+    def refused(fn, code, what):
+        with pytest.raises(binding.DFlashError) as ei:
+            fn()
+        assert ei.value.code == code, (what, ei.value)
+        print(f"{what}: {ei.value}", flush=True)
+
+    refused(lambda: dr.tap_stage(taps, 0, rows_per_req=1), E_SHAPE, "stage of 0 rows")
+    refused(lambda: dr.tap_stage(taps, cfg.max_stage_rows + 1, rows_per_req=1), E_CAPACITY,
+            "stage beyond max_stage_rows")
+    # counts of zero go straight through the C ABI with live buffers, so that the
+    # count check decides (an empty tensor's null pointer is refused first, E_ARG)
+    lib, ctx, st = dr.lib, dr.ctx, binding._stream()
+    rc = lib.dflash_draft_block(ctx, st, tokens.data_ptr(), 0, None, ids.data_ptr(), None, 1)
+    assert rc == E_SHAPE, ("draft of 0 requests", rc)
+    rc = lib.dflash_draft_block_n(ctx, st, tokens.data_ptr(), 1, 0, None, ids.data_ptr(), None, 1)
+    assert rc == E_SHAPE, ("block length 0", rc)
+    refused(lambda: dr.draft_block(tokens[:0], k=1, ids=ids), E_ARG, "draft with a null token pointer")
+    refused(lambda: dr.draft_block(tokens, k=1, ids=ids), E_SHAPE, "draft beyond max_requests")
+    wide = torch.cat([tokens[:1], tokens[:1, :1]], 1).contiguous()
+    refused(lambda: dr.draft_block_n(wide, k=1, ids=ids), E_SHAPE, "block length above the block")
+    refused(lambda: dr.draft_block(tokens[:1].contiguous(), k=3, ids=ids), E_ARG, "k = 3")
+    Rx = cfg.max_requests + 1
+    out = {"accept_len": torch.empty(Rx, dtype=torch.int32, device="cuda"),
+           "emitted": torch.empty((Rx, B), dtype=torch.int32, device="cuda"),
+           "n_emit": torch.empty(Rx, dtype=torch.int32, device="cuda"),
+           "next_tokens": torch.empty((Rx, B), dtype=torch.int32, device="cuda")}
+    rc = lib.dflash_accept(ctx, st, ids.data_ptr(), 16, verify.data_ptr(), 0, -1, None, out["accept_len"].data_ptr(),
+                           out["emitted"].data_ptr(), out["n_emit"].data_ptr(), out["next_tokens"].data_ptr())
+    assert rc == E_SHAPE, ("accept of 0 requests", rc)
+    refused(lambda: dr.accept(ids, 16, verify, out=out), E_SHAPE, "accept beyond max_requests")
+    torch.cuda.synchronize()
+    for a, b in zip(dr.positions(), pos0):
+        assert torch.equal(a, b)
+    for a, b in zip(dr.ring(), ring0):
+        assert torch.equal(a, b)
+    assert dr.check() == 0
+    got = dr.draft_block(tokens[:1].contiguous(), k=1)
+    torch.cuda.synchronize()
+    assert dr.check() == 0 and got.shape == (1, B - 1, 1)
