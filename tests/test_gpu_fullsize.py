@@ -150,3 +150,27 @@ def test_hc_eight_requests_window4096_batched():
         comp, excl = Hn.topk_agrees_away_from_ties(ref["logits"], ids[r].cpu().numpy(), 1, gpu_logits=g)
         print(f"request {r}: logits max err {err:.3g}; argmax compared {comp}, near-ties excluded {excl}", flush=True)
         assert comp > 0
+
+
+def test_qwen3_4b_block8_window4096_top16(big):
+    """The block-8 workload at its full size: the same drafter, one request, the
+    trailing 4096 rows of a 16384-row tap buffer staged, one draft of 7 mask rows
+    with top-16, against the oracle."""
+    binding, cfg0, w, wh = big
+    cfg = cfg0.replace(block=8, ring_capacity=config.ring_for(4096, 8))
+    B, V, W = cfg.block, cfg.vocab, cfg.window
+    print("case: qwen3-4b-shaped B=8 W=4096 top-16, prefill from a 16384-row buffer", flush=True)
+    dr = binding.Drafter(cfg, w)
+    total = 16384
+    taps = synth.make_taps(cfg, total, seed=11, device="cuda")
+    dr.reset(0, total - W, total)
+    dr.tap_stage([t[total - W:] for t in taps], W,
+                 req_of_row=torch.zeros(W, dtype=torch.int32, device="cuda"),
+                 pos_of_row=torch.arange(total - W, total, dtype=torch.int32, device="cuda"))
+    tokens = synth.block_tokens(cfg, 1, seed=12, device="cuda")
+    logits = torch.empty((1, B - 1, V), dtype=torch.float32, device="cuda")
+    ids = dr.draft_block(tokens, k=16, logits=logits)
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    hist = [t.cpu().numpy() for t in taps]
+    _check_round(cfg, wh, hist, tokens[0].cpu().tolist(), total, total - W, logits[0], ids[0], "block 8")
