@@ -180,7 +180,9 @@ def ctx_hidden(cfg, W, taps: Sequence, lo: int, hi: int, mode: str = "mirror") -
     them to its hidden size): x_p = concat_t hc_mean(tap_t[p]), cast to bf16;
     c_p = W_fc x_p; with ``ctx_norm`` an RMSNorm with gain ``ctx_norm`` follows
     (reading: off by default, the pages name only the projection); c is cast to
-    bf16. ``taps[t]`` is indexed by absolute position.
+    bf16. ``taps[t]`` is indexed by absolute position. Pinned by the scalar
+    brute force (hc 1 and 4, ctx norm on and off), by linearity and by one-hot
+    tap columns.
     """
     rnd = _rnd(mode)
     parts = [hc_mean(np.asarray(taps[t])[lo:hi], cfg.hc_streams, cfg.tap_hidden)
@@ -240,6 +242,12 @@ def draft_block(cfg, W, taps: Sequence, tokens, pos: int, valid_from: int = 0,
 
     Returns a dict with ``logits`` [B-1, V], ``z`` [B, H] and, when
     ``want_intermediates``, ``h`` [B, H] and per-layer ``ctx_k``/``ctx_v``.
+
+    Pinned by a scalar brute force written with loops and its own bf16 rounding
+    (exact and mirror modes, 1 or 4 hc streams, ctx norm on and off; every cast
+    point checked to matter), and by the invariants the pages fix
+    (bidirectional block, sliding window, rope offset, GQA = MHA, context
+    length 0 = textbook attention).
     """
     rnd = _rnd(mode)
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -283,11 +291,6 @@ def draft_block(cfg, W, taps: Sequence, tokens, pos: int, valid_from: int = 0,
         inter["h"] = h
         out.update(inter)
     return out
-
-
-def logits_rows(cfg, W, z_rows) -> np.ndarray:
-    """LM head on selected normed rows (for sampled full-size checks)."""
-    return _f64(z_rows) @ _f64(W["lm_head"]).T
 
 
 # ----------------------------------------------------------------------------- selection

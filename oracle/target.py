@@ -57,7 +57,9 @@ class TinyTarget:
         return self.k[0].shape[0]
 
     def _row(self, token: int, position: int):
-        """One causal step: appends this row's K/V, returns (logits [V], taps [L][H])."""
+        """One causal step: appends this row's K/V, returns (logits [V], taps [L][H]).
+        Pinned, in exact and mirror modes, by a scalar causal decoder written with
+        loops (row i attends to rows 0..i at positions 0..i)."""
         cfg, W = self.cfg, self.W
         nq, nkv, hd, eps = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps
         assert position == self.length

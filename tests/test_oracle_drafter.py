@@ -29,92 +29,6 @@ def tiny():
     return cfg, W, taps
 
 
-def _brute_draft(cfg, W, taps, tokens, pos, valid_from):
-    """Independent scalar-loop statement of one draft block (exact fp64)."""
-    H, nq, nkv, hd, F = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn
-    eps = cfg.rms_eps
-    B = len(tokens)
-    lo = max(valid_from, pos - cfg.window, 0)
-    ctx = list(range(lo, pos))
-
-    def norm(vec, g):
-        ms = sum(x * x for x in vec) / len(vec)
-        r = 1.0 / math.sqrt(ms + eps)
-        return [g[i] * vec[i] * r for i in range(len(vec))]
-
-    def matvec(Wm, vec, r0, r1):
-        return [sum(Wm[r][c] * vec[c] for c in range(len(vec))) for r in range(r0, r1)]
-
-    def rot(vec, p):
-        half = hd // 2
-        out = list(vec)
-        for k in range(half):
-            a = p * cfg.rope_theta ** (-2.0 * k / hd)
-            z = complex(vec[k], vec[k + half]) * complex(math.cos(a), math.sin(a))
-            out[k], out[k + half] = z.real, z.imag
-        return out
-
-    # context hidden
-    cvec = []
-    for p in ctx:
-        x = []
-        for t in range(cfg.n_taps):
-            x.extend(taps[t][p][:cfg.tap_hidden])
-        cvec.append(matvec(W["fc"], x, 0, H))
-    h = [list(W["embed"][t]) for t in tokens]
-    for l in range(cfg.n_layers):
-        wqkv = W["wqkv"][l]
-        qoff, koff, voff = 0, nq * hd, (nq + nkv) * hd
-        K = [[None] * (len(ctx) + B) for _ in range(nkv)]
-        Vv = [[None] * (len(ctx) + B) for _ in range(nkv)]
-        for n, p in enumerate(ctx):
-            for g in range(nkv):
-                K[g][n] = rot(norm(matvec(wqkv, cvec[n], koff + g * hd, koff + (g + 1) * hd), W["k_norm"][l]), p)
-                Vv[g][n] = matvec(wqkv, cvec[n], voff + g * hd, voff + (g + 1) * hd)
-        a = [norm(h[i], W["ln_in"][l]) for i in range(B)]
-        Q = [[None] * B for _ in range(nq)]
-        for i in range(B):
-            for j in range(nq):
-                Q[j][i] = rot(norm(matvec(wqkv, a[i], qoff + j * hd, qoff + (j + 1) * hd), W["q_norm"][l]), pos + i)
-            for g in range(nkv):
-                K[g][len(ctx) + i] = rot(norm(matvec(wqkv, a[i], koff + g * hd, koff + (g + 1) * hd), W["k_norm"][l]), pos + i)
-                Vv[g][len(ctx) + i] = matvec(wqkv, a[i], voff + g * hd, voff + (g + 1) * hd)
-        for i in range(B):
-            o = []
-            for j in range(nq):
-                g = j // (nq // nkv)
-                s = [sum(Q[j][i][d] * K[g][t][d] for d in range(hd)) / math.sqrt(hd) for t in range(len(K[g]))]
-                m = max(s)
-                e = [math.exp(x - m) for x in s]
-                o.extend(sum(e[t] * Vv[g][t][d] for t in range(len(e))) / sum(e) for d in range(hd))
-            y = matvec(W["wo"][l], o, 0, H)
-            h[i] = [h[i][c] + y[c] for c in range(H)]
-            a2 = norm(h[i], W["ln_post"][l])
-            gate = matvec(W["wgu"][l], a2, 0, F)
-            up = matvec(W["wgu"][l], a2, F, 2 * F)
-            act = [gate[f] / (1 + math.exp(-gate[f])) * up[f] for f in range(F)]
-            y = matvec(W["wd"][l], act, 0, H)
-            h[i] = [h[i][c] + y[c] for c in range(H)]
-    z = [norm(h[i], W["final_norm"]) for i in range(B)]
-    return np.array(z)
-
-
-@pytest.mark.slow
-def test_draft_block_matches_scalar_brute_force():
-    # a still smaller drafter so pure-Python loops finish quickly
-    cfg = config.tiny(block=3, window=5).replace(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8,
-                                                   ffn=48, vocab=64, tap_hidden=32, mask_id=63)
-    W = {k: ([t.astype(np.float64) for t in v] if isinstance(v, list) else v.astype(np.float64))
-         for k, v in _np_weights(synth.make_weights(cfg, seed=3)).items()}
-    W["embed"] = W["embed"] * 20.0        # make the residual stream large enough to matter
-    taps = [t.numpy().astype(np.float64) for t in synth.make_taps(cfg, 12, seed=3, outliers=False)]
-    tokens = [7, 63, 63]
-    for pos, vf in ((9, 0), (9, 6), (0, 0), (3, 3)):
-        got = D.draft_block(cfg, W, taps, tokens, pos, vf, mode="exact")["z"]
-        ref = _brute_draft(cfg, W, taps, tokens, pos, vf)
-        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
-
-
 def test_block_is_bidirectional(tiny):
     cfg, W, taps = tiny
     base = [11] + [cfg.mask_id] * (cfg.block - 1)
