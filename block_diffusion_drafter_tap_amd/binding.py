@@ -141,6 +141,37 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(t, name: str, dtype, shape=None, min_rows=None, optional: bool = False):
+    """Checks a tensor argument before any pointer of it reaches the library, which
+    cannot check sizes itself: dtype, exact shape (or at least ``min_rows`` rows)
+    and a dense layout. Raises ValueError. ``_on_device`` checks the device after
+    every argument's shape has been checked."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if min_rows is not None and (t.dim() < 1 or t.shape[0] < min_rows):
+        raise ValueError(f"{name} must have at least {min_rows} rows (got {tuple(t.shape)})")
+    if shape is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(**tensors):
+    for name, t in tensors.items():
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
+            raise ValueError(f"{name} must be a device (cuda) tensor")
+        if isinstance(t, (list, tuple)):
+            for i, u in enumerate(t):
+                if isinstance(u, torch.Tensor) and not u.is_cuda:
+                    raise ValueError(f"{name}[{i}] must be a device (cuda) tensor")
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -212,10 +243,27 @@ class Drafter:
                   rows_per_req: int = 0, ptrs: Optional[Sequence[int]] = None):
         """taps: n_taps fp32 tensors whose first row is staged row 0 (or raw
         pointers in ``ptrs``); row_stride defaults to the tensors' row stride."""
-        if ptrs is None:
+        c = self.cfg
+        width = c.hc_streams * c.tap_hidden
+        from_tensors = ptrs is None
+        if from_tensors:
+            if len(taps) != c.n_taps:
+                raise ValueError(f"taps: expected {c.n_taps} tensors (got {len(taps)})")
+            for i, t in enumerate(taps):
+                _need(t, f"taps[{i}]", torch.float32, min_rows=n_rows)
+                if t.dim() != 2 or t.shape[1] < width or t.stride(1) != 1:
+                    raise ValueError(f"taps[{i}] must be [rows, >= {width}] with unit column stride")
             ptrs = [t.data_ptr() for t in taps]
             if row_stride is None:
                 row_stride = taps[0].stride(0)
+            if any(t.stride(0) != row_stride for t in taps):
+                raise ValueError("every tap tensor must have the row stride of the call")
+        elif len(ptrs) != c.n_taps:
+            raise ValueError(f"ptrs: expected {c.n_taps} pointers (got {len(ptrs)})")
+        _need(req_of_row, "req_of_row", torch.int32, shape=(n_rows,), optional=True)
+        _need(pos_of_row, "pos_of_row", torch.int32, shape=(n_rows,), optional=True)
+        _on_device(taps=list(taps) if from_tensors else [], req_of_row=req_of_row,
+                   pos_of_row=pos_of_row)
         arr = (c_void_p * len(ptrs))(*ptrs)
         _check("dflash_tap_stage", self.lib.dflash_tap_stage(
             self.ctx, _stream(), ctypes.cast(arr, PP), int(row_stride), int(n_rows), _ptr(req_of_row),
@@ -225,6 +273,7 @@ class Drafter:
                     ids: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None):
         R = block_tokens.shape[0]
         Bm1 = max(self.cfg.block - 1, 1)
+        self._check_draft(block_tokens, self.cfg.block, k, logits, ids, vals)
         if ids is None:
             ids = torch.empty((R, Bm1, k), dtype=torch.int32, device=self.device)
         _check("dflash_draft_block", self.lib.dflash_draft_block(
@@ -235,16 +284,51 @@ class Drafter:
                       ids: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None):
         """draft_block with the block length of this call = block_tokens.shape[1]."""
         R, b = block_tokens.shape
+        self._check_draft(block_tokens, b, k, logits, ids, vals)
         if ids is None:
             ids = torch.empty((R, max(b - 1, 1), k), dtype=torch.int32, device=self.device)
         _check("dflash_draft_block_n", self.lib.dflash_draft_block_n(
             self.ctx, _stream(), block_tokens.data_ptr(), R, int(b), _ptr(logits), ids.data_ptr(), _ptr(vals), k))
         return ids
 
+    def _check_draft(self, block_tokens, b, k, logits, ids, vals):
+        if not isinstance(block_tokens, torch.Tensor) or block_tokens.dim() != 2:
+            raise ValueError("block_tokens must be an int32 tensor [R, block]")
+        R = block_tokens.shape[0]
+        _need(block_tokens, "block_tokens", torch.int32, shape=(R, b))
+        bm1 = max(b - 1, 1)
+        _need(logits, "logits", torch.float32, shape=(R, bm1, self.cfg.vocab), optional=True)
+        _need(ids, "ids", torch.int32, shape=(R, bm1, k), optional=True)
+        _need(vals, "vals", torch.float32, shape=(R, bm1, k), optional=True)
+        _on_device(block_tokens=block_tokens, logits=logits, ids=ids, vals=vals)
+
+    def _check_accept(self, draft_ids, draft_stride, verify_ids, b, budget, out):
+        if not isinstance(verify_ids, torch.Tensor) or verify_ids.dim() != 2:
+            raise ValueError("verify_ids must be an int32 tensor [R, block]")
+        R = verify_ids.shape[0]
+        _need(verify_ids, "verify_ids", torch.int32, shape=(R, b))
+        if b > 1 or draft_ids is not None:
+            # element (r, j) at (r * (b-1) + j) * draft_stride: [R, b-1] for stride 1, or
+            # [R, b-1, k] top-k ids with stride k
+            n = R * max(b - 1, 1) * int(draft_stride)
+            _need(draft_ids, "draft_ids", torch.int32)
+            if draft_ids.numel() != n or not draft_ids.is_contiguous() or draft_ids.shape[0] != R:
+                raise ValueError(f"draft_ids must be a dense [{R}, {max(b - 1, 1)}(, {draft_stride})] tensor "
+                                 f"(got {tuple(draft_ids.shape)})")
+        _need(budget, "budget", torch.int32, shape=(R,), optional=True)
+        if out is not None:
+            _need(out.get("accept_len"), "out['accept_len']", torch.int32, shape=(R,))
+            _need(out.get("emitted"), "out['emitted']", torch.int32, shape=(R, b))
+            _need(out.get("n_emit"), "out['n_emit']", torch.int32, shape=(R,))
+            _need(out.get("next_tokens"), "out['next_tokens']", torch.int32, shape=(R, b), optional=True)
+        _on_device(verify_ids=verify_ids, draft_ids=draft_ids, budget=budget,
+                   out=[] if out is None else [v for v in out.values() if v is not None])
+
     def accept(self, draft_ids: torch.Tensor, draft_stride: int, verify_ids: torch.Tensor, eos_id: int = -1,
                budget: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None):
-        R = verify_ids.shape[0]
         B = self.cfg.block
+        self._check_accept(draft_ids, draft_stride, verify_ids, B, budget, out)
+        R = verify_ids.shape[0]
         if out is None:
             out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
                    "emitted": torch.empty((R, B), dtype=torch.int32, device=self.device),
@@ -260,6 +344,7 @@ class Drafter:
                  eos_id: int = -1, budget: Optional[torch.Tensor] = None):
         """accept for a round of block length verify_ids.shape[1]."""
         R, b = verify_ids.shape
+        self._check_accept(draft_ids, draft_stride, verify_ids, b, budget, None)
         out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
                "emitted": torch.empty((R, b), dtype=torch.int32, device=self.device),
                "n_emit": torch.empty(R, dtype=torch.int32, device=self.device),
@@ -275,6 +360,15 @@ class Drafter:
         """Verify pass of a target handle: argmax ids [R, b]; the residual rows after
         the tapped layers are written into tap_out (fp32 [R*b, >= hidden])."""
         R, b = block_tokens.shape
+        _need(block_tokens, "block_tokens", torch.int32, shape=(R, b))
+        _need(logits, "logits", torch.float32, shape=(R, b, self.cfg.vocab), optional=True)
+        if len(tap_out) != len(tap_layers):
+            raise ValueError("tap_out and tap_layers must have the same length")
+        for i, t in enumerate(tap_out):
+            _need(t, f"tap_out[{i}]", torch.float32, min_rows=R * b)
+            if t.dim() != 2 or t.shape[1] < self.cfg.hidden or t.stride(1) != 1 or t.stride(0) != tap_out[0].stride(0):
+                raise ValueError(f"tap_out[{i}] must be [rows, >= hidden] with one row pitch for all taps")
+        _on_device(block_tokens=block_tokens, logits=logits, tap_out=list(tap_out))
         ids = torch.empty((R, b), dtype=torch.int32, device=self.device)
         n = len(tap_layers)
         layers = (ctypes.c_int * max(n, 1))(*tap_layers)
@@ -286,6 +380,8 @@ class Drafter:
         return ids
 
     def advance(self, n_emit: torch.Tensor):
+        _need(n_emit, "n_emit", torch.int32, shape=(n_emit.numel(),) if isinstance(n_emit, torch.Tensor) else None)
+        _on_device(n_emit=n_emit)
         _check("dflash_advance", self.lib.dflash_advance(self.ctx, _stream(), n_emit.data_ptr(), n_emit.numel()))
 
     def check(self) -> int:

@@ -257,6 +257,7 @@ GemmArgs base_args(const dflash_ctx* c) {
   a.eps = g.rms_eps;
   a.log2_theta = log2((double)g.rope_theta);
   a.C = g.ring_capacity;
+  a.win = g.window;
   a.Rmax = g.max_requests;
   a.pos = at<int>(c->state, c->sl.pos);
   a.err = at<unsigned>(c->state, c->sl.error);

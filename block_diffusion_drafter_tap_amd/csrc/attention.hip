@@ -48,7 +48,7 @@ DEV Range key_range(const AttnArgs& a, int r, bool report) {
   const int pos = a.pos[r];
   int vf = a.valid_from[r];
   if (vf > pos) {
-    if (report) set_error(a.err, 2u);
+    if (report) set_error(a.err, ERR_BAD_WINDOW);
     vf = pos;
   }
   int lo = pos - a.W;

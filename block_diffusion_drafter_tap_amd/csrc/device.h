@@ -52,45 +52,34 @@ DEV T pick(const T (&arr)[N], int i) {
   return r;
 }
 
-// (value desc, index asc) ordering used by argmax / top-k.
-DEV bool better(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
-
-// Rank-merge tree over sorted top-K lists held in LDS. Lists 0..width-1 (width a
-// power of two) live in bv/bi[0]; every entry is (value, id) with all ids
-// distinct, lists sorted best first. A pair of lists merges in one parallel
-// step: entry A[e] lands at rank e + #{entries of B better than A[e]} (binary
-// search), likewise for B, and only ranks below K are kept. Returns the buffer
-// (0 or 1) whose list 0 holds the merged result. All threads of the block call it.
-template <int K, int L>
-DEV int merge_tree(float (*bv)[L][K], int (*bi)[L][K], int width) {
-  int cur = 0;
-  for (; width > 1; width >>= 1) {
-    const int pairs = width / 2;
-    for (int t = threadIdx.x; t < pairs * 2 * K; t += blockDim.x) {
-      const int p = t / (2 * K), e = t % (2 * K);
-      const int own = e < K ? 2 * p : 2 * p + 1, oth = e < K ? 2 * p + 1 : 2 * p;
-      const int idx = e < K ? e : e - K;
-      const float x = bv[cur][own][idx];
-      const int xi = bi[cur][own][idx];
-      int lo = 0, hi = K;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (better(bv[cur][oth][mid], bi[cur][oth][mid], x, xi)) lo = mid + 1; else hi = mid;
-      }
-      const int rank = idx + lo;
-      if (rank < K) {
-        bv[cur ^ 1][p][rank] = x;
-        bi[cur ^ 1][p][rank] = xi;
-      }
-    }
-    __syncthreads();
-    cur ^= 1;
-  }
-  return cur;
-}
+// Bits of the sticky device error word (the values of include/dflash.h).
+constexpr unsigned ERR_BAD_TOKEN = 1u, ERR_BAD_WINDOW = 2u, ERR_BAD_ROW = 4u, ERR_BAD_POSITION = 8u,
+                   ERR_RING_CAPACITY = 16u;
 
 DEV void set_error(unsigned* err, unsigned bit) {
   if (err) atomicOr(err, bit);
+}
+
+// Request and absolute position of row m of a call that writes K/V rows into
+// the ring (a tap stage, or a block's own rows): the request is req_of_row[m]
+// or m / rows_per_req, the position pos_of_row[m] or pos[req] + m %
+// rows_per_req. Returns 0, or the error bit of a row that must be skipped: a
+// request outside [0, Rmax), a negative position, or a position whose ring
+// slot holds another live row of the request. The live positions are the
+// window and the block, [pos - W, pos + B) with C >= W + B, so a row at p may
+// use slot p mod C only for p in [pos + B - C, pos + C - W).
+template <class A>
+DEV unsigned ring_row(const A& a, int m, int* req, long long* p) {
+  const int r = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
+  *req = r;
+  *p = -1;
+  if (r < 0 || r >= a.Rmax) return ERR_BAD_ROW;
+  const long long base = a.pos[r];
+  const long long q = a.pos_of_row ? (long long)a.pos_of_row[m] : base + m % a.rows_per_req;
+  if (q < 0) return ERR_BAD_POSITION;
+  if (q < base + a.B - a.C || q >= base + a.C - a.win) return ERR_RING_CAPACITY;
+  *p = q;
+  return 0u;
 }
 
 // RoPE. The frequency of pair d, theta^(-2d/hd), is computed in fp64, and so is

@@ -102,12 +102,11 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
   const float s1 = sum_splits(P, S, stride, base + (on ? lane : 0));
   const float s2 = sum_splits(P, S, stride, base + (on ? lane + half : 0));
   const float x1 = on ? s1 : 0.f, x2 = on ? s2 : 0.f;
-  const int req = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
-  long long p = -1;
-  if (req >= 0 && req < a.Rmax)
-    p = a.pos_of_row ? (long long)a.pos_of_row[m] : (long long)a.pos[req] + m % a.rows_per_req;
-  if (p < 0) {
-    if (lane == 0) set_error(a.err, req < 0 || req >= a.Rmax ? 4u : 8u);
+  int req;
+  long long p;
+  const unsigned bad = ring_row(a, m, &req, &p);
+  if (bad) {
+    if (lane == 0) set_error(a.err, bad);
     return;
   }
   const bool is_q = head < a.nq, is_k = !is_q && head < a.nq + a.nkv;

@@ -98,17 +98,6 @@ DEV u32x4 load_x(const GemmArgs& a, int row, int k, float inv) {
   }
 }
 
-// Row -> (request, absolute position) for E_HEAD.
-DEV void row_info(const GemmArgs& a, int m, int* req, long long* p) {
-  int r = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
-  *req = r;
-  if (r < 0 || r >= a.Rmax) {
-    *p = -1;
-    return;
-  }
-  *p = a.pos_of_row ? (long long)a.pos_of_row[m] : (long long)a.pos[r] + m % a.rows_per_req;
-}
-
 template <int GC, int NW>
 DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, int head) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -118,9 +107,9 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
     const int m = m0 + r;
     int req;
     long long p;
-    row_info(a, m, &req, &p);
-    if (p < 0) {
-      if (lane == 0) set_error(a.err, req < 0 || req >= a.Rmax ? 4u : 8u);
+    const unsigned bad = ring_row(a, m, &req, &p);
+    if (bad) {
+      if (lane == 0) set_error(a.err, bad);
       continue;
     }
     if (is_q || is_k) {

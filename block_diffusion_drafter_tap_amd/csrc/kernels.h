@@ -58,13 +58,16 @@ struct GemmArgs {
   uint16_t* ring_k;   // this layer's [Rmax][nkv][C][hd]
   uint16_t* ring_v;   // this layer's [Rmax][nkv][hd][C]
   int C, Rmax;
+  int win;                // window W: staged rows are checked against the ring's live range
   const int* pos;         // state pos[]
   const int* req_of_row;  // NULL -> row / rows_per_req
   const int* pos_of_row;  // NULL -> pos[req] + row % rows_per_req
   int rows_per_req;
   unsigned* err;
-  // LM head: rows m = r*B + i; rows i >= lm_first_row produce logits (1: the
-  // mask rows of a draft; 0: every row of a verify pass)
+  // B: the configured block (the ring's live range is [pos - win, pos + B)),
+  // except for the LM head, where it is the call's block length. LM head: rows
+  // m = r*B + i; rows i >= lm_first_row produce logits (1: the mask rows of a
+  // draft; 0: every row of a verify pass)
   int B, topk, lm_first_row;
 };
 
@@ -177,8 +180,6 @@ hipError_t launch_embed(const int* tokens, const uint16_t* embed, float* h, floa
 hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* a, int M, int H,
                           float eps, hipStream_t st);
 hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hipStream_t st);
-hipError_t launch_topk_final(const float* list_v, const int* list_i, int n_lists, int rows, int k, int* ids,
-                             float* vals, hipStream_t st);
 hipError_t launch_accept(const int* draft, int draft_stride, const int* verify, int R, int B, int stats_b,
                          int eos, const int* budget, int mask_id, int* accept_len,
                          int* emitted, int* n_emit, int* next_tokens, int* pos,

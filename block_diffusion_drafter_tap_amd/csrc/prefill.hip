@@ -51,14 +51,6 @@ __global__ __launch_bounds__(256) void tap_gather_kernel(const TapGather g) {
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_HEADS = 2 };
 
-// Row -> (request, absolute position) of a staged row; p < 0 flags a bad row.
-DEV void staged_row(const GemmArgs& h, int m, int* req, long long* p) {
-  const int r = h.req_of_row ? h.req_of_row[m] : m / h.rows_per_req;
-  *req = r;
-  *p = (r < 0 || r >= h.Rmax) ? -1
-       : (h.pos_of_row ? (long long)h.pos_of_row[m] : (long long)h.pos[r] + m % h.rows_per_req);
-}
-
 // OUT_HEADS: the tile's columns are whole context K heads (k RMSNorm over the
 // head, RoPE at the row's position, rows into the K ring) or V heads (into the
 // transposed V ring, 64 consecutive rows of one dimension per wave store).
@@ -255,8 +247,8 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
     for (int r = tid; r < rows; r += 256) {
       int req;
       long long p;
-      staged_row(h, m0 + r, &req, &p);
-      if (p < 0) set_error(h.err, req < 0 || req >= h.Rmax ? 4u : 8u);
+      const unsigned bad = ring_row(h, m0 + r, &req, &p);
+      if (bad) set_error(h.err, bad);
       s_req[r] = req;
       s_pos[r] = p < 0 ? -1 : (int)p;
     }

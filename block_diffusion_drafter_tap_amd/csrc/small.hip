@@ -1,6 +1,5 @@
 // Latency-bound kernels of the drafter round: state fill, embedding gather with
-// the first RMSNorm, RMSNorm, position set, the final top-k merge and
-// first-mismatch accept.
+// the first RMSNorm, RMSNorm, position set and first-mismatch accept.
 #include "device.h"
 #include "kernels.h"
 
@@ -59,7 +58,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, const uin
   const int m = blockIdx.x;
   int tok = tokens[m];
   if (tok < 0 || tok >= V) {
-    if (threadIdx.x == 0) set_error(err, 1u);
+    if (threadIdx.x == 0) set_error(err, ERR_BAD_TOKEN);
     tok = 0;
   }
   const uint16_t* e = embed + (size_t)tok * H;
@@ -90,41 +89,6 @@ __global__ void set_pos_kernel(int* pos, int* valid_from, int req, int vf, int p
   if (threadIdx.x == 0) {
     pos[req] = p;
     valid_from[req] = vf;
-  }
-}
-
-// Top-k merge of up to 64 candidate lists of one row per workgroup (sorted best
-// first by (value desc, index asc), all keys distinct) with the rank-merge tree.
-// List l of row r is read at in + (l * list_stride + r * row_stride) * K.
-// Missing lists are padded with -inf entries carrying distinct ids.
-template <int K>
-__global__ __launch_bounds__(256) void topk_merge_kernel(const float* in_v, const int* in_i, int n_lists,
-                                                         long long list_stride, long long row_stride,
-                                                         float* out_v, int* out_i, long long out_row_stride) {
-  __shared__ float bv[2][64][K];
-  __shared__ int bi[2][64][K];
-  const int row = blockIdx.x, blk = blockIdx.y;
-  const int l0 = blk * 64;
-  const int nl = min(64, n_lists - l0);
-  int width = 1;
-  while (width < nl) width <<= 1;
-  for (int e = threadIdx.x; e < width * K; e += blockDim.x) {
-    const int l = e / K, j = e % K;
-    if (l < nl) {
-      const size_t o = ((size_t)(l0 + l) * list_stride + (size_t)row * row_stride) * K + j;
-      bv[0][l][j] = in_v[o];
-      bi[0][l][j] = in_i[o];
-    } else {
-      bv[0][l][j] = -INFINITY;
-      bi[0][l][j] = 0x7fffffff - e;
-    }
-  }
-  __syncthreads();
-  const int cur = merge_tree<K, 64>(bv, bi, width);
-  if ((int)threadIdx.x < K) {
-    const size_t o = (size_t)row * out_row_stride + (size_t)blk * K + threadIdx.x;
-    if (out_v) out_v[o] = bv[cur][0][threadIdx.x];
-    out_i[o] = bi[cur][0][threadIdx.x];
   }
 }
 
@@ -224,21 +188,6 @@ hipError_t launch_rmsnorm(const float* h, const uint16_t* gain, uint16_t* a, int
 
 hipError_t launch_set_pos(int* pos, int* valid_from, int req, int vf, int p, hipStream_t st) {
   hipLaunchKernelGGL(set_pos_kernel, dim3(1), dim3(64), 0, st, pos, valid_from, req, vf, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_final(const float* list_v, const int* list_i, int n_lists, int rows, int k, int* ids,
-                             float* vals, hipStream_t st) {
-  if (n_lists > 64) return hipErrorInvalidValue;
-  // lists [rows][n_lists][k] -> ids/vals [rows][k]
-  if (k == 1)
-    hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(rows, 1), dim3(256), 0, st, list_v, list_i, n_lists, 1ll,
-                       (long long)n_lists, vals, ids, 1ll);
-  else if (k == 16)
-    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(rows, 1), dim3(256), 0, st, list_v, list_i, n_lists, 1ll,
-                       (long long)n_lists, vals, ids, 16ll);
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

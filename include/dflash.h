@@ -67,7 +67,16 @@ enum {
   DFLASH_DEV_BAD_TOKEN = 1,      /* a block token outside [0, vocab): row 0 of embed used */
   DFLASH_DEV_BAD_WINDOW = 2,     /* valid_from > pos: the context is treated as empty      */
   DFLASH_DEV_BAD_ROW = 4,        /* a staged row names a request outside [0, max_requests) */
-  DFLASH_DEV_BAD_POSITION = 8    /* a negative position: the row is skipped                */
+  DFLASH_DEV_BAD_POSITION = 8,   /* a negative position: the row is skipped                */
+  /* A K/V row (staged, or a block's own) whose ring slot belongs to another live
+   * row of its request: the live positions are the window and the block,
+   * [pos - window, pos + block), so a row at p is written only if
+   * pos + block - ring_capacity <= p < pos + ring_capacity - window (pos = the
+   * request's state position at the time of the call). Outside that range the
+   * row is skipped and the ring is left as it was. The capacity bound is a hard
+   * bound ("[RFC] DFlash", ExecuTorch PR #20840, author's reply on the draft
+   * cache's capacity). */
+  DFLASH_DEV_RING_CAPACITY = 16
 };
 
 /*

@@ -75,3 +75,35 @@ def topk_agrees_away_from_ties(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k
             else:
                 excluded += 1
     return compared, excluded
+
+
+def topk_within_eps(oracle_logits: np.ndarray, gpu_ids: np.ndarray, gpu_logits: np.ndarray):
+    """Every rank, near-ties included: the oracle's logit of the id the GPU put at
+    rank j lies within 2 * eps_row of the oracle's rank-j value, eps_row being the
+    row's max |gpu - oracle| logit error. This holds for any correct selection
+    (the GPU's rank-j value is its j-th largest logit, which is within eps_row of
+    the oracle's j-th largest, and the GPU's logit of an id is within eps_row of
+    the oracle's), so a wrong id anywhere in the list fails it unless it is a
+    genuine near-tie. Returns the largest |difference| / (2 * eps_row) seen."""
+    L = oracle_logits.reshape(-1, oracle_logits.shape[-1]).astype(np.float64)
+    G = np.asarray(gpu_logits, dtype=np.float64).reshape(L.shape)
+    k = gpu_ids.shape[-1]
+    ids = gpu_ids.reshape(-1, k)
+    worst = 0.0
+    for r in range(L.shape[0]):
+        eps = float(np.max(np.abs(G[r] - L[r])))
+        v = np.sort(L[r])[::-1][:k]
+        d = np.abs(L[r][ids[r]] - v)
+        bound = 2.0 * eps + 1e-12
+        assert np.all(d <= bound), f"row {r}: rank {int(np.argmax(d - bound))} off by {float(np.max(d)):.4g} > {bound:.4g}"
+        worst = max(worst, float(np.max(d)) / bound)
+    return worst
+
+
+def require_compared(comp: int, excl: int, min_frac: float, what: str):
+    """The tie-excluding comparison must still decide a stated share of ranks."""
+    total = comp + excl
+    frac = comp / max(total, 1)
+    print(f"{what}: ranks compared {comp} of {total} ({frac:.0%}; minimum {min_frac:.0%}), near-ties excluded {excl}",
+          flush=True)
+    assert frac >= min_frac, f"{what}: only {comp} of {total} ranks decided by the numerics"

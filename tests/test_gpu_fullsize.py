@@ -35,8 +35,10 @@ def _check_round(cfg, wh, hist, tokens, pos, vf, logits, ids, what):
     gi = ids.cpu().numpy()
     Hn.topk_self_consistent(g, gi)
     comp, excl = Hn.topk_agrees_away_from_ties(ref["logits"], gi, gi.shape[-1], gpu_logits=g)
-    print(f"{what}: top-k ranks compared {comp}, near-ties excluded {excl}", flush=True)
-    assert comp > 0
+    # top-16: the ranks below the first few sit closer than the error; argmax: most rows decide
+    Hn.require_compared(comp, excl, 0.08 if gi.shape[-1] > 1 else 0.40, what)
+    worst = Hn.topk_within_eps(ref["logits"], gi, g)
+    print(f"{what}: every rank within 2*eps of the oracle's (worst {worst:.2f} of the bound)", flush=True)
     return ref
 
 
@@ -58,9 +60,17 @@ def test_qwen3_4b_block16_window4096_rounds(big):
     for rnd in range(3):
         logits = torch.empty((1, B - 1, V), dtype=torch.float32, device="cuda")
         ids = dr.draft_block(tokens, k=16, logits=logits)
+        # the call bench.py times: no logits buffer (the head writes its transposed
+        # scratch and top-16 reads it back), ids and values only
+        ids_b = torch.empty((1, B - 1, 16), dtype=torch.int32, device="cuda")
+        vals_b = torch.empty((1, B - 1, 16), dtype=torch.float32, device="cuda")
+        dr.draft_block(tokens, k=16, ids=ids_b, vals=vals_b)
         torch.cuda.synchronize()
         assert dr.check() == 0
-        ref = _check_round(cfg, wh, hist, tokens[0].cpu().tolist(), pos, vf, logits[0], ids[0], f"round {rnd}")
+        np.testing.assert_array_equal(ids_b.cpu().numpy(), ids.cpu().numpy())
+        np.testing.assert_array_equal(vals_b[0].cpu().numpy(),
+                                      np.take_along_axis(logits[0].cpu().numpy(), ids[0].cpu().numpy(), 1))
+        ref = _check_round(cfg, wh, hist, tokens[0].cpu().tolist(), pos, vf, logits[0], ids_b[0], f"round {rnd}")
         if rnd == 0:   # ring contents at sampled window slots equal the oracle's context K/V
             rk, rv = dr.ring()
             sel = np.array([0, 1, 777, 2048, W - 2, W - 1])
@@ -141,15 +151,31 @@ def test_hc_eight_requests_window4096_batched():
     torch.cuda.synchronize()
     assert dr.check() == 0
     wh = Hn.host_weights(w)
+    rk, rv = dr.ring()
     for r, th in keep.items():
         # the oracle indexes taps by absolute position: rows before the window are never read
         taps_h = [np.concatenate([np.zeros((starts[r] - W, t.shape[1])), t.astype(np.float64)], 0) for t in th]
-        ref = D.draft_block(cfg, wh, taps_h, tokens[r].cpu().tolist(), starts[r], starts[r] - W, mode="mirror")
+        ref = D.draft_block(cfg, wh, taps_h, tokens[r].cpu().tolist(), starts[r], starts[r] - W, mode="mirror",
+                            want_intermediates=True)
+        # staged context K/V (hc mean + prefill tile path) at sampled window rows
+        sel = np.array([0, 1, 1000, 2047, W - 2, W - 1])
+        slots = (starts[r] - W + sel) % cfg.ring_capacity
+        for l in (0, cfg.n_layers - 1):
+            gk = rk[l, r].float().cpu().numpy()[:, slots, :]
+            gv = rv[l, r].float().cpu().numpy()[:, :, slots].transpose(0, 2, 1)
+            ek = Hn.assert_close(gk, ref["ctx_k"][l][:, sel, :], f"request {r} ring K layer {l}")
+            ev = Hn.assert_close(gv, ref["ctx_v"][l][:, sel, :], f"request {r} ring V layer {l}")
+            print(f"request {r} layer {l}: ring K err {ek:.3g} (tol {Hn.tol(ref['ctx_k'][l][:, sel, :]):.3g}), "
+                  f"V err {ev:.3g} (tol {Hn.tol(ref['ctx_v'][l][:, sel, :]):.3g})", flush=True)
         g = logits[r].cpu().numpy()
+        t = Hn.tol(ref["logits"])
         err = Hn.assert_close(g, ref["logits"], f"request {r} logits")
+        rms = float(np.sqrt(np.mean((g - ref["logits"]) ** 2)))
+        print(f"request {r}: logits max err {err:.4g} rms {rms:.3g}, tol {t:.4g} (max|oracle| "
+              f"{np.max(np.abs(ref['logits'])):.3g}), {err / t:.0%} of the tolerance", flush=True)
         comp, excl = Hn.topk_agrees_away_from_ties(ref["logits"], ids[r].cpu().numpy(), 1, gpu_logits=g)
-        print(f"request {r}: logits max err {err:.3g}; argmax compared {comp}, near-ties excluded {excl}", flush=True)
-        assert comp > 0
+        Hn.require_compared(comp, excl, 0.40, f"request {r} argmax")
+        Hn.topk_within_eps(ref["logits"], ids[r].cpu().numpy(), g)
 
 
 def test_qwen3_4b_block8_window4096_top16(big):

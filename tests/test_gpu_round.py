@@ -2,6 +2,8 @@
 
 Everything is called through the C ABI (binding.Drafter). Inputs come from
 synth on the GPU and are copied to the host for the oracle."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -235,36 +237,44 @@ def test_empty_and_oversized_calls_refused_before_any_launch(tiny_setup):
     ids = torch.empty((cfg.max_requests + 1, B, 16), dtype=torch.int32, device="cuda")
     verify = torch.ones((cfg.max_requests + 1, B), dtype=torch.int32, device="cuda")
 
-    def refused(fn, code, what):
-        with pytest.raises(binding.DFlashError) as ei:
-            fn()
-        assert ei.value.code == code, (what, ei.value)
-        print(f"{what}: {ei.value}", flush=True)
-
-    refused(lambda: dr.tap_stage(taps, 0, rows_per_req=1), E_SHAPE, "stage of 0 rows")
-    refused(lambda: dr.tap_stage(taps, cfg.max_stage_rows + 1, rows_per_req=1), E_CAPACITY,
-            "stage beyond max_stage_rows")
-    # counts of zero go straight through the C ABI with live buffers, so that the
-    # count check decides (an empty tensor's null pointer is refused first, E_ARG)
+    # the wrappers check shapes before the C ABI (ValueError); these calls go
+    # straight through the C ABI so that its own checks decide, with live buffers
     lib, ctx, st = dr.lib, dr.ctx, binding._stream()
-    rc = lib.dflash_draft_block(ctx, st, tokens.data_ptr(), 0, None, ids.data_ptr(), None, 1)
-    assert rc == E_SHAPE, ("draft of 0 requests", rc)
-    rc = lib.dflash_draft_block_n(ctx, st, tokens.data_ptr(), 1, 0, None, ids.data_ptr(), None, 1)
-    assert rc == E_SHAPE, ("block length 0", rc)
-    refused(lambda: dr.draft_block(tokens[:0], k=1, ids=ids), E_ARG, "draft with a null token pointer")
-    refused(lambda: dr.draft_block(tokens, k=1, ids=ids), E_SHAPE, "draft beyond max_requests")
-    wide = torch.cat([tokens[:1], tokens[:1, :1]], 1).contiguous()
-    refused(lambda: dr.draft_block_n(wide, k=1, ids=ids), E_SHAPE, "block length above the block")
-    refused(lambda: dr.draft_block(tokens[:1].contiguous(), k=3, ids=ids), E_ARG, "k = 3")
     Rx = cfg.max_requests + 1
+    tp = (ctypes.c_void_p * cfg.n_taps)(*[t.data_ptr() for t in taps])
+    tpp = ctypes.cast(tp, binding.PP)
     out = {"accept_len": torch.empty(Rx, dtype=torch.int32, device="cuda"),
            "emitted": torch.empty((Rx, B), dtype=torch.int32, device="cuda"),
            "n_emit": torch.empty(Rx, dtype=torch.int32, device="cuda"),
            "next_tokens": torch.empty((Rx, B), dtype=torch.int32, device="cuda")}
-    rc = lib.dflash_accept(ctx, st, ids.data_ptr(), 16, verify.data_ptr(), 0, -1, None, out["accept_len"].data_ptr(),
-                           out["emitted"].data_ptr(), out["n_emit"].data_ptr(), out["next_tokens"].data_ptr())
-    assert rc == E_SHAPE, ("accept of 0 requests", rc)
-    refused(lambda: dr.accept(ids, 16, verify, out=out), E_SHAPE, "accept beyond max_requests")
+
+    def acc(n):
+        return lib.dflash_accept(ctx, st, ids.data_ptr(), 16, verify.data_ptr(), n, -1, None,
+                                 out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
+                                 out["next_tokens"].data_ptr())
+
+    cases = [
+        ("stage of 0 rows", E_SHAPE, lambda: lib.dflash_tap_stage(ctx, st, tpp, taps[0].stride(0), 0, None, None, 1)),
+        ("stage beyond max_stage_rows", E_CAPACITY,
+         lambda: lib.dflash_tap_stage(ctx, st, tpp, taps[0].stride(0), cfg.max_stage_rows + 1, None, None, 1)),
+        ("draft of 0 requests", E_SHAPE,
+         lambda: lib.dflash_draft_block(ctx, st, tokens.data_ptr(), 0, None, ids.data_ptr(), None, 1)),
+        ("block length 0", E_SHAPE,
+         lambda: lib.dflash_draft_block_n(ctx, st, tokens.data_ptr(), 1, 0, None, ids.data_ptr(), None, 1)),
+        ("draft with a null token pointer", E_ARG,
+         lambda: lib.dflash_draft_block(ctx, st, None, 1, None, ids.data_ptr(), None, 1)),
+        ("draft beyond max_requests", E_SHAPE,
+         lambda: lib.dflash_draft_block(ctx, st, tokens.data_ptr(), Rx, None, ids.data_ptr(), None, 1)),
+        ("block length above the block", E_SHAPE,
+         lambda: lib.dflash_draft_block_n(ctx, st, tokens.data_ptr(), 1, B + 1, None, ids.data_ptr(), None, 1)),
+        ("k = 3", E_ARG, lambda: lib.dflash_draft_block(ctx, st, tokens.data_ptr(), 1, None, ids.data_ptr(), None, 3)),
+        ("accept of 0 requests", E_SHAPE, lambda: acc(0)),
+        ("accept beyond max_requests", E_SHAPE, lambda: acc(Rx)),
+    ]
+    for what, code, fn in cases:
+        rc = fn()
+        assert rc == code, (what, rc, binding.last_error())
+        print(f"{what}: {binding.STATUS[rc]}: {binding.last_error()}", flush=True)
     torch.cuda.synchronize()
     for a, b in zip(dr.positions(), pos0):
         assert torch.equal(a, b)
@@ -274,3 +284,75 @@ def test_empty_and_oversized_calls_refused_before_any_launch(tiny_setup):
     got = dr.draft_block(tokens[:1].contiguous(), k=1)
     torch.cuda.synchronize()
     assert dr.check() == 0 and got.shape == (1, B - 1, 1)
+
+
+def _stage_rows(dr, taps, positions):
+    """Stage the tap rows of the given absolute positions (request 0)."""
+    pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
+    rows = [t[pos.long()].contiguous() for t in taps]
+    dr.tap_stage(rows, len(positions), req_of_row=torch.zeros_like(pos), pos_of_row=pos)
+
+
+def test_ring_capacity_guard_tiny(tiny_setup):
+    """A staged row whose ring slot holds another live row of its request (the
+    live positions are the window and the block, [pos - W, pos + B)) is skipped
+    and sets DFLASH_DEV_RING_CAPACITY: the ring is left bit for bit as it was,
+    valid rows of the same call are still written, and after the error is
+    cleared the next draft equals the oracle. Checked on the few-row (split-K)
+    staging path and on the prefill (tiled) path."""
+    binding, cfg, w, wh = tiny_setup
+    B, W, C = cfg.block, cfg.window, cfg.ring_capacity
+    P = 300
+    taps, taps_h = _taps_history(cfg, P + 200, seed=13)
+    tokens = synth.block_tokens(cfg, 1, seed=14, device="cuda")
+    RING_CAPACITY = 16
+    hi, lo = P + C - W, P + B - C - 1            # first positions past either end of the rule
+    print(f"case: ring capacity guard, pos={P} W={W} B={B} C={C}: valid [{lo + 1}, {hi})", flush=True)
+
+    # few rows: two bad rows around one valid row (slot of position P - W - 1, outside the window)
+    dr = binding.Drafter(cfg, w)
+    dr.reset(0, P - W, P)
+    _stage_rows(dr, taps, list(range(P - W, P)))
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    before = [t.clone() for t in dr.ring()]
+    _stage_rows(dr, taps, [hi, hi - 1, lo])
+    torch.cuda.synchronize()
+    word = dr.check()
+    assert word == RING_CAPACITY, hex(word)
+    after = dr.ring()
+    ok_slot = (hi - 1) % C
+    keep = np.ones(C, dtype=bool)
+    keep[ok_slot] = False
+    for b, a, name in ((before[0], after[0], "K"), (before[1], after[1], "V")):
+        bb, aa = b.cpu(), a.cpu()
+        sl = (slice(None), slice(None), slice(None), torch.from_numpy(keep)) if name == "K" else \
+             (slice(None), slice(None), slice(None), slice(None), torch.from_numpy(keep))
+        assert torch.equal(bb[sl], aa[sl]), f"ring {name} changed outside the valid row's slot"
+    assert not torch.equal(before[0][:, 0, :, ok_slot], after[0][:, 0, :, ok_slot]), "the valid row was not written"
+    dr.clear_error()
+    logits = torch.empty((1, B - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    dr.draft_block(tokens, k=1, logits=logits)
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    ref = D.draft_block(cfg, wh, taps_h, tokens[0].cpu().tolist(), P, P - W, mode="mirror")
+    Hn.assert_close(logits[0].cpu().numpy(), ref["logits"], "draft after the refused rows")
+
+    # the prefill path (>= 256 rows): the window staged four times over, then again
+    # with one row moved to a position past the upper end
+    n = 4 * W
+    assert n >= 256 and n <= cfg.max_stage_rows
+    dr2 = binding.Drafter(cfg, w)
+    dr2.reset(0, P - W, P)
+    rows = [P - W + (i % W) for i in range(n)]
+    _stage_rows(dr2, taps, rows)
+    torch.cuda.synchronize()
+    assert dr2.check() == 0
+    before = [t.clone() for t in dr2.ring()]
+    rows[5] = hi + 3
+    _stage_rows(dr2, taps, rows)
+    torch.cuda.synchronize()
+    word = dr2.check()
+    assert word == RING_CAPACITY, hex(word)
+    for b, a in zip(before, dr2.ring()):
+        assert torch.equal(b, a), "the prefill path wrote a refused row or changed the window"
