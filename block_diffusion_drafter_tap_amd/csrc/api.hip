@@ -126,7 +126,9 @@ WsLayout ws_layout(const dflash_config& c) {
   L.z = take(Mmax * c.hidden * 2);   // final-normed rows (LM head without LDS staging)
   L.c32 = take(c.ctx_norm ? S * c.hidden * 4 : 0);
   L.c = take(S * c.hidden * 2);
-  L.xg = take(prefill_enabled(c) ? S * c.n_taps * c.tap_hidden * 2 : 0);   // gathered tap rows (prefill)
+  // gathered tap rows as bf16: the prefill path, and every staging call when
+  // the taps carry several hyper-connection streams
+  L.xg = take(prefill_enabled(c) || c.hc_streams > 1 ? S * c.n_taps * c.tap_hidden * 2 : 0);
   L.partials = take((pf ? pf : 1) * 4);
   L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
   L.attn_ml = take(lrg * nch * slots * 2 * 4);
@@ -493,11 +495,33 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   {
     GemmPlan p = plan_for(g, n_rows, H, a.K, GC_DEFAULT, 0, P_FC);
     Timed tm(ctx, DFLASH_K_FC, st);
-    if (p.S > 1) {
-      e = launch_gemm(a, p, X_TAPS, E_PART, wf, st);
-      if (e == hipSuccess) e = launch_finish_store(a.partials, p.S, n_rows, H, a.out, H, !g.ctx_norm, st);
-    } else {
-      e = launch_gemm(a, p, X_TAPS, g.ctx_norm ? E_F32 : E_BF16, wf, st);
+    int xk = X_TAPS;
+    e = hipSuccess;
+    if (g.hc_streams > 1) {
+      // Several streams: their mean (summed in fp64, one rounding to bf16) is
+      // taken once per element by the gather kernel, not by every column group
+      // of the projection that stages the same X slice; the projection then
+      // reads the bf16 rows. The values are those the tap staging would form.
+      TapGather tg;
+      memset(&tg, 0, sizeof tg);
+      for (int t = 0; t < g.n_taps; ++t) tg.taps[t] = taps[t];
+      tg.tap_stride = tap_row_stride;
+      tg.n_taps = g.n_taps;
+      tg.hc = g.hc_streams;
+      tg.tap_hidden = g.tap_hidden;
+      tg.out = at<uint16_t>(ctx->ws, ctx->wl.xg);
+      e = launch_tap_gather(tg, n_rows, st);
+      a.x = tg.out;
+      a.ldx = a.K;
+      xk = X_BF16;
+    }
+    if (e == hipSuccess) {
+      if (p.S > 1) {
+        e = launch_gemm(a, p, xk, E_PART, wf, st);
+        if (e == hipSuccess) e = launch_finish_store(a.partials, p.S, n_rows, H, a.out, H, !g.ctx_norm, st);
+      } else {
+        e = launch_gemm(a, p, xk, g.ctx_norm ? E_F32 : E_BF16, wf, st);
+      }
     }
   }
   if (e != hipSuccess) return hip_fail(e, "stage fc");

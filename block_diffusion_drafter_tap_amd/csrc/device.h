@@ -21,6 +21,59 @@ DEV uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f2bfbits(lo) | ((uint32_t)f2bfbits(hi) << 16);
 }
 
+// fp64 -> bf16 rounded to nearest even in one step: fp64 -> fp32 toward zero
+// with the sticky bit ORed into the last fp32 bit (round to odd), then the
+// fp32 -> bf16 conversion (nearest even). fp32 keeps 16 more significand bits
+// than bf16, so the two steps round exactly like a single one.
+DEV uint16_t f64_to_bf16bits(double x) {
+  float t = __double2float_rz(x);
+  if ((double)t != x) t = __uint_as_float(__float_as_uint(t) | 1u);
+  return f2bfbits(t);
+}
+
+// Eight consecutive values of the per-token mean over hc hyper-connection
+// streams, as bf16x8: p points at stream 0's first value, streams are `ld`
+// floats apart. With one stream the value is the tap itself. Otherwise the
+// streams are summed in fp64 (exact for fp32 inputs of similar magnitude),
+// divided by hc in fp64 and rounded once to bf16, so the result is the
+// correctly rounded mean; an fp32 sum would round first and flip a share of
+// the bf16 casts that follow.
+DEV u32x4 hc_mean8_bf16(const float* p, size_t ld, int hc) {
+  u32x4 r;
+  if (hc == 1) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    r[0] = pack_bf16x2(a[0], a[1]);
+    r[1] = pack_bf16x2(a[2], a[3]);
+    r[2] = pack_bf16x2(b[0], b[1]);
+    r[3] = pack_bf16x2(b[2], b[3]);
+    return r;
+  }
+  double s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.0;
+  for (int st = 0; st < hc; ++st) {
+    const f32x4 a = *(const f32x4*)(p + (size_t)st * ld), b = *(const f32x4*)(p + (size_t)st * ld + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] += (double)a[i];
+      s[4 + i] += (double)b[i];
+    }
+  }
+  if ((hc & (hc - 1)) == 0) {
+    // a power of two: 1/hc is exact, so the product is the quotient
+    const double inv = 1.0 / (double)hc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] *= inv;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] /= (double)hc;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (uint32_t)f64_to_bf16bits(s[2 * i]) | ((uint32_t)f64_to_bf16bits(s[2 * i + 1]) << 16);
+  return r;
+}
+
 // 16-byte loads. Weights stream through once per round: non-temporal so they do
 // not evict activations, partial sums and the context ring from L2/MALL.
 DEV u32x4 ld_nt16(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }

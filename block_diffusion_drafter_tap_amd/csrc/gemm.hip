@@ -80,21 +80,7 @@ DEV u32x4 load_x(const GemmArgs& a, int row, int k, float inv) {
   } else {
     const int t = k / a.tap_hidden;
     const int col = k - t * a.tap_hidden;
-    const float* p = tap_ptr(a, t) + (size_t)row * a.tap_stride + col;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    for (int st = 0; st < a.hc; ++st) {
-      s0 += *(const f32x4*)(p + (size_t)st * a.tap_hidden);
-      s1 += *(const f32x4*)(p + (size_t)st * a.tap_hidden + 4);
-    }
-    const float hinv = 1.0f / (float)a.hc;
-    s0 *= hinv;
-    s1 *= hinv;
-    u32x4 r;
-    r[0] = pack_bf16x2(s0[0], s0[1]);
-    r[1] = pack_bf16x2(s0[2], s0[3]);
-    r[2] = pack_bf16x2(s1[0], s1[1]);
-    r[3] = pack_bf16x2(s1[2], s1[3]);
-    return r;
+    return hc_mean8_bf16(tap_ptr(a, t) + (size_t)row * a.tap_stride + col, (size_t)a.tap_hidden, a.hc);
   }
 }
 

@@ -3,7 +3,8 @@
 // rows) rather than weight streams. bf16 or INT4 (g64) weights.
 //
 //   tap_gather_kernel  X[m][t*H + j] = bf16(mean over the hc streams of tap t)
-//                      (the same arithmetic as the skinny GEMM's tap staging)
+//                      (the same arithmetic as the skinny GEMM's tap staging:
+//                      hc_mean8_bf16)
 //   gemm_tile_kernel   Y[M][N] = X[M][K] . W[N][K]^T, fp32 accumulate, fp32 or
 //                      bf16 out. 128 x BN tiles per workgroup of 4 waves (2 x 2,
 //                      64 x BN/2 per wave, MFMA 16x16x32 bf16); K in stages of 64
@@ -32,21 +33,8 @@ __global__ __launch_bounds__(256) void tap_gather_kernel(const TapGather g) {
 #pragma unroll
   for (int i = 1; i < MAX_TAPS; ++i)
     if (t == i) tp = g.taps[i];
-  const float* p = tp + (size_t)m * g.tap_stride + col;
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  for (int st = 0; st < g.hc; ++st) {
-    s0 += *(const f32x4*)(p + (size_t)st * g.tap_hidden);
-    s1 += *(const f32x4*)(p + (size_t)st * g.tap_hidden + 4);
-  }
-  const float hinv = 1.0f / (float)g.hc;
-  s0 *= hinv;
-  s1 *= hinv;
-  u32x4 r;
-  r[0] = pack_bf16x2(s0[0], s0[1]);
-  r[1] = pack_bf16x2(s0[2], s0[3]);
-  r[2] = pack_bf16x2(s1[0], s1[1]);
-  r[3] = pack_bf16x2(s1[2], s1[3]);
-  *(u32x4*)(g.out + (size_t)m * g.n_taps * g.tap_hidden + e) = r;
+  *(u32x4*)(g.out + (size_t)m * g.n_taps * g.tap_hidden + e) =
+      hc_mean8_bf16(tp + (size_t)m * g.tap_stride + col, (size_t)g.tap_hidden, g.hc);
 }
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_HEADS = 2 };
