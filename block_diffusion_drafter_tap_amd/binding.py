@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH):
         "dflash_tap_stage": (c_int, [P, P, PP, c_ll, c_int, P, P, c_int]),
         "dflash_draft_block": (c_int, [P, P, P, c_int, P, P, P, c_int]),
         "dflash_draft_block_n": (c_int, [P, P, P, c_int, c_int, P, P, P, c_int]),
+        "dflash_draft_block_noalloc": (c_int, [P, P, P, c_int, P, P, P, c_int]),
+        "dflash_draft_scratch_bytes": (c_size_t, [ctypes.POINTER(dflash_config)]),
         "dflash_accept": (c_int, [P, P, P, c_int, P, c_int, c_int, P, P, P, P, P]),
         "dflash_accept_n": (c_int, [P, P, P, c_int, P, c_int, c_int, c_int, P, P, P, P, P]),
         "dflash_check": (c_int, [P, P, ctypes.POINTER(c_uint)]),
@@ -184,6 +186,10 @@ def workspace_bytes(cfg: DFlashConfig) -> int:
     return load().dflash_workspace_bytes(ctypes.byref(c_config(cfg)))
 
 
+def draft_scratch_bytes(cfg: DFlashConfig) -> int:
+    return load().dflash_draft_scratch_bytes(ctypes.byref(c_config(cfg)))
+
+
 def state_layout(cfg: DFlashConfig) -> Dict[str, int]:
     lay = dflash_state_layout()
     _check("dflash_get_state_layout", load().dflash_get_state_layout(ctypes.byref(c_config(cfg)), ctypes.byref(lay)))
@@ -277,6 +283,19 @@ class Drafter:
         if ids is None:
             ids = torch.empty((R, Bm1, k), dtype=torch.int32, device=self.device)
         _check("dflash_draft_block", self.lib.dflash_draft_block(
+            self.ctx, _stream(), block_tokens.data_ptr(), R, _ptr(logits), ids.data_ptr(), _ptr(vals), k))
+        return ids
+
+    def draft_block_noalloc(self, block_tokens: torch.Tensor, k: int = 1, logits: Optional[torch.Tensor] = None,
+                            ids: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None):
+        """draft_block through the allocation-free entry point (the library's static
+        device scratch instead of the bound workspace)."""
+        R = block_tokens.shape[0]
+        Bm1 = max(self.cfg.block - 1, 1)
+        self._check_draft(block_tokens, self.cfg.block, k, logits, ids, vals)
+        if ids is None:
+            ids = torch.empty((R, Bm1, k), dtype=torch.int32, device=self.device)
+        _check("dflash_draft_block_noalloc", self.lib.dflash_draft_block_noalloc(
             self.ctx, _stream(), block_tokens.data_ptr(), R, _ptr(logits), ids.data_ptr(), _ptr(vals), k))
         return ids
 

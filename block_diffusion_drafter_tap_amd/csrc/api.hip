@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/dflash.h"
@@ -81,8 +82,9 @@ int stage_batch(const GemmPlan& p, int M, int N, int n_layers) {
   return b;
 }
 
-// Largest split-K partial buffer over every GEMM a call may launch.
-size_t gemm_scratch(const dflash_config& c) {
+// Largest split-K partial buffer over every GEMM a call may launch (with
+// draft_only, over the block forward's projections alone).
+size_t gemm_scratch(const dflash_config& c, bool draft_only = false) {
   const int H = c.hidden, hd = c.head_dim;
   const GemmShape draft[] = {{(c.n_q_heads + 2 * c.n_kv_heads) * hd, H, hd, 0, P_QKV},
                              {H, c.n_q_heads * hd, GC_DEFAULT, 0, P_O},
@@ -99,19 +101,22 @@ size_t gemm_scratch(const dflash_config& c) {
   };
   for (int R = 1; R <= c.max_requests; ++R)
     for (const auto& s : draft) visit(R * c.block, s, false);
-  for (int M = 1; M <= c.max_stage_rows; ++M) {
+  for (int M = 1; M <= (draft_only ? 0 : c.max_stage_rows); ++M) {
     visit(M, stage[0], false);
     visit(M, stage[1], true);
   }
   return pf;
 }
 
-WsLayout ws_layout(const dflash_config& c) {
+// Workspace sections. With draft_only, only what a block forward (draft or
+// verify pass) uses: the staging sections (c, c32, xg) are empty and the
+// split-K partials cover the block forward's projections alone.
+WsLayout ws_layout(const dflash_config& c, bool draft_only = false) {
   WsLayout L;
   const size_t Mmax = (size_t)c.max_requests * c.block;
-  const size_t S = (size_t)c.max_stage_rows;
+  const size_t S = draft_only ? 0 : (size_t)c.max_stage_rows;
   const size_t qw = (size_t)c.n_q_heads * c.head_dim;
-  const size_t pf = gemm_scratch(c);
+  const size_t pf = gemm_scratch(c, draft_only);
   const size_t slots = (size_t)attn_slots(c.n_q_heads, c.n_kv_heads, c.block);
   const size_t lrg = (size_t)c.max_requests * c.n_kv_heads;
   const size_t nch = (size_t)attn_nchunks(c);
@@ -128,7 +133,7 @@ WsLayout ws_layout(const dflash_config& c) {
   L.c = take(S * c.hidden * 2);
   // gathered tap rows as bf16: the prefill path, and every staging call when
   // the taps carry several hyper-connection streams
-  L.xg = take(prefill_enabled(c) || c.hc_streams > 1 ? S * c.n_taps * c.tap_hidden * 2 : 0);
+  L.xg = take(!draft_only && (prefill_enabled(c) || c.hc_streams > 1) ? S * c.n_taps * c.tap_hidden * 2 : 0);
   L.partials = take((pf ? pf : 1) * 4);
   L.attn_o = take(lrg * nch * slots * c.head_dim * 4);
   L.attn_ml = take(lrg * nch * slots * 2 * 4);
@@ -325,9 +330,9 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
   return DFLASH_OK;
 }
 
-int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int n_req, int block_len, int causal,
-                  const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld, int first_row,
-                  float* logits, int* topk_ids, float* topk_vals, int k);
+int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st, const int* block_tokens, int n_req,
+                  int block_len, int causal, const int* tap_layers, int n_tap_out, float* const* tap_out,
+                  long long tap_ld, int first_row, float* logits, int* topk_ids, float* topk_vals, int k);
 
 }  // namespace
 
@@ -594,8 +599,71 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
   if (k != 1 && k != 16) return fail(DFLASH_E_ARG, "k must be 1 or 16 (got %d)", k);
   if (k > g.vocab) return fail(DFLASH_E_ARG, "k exceeds vocab");
   if (block_len == 1) return DFLASH_OK;   // no mask rows: nothing to draft
-  return forward_block(ctx, (hipStream_t)stream, block_tokens, n_req, block_len, 0, nullptr, 0, nullptr, 0, 1, logits,
-                       topk_ids, topk_vals, k);
+  return forward_block(ctx, ctx->ws, ctx->wl, (hipStream_t)stream, block_tokens, n_req, block_len, 0, nullptr, 0,
+                       nullptr, 0, 1, logits, topk_ids, topk_vals, k);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free draft entry point: one copy on every GPU the
+// library runs on, held until the process ends. Host code never uses this
+// name as an address: the device address comes from hipGetSymbolAddress, once
+// per device, and is kept in g_scratch_ptr.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)DFLASH_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[MAX_DEVICES];
+
+// The current device's copy of `scratch` (looked up on its first use).
+int static_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(DFLASH_E_UNSUPPORTED, "device %d: at most %d devices", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_draft_scratch_bytes(const dflash_config* cfg) {
+  if (validate_config(cfg) != DFLASH_OK) return 0;
+  return ws_layout(*cfg, true).total;
+}
+
+int dflash_draft_block_noalloc(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, float* logits,
+                               int* topk_ids, float* topk_vals, int k) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (ctx->target) return fail(DFLASH_E_STATE, "a target handle runs verify passes, not drafts");
+  const dflash_config& g = ctx->cfg;
+  if (!block_tokens || !topk_ids) return fail(DFLASH_E_ARG, "block_tokens and topk_ids are required");
+  if (n_req < 1 || n_req > g.max_requests)
+    return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (k != 1 && k != 16) return fail(DFLASH_E_ARG, "k must be 1 or 16 (got %d)", k);
+  if (k > g.vocab) return fail(DFLASH_E_ARG, "k exceeds vocab");
+  const WsLayout L = ws_layout(g, true);
+  if (L.total > STATIC_SCRATCH_BYTES)
+    return fail(DFLASH_E_CAPACITY, "this configuration's draft needs %zu bytes of scratch; the static scratch holds %zu",
+                L.total, STATIC_SCRATCH_BYTES);
+  if (g.block == 1) return DFLASH_OK;   // no mask rows: nothing to draft
+  char* ws = nullptr;
+  const int rc = static_scratch(&ws);
+  if (rc) return rc;
+  return forward_block(ctx, ws, L, (hipStream_t)stream, block_tokens, n_req, g.block, 0, nullptr, 0, nullptr, 0, 1,
+                       logits, topk_ids, topk_vals, k);
 }
 
 int dflash_verify_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, int block_len,
@@ -618,8 +686,8 @@ int dflash_verify_block(dflash_ctx* ctx, void* stream, const int* block_tokens, 
     if (!tap_out[t] || ((uintptr_t)tap_out[t] & 15)) return fail(DFLASH_E_ARG, "tap_out[%d] must be 16-byte aligned", t);
   }
   if (n_tap_out > 0 && (tap_ld < g.hidden || tap_ld % 4)) return fail(DFLASH_E_ARG, "tap_ld must be >= hidden, % 4 == 0");
-  return forward_block(ctx, (hipStream_t)stream, block_tokens, n_req, block_len, 1, tap_layers, n_tap_out, tap_out,
-                       tap_ld, 0, logits, ids, nullptr, 1);
+  return forward_block(ctx, ctx->ws, ctx->wl, (hipStream_t)stream, block_tokens, n_req, block_len, 1, tap_layers,
+                       n_tap_out, tap_out, tap_ld, 0, logits, ids, nullptr, 1);
 }
 
 int dflash_advance(dflash_ctx* ctx, void* stream, const int* n_emit, int n_req) {
@@ -641,18 +709,24 @@ namespace {
 // drafter's masked block (bidirectional, the mask rows' top-k) or a causal
 // target's verify pass (block row i sees rows <= i, argmax of every row, the
 // residual rows after the tapped layers copied out).
-int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int n_req, int block_len, int causal,
-                  const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld, int first_row,
-                  float* logits, int* topk_ids, float* topk_vals, int k) {
+int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st, const int* block_tokens, int n_req,
+                  int block_len, int causal, const int* tap_layers, int n_tap_out, float* const* tap_out,
+                  long long tap_ld, int first_row, float* logits, int* topk_ids, float* topk_vals, int k) {
   const dflash_config& g = ctx->cfg;
+  // GEMM arguments with this call's split-K partial buffer
+  auto base = [&]() {
+    GemmArgs a = base_args(ctx);
+    a.partials = at<float>(ws, wl.partials);
+    return a;
+  };
   const int H = g.hidden, hd = g.head_dim, B = block_len;
   const int M = n_req * B;
   const int qw = g.n_q_heads * hd;
-  float* h = at<float>(ctx->ws, ctx->wl.h);
-  float* ssq = at<float>(ctx->ws, ctx->wl.ssq);
-  uint16_t* q = at<uint16_t>(ctx->ws, ctx->wl.q);
-  uint16_t* o = at<uint16_t>(ctx->ws, ctx->wl.o);
-  uint16_t* act = at<uint16_t>(ctx->ws, ctx->wl.act);
+  float* h = at<float>(ws, wl.h);
+  float* ssq = at<float>(ws, wl.ssq);
+  uint16_t* q = at<uint16_t>(ws, wl.q);
+  uint16_t* o = at<uint16_t>(ws, wl.o);
+  uint16_t* act = at<uint16_t>(ws, wl.act);
   unsigned* err = at<unsigned>(ctx->state, ctx->sl.error);
   const int ssq_ld = g.max_requests * g.block;   // row pitch of the ssq buffer
   const int h_blocks = H / GC_DEFAULT;
@@ -674,7 +748,7 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
     uint16_t* rk = at<uint16_t>(ctx->state, ctx->sl.ring_k) + l * rl;
     uint16_t* rv = at<uint16_t>(ctx->state, ctx->sl.ring_v) + l * rl;
     {  // RMSNorm + QKV + q/k head norm + RoPE; the block's K/V go to ring slots [pos, pos+B)
-      GemmArgs a = base_args(ctx);
+      GemmArgs a = base();
       norm_input(a, ctx->ln_in[l], l == 0 ? 1 : h_blocks);
       a.w = ctx->wqkv[l];
       a.wscale = dflash_ctx::sc(ctx->wqkv_s, l);
@@ -716,8 +790,8 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
       t.kc = attn_chunk_keys(hd);
       t.n_chunks = attn_nchunks(g);
       t.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-      t.part_o = at<float>(ctx->ws, ctx->wl.attn_o);
-      t.part_ml = at<float>(ctx->ws, ctx->wl.attn_ml);
+      t.part_o = at<float>(ws, wl.attn_o);
+      t.part_ml = at<float>(ws, wl.attn_ml);
       t.err = err;
       t.causal = causal;
       Timed tm(ctx, DFLASH_K_ATTN, st);
@@ -725,7 +799,7 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
       if (e != hipSuccess) return hip_fail(e, "attention");
     }
     {  // o projection, residual add, row sums of squares for the post-attention norm
-      GemmArgs a = base_args(ctx);
+      GemmArgs a = base();
       a.x = o;
       a.ldx = qw;
       a.w = ctx->wo[l];
@@ -748,7 +822,7 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
       if (e != hipSuccess) return hip_fail(e, "o proj");
     }
     {  // RMSNorm + gate/up with SiLU(gate) * up
-      GemmArgs a = base_args(ctx);
+      GemmArgs a = base();
       norm_input(a, ctx->ln_post[l], h_blocks);
       a.w = ctx->wgu[l];
       a.wscale = dflash_ctx::sc(ctx->wgu_s, l);
@@ -769,7 +843,7 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
       if (e != hipSuccess) return hip_fail(e, "gate/up");
     }
     {  // down projection, residual add, row sums of squares for the next norm
-      GemmArgs a = base_args(ctx);
+      GemmArgs a = base();
       a.x = act;
       a.ldx = g.ffn;
       a.w = ctx->wd[l];
@@ -798,7 +872,7 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
       }
   }
   {  // shared LM head: mask-row logits, then per-row top-k
-    GemmArgs a = base_args(ctx);
+    GemmArgs a = base();
     norm_input(a, ctx->final_norm, h_blocks);
     a.w = ctx->lm_head;
     a.M = M;
@@ -811,14 +885,14 @@ int forward_block(dflash_ctx* ctx, hipStream_t st, const int* block_tokens, int 
     if (p.XL != 1) {
       // more rows than LDS holds: the final RMSNorm once into bf16 rows, which
       // the head streams through LDS windows (or reads from L2)
-      uint16_t* z = at<uint16_t>(ctx->ws, ctx->wl.z);
+      uint16_t* z = at<uint16_t>(ws, wl.z);
       e = launch_lm_norm_rows(a, z, st);
       if (e != hipSuccess) return hip_fail(e, "final norm");
       a.x = z;
     }
-    float* lg = logits ? logits : at<float>(ctx->ws, ctx->wl.logits);
+    float* lg = logits ? logits : at<float>(ws, wl.logits);
     const int tr = logits ? 0 : 1;
-    float* gm = at<float>(ctx->ws, ctx->wl.gmax);
+    float* gm = at<float>(ws, wl.gmax);
     {
       Timed tm(ctx, DFLASH_K_LMHEAD, st);
       e = launch_lm_logits(a, p, lg, tr, gm, st);

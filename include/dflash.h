@@ -225,6 +225,31 @@ int dflash_draft_block_n(dflash_ctx* ctx, void* stream, const int* block_tokens,
                          int block_len, float* logits, int* topk_ids, float* topk_vals, int k);
 
 /*
+ * dflash_draft_block for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same arguments and the same kernels, but the call's scratch (residual rows,
+ * split-K partials, attention chunk partials, the LM head's logits hand-off)
+ * lives in a static device array of the library, DFLASH_STATIC_SCRATCH_BYTES
+ * (64 MiB) on each GPU the library runs on, held until the process ends,
+ * instead of the bound workspace. The call allocates and frees nothing.
+ *   - A configuration whose draft needs more scratch than that
+ *     (dflash_draft_scratch_bytes) is refused with DFLASH_E_CAPACITY before any
+ *     launch. The state (ring, positions) is still the handle's bound state.
+ *   - Every call on one GPU, from any handle, uses that GPU's one array, which
+ *     keeps the last call's contents; nothing in it needs to start at zero
+ *     (each section a call reads is written earlier in the same call). Calls
+ *     that overlap on one GPU (two streams, two threads) race on the array:
+ *     order them.
+ * The device address of the array is looked up once per device, on the
+ * device's first call.
+ */
+#define DFLASH_STATIC_SCRATCH_BYTES (64u << 20)
+int dflash_draft_block_noalloc(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req,
+                               float* logits, int* topk_ids, float* topk_vals, int k);
+/* Scratch bytes dflash_draft_block_noalloc needs for `cfg` (0 on an invalid config). */
+size_t dflash_draft_scratch_bytes(const dflash_config* cfg);
+
+/*
  * First-mismatch accept for requests r < n_req.
  *   draft_ids:   element (r, j) at draft_ids[(r*(B-1) + j)*draft_stride], j < B-1
  *                (pass topk_ids with draft_stride = k).
