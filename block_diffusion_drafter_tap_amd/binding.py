@@ -98,6 +98,11 @@ def load(path: str = LIB_PATH):
                                          ctypes.POINTER(P)]),
         "dflash_verify_block": (c_int, [P, P, P, c_int, c_int, P, c_int, PP, c_ll, P, P]),
         "dflash_advance": (c_int, [P, P, P, c_int]),
+        "dflash_tree_build": (c_int, [P, P, P, P, P, c_int, c_int, c_int, P, P, P]),
+        "dflash_verify_tree": (c_int, [P, P, P, P, P, c_int, c_int, P, c_int, PP, c_ll, P, P]),
+        "dflash_tree_accept": (c_int, [P, P, P, P, c_int, P, c_int, c_int, P, P, P, P, P, P, P, P]),
+        "dflash_tree_commit": (c_int, [P, P, P, c_int, P, c_int]),
+        "dflash_tap_stage_rows": (c_int, [P, P, PP, c_ll, c_int, P, P, P, c_int]),
         "dflash_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -397,6 +402,98 @@ class Drafter:
             self.ctx, _stream(), block_tokens.data_ptr(), R, int(b), ctypes.cast(layers, c_void_p) if n else None, n,
             ctypes.cast(outs, PP) if n else None, int(ld), _ptr(logits), ids.data_ptr()))
         return ids
+
+    # ---------------------------------------------------------------- candidate trees
+    def tree_build(self, block_tokens: torch.Tensor, ids: torch.Tensor, vals: torch.Tensor, n_nodes: int):
+        """(tokens, parent, depth) int32 [R, n_nodes] of the candidate trees built from
+        the draft's top-k ids/values [R, block-1, k]."""
+        R, B = block_tokens.shape
+        k = ids.shape[-1]
+        _need(block_tokens, "block_tokens", torch.int32, shape=(R, self.cfg.block))
+        _need(ids, "ids", torch.int32, shape=(R, self.cfg.block - 1, k))
+        _need(vals, "vals", torch.float32, shape=(R, self.cfg.block - 1, k))
+        _on_device(block_tokens=block_tokens, ids=ids, vals=vals)
+        out = [torch.empty((R, n_nodes), dtype=torch.int32, device=self.device) for _ in range(3)]
+        _check("dflash_tree_build", self.lib.dflash_tree_build(
+            self.ctx, _stream(), block_tokens.data_ptr(), ids.data_ptr(), vals.data_ptr(), int(k), R, int(n_nodes),
+            *[t.data_ptr() for t in out]))
+        return tuple(out)
+
+    def verify_tree(self, tokens: torch.Tensor, parent: torch.Tensor, depth: torch.Tensor,
+                    tap_layers: Sequence[int] = (), tap_out: Sequence[torch.Tensor] = (),
+                    logits: Optional[torch.Tensor] = None):
+        """Tree-masked verify pass of a target handle: ids [R, n] (each node's greedy next token)."""
+        R, n = tokens.shape
+        for name, t in (("tokens", tokens), ("parent", parent), ("depth", depth)):
+            _need(t, name, torch.int32, shape=(R, n))
+        _need(logits, "logits", torch.float32, shape=(R, n, self.cfg.vocab), optional=True)
+        if len(tap_out) != len(tap_layers):
+            raise ValueError("tap_out and tap_layers must have the same length")
+        for i, t in enumerate(tap_out):
+            _need(t, f"tap_out[{i}]", torch.float32, min_rows=R * n)
+            if t.dim() != 2 or t.shape[1] < self.cfg.hidden or t.stride(1) != 1 or t.stride(0) != tap_out[0].stride(0):
+                raise ValueError(f"tap_out[{i}] must be [rows, >= hidden] with one row pitch for all taps")
+        _on_device(tokens=tokens, parent=parent, depth=depth, logits=logits, tap_out=list(tap_out))
+        ids = torch.empty((R, n), dtype=torch.int32, device=self.device)
+        m = len(tap_layers)
+        layers = (ctypes.c_int * max(m, 1))(*tap_layers)
+        outs = (c_void_p * max(m, 1))(*[t.data_ptr() for t in tap_out])
+        ld = tap_out[0].stride(0) if m else 0
+        _check("dflash_verify_tree", self.lib.dflash_verify_tree(
+            self.ctx, _stream(), tokens.data_ptr(), parent.data_ptr(), depth.data_ptr(), R, int(n),
+            ctypes.cast(layers, c_void_p) if m else None, m, ctypes.cast(outs, PP) if m else None, int(ld),
+            _ptr(logits), ids.data_ptr()))
+        return ids
+
+    def tree_accept(self, tokens: torch.Tensor, parent: torch.Tensor, verify_ids: torch.Tensor, eos_id: int = -1,
+                    budget: Optional[torch.Tensor] = None):
+        """Tree accept on a drafter handle; returns the outputs of dflash_tree_accept."""
+        R, n = tokens.shape
+        B = self.cfg.block
+        for name, t in (("tokens", tokens), ("parent", parent), ("verify_ids", verify_ids)):
+            _need(t, name, torch.int32, shape=(R, n))
+        _need(budget, "budget", torch.int32, shape=(R,), optional=True)
+        _on_device(tokens=tokens, parent=parent, verify_ids=verify_ids, budget=budget)
+        out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
+               "n_emit": torch.empty(R, dtype=torch.int32, device=self.device)}
+        for name in ("emitted", "next_tokens", "path_nodes", "stage_rows", "stage_pos"):
+            out[name] = torch.empty((R, B), dtype=torch.int32, device=self.device)
+        _check("dflash_tree_accept", self.lib.dflash_tree_accept(
+            self.ctx, _stream(), tokens.data_ptr(), parent.data_ptr(), int(n), verify_ids.data_ptr(), R, int(eos_id),
+            _ptr(budget), out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
+            out["next_tokens"].data_ptr(), out["path_nodes"].data_ptr(), out["stage_rows"].data_ptr(),
+            out["stage_pos"].data_ptr()))
+        return out
+
+    def tree_commit(self, path_nodes: torch.Tensor, n_emit: torch.Tensor):
+        """Commit a target's tree pass (K/V of the committed nodes into place, pos += n_emit)."""
+        R, ld = path_nodes.shape
+        _need(path_nodes, "path_nodes", torch.int32, shape=(R, ld))
+        _need(n_emit, "n_emit", torch.int32, shape=(R,))
+        _on_device(path_nodes=path_nodes, n_emit=n_emit)
+        _check("dflash_tree_commit", self.lib.dflash_tree_commit(
+            self.ctx, _stream(), path_nodes.data_ptr(), int(ld), n_emit.data_ptr(), R))
+
+    def tap_stage_rows(self, taps: Sequence[torch.Tensor], src_row: torch.Tensor, pos_of_row: torch.Tensor,
+                       rows_per_req: int, req_of_row: Optional[torch.Tensor] = None):
+        """Stage the tap rows src_row[m] of `taps` (e.g. a tree pass's committed nodes)."""
+        c = self.cfg
+        n_rows = src_row.numel()
+        if len(taps) != c.n_taps:
+            raise ValueError(f"taps: expected {c.n_taps} tensors (got {len(taps)})")
+        for i, t in enumerate(taps):
+            _need(t, f"taps[{i}]", torch.float32)
+            if t.dim() != 2 or t.shape[1] < c.hc_streams * c.tap_hidden or t.stride(1) != 1 or \
+                    t.stride(0) != taps[0].stride(0):
+                raise ValueError(f"taps[{i}] must be [rows, >= {c.hc_streams * c.tap_hidden}] with one row pitch")
+        _need(src_row, "src_row", torch.int32, shape=(n_rows,))
+        _need(pos_of_row, "pos_of_row", torch.int32, shape=(n_rows,))
+        _need(req_of_row, "req_of_row", torch.int32, shape=(n_rows,), optional=True)
+        _on_device(taps=list(taps), src_row=src_row, pos_of_row=pos_of_row, req_of_row=req_of_row)
+        arr = (c_void_p * len(taps))(*[t.data_ptr() for t in taps])
+        _check("dflash_tap_stage_rows", self.lib.dflash_tap_stage_rows(
+            self.ctx, _stream(), ctypes.cast(arr, PP), int(taps[0].stride(0)), int(n_rows), src_row.data_ptr(),
+            _ptr(req_of_row), pos_of_row.data_ptr(), int(rows_per_req)))
 
     def advance(self, n_emit: torch.Tensor):
         _need(n_emit, "n_emit", torch.int32, shape=(n_emit.numel(),) if isinstance(n_emit, torch.Tensor) else None)

@@ -64,7 +64,7 @@ int attn_nchunks(const dflash_config& c) {
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, z, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, total;
+  size_t h, ssq, q, o, act, z, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, anc, total;
 };
 
 struct GemmShape {
@@ -140,6 +140,7 @@ WsLayout ws_layout(const dflash_config& c, bool draft_only = false) {
   const size_t lm_rows = Mmax <= 16 ? 16 : (Mmax <= 32 ? 32 : 64 * ((Mmax + 63) / 64));
   L.logits = take(lm_rows * c.vocab * 4);           // transposed logits when the caller passes none
   L.gmax = take(out_rows * ((c.vocab + 15) / 16) * 4);   // per-16-column maxima of the logits
+  L.anc = take(Mmax * 8);                                  // ancestor masks of a tree pass's rows
   L.total = off;
   return L;
 }
@@ -281,7 +282,7 @@ size_t ring_layer_elems(const dflash_config& g) {
 // layer's context K/V as tiled GEMMs (the K/V tiles end in the head epilogue:
 // k RMSNorm, RoPE at each row's position, K and V into the rings).
 int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, long long tap_row_stride, int n_rows,
-                  const int* req_of_row, const int* pos_of_row, int rows_per_req) {
+                  const int* src_row, const int* req_of_row, const int* pos_of_row, int rows_per_req) {
   const dflash_config& g = ctx->cfg;
   const int H = g.hidden, hd = g.head_dim, TW = g.n_taps * g.tap_hidden;
   const int nkv_w = 2 * g.n_kv_heads * hd;
@@ -294,6 +295,7 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     memset(&tg, 0, sizeof tg);
     for (int t = 0; t < g.n_taps; ++t) tg.taps[t] = taps[t];
     tg.tap_stride = tap_row_stride;
+    tg.src_row = src_row;
     tg.n_taps = g.n_taps;
     tg.hc = g.hc_streams;
     tg.tap_hidden = g.tap_hidden;
@@ -332,7 +334,8 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
 
 int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st, const int* block_tokens, int n_req,
                   int block_len, int causal, const int* tap_layers, int n_tap_out, float* const* tap_out,
-                  long long tap_ld, int first_row, float* logits, int* topk_ids, float* topk_vals, int k);
+                  long long tap_ld, int first_row, float* logits, int* topk_ids, float* topk_vals, int k,
+                  const int* rope_off = nullptr);
 
 }  // namespace
 
@@ -456,8 +459,12 @@ int dflash_reset(dflash_ctx* ctx, void* stream, int req, int valid_from, int pos
   return DFLASH_OK;
 }
 
-int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, long long tap_row_stride,
-                     int n_rows, const int* req_of_row, const int* pos_of_row, int rows_per_req) {
+}  // extern "C"
+
+namespace {
+
+int tap_stage_impl(dflash_ctx* ctx, void* stream, const float* const* taps, long long tap_row_stride, int n_rows,
+                   const int* src_row, const int* req_of_row, const int* pos_of_row, int rows_per_req) {
   if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
   if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
   const dflash_config& g = ctx->cfg;
@@ -479,12 +486,13 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
   const int H = g.hidden, hd = g.head_dim;
   hipError_t e;
   if (n_rows >= PREFILL_MIN_ROWS && prefill_enabled(g))
-    return stage_prefill(ctx, st, taps, tap_row_stride, n_rows, req_of_row, pos_of_row, rows_per_req);
+    return stage_prefill(ctx, st, taps, tap_row_stride, n_rows, src_row, req_of_row, pos_of_row, rows_per_req);
 
   // fc over the gathered taps
   GemmArgs a = base_args(ctx);
   for (int t = 0; t < g.n_taps; ++t) a.taps[t] = taps[t];
   a.tap_stride = tap_row_stride;
+  a.src_row = src_row;
   a.n_taps = g.n_taps;
   a.hc = g.hc_streams;
   a.tap_hidden = g.tap_hidden;
@@ -511,6 +519,7 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
       memset(&tg, 0, sizeof tg);
       for (int t = 0; t < g.n_taps; ++t) tg.taps[t] = taps[t];
       tg.tap_stride = tap_row_stride;
+      tg.src_row = src_row;
       tg.n_taps = g.n_taps;
       tg.hc = g.hc_streams;
       tg.tap_hidden = g.tap_hidden;
@@ -577,6 +586,22 @@ int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, lo
     if (e != hipSuccess) return hip_fail(e, "stage kv");
   }
   return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_tap_stage(dflash_ctx* ctx, void* stream, const float* const* taps, long long tap_row_stride,
+                     int n_rows, const int* req_of_row, const int* pos_of_row, int rows_per_req) {
+  return tap_stage_impl(ctx, stream, taps, tap_row_stride, n_rows, nullptr, req_of_row, pos_of_row, rows_per_req);
+}
+
+int dflash_tap_stage_rows(dflash_ctx* ctx, void* stream, const float* const* taps, long long tap_row_stride,
+                          int n_rows, const int* src_row, const int* req_of_row, const int* pos_of_row,
+                          int rows_per_req) {
+  if (!src_row) return fail(DFLASH_E_ARG, "src_row is required");
+  return tap_stage_impl(ctx, stream, taps, tap_row_stride, n_rows, src_row, req_of_row, pos_of_row, rows_per_req);
 }
 
 int dflash_draft_block(dflash_ctx* ctx, void* stream, const int* block_tokens, int n_req, float* logits,
@@ -690,6 +715,94 @@ int dflash_verify_block(dflash_ctx* ctx, void* stream, const int* block_tokens, 
                        n_tap_out, tap_out, tap_ld, 0, logits, ids, nullptr, 1);
 }
 
+int dflash_tree_build(dflash_ctx* ctx, void* stream, const int* block_tokens, const int* topk_ids,
+                      const float* topk_vals, int k, int n_req, int n_nodes, int* tree_tokens, int* tree_parent,
+                      int* tree_depth) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  const dflash_config& g = ctx->cfg;
+  if (!block_tokens || !topk_ids || !topk_vals || !tree_tokens || !tree_parent || !tree_depth)
+    return fail(DFLASH_E_ARG, "block_tokens, topk_ids, topk_vals and the three tree outputs are required");
+  if (n_req < 1 || n_req > g.max_requests) return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (g.block < 2) return fail(DFLASH_E_SHAPE, "a tree needs draft positions (block >= 2)");
+  if (k < 1 || k > 16) return fail(DFLASH_E_ARG, "k must be in [1, 16] (got %d)", k);
+  if (n_nodes < 1 || n_nodes > 64) return fail(DFLASH_E_SHAPE, "n_nodes %d outside [1, 64]", n_nodes);
+  // nodes available: 1 + k + k^2 + ... + k^(B-1), saturated
+  long long avail = 1, level = 1;
+  for (int d = 1; d < g.block && avail < n_nodes; ++d) {
+    level = level * k > 64 ? 64 : level * k;
+    avail += level;
+  }
+  if (n_nodes > avail) return fail(DFLASH_E_SHAPE, "n_nodes %d exceeds the %lld nodes the lists offer", n_nodes, avail);
+  hipError_t e = launch_tree_build(block_tokens, g.block, topk_ids, topk_vals, k, n_req, n_nodes, tree_tokens,
+                                   tree_parent, tree_depth, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree build");
+  return DFLASH_OK;
+}
+
+int dflash_verify_tree(dflash_ctx* ctx, void* stream, const int* tree_tokens, const int* tree_parent,
+                       const int* tree_depth, int n_req, int n_nodes, const int* tap_layers, int n_tap_out,
+                       float* const* tap_out, long long tap_ld, float* logits, int* ids) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (!ctx->target) return fail(DFLASH_E_STATE, "verify passes need a target handle (dflash_create_target)");
+  const dflash_config& g = ctx->cfg;
+  if (!tree_tokens || !tree_parent || !tree_depth || !ids)
+    return fail(DFLASH_E_ARG, "tree_tokens, tree_parent, tree_depth and ids are required");
+  if (n_req < 1 || n_req > g.max_requests) return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (n_nodes < 1 || n_nodes > g.block || n_nodes > 64)
+    return fail(DFLASH_E_SHAPE, "n_nodes %d outside [1, min(block %d, 64)]", n_nodes, g.block);
+  if (n_tap_out < 0 || n_tap_out > MAX_TAPS || (n_tap_out > 0 && (!tap_layers || !tap_out)))
+    return fail(DFLASH_E_ARG, "n_tap_out must be in [0, %d] with tap_layers and tap_out given", MAX_TAPS);
+  for (int t = 0; t < n_tap_out; ++t) {
+    if (tap_layers[t] < 0 || tap_layers[t] >= g.n_layers)
+      return fail(DFLASH_E_ARG, "tap_layers[%d] = %d outside [0, %d)", t, tap_layers[t], g.n_layers);
+    if (!tap_out[t] || ((uintptr_t)tap_out[t] & 15)) return fail(DFLASH_E_ARG, "tap_out[%d] must be 16-byte aligned", t);
+  }
+  if (n_tap_out > 0 && (tap_ld < g.hidden || tap_ld % 4)) return fail(DFLASH_E_ARG, "tap_ld must be >= hidden, % 4 == 0");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_tree_anc(tree_parent, n_nodes, n_nodes, n_req, at<unsigned long long>(ctx->ws, ctx->wl.anc), st);
+  if (e != hipSuccess) return hip_fail(e, "tree masks");
+  return forward_block(ctx, ctx->ws, ctx->wl, st, tree_tokens, n_req, n_nodes, 2, tap_layers, n_tap_out, tap_out,
+                       tap_ld, 0, logits, ids, nullptr, 1, tree_depth);
+}
+
+int dflash_tree_accept(dflash_ctx* ctx, void* stream, const int* tree_tokens, const int* tree_parent, int n_nodes,
+                       const int* verify_ids, int n_req, int eos_id, const int* budget, int* accept_len, int* emitted,
+                       int* n_emit, int* next_tokens, int* path_nodes, int* stage_rows, int* stage_pos) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  const dflash_config& g = ctx->cfg;
+  if (!tree_tokens || !tree_parent || !verify_ids || !accept_len || !emitted || !n_emit || !path_nodes ||
+      !stage_rows || !stage_pos)
+    return fail(DFLASH_E_ARG, "the tree, verify_ids and every output except next_tokens are required");
+  if (n_req < 1 || n_req > g.max_requests) return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (n_nodes < 1 || n_nodes > 64) return fail(DFLASH_E_SHAPE, "n_nodes %d outside [1, 64]", n_nodes);
+  hipError_t e = launch_tree_accept(tree_tokens, tree_parent, n_nodes, verify_ids, n_req, g.block, g.block, eos_id,
+                                    budget, g.mask_id, accept_len, emitted, n_emit, next_tokens, path_nodes,
+                                    stage_rows, stage_pos, at<int>(ctx->state, ctx->sl.pos),
+                                    at<unsigned long long>(ctx->state, ctx->sl.stats), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree accept");
+  return DFLASH_OK;
+}
+
+int dflash_tree_commit(dflash_ctx* ctx, void* stream, const int* path_nodes, int path_ld, const int* n_emit,
+                       int n_req) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  if (!ctx->target) return fail(DFLASH_E_STATE, "only a target handle commits a tree pass");
+  const dflash_config& g = ctx->cfg;
+  if (!path_nodes || !n_emit) return fail(DFLASH_E_ARG, "path_nodes and n_emit are required");
+  if (n_req < 1 || n_req > g.max_requests) return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (path_ld < 1 || path_ld > 64) return fail(DFLASH_E_ARG, "path_ld %d outside [1, 64]", path_ld);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_tree_commit(at<uint16_t>(ctx->state, ctx->sl.ring_k), at<uint16_t>(ctx->state, ctx->sl.ring_v),
+                                    ring_layer_elems(g), g.n_layers, n_req, g.n_kv_heads, g.head_dim,
+                                    g.ring_capacity, at<int>(ctx->state, ctx->sl.pos), path_nodes, path_ld, n_emit, st);
+  if (e == hipSuccess) e = launch_advance(at<int>(ctx->state, ctx->sl.pos), n_emit, n_req, st);
+  if (e != hipSuccess) return hip_fail(e, "tree commit");
+  return DFLASH_OK;
+}
+
 int dflash_advance(dflash_ctx* ctx, void* stream, const int* n_emit, int n_req) {
   if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
   if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
@@ -711,7 +824,8 @@ namespace {
 // residual rows after the tapped layers copied out).
 int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st, const int* block_tokens, int n_req,
                   int block_len, int causal, const int* tap_layers, int n_tap_out, float* const* tap_out,
-                  long long tap_ld, int first_row, float* logits, int* topk_ids, float* topk_vals, int k) {
+                  long long tap_ld, int first_row, float* logits, int* topk_ids, float* topk_vals, int k,
+                  const int* rope_off) {
   const dflash_config& g = ctx->cfg;
   // GEMM arguments with this call's split-K partial buffer
   auto base = [&]() {
@@ -762,6 +876,7 @@ int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st,
       a.ring_k = rk;
       a.ring_v = rv;
       a.rows_per_req = B;
+      a.rope_off = rope_off;
       GemmPlan p = plan_for(g, M, a.N, H, hd, 0, P_QKV);
       Timed tm(ctx, DFLASH_K_QKV, st);
       if (p.S > 1) {
@@ -794,6 +909,7 @@ int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st,
       t.part_ml = at<float>(ws, wl.attn_ml);
       t.err = err;
       t.causal = causal;
+      t.anc = causal == 2 ? at<unsigned long long>(ws, wl.anc) : nullptr;
       Timed tm(ctx, DFLASH_K_ATTN, st);
       e = launch_attention(t, n_req, st);
       if (e != hipSuccess) return hip_fail(e, "attention");

@@ -1,7 +1,8 @@
 // Block attention for gfx950: every block query attends to the context window
 // [lo, pos) and to all B block rows [pos, pos+B), with no mask inside (the block
 // is bidirectional; a causal target's verify pass sets `causal`, and block row i
-// then sees block rows j <= i only). Keys and values of both live in the per-request ring (the
+// then sees block rows j <= i only; a tree pass, causal = 2, lets row i see the
+// block rows that are its ancestors in the candidate tree, itself included). Keys and values of both live in the per-request ring (the
 // block's own K/V were written to slots pos..pos+B-1 by the QKV epilogue), so a
 // query sees one contiguous position range [lo, pos+B).
 //
@@ -134,6 +135,11 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
   // phase 1: scores of sub-tile `wave`; lane holds, for query slot qt*16 + lr,
   // keys k0 + 8*lg + e (e = 4*kt + i)
   float p[QT][8];
+  // a tree pass: the ancestor mask of each of this lane's query rows
+  unsigned long long anc[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+    anc[qt] = a.causal == 2 ? a.anc[(size_t)r * a.B + (s0 + qt * 16 + lr) % a.B] : 0ull;
   // no per-key mask needed: the sub-tile lies inside the window (and, for a
   // causal pass, before the block)
   const bool interior = k0 >= kr.lo && k0 + 32 <= (a.causal ? kr.pos : kr.hi);
@@ -150,7 +156,11 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 8 * lg + 4 * kt + i;
-        const bool ok = interior || (key >= kr.lo && key < kr.hi && (!a.causal || key <= kr.pos + iq));
+        bool ok = interior || (key >= kr.lo && key < kr.hi);
+        if (!interior && key >= kr.pos) {
+          if (a.causal == 1) ok = ok && key <= kr.pos + iq;
+          else if (a.causal == 2) ok = ok && ((anc[qt] >> (key - kr.pos)) & 1ull);
+        }
         p[qt][4 * kt + i] = ok ? acc[i] * a.scale_log2 : -INFINITY;
       }
     }

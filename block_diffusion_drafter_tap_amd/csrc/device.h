@@ -121,17 +121,22 @@ DEV void set_error(unsigned* err, unsigned bit) {
 // slot holds another live row of the request. The live positions are the
 // window and the block, [pos - W, pos + B) with C >= W + B, so a row at p may
 // use slot p mod C only for p in [pos + B - C, pos + C - W).
+// *rp is the position RoPE uses: the row's own, or pos[req] + rope_off[m] for a
+// tree row, whose ring slot follows its row index but whose position is pos +
+// its depth.
 template <class A>
-DEV unsigned ring_row(const A& a, int m, int* req, long long* p) {
+DEV unsigned ring_row(const A& a, int m, int* req, long long* p, long long* rp) {
   const int r = a.req_of_row ? a.req_of_row[m] : m / a.rows_per_req;
   *req = r;
   *p = -1;
+  *rp = -1;
   if (r < 0 || r >= a.Rmax) return ERR_BAD_ROW;
   const long long base = a.pos[r];
   const long long q = a.pos_of_row ? (long long)a.pos_of_row[m] : base + m % a.rows_per_req;
   if (q < 0) return ERR_BAD_POSITION;
   if (q < base + a.B - a.C || q >= base + a.C - a.win) return ERR_RING_CAPACITY;
   *p = q;
+  *rp = a.rope_off ? base + a.rope_off[m] : q;
   return 0u;
 }
 

@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
   const float s2 = sum_splits(P, S, stride, base + (on ? lane + half : 0));
   const float x1 = on ? s1 : 0.f, x2 = on ? s2 : 0.f;
   int req;
-  long long p;
-  const unsigned bad = ring_row(a, m, &req, &p);
+  long long p, rp;
+  const unsigned bad = ring_row(a, m, &req, &p, &rp);
   if (bad) {
     if (lane == 0) set_error(a.err, bad);
     return;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
     const float y1 = x1 * inv * bfbits2f(g[lane]);
     const float y2 = x2 * inv * bfbits2f(g[lane + half]);
     float c, s;
-    rope_cos_sin(p, lane, hd, a.log2_theta, &c, &s);
+    rope_cos_sin(rp, lane, hd, a.log2_theta, &c, &s);
     uint16_t* o = is_q ? a.q_out + (size_t)m * a.nq * hd + (size_t)head * hd
                        : ring_k + (((size_t)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * hd;
     o[lane] = f2bfbits(y1 * c - y2 * s);

@@ -80,7 +80,8 @@ DEV u32x4 load_x(const GemmArgs& a, int row, int k, float inv) {
   } else {
     const int t = k / a.tap_hidden;
     const int col = k - t * a.tap_hidden;
-    return hc_mean8_bf16(tap_ptr(a, t) + (size_t)row * a.tap_stride + col, (size_t)a.tap_hidden, a.hc);
+    const int src = a.src_row ? a.src_row[row] : row;
+    return hc_mean8_bf16(tap_ptr(a, t) + (size_t)src * a.tap_stride + col, (size_t)a.tap_hidden, a.hc);
   }
 }
 
@@ -92,8 +93,8 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
   for (int r = wave; r < rows; r += NW) {
     const int m = m0 + r;
     int req;
-    long long p;
-    const unsigned bad = ring_row(a, m, &req, &p);
+    long long p, rp;
+    const unsigned bad = ring_row(a, m, &req, &p, &rp);
     if (bad) {
       if (lane == 0) set_error(a.err, bad);
       continue;
@@ -108,7 +109,7 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
         const float x1 = tile[r][d] * inv * bfbits2f(g[d]);
         const float x2 = tile[r][d + half] * inv * bfbits2f(g[d + half]);
         float c, s;
-        rope_cos_sin(p, d, hd, a.log2_theta, &c, &s);
+        rope_cos_sin(rp, d, hd, a.log2_theta, &c, &s);
         const uint16_t y1 = f2bfbits(x1 * c - x2 * s);
         const uint16_t y2 = f2bfbits(x2 * c + x1 * s);
         if (is_q) {

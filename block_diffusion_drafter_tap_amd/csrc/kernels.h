@@ -63,6 +63,8 @@ struct GemmArgs {
   const int* req_of_row;  // NULL -> row / rows_per_req
   const int* pos_of_row;  // NULL -> pos[req] + row % rows_per_req
   int rows_per_req;
+  const int* rope_off;    // NULL, or per row: RoPE at pos[req] + rope_off[row] (a tree row's depth), ring slot unchanged
+  const int* src_row;     // NULL, or per row: the tap row X_TAPS reads for it
   unsigned* err;
   // B: the configured block (the ring's live range is [pos - win, pos + B)),
   // except for the LM head, where it is the call's block length. LM head: rows
@@ -116,7 +118,9 @@ struct AttnArgs {
   const int* pos;
   const int* valid_from;
   int B, W, C, nq, nkv, hd, kc, n_chunks;
-  int causal;              // 1: block query i sees block keys j <= i only (a target verify pass)
+  int causal;              // 1: block query i sees block keys j <= i only (a target verify pass);
+                           // 2: block query i sees block key j iff bit j of anc[r * B + i] is set (a tree pass)
+  const unsigned long long* anc;   // [R][B] ancestor masks of the tree rows (causal == 2)
   int R;                   // requests of this launch (set by launch_attention)
   int hs;                  // query-slot parts per (chunk, kv head) (set by launch_attention)
   float scale_log2;        // log2(e) / sqrt(hd)
@@ -147,6 +151,7 @@ hipError_t launch_finish_store(const float* P, int S, int M, int N, void* out, i
 struct TapGather {
   const float* taps[MAX_TAPS];
   long long tap_stride;
+  const int* src_row;   // NULL, or the tap row to read for each output row
   int n_taps, hc, tap_hidden;
   uint16_t* out;   // [M][n_taps * tap_hidden]
 };
@@ -169,6 +174,20 @@ hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStrea
 // Verify pass of a causal target: copy the residual rows h [M][H] of a tapped
 // layer to a tap buffer with row pitch ld; add n_emit to the positions.
 hipError_t launch_copy_rows(const float* h, int M, int H, float* dst, long long ld, hipStream_t st);
+
+// Candidate trees (tree.hip): build from top-k lists, accept, ancestor masks of
+// the tree rows, and the commit of a target's tree pass (K/V of the committed
+// nodes to consecutive ring slots).
+hipError_t launch_tree_build(const int* block_tokens, int B, const int* ids, const float* vals, int k, int R, int n,
+                             int* tok, int* par, int* dep, hipStream_t st);
+hipError_t launch_tree_accept(const int* tok, const int* par, int n, const int* verify, int R, int B, int stats_b,
+                              int eos, const int* budget, int mask_id, int* accept_len, int* emitted, int* n_emit,
+                              int* next_tokens, int* path_nodes, int* stage_rows, int* stage_pos, int* pos,
+                              unsigned long long* stats, hipStream_t st);
+hipError_t launch_tree_anc(const int* par, int n, int rows, int R, unsigned long long* anc, hipStream_t st);
+hipError_t launch_tree_commit(uint16_t* ring_k, uint16_t* ring_v, size_t layer_elems, int L, int R, int nkv, int hd,
+                              int C, const int* pos, const int* path_nodes, int path_ld, const int* n_emit,
+                              hipStream_t st);
 hipError_t launch_advance(int* pos, const int* n_emit, int n_req, hipStream_t st);
 
 // Small kernels.

@@ -33,8 +33,9 @@ __global__ __launch_bounds__(256) void tap_gather_kernel(const TapGather g) {
 #pragma unroll
   for (int i = 1; i < MAX_TAPS; ++i)
     if (t == i) tp = g.taps[i];
+  const int src = g.src_row ? g.src_row[m] : m;
   *(u32x4*)(g.out + (size_t)m * g.n_taps * g.tap_hidden + e) =
-      hc_mean8_bf16(tp + (size_t)m * g.tap_stride + col, (size_t)g.tap_hidden, g.hc);
+      hc_mean8_bf16(tp + (size_t)src * g.tap_stride + col, (size_t)g.tap_hidden, g.hc);
 }
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_HEADS = 2 };
@@ -234,8 +235,8 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
     const int rows = min(PF_BM, a.M - m0);
     for (int r = tid; r < rows; r += 256) {
       int req;
-      long long p;
-      const unsigned bad = ring_row(h, m0 + r, &req, &p);
+      long long p, rp;
+      const unsigned bad = ring_row(h, m0 + r, &req, &p, &rp);
       if (bad) set_error(h.err, bad);
       s_req[r] = req;
       s_pos[r] = p < 0 ? -1 : (int)p;

@@ -310,6 +310,81 @@ int dflash_verify_block(dflash_ctx* ctx, void* stream, const int* block_tokens, 
                         const int* tap_layers, int n_tap_out, float* const* tap_out, long long tap_ld,
                         float* logits, int* ids);
 
+/*
+ * Candidate trees from the drafter's top-k lists (tree speculation). The pages
+ * keep top-16 candidates per draft position and hand them to a path selector
+ * ("feat: DFlash2 block-diffusion drafter for Qwen 3.8", Mference PR #22,
+ * "What's here" and the Metal-port commit; a tree verify round appears in
+ * "dflash: the chain verify builds pipelined ...", mlx-serve PR #937) without
+ * giving its rule. The rule here: node 0 is the root (block token 0 of the
+ * request); a node at depth d holds one of the k candidates of draft position
+ * d and its children are the candidates of position d + 1; candidate j of a
+ * list has log-probability lp = (v[j] - v[0]) - log(sum_j' exp(v[j'] - v[0]))
+ * (fp64, list order) and a node's score is the sum of lp along its path. The
+ * tree is the root, the top-1 chain (up to depth min(block - 1, n_nodes - 1)),
+ * then, best first, the highest-scoring child of any node in the tree, ties
+ * to the smaller depth, then the smaller parent index, then the smaller rank;
+ * nodes are numbered in that order (a parent precedes its children).
+ *   block_tokens: [n_req, block]; topk_ids / topk_vals: [n_req, block-1, k], as
+ *                 dflash_draft_block writes them (k in [1, 16]);
+ *   n_nodes:      1..64, at most the number of nodes the lists offer;
+ *   tree_tokens, tree_parent (-1 for the root), tree_depth: int32 [n_req, n_nodes].
+ */
+int dflash_tree_build(dflash_ctx* ctx, void* stream, const int* block_tokens, const int* topk_ids,
+                      const float* topk_vals, int k, int n_req, int n_nodes, int* tree_tokens,
+                      int* tree_parent, int* tree_depth);
+
+/*
+ * Tree-masked verify pass of a target handle: node i of request r is a row at
+ * position pos[r] + tree_depth[r][i] that attends to the window and to its own
+ * ancestors (itself included); its K/V go to ring slot pos[r] + i. Outputs as
+ * dflash_verify_block with block_len = n_nodes (n_nodes <= cfg.block): ids
+ * [n_req, n_nodes] = the target's greedy next token after each node's path,
+ * tap rows [n_req * n_nodes] (pitch tap_ld), optional logits. Follow with
+ * dflash_tree_commit once the accept is known.
+ */
+int dflash_verify_tree(dflash_ctx* ctx, void* stream, const int* tree_tokens, const int* tree_parent,
+                       const int* tree_depth, int n_req, int n_nodes, const int* tap_layers, int n_tap_out,
+                       float* const* tap_out, long long tap_ld, float* logits, int* ids);
+
+/*
+ * Tree accept on a drafter handle: from the root, move to the child whose
+ * token equals the target's token at the current node (verify_ids [n_req,
+ * n_nodes] from dflash_verify_tree), while one exists; emitted = the walked
+ * tokens then the target's token at the last node; EOS/budget clamps as in
+ * dflash_accept; pos[r] += n_emit[r]. Outputs (int32, [n_req, cfg.block] unless
+ * noted): accept_len [n_req], emitted (padded with -1), n_emit [n_req],
+ * next_tokens (nullable) = [last emitted, mask_id, ...], path_nodes = the
+ * committed nodes (root first; entries past n_emit repeat the last one),
+ * stage_rows = r * n_nodes + path_nodes (the verify tap rows to stage) and
+ * stage_pos = the old pos[r] + d: the arguments of dflash_tap_stage_rows for
+ * the committed rows (entries past n_emit stage at positions the next round
+ * overwrites, as the chain's rejected verify rows are).
+ */
+int dflash_tree_accept(dflash_ctx* ctx, void* stream, const int* tree_tokens, const int* tree_parent, int n_nodes,
+                       const int* verify_ids, int n_req, int eos_id, const int* budget, int* accept_len,
+                       int* emitted, int* n_emit, int* next_tokens, int* path_nodes, int* stage_rows,
+                       int* stage_pos);
+
+/*
+ * Commit of a target's tree pass: for every layer, the K/V of node
+ * path_nodes[r][d] (ring slot pos + node) moves to slot pos + d, d < n_emit[r];
+ * then pos[r] += n_emit[r]. path_nodes: [n_req, path_ld] (dflash_tree_accept's,
+ * path_ld = the drafter's block).
+ */
+int dflash_tree_commit(dflash_ctx* ctx, void* stream, const int* path_nodes, int path_ld, const int* n_emit,
+                       int n_req);
+
+/*
+ * dflash_tap_stage where row m of the call reads tap row src_row[m] (device
+ * int32 [n_rows]) of the tap buffers: stages a subset of a verify pass's rows,
+ * e.g. the committed nodes of a tree pass (dflash_tree_accept's stage_rows with
+ * pos_of_row = its stage_pos and rows_per_req = the drafter's block).
+ */
+int dflash_tap_stage_rows(dflash_ctx* ctx, void* stream, const float* const* taps, long long tap_row_stride,
+                          int n_rows, const int* src_row, const int* req_of_row, const int* pos_of_row,
+                          int rows_per_req);
+
 /* pos[r] += n_emit[r] for r < n_req (n_emit: device int32 [n_req], e.g. the
  * drafter's dflash_accept output), enqueued on `stream`: commits a target's
  * accepted rows. */
