@@ -174,6 +174,101 @@ def verify_report(cfg, dev, n_layers: int = 36, steps: int = 20) -> dict:
             "graph_frac": None if graph_ms is None else round(nbytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def tree_report(cfg, dr, tokens, k: int, dev, node_counts=(16, 32, 64), rounds: int = 200, seed: int = 5) -> dict:
+    """Candidate trees from this drafter's top-16 lists: the mean tokens per
+    round of trees of node_counts verify rows against the top-1 chain (block
+    rows) under a synthetic target, and the time of the tree build and tree
+    accept kernels (back-to-back launches of the largest tree). The synthetic
+    target's token at draft position d is the drafter's rank-j candidate: rank 0
+    with probability 0.75 (the chain's geometric accept profile), a listed rank
+    1..15 with probability 0.2 (rank j with weight 2^-j), otherwise a token
+    outside the list. Every tree and the chain walk the same draws. The tree
+    takes the whole top-1 chain first, so with block B a tree gains over the
+    chain only beyond B nodes."""
+    import numpy as np
+    import torch
+    from block_diffusion_drafter_tap_amd import binding, config, synth
+
+    B = cfg.block
+    if k != 16 or B < 2:
+        return None
+    ids = torch.empty((1, B - 1, 16), dtype=torch.int32, device=dev)
+    vals = torch.empty((1, B - 1, 16), dtype=torch.float32, device=dev)
+    blk = tokens[:1].contiguous()
+    # an accept-only handle of the same block (the accept needs the block, the mask id and positions)
+    acfg = config.tiny(block=B)
+    acc_h = binding.Drafter(acfg, synth.make_weights(acfg, seed=0, device=dev), device=dev)
+    rng = np.random.default_rng(seed)
+    w_rank = 0.5 ** np.arange(1, 16)
+    w_rank /= w_rank.sum()
+    tau = {n: 0 for n in node_counts}
+    tau_chain = 0
+    for _ in range(rounds):
+        dr.draft_block(blk, k=16, ids=ids, vals=vals)
+        u = rng.random(B - 1)
+        ranks = np.where(u < 0.75, 0, np.where(u < 0.95, 1 + rng.choice(15, size=B - 1, p=w_rank), -1))
+        il = ids[0].cpu().numpy()
+        g = np.array([il[d, r] if r >= 0 else cfg.vocab + d for d, r in enumerate(ranks)] + [0], dtype=np.int32)
+        tau_chain += 1 + int(next((d for d, r in enumerate(ranks) if r != 0), B - 1))
+        for n in node_counts:
+            tok, par, dep = dr.tree_build(blk, ids, vals, n)
+            verify = torch.from_numpy(g[np.minimum(dep[0].cpu().numpy(), B - 1)]).view(1, -1).to(dev)
+            acc_h.reset(0, 0, 100)
+            tau[n] += int(acc_h.tree_accept(tok, par, verify)["n_emit"][0])
+    n = max(node_counts)
+    tok, par, dep = dr.tree_build(blk, ids, vals, n)
+    verify = torch.zeros((1, n), dtype=torch.int32, device=dev)
+    acc_h.reset(0, 0, 100)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps = 100
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        dr.tree_build(blk, ids, vals, n)
+    ev[1].record()
+    for _ in range(reps):
+        acc_h.tree_accept(tok, par, verify)
+    ev[2].record()
+    torch.cuda.synchronize()
+    del acc_h
+    return {"rounds": rounds, "block": B, "tau_chain": round(tau_chain / rounds, 3),
+            "tau_tree": {str(m): round(tau[m] / rounds, 3) for m in node_counts},
+            "target_model": "synthetic: the target's token is the drafter's rank-0 candidate w.p. 0.75, "
+                            "a listed rank 1..15 (weight 2^-j) w.p. 0.2, unlisted otherwise",
+            "timed_nodes": n, "build_us": round(ev[0].elapsed_time(ev[1]) / reps * 1e3, 2),
+            "accept_us": round(ev[1].elapsed_time(ev[2]) / reps * 1e3, 2)}
+
+
+def sampling_report(cfg, dev, reps: int = 50) -> dict:
+    """Sampling-mode accept (typical acceptance 0.2, T 1.0, top-p 0.95, top-k
+    20) over one block of verify logits [R, B, V] fp32: the kernel pair's time
+    and its rate against the logits' bytes (read once algorithmically)."""
+    import numpy as np
+    import torch
+    from block_diffusion_drafter_tap_amd import binding, config, synth
+
+    R, B, V = cfg.max_requests, cfg.block, cfg.vocab
+    acfg = config.tiny(block=B, max_requests=R).replace(vocab=V)
+    h = binding.Drafter(acfg, synth.make_weights(acfg, seed=0, device=dev), device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    z = torch.randn((R, B, V), generator=g, device=dev) * 2.0
+    d = torch.argmax(z[:, : B - 1], dim=2).to(torch.int32).contiguous()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(reps + 5):
+        if i == 5:
+            ev[0].record()
+        h.accept_sampled(d, 1, z, temperature=1.0, top_k=20, top_p=0.95, eps=0.2, seed=1, round=i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+    nbytes = R * B * V * 4
+    del h
+    return {"logits_shape": [R, B, V], "us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "params": "typical 0.2, T 1.0, top-p 0.95, top-k 20"}
+
+
 def prefill_report(cfg, rows: int, ms: float) -> dict:
     """Prefill staging of one request's window (fc over the gathered taps, then
     every layer's context K/V into the ring): a dense contraction, reported
@@ -476,7 +571,12 @@ def main():
         "hbm_read_reference_gbps": round(read_gbps, 1),
         "draft_ms_by_block": draft_ms_by_block,
         "verify": None,
+        "tree": None,
+        "sampling": None,
     }
+    if R == 1 and not args.no_sweep:
+        result["tree"] = tree_report(cfg, dr, tokens, k, dev)
+        result["sampling"] = sampling_report(cfg, dev)
     if not args.no_verify and R == 1 and cfg.wfmt == config.WFMT_BF16:
         result["verify"] = verify_report(cfg, dev)
     if not args.no_cpu_baseline:

@@ -56,6 +56,15 @@ class dflash_state_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("pos", "valid_from", "error", "stats", "ring_k", "ring_v", "total")]
 
 
+class dflash_sampling(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("top_k", c_int), ("top_p", c_float), ("typical_eps", c_float),
+                ("typical_delta", c_float)]
+
+
+class dflash_block_policy(ctypes.Structure):
+    _fields_ = [("block", c_int), ("weight", ctypes.c_double), ("mean", ctypes.c_double)]
+
+
 class DFlashError(RuntimeError):
     def __init__(self, fn: str, code: int, msg: str):
         super().__init__(f"{fn} -> {STATUS.get(code, code)}: {msg}")
@@ -98,6 +107,11 @@ def load(path: str = LIB_PATH):
                                          ctypes.POINTER(P)]),
         "dflash_verify_block": (c_int, [P, P, P, c_int, c_int, P, c_int, PP, c_ll, P, P]),
         "dflash_advance": (c_int, [P, P, P, c_int]),
+        "dflash_accept_sampled": (c_int, [P, P, P, c_int, P, c_int, c_int, ctypes.POINTER(dflash_sampling),
+                                          ctypes.c_ulonglong, c_uint, c_int, P, P, P, P, P]),
+        "dflash_policy_init": (None, [ctypes.POINTER(dflash_block_policy), c_int, ctypes.c_double]),
+        "dflash_policy_next": (c_int, [ctypes.POINTER(dflash_block_policy)]),
+        "dflash_policy_update": (None, [ctypes.POINTER(dflash_block_policy), c_int]),
         "dflash_tree_build": (c_int, [P, P, P, P, P, c_int, c_int, c_int, P, P, P]),
         "dflash_verify_tree": (c_int, [P, P, P, P, P, c_int, c_int, P, c_int, PP, c_ll, P, P]),
         "dflash_tree_accept": (c_int, [P, P, P, P, c_int, P, c_int, c_int, P, P, P, P, P, P, P, P]),
@@ -403,6 +417,28 @@ class Drafter:
             ctypes.cast(outs, PP) if n else None, int(ld), _ptr(logits), ids.data_ptr()))
         return ids
 
+    def accept_sampled(self, draft_ids: Optional[torch.Tensor], draft_stride: int, target_logits: torch.Tensor,
+                       temperature: float = 1.0, top_k: int = 20, top_p: float = 0.95, eps: float = 0.2,
+                       delta: float = 0.0, seed: int = 0, round: int = 0, eos_id: int = -1,
+                       budget: Optional[torch.Tensor] = None):
+        """Sampling-mode accept of a round of block length target_logits.shape[1]."""
+        R, b, V = target_logits.shape
+        _need(target_logits, "target_logits", torch.float32, shape=(R, b, self.cfg.vocab))
+        self._check_accept(draft_ids, draft_stride, torch.empty((R, b), dtype=torch.int32, device=target_logits.device),
+                           b, budget, None)
+        _on_device(target_logits=target_logits)
+        out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
+               "emitted": torch.empty((R, b), dtype=torch.int32, device=self.device),
+               "n_emit": torch.empty(R, dtype=torch.int32, device=self.device),
+               "next_tokens": torch.empty((R, b), dtype=torch.int32, device=self.device)}
+        prm = dflash_sampling(float(temperature), int(top_k), float(top_p), float(eps), float(delta))
+        _check("dflash_accept_sampled", self.lib.dflash_accept_sampled(
+            self.ctx, _stream(), _ptr(draft_ids), int(draft_stride), target_logits.data_ptr(), R, int(b),
+            ctypes.byref(prm), int(seed) & (2 ** 64 - 1), int(round) & 0xFFFFFFFF, int(eos_id), _ptr(budget),
+            out["accept_len"].data_ptr(), out["emitted"].data_ptr(), out["n_emit"].data_ptr(),
+            out["next_tokens"].data_ptr()))
+        return out
+
     # ---------------------------------------------------------------- candidate trees
     def tree_build(self, block_tokens: torch.Tensor, ids: torch.Tensor, vals: torch.Tensor, n_nodes: int):
         """(tokens, parent, depth) int32 [R, n_nodes] of the candidate trees built from
@@ -539,3 +575,22 @@ class Drafter:
         v = self.state[L["ring_v"]:L["ring_v"] + 2 * n].view(torch.bfloat16).view(
             c.n_layers, c.max_requests, c.n_kv_heads, c.head_dim, c.ring_capacity)
         return k, v
+
+
+class BlockPolicy:
+    """The library's adaptive block-length policy for one request (host code)."""
+
+    def __init__(self, block: int, weight: float = 0.5):
+        self.lib = load()
+        self.p = dflash_block_policy()
+        self.lib.dflash_policy_init(ctypes.byref(self.p), int(block), float(weight))
+
+    def next_block(self) -> int:
+        return int(self.lib.dflash_policy_next(ctypes.byref(self.p)))
+
+    def update(self, accepted: int):
+        self.lib.dflash_policy_update(ctypes.byref(self.p), int(accepted))
+
+    @property
+    def mean(self) -> float:
+        return float(self.p.mean)

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
 SOURCES = ["api.hip", "gemm.hip", "finish.hip", "lmhead.hip", "attention.hip", "small.hip", "prefill.hip",
-           "tree.hip"]
+           "tree.hip", "sampling.hip"]
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/dflash.h: configuration guards,
 // state/workspace layout and the per-call launch sequences. No device memory is
 // allocated here; every launch goes to the caller's stream.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -64,7 +65,8 @@ int attn_nchunks(const dflash_config& c) {
 }
 
 struct WsLayout {
-  size_t h, ssq, q, o, act, z, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, anc, total;
+  size_t h, ssq, q, o, act, z, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, anc, row_ok, cand_idx,
+      cand_val, part_key, part_idx, part_m, part_z, part_s, total;
 };
 
 struct GemmShape {
@@ -141,6 +143,15 @@ WsLayout ws_layout(const dflash_config& c, bool draft_only = false) {
   L.logits = take(lm_rows * c.vocab * 4);           // transposed logits when the caller passes none
   L.gmax = take(out_rows * ((c.vocab + 15) / 16) * 4);   // per-16-column maxima of the logits
   L.anc = take(Mmax * 8);                                  // ancestor masks of a tree pass's rows
+  L.row_ok = take(Mmax * 4);                               // sampled accept: per-row test of the draft
+  L.cand_idx = take(Mmax * 64 * 4);                        // sampled accept: each row's top-k ids
+  L.cand_val = take(Mmax * 64 * 4);                        // and logits
+  const size_t sch = (size_t)sample_chunks(c.vocab);       // sampled accept, per chunk of the vocabulary:
+  L.part_key = take(Mmax * sch * 64 * 4);                  //   the chunk's top-k keys
+  L.part_idx = take(Mmax * sch * 64 * 4);                  //   and ids,
+  L.part_m = take(Mmax * sch * 4);                         //   its max,
+  L.part_z = take(Mmax * sch * 8);                         //   sum of exp
+  L.part_s = take(Mmax * sch * 8);                         //   and sum of exp * x
   L.total = off;
   return L;
 }
@@ -1050,6 +1061,84 @@ int dflash_accept_n(dflash_ctx* ctx, void* stream, const int* draft_ids, int dra
                                at<unsigned long long>(ctx->state, ctx->sl.stats), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "accept");
   return DFLASH_OK;
+}
+
+int dflash_accept_sampled(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride,
+                          const float* target_logits, int n_req, int block_len, const dflash_sampling* params,
+                          unsigned long long seed, unsigned round, int eos_id, const int* budget, int* accept_len,
+                          int* emitted, int* n_emit, int* next_tokens) {
+  if (!ctx) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!ctx->state) return fail(DFLASH_E_STATE, "handle not bound");
+  const dflash_config& g = ctx->cfg;
+  if (block_len < 1 || block_len > g.block)
+    return fail(DFLASH_E_SHAPE, "block_len %d outside [1, %d]", block_len, g.block);
+  if ((!draft_ids && block_len > 1) || !target_logits || !params || !accept_len || !emitted || !n_emit)
+    return fail(DFLASH_E_ARG, "draft_ids, target_logits, params, accept_len, emitted and n_emit are required");
+  if (n_req < 1 || n_req > g.max_requests) return fail(DFLASH_E_SHAPE, "n_req %d outside [1, %d]", n_req, g.max_requests);
+  if (draft_stride < 1) return fail(DFLASH_E_ARG, "draft_stride must be >= 1");
+  if (!(params->temperature > 0.f) || params->top_k < 1 || params->top_k > 64 || !(params->top_p > 0.f) ||
+      params->top_p > 1.f || !(params->typical_eps >= 0.f))
+    return fail(DFLASH_E_ARG, "need temperature > 0, top_k in [1, 64], top_p in (0, 1], typical_eps >= 0");
+  SampleArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = target_logits;
+  a.draft = draft_ids;
+  a.draft_stride = draft_stride;
+  a.R = n_req;
+  a.b = block_len;
+  a.V = g.vocab;
+  a.stats_b = g.block;
+  a.mask_id = g.mask_id;
+  a.eos = eos_id;
+  a.T = params->temperature;
+  a.top_p = params->top_p;
+  a.eps = params->typical_eps;
+  a.delta = params->typical_delta;
+  a.top_k = params->top_k;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.round = round;
+  a.budget = budget;
+  a.accept_len = accept_len;
+  a.emitted = emitted;
+  a.n_emit = n_emit;
+  a.next_tokens = next_tokens;
+  a.pos = at<int>(ctx->state, ctx->sl.pos);
+  a.stats = at<unsigned long long>(ctx->state, ctx->sl.stats);
+  a.row_ok = at<int>(ctx->ws, ctx->wl.row_ok);
+  a.cand_idx = at<int>(ctx->ws, ctx->wl.cand_idx);
+  a.cand_val = at<float>(ctx->ws, ctx->wl.cand_val);
+  a.n_chunks = sample_chunks(g.vocab);
+  a.part_key = at<unsigned>(ctx->ws, ctx->wl.part_key);
+  a.part_idx = at<int>(ctx->ws, ctx->wl.part_idx);
+  a.part_m = at<float>(ctx->ws, ctx->wl.part_m);
+  a.part_z = at<double>(ctx->ws, ctx->wl.part_z);
+  a.part_s = at<double>(ctx->ws, ctx->wl.part_s);
+  if (a.n_chunks > SAMPLE_MAX_CHUNKS)
+    return fail(DFLASH_E_SHAPE, "sampled accept supports vocabularies up to %d (got %d)",
+                SAMPLE_CHUNK * SAMPLE_MAX_CHUNKS, g.vocab);
+  hipError_t e = launch_sampled_accept(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sampled accept");
+  return DFLASH_OK;
+}
+
+void dflash_policy_init(dflash_block_policy* p, int block, double weight) {
+  if (!p) return;
+  p->block = block;
+  p->weight = weight;
+  p->mean = (double)(block - 1);
+}
+
+int dflash_policy_next(const dflash_block_policy* p) {
+  if (!p) return 0;
+  int b = (int)floor(p->mean + 0.5) + 2;
+  b = b < p->block ? b : p->block;
+  return b > 2 ? b : (p->block < 2 ? p->block : 2);
+}
+
+void dflash_policy_update(dflash_block_policy* p, int accepted) {
+  if (!p) return;
+  p->mean = (1.0 - p->weight) * p->mean + p->weight * (double)accepted;
 }
 
 int dflash_check(dflash_ctx* ctx, void* stream, unsigned* word) {

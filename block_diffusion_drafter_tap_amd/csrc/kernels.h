@@ -175,6 +175,33 @@ hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStrea
 // layer to a tap buffer with row pitch ld; add n_emit to the positions.
 hipError_t launch_copy_rows(const float* h, int M, int H, float* dst, long long ld, hipStream_t st);
 
+// Sampling-mode acceptance (sampling.hip): typical acceptance of the drafts
+// against the target's verify logits, card sampling of the next token.
+struct SampleArgs {
+  const float* logits;     // [R][b][V] target logits of the verify rows
+  const int* draft;        // element (r, j) at draft[(r * (b-1) + j) * draft_stride]
+  int draft_stride;
+  int R, b, V, stats_b, mask_id, eos;
+  float T, top_p, eps, delta;   // delta <= 0: sqrt(eps)
+  int top_k;                    // 1..64
+  uint32_t seed_lo, seed_hi, round;
+  const int* budget;
+  int *accept_len, *emitted, *n_emit, *next_tokens, *pos;
+  unsigned long long* stats;
+  int* row_ok;             // workspace [R][b]
+  int* cand_idx;           // workspace [R][b][64]
+  float* cand_val;         // workspace [R][b][64]
+  int n_chunks;            // ceil(V / SAMPLE_CHUNK)
+  unsigned* part_key;      // workspace [R][b][n_chunks][64]: each chunk's top-k (order keys)
+  int* part_idx;           //   and ids
+  float* part_m;           // workspace [R][b][n_chunks]: chunk max
+  double *part_z, *part_s; //   sum exp(x), sum exp(x) x at the chunk max
+};
+constexpr int SAMPLE_CHUNK = 4096;        // logits per stage-1 workgroup (16 KiB of LDS)
+constexpr int SAMPLE_MAX_CHUNKS = 64;     // vocabularies up to 262144
+inline int sample_chunks(int V) { return (V + SAMPLE_CHUNK - 1) / SAMPLE_CHUNK; }
+hipError_t launch_sampled_accept(const SampleArgs& a, hipStream_t st);
+
 // Candidate trees (tree.hip): build from top-k lists, accept, ancestor masks of
 // the tree rows, and the commit of a target's tree pass (K/V of the committed
 // nodes to consecutive ring slots).

@@ -276,6 +276,57 @@ int dflash_accept_n(dflash_ctx* ctx, void* stream, const int* draft_ids, int dra
                     int* accept_len, int* emitted, int* n_emit, int* next_tokens);
 
 /*
+ * Sampling-mode acceptance (the pages run the drafter with "typical 0.2" and
+ * card sampling T 1.0, top-p 0.95, top-k 20: "dflash: the chain verify builds
+ * pipelined ...", mlx-serve PR #937, "Measured"; the pages give no formulas).
+ * For request r and verify row i (target logits z = target_logits[r][i][:],
+ * fp32, e.g. dflash_verify_block's logits output): p = softmax(z / T), H =
+ * -sum p log p; draft token i is accepted iff p(draft) > min(eps, delta *
+ * exp(-H)) (delta <= 0 means sqrt(eps)), and acceptance stops at the first
+ * rejected row a (a = b-1 if none). The next token is drawn from row a: its
+ * top_k logits (value desc, index asc), q = softmax(z / T) over them (fp64),
+ * the shortest prefix whose q sum reaches top_p, and in it the first token
+ * whose running q sum exceeds u * the prefix's sum, with u = (word 0 >> 8) *
+ * 2^-24 of Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as
+ * 1, 2, 3", SC 2011) at key = seed, counter = (round, r, a, 0). Emitted =
+ * accepted drafts + that token; EOS, budget, pos, next_tokens and the
+ * statistics as in dflash_accept_n. Decisions within about 1e-6 (relative) of
+ * the acceptance threshold may differ from an fp64 evaluation: the row sums
+ * are fp32 exponentials added in fp64.
+ */
+typedef struct {
+  float temperature;     /* > 0 */
+  int top_k;             /* 1..64 */
+  float top_p;           /* (0, 1] */
+  float typical_eps;     /* >= 0; 0 accepts every draft */
+  float typical_delta;   /* <= 0: sqrt(typical_eps) */
+} dflash_sampling;
+
+int dflash_accept_sampled(dflash_ctx* ctx, void* stream, const int* draft_ids, int draft_stride,
+                          const float* target_logits, int n_req, int block_len, const dflash_sampling* params,
+                          unsigned long long seed, unsigned round, int eos_id, const int* budget,
+                          int* accept_len, int* emitted, int* n_emit, int* next_tokens);
+
+/*
+ * Adaptive block length (the round policy of "dflash: the chain verify builds
+ * pipelined ...", mlx-serve PR #937, hyper-connection-stream commit, whose rule
+ * the pages do not give). Host-side, one per request: an exponential average m
+ * of the accepted drafts, m <- (1 - weight) m + weight * accepted, starting at
+ * block - 1; the next round's block length is clamp(floor(m + 1/2) + 2, 2,
+ * block), for dflash_draft_block_n / dflash_accept_n. A serving loop reads each
+ * round's accept lengths anyway (it streams the emitted tokens), so the policy
+ * needs no extra synchronization.
+ */
+typedef struct {
+  int block;
+  double weight;
+  double mean;
+} dflash_block_policy;
+void dflash_policy_init(dflash_block_policy* p, int block, double weight);
+int dflash_policy_next(const dflash_block_policy* p);
+void dflash_policy_update(dflash_block_policy* p, int accepted);
+
+/*
  * Causal target (the verify side of the loop). A target handle is created from
  * the same config and weight structs (fc, fc_scales and ctx_norm are not used):
  * a Qwen3-shaped causal decoder whose own per-layer K/V live in the ring of its

@@ -29,7 +29,7 @@ R34 adaptive block policy. Per request an exponential average of the
     accepted drafts, m <- (1 - w) m + w * acc (m starts at block - 1, w = 1/2);
     the next round's block is clamp(floor(m + 1/2) + 2, 2, block): two rows
     beyond the expected accept (rounded to nearest), so a verify pass is not
-    wider than the drafter can fill.
+    wider than the drafter can fill (block itself when block < 2).
 """
 from __future__ import annotations
 
@@ -119,7 +119,8 @@ class BlockPolicy:
         self.mean = float(block - 1)
 
     def next_block(self) -> int:
-        return max(2, min(self.block, int(math.floor(self.mean + 0.5)) + 2))
+        # for block < 2 the range [2, block] is empty: the block itself (target-only rounds)
+        return max(min(2, self.block), min(self.block, int(math.floor(self.mean + 0.5)) + 2))
 
     def update(self, accepted: int):
         self.mean = (1.0 - self.w) * self.mean + self.w * float(accepted)

@@ -98,3 +98,23 @@ def test_verify_and_advance_argument_checks(dr):
         dr.verify_block(_i32(1, 4), [0], [_f32(3, c.hidden)])
     with pytest.raises(ValueError, match="int32"):
         dr.advance(torch.zeros(2, dtype=torch.int64))
+
+
+def test_block_policy_host_functions_match_the_oracle():
+    """dflash_policy_init/next/update (host code of the library) against the
+    oracle's adaptive block policy over random accept sequences."""
+    import numpy as np
+
+    from block_diffusion_drafter_tap_amd import binding as Bd
+    from oracle import sampling as S
+    rng = np.random.default_rng(0)
+    for block in (1, 2, 3, 8, 16):
+        for w in (0.5, 0.25, 1.0):
+            p, q = Bd.BlockPolicy(block, w), S.BlockPolicy(block, w)
+            for _ in range(200):
+                b = p.next_block()
+                assert b == q.next_block() and 1 <= b <= max(block, 1)
+                a = int(rng.integers(0, max(b, 1)))
+                p.update(a)
+                q.update(a)
+                assert p.mean == q.mean

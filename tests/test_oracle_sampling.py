@@ -115,3 +115,12 @@ def test_block_policy_closed_form():
     for a in seq:
         m = 0.5 * m + 0.5 * a
     assert q.mean == m and q.next_block() == min(16, max(2, math.floor(m + 0.5) + 2))
+
+
+def test_block_policy_degenerate_blocks():
+    """Block 1 (target-only rounds) stays 1; block 2 stays 2 whatever is accepted."""
+    p1, p2 = S.BlockPolicy(1), S.BlockPolicy(2)
+    for a in (0, 0, 1, 0):
+        assert p1.next_block() == 1 and p2.next_block() == 2
+        p1.update(0)
+        p2.update(a)
