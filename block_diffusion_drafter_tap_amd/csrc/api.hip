@@ -66,7 +66,7 @@ int attn_nchunks(const dflash_config& c) {
 
 struct WsLayout {
   size_t h, ssq, q, o, act, z, c32, c, xg, partials, attn_o, attn_ml, logits, gmax, anc, row_ok, cand_idx,
-      cand_val, part_key, part_idx, part_m, part_z, part_s, total;
+      cand_key, part_key, part_idx, part_m, part_z, part_s, total;
 };
 
 struct GemmShape {
@@ -145,7 +145,7 @@ WsLayout ws_layout(const dflash_config& c, bool draft_only = false) {
   L.anc = take(Mmax * 8);                                  // ancestor masks of a tree pass's rows
   L.row_ok = take(Mmax * 4);                               // sampled accept: per-row test of the draft
   L.cand_idx = take(Mmax * 64 * 4);                        // sampled accept: each row's top-k ids
-  L.cand_val = take(Mmax * 64 * 4);                        // and logits
+  L.cand_key = take(Mmax * 64 * 4);                        // and their logits (order keys)
   const size_t sch = (size_t)sample_chunks(c.vocab);       // sampled accept, per chunk of the vocabulary:
   L.part_key = take(Mmax * sch * 64 * 4);                  //   the chunk's top-k keys
   L.part_idx = take(Mmax * sch * 64 * 4);                  //   and ids,
@@ -1107,7 +1107,7 @@ int dflash_accept_sampled(dflash_ctx* ctx, void* stream, const int* draft_ids, i
   a.stats = at<unsigned long long>(ctx->state, ctx->sl.stats);
   a.row_ok = at<int>(ctx->ws, ctx->wl.row_ok);
   a.cand_idx = at<int>(ctx->ws, ctx->wl.cand_idx);
-  a.cand_val = at<float>(ctx->ws, ctx->wl.cand_val);
+  a.cand_key = at<unsigned>(ctx->ws, ctx->wl.cand_key);
   a.n_chunks = sample_chunks(g.vocab);
   a.part_key = at<unsigned>(ctx->ws, ctx->wl.part_key);
   a.part_idx = at<int>(ctx->ws, ctx->wl.part_idx);

@@ -190,7 +190,7 @@ struct SampleArgs {
   unsigned long long* stats;
   int* row_ok;             // workspace [R][b]
   int* cand_idx;           // workspace [R][b][64]
-  float* cand_val;         // workspace [R][b][64]
+  unsigned* cand_key;      // workspace [R][b][64]: order keys of the row's top-k logits
   int n_chunks;            // ceil(V / SAMPLE_CHUNK)
   unsigned* part_key;      // workspace [R][b][n_chunks][64]: each chunk's top-k (order keys)
   int* part_idx;           //   and ids

@@ -20,18 +20,57 @@
 
 namespace {
 
-// (score desc, depth asc, parent asc) of two offers; true if a beats b
-DEV bool offer_better(double sa, int da, int pa, double sb, int db, int pb) {
-  if (sa != sb) return sa > sb;
-  if (da != db) return da < db;
-  return pa < pb;
+// Whole-wave lane shifts (DPP wave_shl:1 / wave_shr:1): dst[l] = src[l + 1] and
+// dst[l] = src[l - 1]; the lane without a source keeps `old`.
+DEV int wave_shl1(int old, int v) { return __builtin_amdgcn_update_dpp(old, v, 0x130, 0xF, 0xF, false); }
+DEV int wave_shr1(int old, int v) { return __builtin_amdgcn_update_dpp(old, v, 0x138, 0xF, 0xF, false); }
+
+DEV int lo32(double x) { return (int)(uint32_t)__double_as_longlong(x); }
+DEV int hi32(double x) { return (int)(uint32_t)((unsigned long long)__double_as_longlong(x) >> 32); }
+DEV double mk64(int lo, int hi) {
+  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
 }
+DEV double lane_d(double x, int l) {
+  return mk64(__builtin_amdgcn_readlane(lo32(x), l), __builtin_amdgcn_readlane(hi32(x), l));
+}
+
+// An offer: the score of the child and a packed (depth << 16 | parent << 8 |
+// rank). Ordered by (score desc, depth asc, parent asc); a node has at most one
+// offer outstanding, so (depth, parent) never ties.
+DEV bool offer_beats(double sa, int pa, double sb, int pb) { return sa > sb || (sa == sb && pa < pb); }
+
+// The offers outstanding, best first, one per lane (lanes past the last hold
+// (-inf, INT_MAX)); insert keeps the order: the lanes before the new offer's
+// place keep theirs, the rest shift up by one lane.
+struct OfferQueue {
+  double s;
+  int p;
+  DEV void pop() {
+    const int lo = wave_shl1(lo32(-INFINITY), lo32(s)), hi = wave_shl1(hi32(-INFINITY), hi32(s));
+    s = mk64(lo, hi);
+    p = wave_shl1(0x7fffffff, p);
+  }
+  DEV void insert(double xs, int xp, int lane) {
+    const int at = __popcll(__ballot(offer_beats(s, p, xs, xp)));
+    const double us = mk64(wave_shr1(lo32(s), lo32(s)), wave_shr1(hi32(s), hi32(s)));
+    const int up = wave_shr1(p, p);
+    if (lane == at) {
+      s = xs;
+      p = xp;
+    } else if (lane > at) {
+      s = us;
+      p = up;
+    }
+  }
+};
 
 // One wave per request: lane i holds node i.
 __global__ __launch_bounds__(64) void tree_build_kernel(const int* block_tokens, int B, const int* ids,
                                                         const float* vals, int k, int n, int* out_tok,
                                                         int* out_par, int* out_dep) {
   __shared__ double s_lp[64][16];
+  __shared__ double s_qs[64];
+  __shared__ int s_qp[64];
   const int r = blockIdx.x, lane = threadIdx.x;
   const int Dm = B - 1;
   const int* rid = ids + (size_t)r * Dm * k;
@@ -39,53 +78,70 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int* block_tokens,
   // list log-probabilities of position d = lane + 1
   if (lane < Dm) {
     const float* v = rval + (size_t)lane * k;
-    const double v0 = (double)v[0];
+    float vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) vv[j] = j < k ? v[j] : 0.f;
+    const double v0 = (double)vv[0];
     double s = 0.0;
-    for (int j = 0; j < k; ++j) s += exp((double)v[j] - v0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) s += exp((double)vv[j] - v0);
     const double lse = log(s);
-    for (int j = 0; j < k; ++j) s_lp[lane][j] = ((double)v[j] - v0) - lse;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) s_lp[lane][j] = ((double)vv[j] - v0) - lse;
   }
   __syncthreads();
   // root and the top-1 chain (nodes 1..dc at depths 1..dc)
   const int dc = min(Dm, n - 1);
-  int tok = -1, par = -1, dep = 0, nxt = 0;
+  int tok = -1, par = -1, dep = 0, src = -1;
   double score = 0.0;
   if (lane == 0) {
     tok = block_tokens[(size_t)r * B];
-    nxt = dc >= 1 ? 1 : 0;
   } else if (lane <= dc) {
     tok = rid[(size_t)(lane - 1) * k];
     par = lane - 1;
     dep = lane;
-    nxt = lane < dc ? 1 : 0;
     for (int e = 0; e < lane; ++e) score += s_lp[e][0];   // depth order, as the scores add up along the path
   }
-  // best first
+  // the chain's outstanding offers: rank 1 below every chain node but the last,
+  // rank 0 below the last (when it may have children)
+  const int orank = lane < dc ? 1 : 0;
+  const bool offers = lane <= dc && dep < Dm && orank < k;
+  const double os = offers ? score + s_lp[dep][orank] : -INFINITY;
+  const int opk = offers ? ((dep + 1) << 16 | lane << 8 | orank) : 0x7fffffff;
+  int place = 0;
+  for (int m = 0; m <= dc; ++m) {
+    const double ms = lane_d(os, m);
+    const int mp = __builtin_amdgcn_readlane(opk, m);
+    place += (m != lane && offer_beats(ms, mp, os, opk)) ? 1 : 0;
+  }
+  s_qs[lane] = -INFINITY;
+  s_qp[lane] = 0x7fffffff;
+  __syncthreads();
+  if (offers) {
+    s_qs[place] = os;
+    s_qp[place] = opk;
+  }
+  __syncthreads();
+  OfferQueue q{s_qs[lane], s_qp[lane]};
+  // best first: pop the best offer as node cnt, then queue its parent's next
+  // rank and its own first child
   for (int cnt = dc + 1; cnt < n; ++cnt) {
-    const bool offers = lane < cnt && dep < Dm && nxt < k;
-    double os = offers ? score + s_lp[dep][nxt] : -INFINITY;
-    int od = offers ? dep + 1 : 0x7fffffff, op = offers ? lane : 0x7fffffff;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double s2 = __shfl_xor(os, o, 64);
-      const int d2 = __shfl_xor(od, o, 64), p2 = __shfl_xor(op, o, 64);
-      if (offer_better(s2, d2, p2, os, od, op)) {
-        os = s2;
-        od = d2;
-        op = p2;
-      }
-    }
-    // op is the winning parent (the host guarantees an offer remains)
-    const int wrank = __shfl(nxt, op, 64);
-    if (lane == op) ++nxt;
+    const double ts = lane_d(q.s, 0);
+    const int tp = __builtin_amdgcn_readlane(q.p, 0);   // the host guarantees an offer remains
+    const int od = tp >> 16, op = (tp >> 8) & 255, j = tp & 255;
+    q.pop();
     if (lane == cnt) {
-      tok = rid[(size_t)(od - 1) * k + wrank];
+      src = (od - 1) * k + j;   // the token is read after the loop, off its critical path
       par = op;
       dep = od;
-      nxt = 0;
-      score = os;
+      score = ts;
     }
+    if (j + 1 < k) q.insert(lane_d(score, op) + s_lp[od - 1][j + 1], od << 16 | op << 8 | (j + 1), lane);
+    if (od < Dm) q.insert(ts + s_lp[od][0], (od + 1) << 16 | cnt << 8, lane);
   }
+  if (src >= 0) tok = rid[src];
   if (lane < n) {
     out_tok[(size_t)r * n + lane] = tok;
     out_par[(size_t)r * n + lane] = par;

@@ -154,7 +154,8 @@ def test_sampled_accept_matches_oracle(vocab):
 def test_sampled_accept_ties_at_the_kth_value(V):
     """Logits on a coarse grid: many tokens share the k-th value, and the card
     keeps the lowest indices among them (within one 4096-logit chunk, and
-    across chunks)."""
+    across chunks); flat rows, where every logit ties, take the selection's
+    radix path."""
     binding = _binding()
     R, b = 4, 4
     cfg = config.tiny(max_requests=R).replace(vocab=V)
@@ -165,6 +166,8 @@ def test_sampled_accept_ties_at_the_kth_value(V):
     for trial in range(8):
         z = np.floor(rng.standard_normal((R, b, V)) * 1.5).astype(np.float32)
         z[:, :, rng.integers(0, V, 5)] = 9.0          # five tied maxima
+        if trial % 4 == 3:
+            z[:2] = 0.5                               # flat rows: every logit ties
         d = _drafts(rng, z, 1)
         prm = dict(T=1.0, top_k=[3, 8, 20, 64][trial % 4], top_p=1.0, eps=0.2, delta=0.0)
         c, e = _compare(dr, cfg, z, d, prm, seed=77, rnd=trial, eos=-1, budget=None, p0=10, what=f"ties {trial}")
