@@ -20,7 +20,9 @@ import torch
 from .config import DFlashConfig
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdflash.so")
+# DFLASH_LIB selects another build of the same library (the host-sanitized copy
+# in the CPU sanitizer test); there is no fallback when it is missing.
+LIB_PATH = os.environ.get("DFLASH_LIB", os.path.join(HERE, "libdflash.so"))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "dflash.h")
 
 c_int, c_void_p, c_size_t, c_float, c_ll, c_uint = (ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,

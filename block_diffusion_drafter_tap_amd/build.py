@@ -63,5 +63,60 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (preloaded into the host
+    process that loads a sanitized library)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of hipcc's clang was not found")
+    return path
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """A copy of the library whose host code (api.hip: argument validation,
+    config guards, state / workspace layouts, the block policy) is built with
+    AddressSanitizer and UndefinedBehaviorSanitizer; device code is unchanged.
+    For CPU-only checks of the host paths; it lands in _build/, never next to
+    the package."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    newest_header = max(os.path.getmtime(h) for h in headers)
+
+    def stale(src: str) -> bool:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        return not os.path.exists(obj) or os.path.getmtime(obj) < max(newest_header,
+                                                                      os.path.getmtime(os.path.join(CSRC, src)))
+    todo = [s for s in SOURCES if s != "api.hip" and stale(s)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, len(todo))) as ex:
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    out_dir = os.path.join(BUILD_DIR, "host_sanitized")
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, "api.o")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-c", *DEVICE_FLAGS, *HOST_SANITIZE,
+           "-I", INCLUDE, os.path.join(CSRC, "api.hip"), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the sanitized api.hip:\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.hip"]
+    lib = os.path.join(out_dir, "libdflash.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-shared-libsan", *HOST_SANITIZE,
+           *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the sanitized library failed:\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -1131,9 +1131,11 @@ void dflash_policy_init(dflash_block_policy* p, int block, double weight) {
 
 int dflash_policy_next(const dflash_block_policy* p) {
   if (!p) return 0;
-  int b = (int)floor(p->mean + 0.5) + 2;
-  b = b < p->block ? b : p->block;
-  return b > 2 ? b : (p->block < 2 ? p->block : 2);
+  const int hi = p->block, lo = hi < 2 ? hi : 2;
+  const double b = floor(p->mean + 0.5) + 2.0;   // compared in fp64: no int conversion of an unbounded mean
+  if (!(b > (double)lo)) return lo;               // a NaN mean too
+  if (b >= (double)hi) return hi;
+  return (int)b;
 }
 
 void dflash_policy_update(dflash_block_policy* p, int accepted) {

@@ -118,3 +118,14 @@ def test_block_policy_host_functions_match_the_oracle():
                 p.update(a)
                 q.update(a)
                 assert p.mean == q.mean
+
+
+def test_block_policy_stays_in_range_for_any_accept_value():
+    from block_diffusion_drafter_tap_amd import binding as Bd
+    for acc in (10 ** 9, -10 ** 9, 2 ** 31 - 1, -2 ** 31):
+        p = Bd.BlockPolicy(8, 1.0)
+        p.update(acc)
+        assert 2 <= p.next_block() <= 8
+    p = Bd.BlockPolicy(8, float("nan"))
+    p.update(3)
+    assert p.next_block() == 2
