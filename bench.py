@@ -174,6 +174,38 @@ def verify_report(cfg, dev, n_layers: int = 36, steps: int = 20) -> dict:
             "graph_frac": None if graph_ms is None else round(nbytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def graph_us(fn, reps: int = 20, inner: int = 10):
+    """Microseconds per call of fn replayed from a HIP graph: inner calls
+    captured once, the graph replayed reps times between HIP events, so the
+    figure is the device time of the calls' launches, without the host's
+    per-call work or a graph launch per call. None when capture fails."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(inner):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (reps * inner) * 1e3
+        del g
+        return round(us, 2)
+    except RuntimeError:
+        return None
+
+
 def tree_report(cfg, dr, tokens, k: int, dev, node_counts=(16, 32, 64), rounds: int = 200, seed: int = 5) -> dict:
     """Candidate trees from this drafter's top-16 lists: the mean tokens per
     round of trees of node_counts verify rows against the top-1 chain (block
@@ -219,31 +251,21 @@ def tree_report(cfg, dr, tokens, k: int, dev, node_counts=(16, 32, 64), rounds: 
     tok, par, dep = dr.tree_build(blk, ids, vals, n)
     verify = torch.zeros((1, n), dtype=torch.int32, device=dev)
     acc_h.reset(0, 0, 100)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    reps = 100
-    torch.cuda.synchronize()
-    ev[0].record()
-    for _ in range(reps):
-        dr.tree_build(blk, ids, vals, n)
-    ev[1].record()
-    for _ in range(reps):
-        acc_h.tree_accept(tok, par, verify)
-    ev[2].record()
-    torch.cuda.synchronize()
+    build_us = graph_us(lambda: dr.tree_build(blk, ids, vals, n))
+    accept_us = graph_us(lambda: acc_h.tree_accept(tok, par, verify))
     del acc_h
     return {"rounds": rounds, "block": B, "tau_chain": round(tau_chain / rounds, 3),
             "tau_tree": {str(m): round(tau[m] / rounds, 3) for m in node_counts},
             "target_model": "synthetic: the target's token is the drafter's rank-0 candidate w.p. 0.75, "
                             "a listed rank 1..15 (weight 2^-j) w.p. 0.2, unlisted otherwise",
-            "timed_nodes": n, "build_us": round(ev[0].elapsed_time(ev[1]) / reps * 1e3, 2),
-            "accept_us": round(ev[1].elapsed_time(ev[2]) / reps * 1e3, 2)}
+            "timed_nodes": n, "build_us": build_us, "accept_us": accept_us, "timing": "HIP graph replay"}
 
 
-def sampling_report(cfg, dev, reps: int = 50) -> dict:
+def sampling_report(cfg, dev) -> dict:
     """Sampling-mode accept (typical acceptance 0.2, T 1.0, top-p 0.95, top-k
-    20) over one block of verify logits [R, B, V] fp32: the kernel pair's time
-    and its rate against the logits' bytes (read once algorithmically)."""
-    import numpy as np
+    20) over one block of verify logits [R, B, V] fp32: the device time of its
+    three kernels (HIP graph replay) and its rate against the logits' bytes
+    (read once algorithmically)."""
     import torch
     from block_diffusion_drafter_tap_amd import binding, config, synth
 
@@ -254,19 +276,15 @@ def sampling_report(cfg, dev, reps: int = 50) -> dict:
     g.manual_seed(3)
     z = torch.randn((R, B, V), generator=g, device=dev) * 2.0
     d = torch.argmax(z[:, : B - 1], dim=2).to(torch.int32).contiguous()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for i in range(reps + 5):
-        if i == 5:
-            ev[0].record()
-        h.accept_sampled(d, 1, z, temperature=1.0, top_k=20, top_p=0.95, eps=0.2, seed=1, round=i)
-    ev[1].record()
-    torch.cuda.synchronize()
-    us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+    us = graph_us(lambda: h.accept_sampled(d, 1, z, temperature=1.0, top_k=20, top_p=0.95, eps=0.2, seed=1,
+                                            round=7))
+    if us is None:
+        return None
     nbytes = R * B * V * 4
     del h
     return {"logits_shape": [R, B, V], "us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "params": "typical 0.2, T 1.0, top-p 0.95, top-k 20"}
+            "params": "typical 0.2, T 1.0, top-p 0.95, top-k 20", "timing": "HIP graph replay"}
 
 
 def prefill_report(cfg, rows: int, ms: float) -> dict:
