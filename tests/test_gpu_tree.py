@@ -262,3 +262,59 @@ def test_tree_loop_lossless_tiny(lists):
         assert all(a >= c for a, c in zip(accepts[:-1], chain_accepts[:-1]))
         assert sum(accepts) > sum(chain_accepts)
         print(f"chain alone would accept {chain_accepts}", flush=True)
+
+
+def test_tree_verify_fullsize_vs_oracle_target():
+    """A 16-node tree pass at the qwen3-4b layer shape (hidden 2560, 32/8 heads x
+    128, ffn 9728, vocab 151936; 4 layers, window 4096) after a 300-row prompt,
+    against the mirror oracle target walking the tree depth first: each node is
+    one row at pos + depth over the prompt and the node's ancestors (logits,
+    argmax away from ties, the taps after layers 1 and 3)."""
+    binding = _binding()
+    tcfg = config.qwen3_4b(block=16, window=4096, max_stage_rows=16).replace(n_layers=4)
+    V, H, P, n = tcfg.vocab, tcfg.hidden, 300, 16
+    print("case: qwen3-4b-shaped 4-layer target, prompt 300, 16-node tree from block-8 lists", flush=True)
+    wt = synth.make_weights(tcfg, seed=21, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(23)
+    prompt = torch.randint(0, V - 1, (P,), generator=g, device="cuda", dtype=torch.int32).cpu().tolist()
+    tg = binding.Drafter(tcfg, wt, target=True)
+    tg.reset(0, 0, 0)
+    for r0 in range(0, P, 16):
+        chunk = prompt[r0:r0 + 16]
+        tg.verify_block(torch.tensor([chunk], dtype=torch.int32, device="cuda"))
+        tg.advance(torch.tensor([len(chunk)], dtype=torch.int32, device="cuda"))
+    rng = np.random.default_rng(24)
+    si, sv = _synthetic_lists(rng, 1, 7, 16, V - 1)
+    tree = TR.build_tree(int(rng.integers(0, V - 1)), si[0], sv[0], n)
+    tok = torch.tensor([tree["tokens"]], dtype=torch.int32, device="cuda")
+    par = torch.tensor([tree["parent"]], dtype=torch.int32, device="cuda")
+    dep = torch.tensor([tree["depth"]], dtype=torch.int32, device="cuda")
+    taps = [torch.empty((n, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+    logits = torch.empty((1, n, V), dtype=torch.float32, device="cuda")
+    ids = tg.verify_tree(tok, par, dep, [1, 3], taps, logits)
+    torch.cuda.synchronize()
+    assert tg.check() == 0
+    assert int(tg.positions()[0][0]) == P
+    ref = T.TinyTarget(tcfg, _np(wt), n_layers=4, mode="mirror")
+    ref.prefill(prompt)
+    children = [[] for _ in range(n)]
+    for i in range(1, n):
+        children[tree["parent"][i]].append(i)
+    lg_o = np.zeros((n, V))
+    taps_o = [np.zeros((n, H), dtype=np.float32) for _ in range(2)]
+    stack = [0]
+    while stack:                       # depth first: the cache holds the prompt and the node's ancestors
+        v = stack.pop()
+        d = tree["depth"][v]
+        ref.truncate(P + d)
+        _, tr, lg = ref.feed([tree["tokens"][v]], P + d, want_logits=True)
+        lg_o[v] = lg[0]
+        taps_o[0][v], taps_o[1][v] = tr[1][0], tr[3][0]
+        stack.extend(reversed(children[v]))
+    gl = logits[0].cpu().numpy()
+    err = Hn.assert_close(gl, lg_o, "tree verify logits (full size)")
+    comp, excl = Hn.topk_agrees_away_from_ties(lg_o, ids.cpu().numpy().reshape(-1, 1), 1, gpu_logits=gl)
+    Hn.require_compared(comp, excl, 0.5, "tree verify argmax (full size)")
+    et = [Hn.assert_close(taps[i].cpu().numpy(), taps_o[i], f"tree tap after layer {l}") for i, l in enumerate((1, 3))]
+    print(f"full-size tree verify: logits err {err:.3g}, tap errs {et[0]:.3g} {et[1]:.3g}, argmax compared {comp}, "
+          f"near-ties {excl}", flush=True)
