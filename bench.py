@@ -103,6 +103,23 @@ def round_bytes(cfg, R: int, k: int) -> dict:
             "ring_read": ring_read}
 
 
+def class_bytes(cfg, R: int) -> dict:
+    """Algorithmic HBM bytes per launch of each timed kernel class: a projection's
+    weights (bf16, or packed INT4 with its scales), attention's context and block
+    K/V of every request, fc's weights and tap rows, the layer-batched context K/V
+    staging's weights, the LM head's bytes as in round_bytes."""
+    from block_diffusion_drafter_tap_amd import config
+
+    H, hd, L = cfg.hidden, cfg.head_dim, cfg.n_layers
+    wb = 0.5 + 2.0 / 64 if cfg.wfmt == config.WFMT_INT4_G64 else 2
+    keys = cfg.window + cfg.block
+    return {"qkv": int(cfg.qkv_rows * H * wb), "attn": R * cfg.n_kv_heads * keys * hd * 2 * 2,
+            "o": int(H * cfg.n_q_heads * hd * wb), "gate_up": int(2 * cfg.ffn * H * wb),
+            "down": int(H * cfg.ffn * wb),
+            "fc": int(H * cfg.tap_width * wb) + R * cfg.block * cfg.n_taps * cfg.hc_streams * cfg.tap_hidden * 4,
+            "stage_kv": int(L * 2 * cfg.n_kv_heads * hd * H * wb)}
+
+
 def verify_report(cfg, dev, n_layers: int = 36, steps: int = 20) -> dict:
     """One causal verify pass of a target with the drafter's layer shape at
     Qwen3-4B depth (36 layers): the block's B rows at context W, every row's
@@ -485,6 +502,39 @@ def main():
     torch.cuda.synchronize()
     per_round = np.array([rev[j].elapsed_time(rev[j + 1]) for j in range(args.steps)])
 
+    # per kernel class: HIP events around every launch of the class (a projection's
+    # GEMM with its finish kernel, attention with its combine) in one more pass of
+    # the same rounds
+    L = cfg.n_layers
+    classes = [("qkv", binding.K_QKV, L), ("attn", binding.K_ATTN, L), ("o", binding.K_O, L),
+               ("gate_up", binding.K_GATEUP, L), ("down", binding.K_DOWN, L), ("fc", binding.K_FC, 1),
+               ("stage_kv", binding.K_STAGE_KV, 1)]
+    cev = {}
+    for name, kc, per in classes:
+        cev[name] = ([torch.cuda.Event(enable_timing=True) for _ in range(args.steps * per)],
+                     [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * per)])
+        for e in cev[name][0] + cev[name][1]:
+            e.record()
+    torch.cuda.synchronize()
+    for name, kc, per in classes:
+        dr.set_timing_events(kc, *cev[name])
+    for i in range(args.warmup, n_rounds):
+        one_round(i)
+    torch.cuda.synchronize()
+    for name, kc, per in classes:
+        dr.set_timing_events(kc, [], [])
+    cb = class_bytes(cfg, R)
+    rb_lm = round_bytes(cfg, R, k)["lm_head"]
+    kernels = {}
+    for name, kc, per in classes:
+        us = float(np.mean([b.elapsed_time(a) for b, a in zip(*cev[name])])) * 1e3
+        gbps = cb[name] / (us * 1e-6) / 1e9
+        kernels[name] = {"us": round(us, 2), "launches_per_round": per, "bytes_per_launch": cb[name],
+                         "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    kernels["lm_head"] = {"us": round(lm_ms * 1e3, 2), "launches_per_round": 1, "bytes_per_launch": rb_lm,
+                          "gbps": round(rb_lm / (lm_ms * 1e-3) / 1e9, 1),
+                          "frac": round(rb_lm / (lm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
     # the same round captured once into a HIP graph and replayed: launch cost
     # vs plain launches (the replays restage the same verify rows)
     graph = None
@@ -582,6 +632,7 @@ def main():
                      "avg_launch_us": round(lm_ms * 1e3, 2), "bytes_per_launch": rb["lm_head"]},
         "cpu_baseline": None,
         "prefill": prefill_report(cfg, W, prefill_ms),
+        "kernels": kernels,
         "round_ms": {"p10": round(float(np.percentile(per_round, 10)), 4),
                      "p50": round(float(np.percentile(per_round, 50)), 4),
                      "p90": round(float(np.percentile(per_round, 90)), 4)},

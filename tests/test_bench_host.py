@@ -42,3 +42,17 @@ def test_algorithmic_bytes_of_the_benchmark_round():
     assert rb["lm_head"] == V * H * 2 + 16 * H * 2 + 15 * 16 * 8 == 777_996_160
     assert rb["ring_read"] == L * 2 * 8 * (4096 + 16) * 128 * 2
     assert rb["total"] == 1_938_579_840
+
+
+def test_per_class_bytes_of_the_benchmark_round():
+    """Per-launch algorithmic bytes of the kernel classes, counted from the shapes
+    (qwen3-4b drafter, block 16, window 4096, one request)."""
+    cfg = config.qwen3_4b(block=16, window=4096)
+    cb = bench.class_bytes(cfg, 1)
+    H, F, hd = 2560, 9728, 128
+    assert cb["qkv"] == (32 + 16) * hd * H * 2
+    assert cb["o"] == H * 32 * hd * 2
+    assert cb["gate_up"] == 2 * F * H * 2 and cb["down"] == H * F * 2
+    assert cb["attn"] == 8 * (4096 + 16) * hd * 2 * 2
+    assert cb["fc"] == H * 5 * H * 2 + 16 * 5 * H * 4
+    assert cb["stage_kv"] == 5 * 2 * 8 * hd * H * 2
