@@ -347,6 +347,16 @@ class Drafter:
             raise ValueError("verify_ids must be an int32 tensor [R, block]")
         R = verify_ids.shape[0]
         _need(verify_ids, "verify_ids", torch.int32, shape=(R, b))
+        self._check_drafts(draft_ids, draft_stride, R, b, budget)
+        if out is not None:
+            _need(out.get("accept_len"), "out['accept_len']", torch.int32, shape=(R,))
+            _need(out.get("emitted"), "out['emitted']", torch.int32, shape=(R, b))
+            _need(out.get("n_emit"), "out['n_emit']", torch.int32, shape=(R,))
+            _need(out.get("next_tokens"), "out['next_tokens']", torch.int32, shape=(R, b), optional=True)
+        _on_device(verify_ids=verify_ids, draft_ids=draft_ids, budget=budget,
+                   out=[] if out is None else [v for v in out.values() if v is not None])
+
+    def _check_drafts(self, draft_ids, draft_stride, R, b, budget):
         if b > 1 or draft_ids is not None:
             # element (r, j) at (r * (b-1) + j) * draft_stride: [R, b-1] for stride 1, or
             # [R, b-1, k] top-k ids with stride k
@@ -356,13 +366,6 @@ class Drafter:
                 raise ValueError(f"draft_ids must be a dense [{R}, {max(b - 1, 1)}(, {draft_stride})] tensor "
                                  f"(got {tuple(draft_ids.shape)})")
         _need(budget, "budget", torch.int32, shape=(R,), optional=True)
-        if out is not None:
-            _need(out.get("accept_len"), "out['accept_len']", torch.int32, shape=(R,))
-            _need(out.get("emitted"), "out['emitted']", torch.int32, shape=(R, b))
-            _need(out.get("n_emit"), "out['n_emit']", torch.int32, shape=(R,))
-            _need(out.get("next_tokens"), "out['next_tokens']", torch.int32, shape=(R, b), optional=True)
-        _on_device(verify_ids=verify_ids, draft_ids=draft_ids, budget=budget,
-                   out=[] if out is None else [v for v in out.values() if v is not None])
 
     def accept(self, draft_ids: torch.Tensor, draft_stride: int, verify_ids: torch.Tensor, eos_id: int = -1,
                budget: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None):
@@ -424,11 +427,12 @@ class Drafter:
                        delta: float = 0.0, seed: int = 0, round: int = 0, eos_id: int = -1,
                        budget: Optional[torch.Tensor] = None):
         """Sampling-mode accept of a round of block length target_logits.shape[1]."""
-        R, b, V = target_logits.shape
+        if not isinstance(target_logits, torch.Tensor) or target_logits.dim() != 3:
+            raise ValueError("target_logits must be a float32 tensor [R, block, vocab]")
+        R, b, _ = target_logits.shape
         _need(target_logits, "target_logits", torch.float32, shape=(R, b, self.cfg.vocab))
-        self._check_accept(draft_ids, draft_stride, torch.empty((R, b), dtype=torch.int32, device=target_logits.device),
-                           b, budget, None)
-        _on_device(target_logits=target_logits)
+        self._check_drafts(draft_ids, draft_stride, R, b, budget)
+        _on_device(target_logits=target_logits, draft_ids=draft_ids, budget=budget)
         out = {"accept_len": torch.empty(R, dtype=torch.int32, device=self.device),
                "emitted": torch.empty((R, b), dtype=torch.int32, device=self.device),
                "n_emit": torch.empty(R, dtype=torch.int32, device=self.device),

@@ -129,3 +129,19 @@ def test_block_policy_stays_in_range_for_any_accept_value():
     p = Bd.BlockPolicy(8, float("nan"))
     p.update(3)
     assert p.next_block() == 2
+
+
+def test_sampled_accept_argument_checks(dr):
+    import torch
+    V = dr.cfg.vocab
+    z = torch.zeros((2, 4, V), dtype=torch.float32)
+    with pytest.raises(ValueError, match="target_logits"):
+        dr.accept_sampled(torch.zeros((2, 3), dtype=torch.int32), 1, torch.zeros((2, 4), dtype=torch.float32))
+    with pytest.raises(ValueError, match="target_logits"):
+        dr.accept_sampled(torch.zeros((2, 3), dtype=torch.int32), 1, torch.zeros((2, 4, V - 1), dtype=torch.float32))
+    with pytest.raises(ValueError, match="draft_ids"):
+        dr.accept_sampled(torch.zeros((2, 2), dtype=torch.int32), 1, z)
+    with pytest.raises(ValueError, match="budget"):
+        dr.accept_sampled(torch.zeros((2, 3), dtype=torch.int32), 1, z, budget=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device"):
+        dr.accept_sampled(torch.zeros((2, 3), dtype=torch.int32), 1, z)
