@@ -79,6 +79,21 @@ WORKLOADS = {
 }
 
 
+def lm_kernel_label(hidden: int, vocab: int, rows: int) -> str:
+    """Name of the LM-head logits kernel the library launches for this shape: the
+    variant that streams the weights through LDS needs one 16-row tile of normed
+    rows staged whole beside its ring of 16 weight slots (8 waves x 2 chunks x
+    4 KB) within 159 KB of LDS, a hidden size in whole 128-column chunks, and at
+    most 8 column groups of 128 per workgroup."""
+    groups = (vocab + 127) // 128
+    x = (16 * (hidden + 8) * 2 + 15) & ~15
+    fits = (rows <= 16 and hidden % 128 == 0 and hidden // 128 >= 2 and x + 8 * 2 * 4096 <= 159 * 1024
+            and -(-groups // 256) <= 8)
+    if fits:
+        return "lm_logits_lds_kernel (shared LM head logits + 16-column maxima, weights streamed through LDS)"
+    return "lm_logits_kernel (shared LM head logits + 16-column maxima)"
+
+
 def round_bytes(cfg, R: int, k: int) -> dict:
     """Algorithmic HBM bytes of one round: every weight once, each request's
     context K/V window read once per layer, new ring rows written, taps read,
@@ -626,7 +641,7 @@ def main():
         "drafted_tokens_per_s": round(blocks_s * (B - 1), 1),
         "accepted_tokens_per_s": round(blocks_s * tau, 1),
         "tau": round(tau, 3),
-        "roofline": {"bound": "hbm", "kernel": "lm_logits_kernel (shared LM head logits + 16-column maxima)",
+        "roofline": {"bound": "hbm", "kernel": lm_kernel_label(cfg.hidden, cfg.vocab, R * B),
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": lm_traffic(args.workload),
                      "avg_launch_us": round(lm_ms * 1e3, 2), "bytes_per_launch": rb["lm_head"]},

@@ -96,8 +96,10 @@ size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
 // gmax[R*(B-1)][ceil(N/16)]; then the exact per-row top-k to ids/vals
 // [R*(B-1)][topk] (topk <= 16).
 struct LmPlan {
-  int MT, XL, groups, P;   // XL: 1 rows staged in LDS, 2 LDS windows of bf16 rows, 0 rows from L2
-  int slots, defer_off;    // groups per workgroup whose epilogue waits for the last load; their LDS offset
+  int MT, XL, groups, P;   // XL: 1 rows staged in LDS, 2 LDS windows of bf16 rows, 0 rows from L2,
+                           // 3 rows staged and W through LDS (direct loads)
+  int slots, defer_off;    // groups per workgroup whose epilogue waits for the last load; their LDS
+                           // offset (XL 3: the offset of the W slots)
   size_t lds;
 };
 LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu);

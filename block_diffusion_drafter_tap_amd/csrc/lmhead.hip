@@ -61,6 +61,38 @@ __global__ __launch_bounds__(256) void lm_norm_rows_kernel(const GemmArgs a, uin
   }
 }
 
+// Logits: the caller's layout [R*(B-1)][N] (mask rows only), or the transposed
+// scratch layout [N][16*MT] (every row), where a wave's 16 columns x 16 rows of a
+// tile are one contiguous 1 KB store. The 16 lanes of a lane group also reduce
+// their row's max over the wave's 16 columns (one entry per 16-column group, for
+// the top-k filter).
+template <int MT>
+DEV void lm_epilogue(const GemmArgs& a, int gg, const f32x4 (&ac)[MT], float* logits, int transposed, float* gmax) {
+  constexpr int GC = 128, ROWS = MT * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n = gg * GC + wave * 16 + lr;
+  const int ng = (a.N + 15) / 16, grp16 = gg * (GC / 16) + wave;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (transposed && n < a.N) *(f32x4*)(logits + (size_t)n * ROWS + mt * 16 + 4 * lg) = ac[mt];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + 4 * lg + i;
+      const int bi = m % a.B, r0 = a.lm_first_row;
+      const bool row_ok = m < a.M && bi >= r0;
+      const size_t orow = (size_t)((m / a.B) * (a.B - r0) + bi - r0);
+      if (!transposed && row_ok && n < a.N) logits[orow * a.N + n] = ac[mt][i];
+      float v = n < a.N ? ac[mt][i] : -INFINITY;
+      v = fmaxf(v, __shfl_xor(v, 1, 64));
+      v = fmaxf(v, __shfl_xor(v, 2, 64));
+      v = fmaxf(v, __shfl_xor(v, 4, 64));
+      v = fmaxf(v, __shfl_xor(v, 8, 64));
+      if (row_ok && lr == 0 && grp16 < ng) gmax[orow * ng + grp16] = v;
+    }
+  }
+}
+
 template <int MT, int XL, int D>
 __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_groups, float* logits, int transposed,
                                                         float* gmax, int nslots, int defer_off) {
@@ -169,33 +201,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     return ld16(a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + kk + 8 * lg);
   };
 
-  // Logits: the caller's layout [R*(B-1)][N] (mask rows only), or the
-  // transposed scratch layout [N][16*MT] (every row), where a wave's 16
-  // columns x 16 rows of a tile are one contiguous 1 KB store.
-  // The 16 lanes of a lane group also reduce their row's max over the wave's
-  // 16 columns (one entry per 16-column group, for the top-k filter).
-  auto epilogue = [&](int gg, const f32x4 (&ac)[MT]) {
-    const int n = gg * GC + wave * 16 + lr;
-    const int ng = (a.N + 15) / 16, grp16 = gg * (GC / 16) + wave;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (transposed && n < a.N) *(f32x4*)(logits + (size_t)n * ROWS + mt * 16 + 4 * lg) = ac[mt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + 4 * lg + i;
-        const int bi = m % a.B, r0 = a.lm_first_row;
-        const bool row_ok = m < a.M && bi >= r0;
-        const size_t orow = (size_t)((m / a.B) * (a.B - r0) + bi - r0);
-        if (!transposed && row_ok && n < a.N) logits[orow * a.N + n] = ac[mt][i];
-        float v = n < a.N ? ac[mt][i] : -INFINITY;
-        v = fmaxf(v, __shfl_xor(v, 1, 64));
-        v = fmaxf(v, __shfl_xor(v, 2, 64));
-        v = fmaxf(v, __shfl_xor(v, 4, 64));
-        v = fmaxf(v, __shfl_xor(v, 8, 64));
-        if (row_ok && lr == 0 && grp16 < ng) gmax[orow * ng + grp16] = v;
-      }
-    }
-  };
+  auto epilogue = [&](int gg, const f32x4 (&ac)[MT]) { lm_epilogue<MT>(a, gg, ac, logits, transposed, gmax); };
 
   for (; g < n_groups; g += gridDim.x) {
     const int gnext = g + gridDim.x;
@@ -245,6 +251,140 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) ac[mt] = dslot[((size_t)(gi * NW + wave) * MT + mt) * 64 + lane];
     epilogue(gg, ac);
+  }
+}
+
+// W through LDS (16 rows, the normed rows staged whole): every weight load is a
+// direct-to-LDS, nontemporal 16-byte load, and one load instruction covers 4
+// whole W rows x 256 bytes, so the 128-byte lines of the stream are each read
+// by one instruction. (The MFMA operand pattern, 16 rows x 64 bytes per
+// instruction, leaves every line to two instructions; read nontemporally it
+// fell to 4.8 TB/s against 7.0 for whole lines, in a bare-load probe on this
+// grid.) A wave's 16-row x 128-k chunk is one 4 KB LDS slot, D slots per wave.
+// In the slot, W row r's k-block b (8 values) sits at piece
+// (r / 4) * 64 + (r % 4) * 16 + ((b + r) % 16): load instruction s fills pieces
+// 64s .. 64s + 63 with rows 4s .. 4s + 3, and the MFMA B fragment of step s2
+// (lane L: row L % 16, k-block 4 s2 + L / 16) reads 16 lanes' pieces from 16
+// distinct bank groups. The loads write LDS behind the compiler's back, so
+// the wait for a slot is an explicit vmcnt: the only vector memory operations
+// in the streaming loop are these loads (4 per chunk), with D chunks in flight
+// (after the last group's last refill, a wait is for every load).
+// Each wave's accumulators of its (at most LM_LDS_MAX_GROUPS) groups stay in
+// registers until the last load is out, so no store interleaves with the
+// stream. The MFMA inputs and their order equal lm_logits_kernel's, so the
+// logits are the same bit for bit.
+constexpr int LM_LDS_MAX_GROUPS = 8;
+constexpr int LM_LDS_DEPTH = 2;   // W chunks in flight per wave (measured in the probe: 2 as fast as 3 or 4)
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited for
+  constexpr int n = 4 * (D - 1);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_groups, float* logits,
+                                                            int transposed, float* gmax, int w_off) {
+  constexpr int GC = 128, ROWS = 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ float s_inv[ROWS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = a.K, nchunks = K / 128, ldl = K + 8;
+  uint16_t* xs = (uint16_t*)smem;
+  char* wring = smem + w_off + (size_t)wave * D * 4096;
+  const uint16_t* W = (const uint16_t*)a.w;
+  auto issue = [&](int gg, int c, int slot) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int row = 4 * s + lg, kb = (lane - row) & 15;
+      const uint16_t* src = W + (size_t)min(gg * GC + wave * 16 + row, a.N - 1) * K + c * 128 + kb * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(wring + slot * 4096 + s * 1024), 16, 0, 2);
+    }
+  };
+  const int g0 = blockIdx.x;
+  if (g0 < n_groups) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue(g0, j, j);
+  }
+  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
+    const int m = min(r, a.M - 1);
+    float ss = 0.f;
+    for (int b0 = 0; b0 < a.n_ssq; b0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.ssq_in[(size_t)min(b0 + u, a.n_ssq - 1) * a.ssq_ld + m];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < a.n_ssq) ss += v[u];
+    }
+    s_inv[r] = 1.0f / sqrtf(ss / (float)K + a.eps);
+  }
+  __syncthreads();
+  {
+    const int per_row = K / 8, total = ROWS * per_row;
+    for (int e0 = threadIdx.x; e0 < total; e0 += 8 * blockDim.x) {
+      f32x4 h0[8], h1[8];
+      u32x4 gg[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(e0 + u * (int)blockDim.x, total - 1);
+        const int r = e / per_row, c = e % per_row;
+        const float* p = a.xf + (size_t)min(r, a.M - 1) * a.ldx + 8 * c;
+        h0[u] = *(const f32x4*)p;
+        h1[u] = *(const f32x4*)(p + 4);
+        gg[u] = ld16(a.xgain + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * (int)blockDim.x;
+        if (e < total) {
+          const int r = e / per_row, c = e % per_row;
+          *(u32x4*)(xs + r * ldl + 8 * c) = norm8(h0[u], h1[u], gg[u], s_inv[r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  f32x4 park[LM_LDS_MAX_GROUPS];
+  int slot = 0;
+#pragma unroll
+  for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) {
+    const int g = g0 + gi * (int)gridDim.x;
+    if (g < n_groups) {
+      const int gn = g + (int)gridDim.x;
+      const bool last = gn >= n_groups;   // no refills past its end: its last D - 1 chunks wait for every load
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < nchunks; ++c) {
+        if (last && c > nchunks - D) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+        else wait_w_chunk<D>();
+        const char* sl = wring + slot * 4096;
+        u32x4 f[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int b = 4 * s2 + lg;
+          f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          acc = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + lr * ldl + 128 * c + 32 * s2 + 8 * lg)), as_bf16x8(f[s2]),
+                             acc);
+        const int nc = c + D;
+        if (nc < nchunks) issue(g, nc, slot);
+        else if (!last) issue(gn, nc - nchunks, slot);
+        slot = slot + 1 == D ? 0 : slot + 1;
+      }
+      park[gi] = acc;
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) {
+    const int g = g0 + gi * (int)gridDim.x;
+    if (g < n_groups) {
+      const f32x4 ac[1] = {park[gi]};
+      lm_epilogue<1>(a, g, ac, logits, transposed, gmax);
+    }
   }
 }
 
@@ -545,6 +685,16 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   const size_t xbytes = (size_t)rows * (K + 8) * 2;            // the whole normed rows
   const size_t wbytes = (size_t)2 * rows * (4 * 128 + 8) * 2;  // two windows of 4 chunks
   p.XL = xbytes <= LM_XL_MAX_BYTES ? 1 : (K % 512 == 0 && wbytes <= LM_XL_MAX_BYTES ? 2 : 0);
+  // one row tile, staged whole, with room for the W slots: W through LDS (XL 3)
+  const size_t xoff = (xbytes + 15) & ~(size_t)15;
+  if (p.MT == 1 && K % 128 == 0 && K / 128 >= LM_LDS_DEPTH && per <= LM_LDS_MAX_GROUPS &&
+      xoff + (size_t)8 * LM_LDS_DEPTH * 4096 <= LM_XL_MAX_BYTES) {
+    p.XL = 3;
+    p.defer_off = (int)xoff;   // the W slots
+    p.slots = 0;
+    p.lds = xoff + (size_t)8 * LM_LDS_DEPTH * 4096;
+    return p;
+  }
   p.lds = p.XL == 1 ? xbytes : (p.XL == 2 ? wbytes : 0);
   // LDS left over holds the deferred accumulator fragments (8 waves x MT x 1 KB per group)
   p.defer_off = (int)((p.lds + 15) & ~(size_t)15);
@@ -564,6 +714,14 @@ hipError_t launch_lm_norm_rows(const GemmArgs& a, uint16_t* z, hipStream_t st) {
 hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, int transposed, float* gmax,
                             hipStream_t st) {
   if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
+  if (p.XL == 3) {
+    if (p.MT != 1 || a.K % 128 || a.K / 128 < LM_LDS_DEPTH || a.M > 16 ||
+        (long long)p.P * LM_LDS_MAX_GROUPS < p.groups)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
+                       transposed, gmax, p.defer_off);
+    return hipGetLastError();
+  }
   hipError_t e;
 #define LM(MT)                                                                              \
   e = p.XL == 1   ? launch_lm<MT, 1>(a, p, logits, transposed, gmax, st) \
