@@ -21,8 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["api.hip", "gemm.hip", "finish.hip", "lmhead.hip", "attention.hip", "small.hip", "prefill.hip",
-           "tree.hip", "sampling.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gateup.hip", "finish.hip", "lmhead.hip", "attention.hip", "small.hip",
+           "prefill.hip", "tree.hip", "sampling.hip"]
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -961,7 +961,9 @@ int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st,
       a.ldo = g.ffn;
       GemmPlan p = plan_for(g, M, g.ffn, H, GC_DEFAULT, 1, P_GATEUP);
       Timed tm(ctx, DFLASH_K_GATEUP, st);
-      if (p.S > 1) {
+      if (wf == WF_BF16 && gateup_lds_bytes(M, H)) {
+        e = launch_gateup_lds(a, p.ks, st);   // same sums as the split plan p, one launch
+      } else if (p.S > 1) {
         e = launch_gemm(a, p, X_NORM, E_PARTP, wf, st);
         if (e == hipSuccess) e = launch_finish_silu(a.partials, p.S, M, g.ffn, act, g.ffn, st);
       } else {

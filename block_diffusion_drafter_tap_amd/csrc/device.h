@@ -17,8 +17,29 @@ DEV float bfbits2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 DEV __bf16 f2bf(float v) { return (__bf16)v; }
 DEV uint16_t f2bfbits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
+// Two values as a bf16 pair (lo in the low half), rounded to nearest even: one
+// v_cvt_pk_bf16_f32, the same conversion f2bfbits makes for each value alone.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bfbits(lo) | ((uint32_t)f2bfbits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// RMSNorm of 8 consecutive values: bf16x8 of (h * inv) * g, with h the fp32
+// values in h0, h1, inv the row's 1/rms and g their 8 bf16 gains. Every path
+// that stages normed rows uses this, so a row's bf16 operand is the same bits
+// whichever kernel stages it.
+DEV u32x4 norm8(f32x4 h0, f32x4 h1, u32x4 g, float inv) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x4 h = i ? h1 : h0;
+    r[2 * i] = pack_bf16x2(h[0] * inv * __uint_as_float(g[2 * i] << 16),
+                           h[1] * inv * __uint_as_float(g[2 * i] & 0xffff0000u));
+    r[2 * i + 1] = pack_bf16x2(h[2] * inv * __uint_as_float(g[2 * i + 1] << 16),
+                               h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
+  }
+  return r;
 }
 
 // fp64 -> bf16 rounded to nearest even in one step: fp64 -> fp32 toward zero

@@ -1,0 +1,204 @@
+// Gate/up projection of the MLP sublayer in one launch for up to 16 rows:
+// act = SiLU(x W_gate^T) * (x W_up^T), x the RMS-normed rows (bf16), act bf16.
+// The drafter layer's MLP is the Qwen3 one (ExecuTorch PR #20840, "[RFC] DFlash",
+// landing criteria, item 2: the draft layer reuses the Qwen3 RMSNorm and MLP).
+//
+// One workgroup of 2 NP waves per 16 NP output columns: waves 0..NP-1 stream
+// the gate rows of W, waves NP..2NP-1 the matching up rows, each wave 16 rows
+// over the whole of K. The normed rows are staged once in LDS (16 x K bf16); the weights
+// go from HBM straight into a per-wave LDS ring of D slots of 4 KB, one
+// 16-row x 128-column chunk per slot, with nontemporal direct-to-LDS loads of
+// 4 rows x 256 B per instruction (whole 128-byte lines). The ring layout is
+// swizzled through the piece each lane fetches (row r's 16-byte piece b at
+// (r/4)*64 + (r%4)*16 + (b+r)%16), so the 16 lanes that read one piece index of
+// 16 rows for an MFMA B fragment hit 16 different bank groups.
+//
+// A single workgroup per CU streams about 30-35 GB/s this way, so the ~200
+// workgroups of a qwen3-sized gate/up move its weights about as fast as the
+// split-K GEMM's 760, without the split partials' round trip through memory
+// and the separate SiLU kernel.
+//
+// Rounding: the sums are formed exactly as the split-K GEMM and its finish
+// kernel form them for the same split plan (ks columns per split): each split's
+// chunks accumulate in one MFMA chain from zero, the split sums are added in
+// split order starting from +0, and SiLU(g) * u is evaluated with the same
+// expression. A row's result is therefore bit-identical on both paths, so it
+// does not depend on how many rows share the call.
+#include "device.h"
+#include "kernels.h"
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 3 wave pairs: ~200 workgroups at a qwen3-sized ffn keep more CUs streaming than
+// 4 pairs' ~150 (measured 1.5-2 us faster per launch); a deeper ring measured no
+// faster
+constexpr int GU_PAIRS = 3;   // gate/up wave pairs per workgroup
+constexpr int GU_DEPTH = 2;   // ring slots per wave
+constexpr int GU_XP = 16;     // X pieces per thread (a multiple of 8): K / 8 <= GU_XP x (128 GU_PAIRS / 16)
+constexpr int GU_SSQ = 24;    // the producer's column groups of 128 per row: K / 128 <= GU_SSQ
+constexpr size_t GU_LDS_MAX = 159 * 1024;
+
+template <int D>
+DEV void wait_chunk_ring() {   // vmcnt <= 4 (D - 1): the oldest chunk has landed
+  constexpr int n = 4 * (D - 1);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+DEV void wait_all_loads() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }   // vmcnt(0)
+
+// LDS: the staged rows [16][K + 8] bf16, the gains (whole KB), then the rings
+__host__ __device__ inline size_t gu_gain_bytes(int K) { return ((size_t)K * 2 + 1023) & ~(size_t)1023; }
+__host__ __device__ inline size_t gu_x_bytes(int K) {
+  return (((size_t)16 * (K + 8) * 2 + 15) & ~(size_t)15) + gu_gain_bytes(K);
+}
+
+template <int NP, int D, int XP>
+__global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) {
+  constexpr int ROWS = 16, COLS = 16 * NP;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = a.K, nchunks = K / 128, ldl = K + 8;
+  const int split_chunks = a.ks / 128;
+  uint16_t* xs = (uint16_t*)smem;
+  const size_t ring_off = gu_x_bytes(K);
+  char* ring = smem + ring_off + (size_t)wave * D * 4096;
+  const uint16_t* W = (const uint16_t*)a.w;
+  const bool is_up = wave >= NP;
+  const int col0 = blockIdx.x * COLS + (wave - (is_up ? NP : 0)) * 16;   // this wave's first logical column
+  const size_t row_add = is_up ? (size_t)a.pair_off : 0;
+
+  // chunk c of this wave's 16 rows into ring slot `slot`: instruction s loads
+  // rows 4s..4s+3, lane l taking piece (l - row) & 15 of row 4s + l/16
+  auto issue = [&](int c, int slot) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int row = 4 * s + lg, kb = (lane - row) & 15;
+      const uint16_t* src = W + ((size_t)min(col0 + row, a.N - 1) + row_add) * K + c * 128 + kb * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(ring + slot * 4096 + s * 1024), 16, 0, 2);
+    }
+  };
+  // Prologue: every load goes out at once and lands together, about one HBM
+  // latency after the start: the ring's first D chunks and the gains (straight
+  // to LDS), then, for this thread's row (TPR threads per row), the producer's
+  // per-column-group sums of squares and this thread's X pieces (8 values each,
+  // pieces t % TPR + TPR u of the row). Each thread forms its row's 1/rms from
+  // the sums added in group order, and x = h * inv * gain is rounded to bf16 and
+  // staged whole.
+  constexpr int TPR = 128 * NP / ROWS;
+  const int per_row = K / 8;
+  const int row = threadIdx.x / TPR, pc0 = threadIdx.x % TPR;
+  const int m = min(row, a.M - 1);
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue(j, j);
+  const uint16_t* gains = (const uint16_t*)(smem + ring_off - gu_gain_bytes(K));
+  for (int i = wave; i < gu_gain_bytes(K) / 1024; i += 2 * NP)   // 1 KB of gains per instruction
+    __builtin_amdgcn_global_load_lds((const void*)(a.xgain + min(512 * i + 8 * lane, K - 8)),
+                                     (lds_void*)(gains + 512 * i), 16, 0, 0);
+  // (every use comes after the scheduling barrier, and the sums of squares are
+  // loaded unconditionally, clamped to the last group: one wait then covers the
+  // whole prologue)
+  float sq[GU_SSQ];
+#pragma unroll
+  for (int b = 0; b < GU_SSQ; ++b) sq[b] = a.ssq_in[(size_t)min(b, a.n_ssq - 1) * a.ssq_ld + m];
+  f32x4 h0[XP], h1[XP];
+  const float* hrow = a.xf + (size_t)m * a.ldx;
+#pragma unroll
+  for (int u = 0; u < XP; ++u) {
+    const int pc = pc0 + TPR * u;
+    if (pc < per_row) {
+      h0[u] = *(const f32x4*)(hrow + 8 * pc);
+      h1[u] = *(const f32x4*)(hrow + 8 * pc + 4);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float ss = 0.f;
+#pragma unroll
+  for (int b = 0; b < GU_SSQ; ++b)
+    if (b < a.n_ssq) ss += sq[b];
+  const float inv = 1.0f / sqrtf(ss / (float)K + a.eps);
+  __syncthreads();   // the gains have landed in every wave
+#pragma unroll
+  for (int u0 = 0; u0 < XP; u0 += 8) {   // the gains of 8 pieces read together, then converted
+    u32x4 g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g[j] = *(const u32x4*)(gains + 8 * min(pc0 + TPR * (u0 + j), per_row - 1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pc = pc0 + TPR * (u0 + j);
+      if (pc < per_row) *(u32x4*)(xs + row * ldl + 8 * pc) = norm8(h0[u0 + j], h1[u0 + j], g[j], inv);
+    }
+  }
+  __syncthreads();
+
+  // stream: chunk c's slot is read as 4 MFMA B fragments, then refilled with
+  // chunk c + D; a split's chain is added to the running sum when it ends
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f}, acc = {0.f, 0.f, 0.f, 0.f};
+  int slot = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + D <= nchunks) wait_chunk_ring<D>();
+    else wait_all_loads();
+    const char* sl = ring + slot * 4096;
+    u32x4 f[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int b = 4 * s2 + lg;
+      f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      acc = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + lr * ldl + 128 * c + 32 * s2 + 8 * lg)), as_bf16x8(f[s2]),
+                         acc);
+    if (c + D < nchunks) issue(c + D, slot);
+    slot = slot + 1 == D ? 0 : slot + 1;
+    if ((c + 1) % split_chunks == 0 || c + 1 == nchunks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[i] = tot[i] + acc[i];
+      acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // lane holds C[4 lg + i][lr] of its wave's 16 columns; the up waves hand
+  // theirs to the gate waves through LDS (the ring is dead once every wave
+  // has passed the barrier: its last chunks waited for every load)
+  __syncthreads();
+  float* up = (float*)(smem + ring_off);   // [16][COLS]
+  if (is_up) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) up[(4 * lg + i) * COLS + (wave - NP) * 16 + lr] = tot[i];
+  }
+  __syncthreads();
+  if (!is_up) {
+    const int n = col0 + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * lg + i;
+      if (m < a.M && n < a.N) {
+        const float g = tot[i], u = up[m * COLS + wave * 16 + lr];
+        ((uint16_t*)a.out)[(size_t)m * a.ldo + n] = f2bfbits(g / (1.0f + expf(-g)) * u);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t gateup_lds_bytes(int M, int K) {
+  // rows, whole chunks, a full ring, and one producer sum of squares per thread
+  if (M < 1 || M > 16 || K % 128 || K / 128 < GU_DEPTH || K / 128 > GU_SSQ || K / 8 > GU_XP * 8 * GU_PAIRS) return 0;
+  const size_t b = gu_x_bytes(K) + (size_t)2 * GU_PAIRS * GU_DEPTH * 4096;
+  return b <= GU_LDS_MAX ? b : 0;
+}
+
+hipError_t launch_gateup_lds(const GemmArgs& a, int ks, hipStream_t st) {
+  const size_t lds = gateup_lds_bytes(a.M, a.K);
+  if (!lds || ks < 128 || ks % 128 || a.pair_off < a.N || a.N < 1 || a.n_ssq < 1 || a.n_ssq > GU_SSQ)
+    return hipErrorInvalidValue;
+  GemmArgs b = a;
+  b.ks = ks;
+  constexpr int cols = 16 * GU_PAIRS;
+  hipLaunchKernelGGL((gateup_lds_kernel<GU_PAIRS, GU_DEPTH, GU_XP>), dim3((a.N + cols - 1) / cols), dim3(128 * GU_PAIRS), lds,
+                     st, b);
+  return hipGetLastError();
+}

@@ -65,18 +65,7 @@ DEV u32x4 load_x(const GemmArgs& a, int row, int k, float inv) {
     return ld16(a.x + (size_t)row * a.ldx + k);
   } else if constexpr (XK == X_NORM) {
     const float* p = a.xf + (size_t)row * a.ldx + k;
-    const f32x4 h0 = *(const f32x4*)p, h1 = *(const f32x4*)(p + 4);
-    const u32x4 g = ld16(a.xgain + k);
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const f32x4 h = i ? h1 : h0;
-      r[2 * i] = pack_bf16x2(h[0] * inv * __uint_as_float(g[2 * i] << 16),
-                             h[1] * inv * __uint_as_float(g[2 * i] & 0xffff0000u));
-      r[2 * i + 1] = pack_bf16x2(h[2] * inv * __uint_as_float(g[2 * i + 1] << 16),
-                                 h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
-    }
-    return r;
+    return norm8(*(const f32x4*)p, *(const f32x4*)(p + 4), ld16(a.xgain + k), inv);
   } else {
     const int t = k / a.tap_hidden;
     const int col = k - t * a.tap_hidden;

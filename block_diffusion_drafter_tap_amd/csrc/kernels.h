@@ -87,6 +87,14 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, int xk, int epi, in
                        hipStream_t st);
 size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
 
+// Gate/up of the MLP in one launch for up to 16 rows (bf16 weights [2N][K], the
+// up rows at pair_off = N; X_NORM fields of GemmArgs): act = SiLU(gate) * up as
+// bf16 to out [M][ldo]. The sums are formed as the split-K GEMM with `ks`
+// columns per split and its finish form them, so the bits match that path.
+// gateup_lds_bytes: dynamic LDS of a launch, 0 when the shape does not fit.
+size_t gateup_lds_bytes(int M, int K);
+hipError_t launch_gateup_lds(const GemmArgs& a, int ks, hipStream_t st);
+
 // LM head: persistent logits GEMM over the block rows (GemmArgs X_NORM fields
 // xf, xgain, ssq_*, w = W_lm, M = R*B, N = vocab, K, B, topk; when the plan does
 // not stage the rows in LDS (XL = 0), x / ldx instead hold the final-normed rows

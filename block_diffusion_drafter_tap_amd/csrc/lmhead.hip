@@ -26,20 +26,6 @@ namespace {
 // CU, so nearly all of the 160 KB of a gfx950 CU)
 constexpr size_t LM_XL_MAX_BYTES = 159 * 1024;
 
-// bf16x8 of (h0, h1) * inv * g (g: 8 bf16 gains)
-DEV u32x4 norm8(f32x4 h0, f32x4 h1, u32x4 g, float inv) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const f32x4 h = i ? h1 : h0;
-    r[2 * i] = pack_bf16x2(h[0] * inv * __uint_as_float(g[2 * i] << 16),
-                           h[1] * inv * __uint_as_float(g[2 * i] & 0xffff0000u));
-    r[2 * i + 1] = pack_bf16x2(h[2] * inv * __uint_as_float(g[2 * i + 1] << 16),
-                               h[3] * inv * __uint_as_float(g[2 * i + 1] & 0xffff0000u));
-  }
-  return r;
-}
-
 // The final-normed rows as bf16 for the path that does not stage them in LDS,
 // with the staging's arithmetic (sums of squares added in column-group order,
 // the same normalize-and-round per 8 values), so a row's logits do not depend
