@@ -24,20 +24,16 @@
 // split order starting from +0, and SiLU(g) * u is evaluated with the same
 // expression. A row's result is therefore bit-identical on both paths, so it
 // does not depend on how many rows share the call.
-#include "device.h"
-#include "kernels.h"
+#include "norm_stage.h"
 
 namespace {
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // 3 wave pairs: ~200 workgroups at a qwen3-sized ffn keep more CUs streaming than
 // 4 pairs' ~150 (measured 1.5-2 us faster per launch); a deeper ring measured no
 // faster
 constexpr int GU_PAIRS = 3;   // gate/up wave pairs per workgroup
 constexpr int GU_DEPTH = 2;   // ring slots per wave
-constexpr int GU_XP = 16;     // X pieces per thread (a multiple of 8): K / 8 <= GU_XP x (128 GU_PAIRS / 16)
-constexpr int GU_SSQ = 24;    // the producer's column groups of 128 per row: K / 128 <= GU_SSQ
+constexpr int GU_XP = 16;     // staged X pieces per thread
 constexpr size_t GU_LDS_MAX = 159 * 1024;
 
 template <int D>
@@ -48,14 +44,11 @@ DEV void wait_chunk_ring() {   // vmcnt <= 4 (D - 1): the oldest chunk has lande
 DEV void wait_all_loads() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }   // vmcnt(0)
 
 // LDS: the staged rows [16][K + 8] bf16, the gains (whole KB), then the rings
-__host__ __device__ inline size_t gu_gain_bytes(int K) { return ((size_t)K * 2 + 1023) & ~(size_t)1023; }
-__host__ __device__ inline size_t gu_x_bytes(int K) {
-  return (((size_t)16 * (K + 8) * 2 + 15) & ~(size_t)15) + gu_gain_bytes(K);
-}
+__host__ __device__ inline size_t gu_x_bytes(int K) { return norm_rows_bytes(K) + norm_gain_bytes(K); }
 
 template <int NP, int D, int XP>
 __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) {
-  constexpr int ROWS = 16, COLS = 16 * NP;
+  constexpr int COLS = 16 * NP;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -79,58 +72,14 @@ __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) 
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(ring + slot * 4096 + s * 1024), 16, 0, 2);
     }
   };
-  // Prologue: every load goes out at once and lands together, about one HBM
-  // latency after the start: the ring's first D chunks and the gains (straight
-  // to LDS), then, for this thread's row (TPR threads per row), the producer's
-  // per-column-group sums of squares and this thread's X pieces (8 values each,
-  // pieces t % TPR + TPR u of the row). Each thread forms its row's 1/rms from
-  // the sums added in group order, and x = h * inv * gain is rounded to bf16 and
-  // staged whole.
-  constexpr int TPR = 128 * NP / ROWS;
-  const int per_row = K / 8;
-  const int row = threadIdx.x / TPR, pc0 = threadIdx.x % TPR;
-  const int m = min(row, a.M - 1);
+  // Prologue: the ring's first D chunks, then the normed rows' loads; one wait
+  // covers all of them, about one HBM latency after the start.
 #pragma unroll
   for (int j = 0; j < D; ++j) issue(j, j);
-  const uint16_t* gains = (const uint16_t*)(smem + ring_off - gu_gain_bytes(K));
-  for (int i = wave; i < gu_gain_bytes(K) / 1024; i += 2 * NP)   // 1 KB of gains per instruction
-    __builtin_amdgcn_global_load_lds((const void*)(a.xgain + min(512 * i + 8 * lane, K - 8)),
-                                     (lds_void*)(gains + 512 * i), 16, 0, 0);
-  // (every use comes after the scheduling barrier, and the sums of squares are
-  // loaded unconditionally, clamped to the last group: one wait then covers the
-  // whole prologue)
-  float sq[GU_SSQ];
-#pragma unroll
-  for (int b = 0; b < GU_SSQ; ++b) sq[b] = a.ssq_in[(size_t)min(b, a.n_ssq - 1) * a.ssq_ld + m];
-  f32x4 h0[XP], h1[XP];
-  const float* hrow = a.xf + (size_t)m * a.ldx;
-#pragma unroll
-  for (int u = 0; u < XP; ++u) {
-    const int pc = pc0 + TPR * u;
-    if (pc < per_row) {
-      h0[u] = *(const f32x4*)(hrow + 8 * pc);
-      h1[u] = *(const f32x4*)(hrow + 8 * pc + 4);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  float ss = 0.f;
-#pragma unroll
-  for (int b = 0; b < GU_SSQ; ++b)
-    if (b < a.n_ssq) ss += sq[b];
-  const float inv = 1.0f / sqrtf(ss / (float)K + a.eps);
-  __syncthreads();   // the gains have landed in every wave
-#pragma unroll
-  for (int u0 = 0; u0 < XP; u0 += 8) {   // the gains of 8 pieces read together, then converted
-    u32x4 g[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) g[j] = *(const u32x4*)(gains + 8 * min(pc0 + TPR * (u0 + j), per_row - 1));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int pc = pc0 + TPR * (u0 + j);
-      if (pc < per_row) *(u32x4*)(xs + row * ldl + 8 * pc) = norm8(h0[u0 + j], h1[u0 + j], g[j], inv);
-    }
-  }
-  __syncthreads();
+  uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(K));
+  NormRowsLoads<XP> L;
+  norm_rows_issue<128 * NP, XP>(a, gains, L);
+  norm_rows_store<128 * NP, XP>(a, gains, xs, ldl, L);
 
   // stream: chunk c's slot is read as 4 MFMA B fragments, then refilled with
   // chunk c + D; a split's chain is added to the running sum when it ends
@@ -186,14 +135,14 @@ __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) 
 
 size_t gateup_lds_bytes(int M, int K) {
   // rows, whole chunks, a full ring, and one producer sum of squares per thread
-  if (M < 1 || M > 16 || K % 128 || K / 128 < GU_DEPTH || K / 128 > GU_SSQ || K / 8 > GU_XP * 8 * GU_PAIRS) return 0;
+  if (M < 1 || M > 16 || K / 128 < GU_DEPTH || !norm_rows_fit(K, 128 * GU_PAIRS, GU_XP)) return 0;
   const size_t b = gu_x_bytes(K) + (size_t)2 * GU_PAIRS * GU_DEPTH * 4096;
   return b <= GU_LDS_MAX ? b : 0;
 }
 
 hipError_t launch_gateup_lds(const GemmArgs& a, int ks, hipStream_t st) {
   const size_t lds = gateup_lds_bytes(a.M, a.K);
-  if (!lds || ks < 128 || ks % 128 || a.pair_off < a.N || a.N < 1 || a.n_ssq < 1 || a.n_ssq > GU_SSQ)
+  if (!lds || ks < 128 || ks % 128 || a.pair_off < a.N || a.N < 1 || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX)
     return hipErrorInvalidValue;
   GemmArgs b = a;
   b.ks = ks;

@@ -17,8 +17,7 @@
 
 #include <algorithm>
 
-#include "device.h"
-#include "kernels.h"
+#include "norm_stage.h"
 
 namespace {
 
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 // logits are the same bit for bit.
 constexpr int LM_LDS_MAX_GROUPS = 8;
 constexpr int LM_LDS_DEPTH = 2;   // W chunks in flight per wave (measured in the probe: 2 as fast as 3 or 4)
-typedef __attribute__((address_space(3))) void lds_void;
+constexpr int LM_LDS_XP = 12;     // staged X pieces per thread
 
 template <int D>
 DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited for
@@ -272,9 +271,8 @@ DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited
 template <int D>
 __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_groups, float* logits,
                                                             int transposed, float* gmax, int w_off) {
-  constexpr int GC = 128, ROWS = 16;
+  constexpr int GC = 128;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ float s_inv[ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = a.K, nchunks = K / 128, ldl = K + 8;
@@ -289,50 +287,17 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(wring + slot * 4096 + s * 1024), 16, 0, 2);
     }
   };
+  // the first group's first D chunks, then the normed rows' loads; one wait
+  // covers all of them
   const int g0 = blockIdx.x;
   if (g0 < n_groups) {
 #pragma unroll
     for (int j = 0; j < D; ++j) issue(g0, j, j);
   }
-  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
-    const int m = min(r, a.M - 1);
-    float ss = 0.f;
-    for (int b0 = 0; b0 < a.n_ssq; b0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.ssq_in[(size_t)min(b0 + u, a.n_ssq - 1) * a.ssq_ld + m];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (b0 + u < a.n_ssq) ss += v[u];
-    }
-    s_inv[r] = 1.0f / sqrtf(ss / (float)K + a.eps);
-  }
-  __syncthreads();
-  {
-    const int per_row = K / 8, total = ROWS * per_row;
-    for (int e0 = threadIdx.x; e0 < total; e0 += 8 * blockDim.x) {
-      f32x4 h0[8], h1[8];
-      u32x4 gg[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = min(e0 + u * (int)blockDim.x, total - 1);
-        const int r = e / per_row, c = e % per_row;
-        const float* p = a.xf + (size_t)min(r, a.M - 1) * a.ldx + 8 * c;
-        h0[u] = *(const f32x4*)p;
-        h1[u] = *(const f32x4*)(p + 4);
-        gg[u] = ld16(a.xgain + 8 * c);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * (int)blockDim.x;
-        if (e < total) {
-          const int r = e / per_row, c = e % per_row;
-          *(u32x4*)(xs + r * ldl + 8 * c) = norm8(h0[u], h1[u], gg[u], s_inv[r]);
-        }
-      }
-    }
-    __syncthreads();
-  }
+  uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(K));
+  NormRowsLoads<LM_LDS_XP> L;
+  norm_rows_issue<512, LM_LDS_XP>(a, gains, L);
+  norm_rows_store<512, LM_LDS_XP>(a, gains, xs, ldl, L);
   f32x4 park[LM_LDS_MAX_GROUPS];
   int slot = 0;
 #pragma unroll
@@ -671,9 +636,9 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   const size_t xbytes = (size_t)rows * (K + 8) * 2;            // the whole normed rows
   const size_t wbytes = (size_t)2 * rows * (4 * 128 + 8) * 2;  // two windows of 4 chunks
   p.XL = xbytes <= LM_XL_MAX_BYTES ? 1 : (K % 512 == 0 && wbytes <= LM_XL_MAX_BYTES ? 2 : 0);
-  // one row tile, staged whole, with room for the W slots: W through LDS (XL 3)
-  const size_t xoff = (xbytes + 15) & ~(size_t)15;
-  if (p.MT == 1 && K % 128 == 0 && K / 128 >= LM_LDS_DEPTH && per <= LM_LDS_MAX_GROUPS &&
+  // one row tile, staged whole with its gains, with room for the W slots: W through LDS (XL 3)
+  const size_t xoff = norm_rows_bytes(K) + norm_gain_bytes(K);
+  if (p.MT == 1 && norm_rows_fit(K, 512, LM_LDS_XP) && K / 128 >= LM_LDS_DEPTH && per <= LM_LDS_MAX_GROUPS &&
       xoff + (size_t)8 * LM_LDS_DEPTH * 4096 <= LM_XL_MAX_BYTES) {
     p.XL = 3;
     p.defer_off = (int)xoff;   // the W slots
@@ -701,8 +666,8 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
                             hipStream_t st) {
   if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
   if (p.XL == 3) {
-    if (p.MT != 1 || a.K % 128 || a.K / 128 < LM_LDS_DEPTH || a.M > 16 ||
-        (long long)p.P * LM_LDS_MAX_GROUPS < p.groups)
+    if (p.MT != 1 || !norm_rows_fit(a.K, 512, LM_LDS_XP) || a.K / 128 < LM_LDS_DEPTH || a.M > 16 ||
+        a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX || (long long)p.P * LM_LDS_MAX_GROUPS < p.groups)
       return hipErrorInvalidValue;
     hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
                        transposed, gmax, p.defer_off);
