@@ -441,6 +441,9 @@ def main():
     # per-round offsets of the verify ids: 0 where the target agrees with the draft
     # (j < a), else 1 + noise in [1, V-1], so (draft + offset) mod V differs there
     delta = torch.where(keep, torch.zeros_like(noise1), noise1)[:, :, :B - 1].contiguous()
+    # with an even vocabulary the same agreement pattern is one launch: draft XOR 1
+    # is another id in [0, V) wherever the target disagrees
+    flip = (~keep).to(torch.int32)[:, :, :B - 1].contiguous() if V % 2 == 0 else None
 
     tokens = synth.block_tokens(cfg, R, seed=0, device=dev)
     ids = torch.empty((R, B - 1, k), dtype=torch.int32, device=dev)
@@ -456,8 +459,11 @@ def main():
 
     def one_round(i: int):
         dr.draft_block(tokens, k=k, ids=ids, vals=vals)
-        torch.add(ids[:, :, 0], delta[i], out=vview)
-        vview.remainder_(V)
+        if flip is not None:
+            torch.bitwise_xor(ids[:, :, 0], flip[i], out=vview)
+        else:
+            torch.add(ids[:, :, 0], delta[i], out=vview)
+            vview.remainder_(V)
         off = (i * B) % (pool_rows - B)
         if R == 1:
             ptrs = [pool_cat[t][0, off:].data_ptr() for t in range(cfg.n_taps)]
