@@ -483,10 +483,15 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
   // candidate logits as (key << 32 | ~index): one unsigned compare orders them
   // by (value desc, index asc)
   __shared__ __attribute__((aligned(16))) unsigned long long cb[512];
+  __shared__ unsigned long long cf[512];   // the candidates at or above T
+  __shared__ int s_nf;                      // their count
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ng = (N + 15) / 16;
   const float* gm = gmax + (size_t)row * ng;
-  if (t == 0) scratch[3] = 0;
+  if (t == 0) {
+    scratch[3] = 0;
+    s_nf = 0;
+  }
   // thread t owns groups t + 256*j: coalesced loads, all in flight together
   float gv[PER];
 #pragma unroll
@@ -559,45 +564,31 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
     // past the vocabulary: key 0 (below every logit's key), distinct per slot
     cb[e] = n < N ? ((unsigned long long)fkey(v) << 32) | (unsigned)~n : (unsigned long long)e;
   }
-  // pad to whole steps of 8 entries (four 16-byte reads) with entries that rank
-  // below every logit
-  const int ncp = (nc + 7) & ~7;
-  for (int e = nc + t; e < ncp; e += 256) cb[e] = (unsigned long long)e;
   __syncthreads();
-  // rank = number of entries with a larger combined key. Thread t ranks entries
-  // t and t + 256 in one branch-free pass over the list, four 16-byte reads
-  // (eight entries) per step so that the LDS reads overlap.
-  if (t < nc) {
-    const u32x4* c4 = (const u32x4*)cb;
-    const unsigned long long ca = cb[t];
-    const bool two = t + 256 < nc;
-    const unsigned long long cbv = two ? cb[t + 256] : ~0ull;
-    int ra = 0, rb = 0;
-    for (int j = 0; j < ncp / 2; j += 4) {
-      u32x4 q[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = c4[j + u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const unsigned long long c = ((unsigned long long)q[u][2 * h + 1] << 32) | q[u][2 * h];
-          ra += c > ca ? 1 : 0;
-          rb += c > cbv ? 1 : 0;
-        }
-    }
-    auto put = [&](unsigned long long c, int rank) {
-      if (rank < k) {
-        ids[(size_t)row * k + rank] = (int)~(unsigned)c;
-        if (vals) {
-          const unsigned kk = (unsigned)(c >> 32);
-          const unsigned u = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;   // inverse of fkey
-          vals[(size_t)row * k + rank] = __uint_as_float(u);
-        }
+  // Every top-k logit's key reaches T (at least k logits, the group maxima that
+  // made T, do), so only the candidates at or above T are ranked: ranks counted
+  // within that set are the exact ranks of its best k. With fewer groups than k
+  // every candidate is ranked. The set's order in LDS depends on the atomics;
+  // the ranks do not.
+  const unsigned Tf = kg < k ? 0u : T;
+  for (int e = t; e < nc; e += 256) {
+    const unsigned long long c = cb[e];
+    if ((unsigned)(c >> 32) >= Tf) cf[atomicAdd(&s_nf, 1)] = c;
+  }
+  __syncthreads();
+  const int nf = s_nf;
+  for (int e = t; e < nf; e += 256) {
+    const unsigned long long c = cf[e];
+    int rank = 0;
+    for (int j = 0; j < nf; ++j) rank += cf[j] > c ? 1 : 0;
+    if (rank < k) {
+      ids[(size_t)row * k + rank] = (int)~(unsigned)c;
+      if (vals) {
+        const unsigned kk = (unsigned)(c >> 32);
+        const unsigned u = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;   // inverse of fkey
+        vals[(size_t)row * k + rank] = __uint_as_float(u);
       }
-    };
-    put(ca, ra);
-    if (two) put(cbv, rb);
+    }
   }
 }
 

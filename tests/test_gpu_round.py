@@ -215,6 +215,43 @@ def test_topk_exact_ties_tiny(tiny_setup):
     np.testing.assert_array_equal(ids1.cpu().numpy()[0, :, 0], g_ids[:, 0])
 
 
+@pytest.mark.parametrize("V", [128, 200])
+def test_topk_vocab_below_k_groups_tiny(tiny_setup, V):
+    """A vocabulary of fewer 16-column groups than k (8 and 13 groups for k 16):
+    every candidate is ranked, so the top-16 is still the stable sort of the
+    GPU's own logits, in the caller's layout and in the transposed scratch."""
+    binding, cfg0, _, _ = tiny_setup
+    cfg = cfg0.replace(vocab=V, mask_id=V - 1)
+    print(f"case: tiny top-16 with vocab {V}", flush=True)
+    w = synth.make_weights(cfg, seed=4, device="cuda")
+    wh = Hn.host_weights(w)
+    dr = binding.Drafter(cfg, w)
+    P = 60
+    taps, taps_h = _taps_history(cfg, P, seed=6)
+    dr.reset(0, 0, P)
+    rows = torch.arange(0, P, dtype=torch.int32, device="cuda")
+    dr.tap_stage([t[:P] for t in taps], P, req_of_row=torch.zeros_like(rows), pos_of_row=rows)
+    tokens = synth.block_tokens(cfg, 1, seed=2, device="cuda")
+    logits = torch.empty((1, cfg.block - 1, V), dtype=torch.float32, device="cuda")
+    vals = torch.empty((1, cfg.block - 1, 16), dtype=torch.float32, device="cuda")
+    ids = dr.draft_block(tokens, k=16, logits=logits, vals=vals)
+    vals_t = torch.empty((1, cfg.block - 1, 16), dtype=torch.float32, device="cuda")
+    ids_t = dr.draft_block(tokens, k=16, vals=vals_t)   # no caller logits: the transposed scratch
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    g_logits = logits[0].cpu().numpy()
+    g_ids = ids.cpu().numpy()[0]
+    Hn.topk_self_consistent(g_logits, g_ids)
+    np.testing.assert_array_equal(vals[0].cpu().numpy(), np.take_along_axis(g_logits, g_ids, 1))
+    np.testing.assert_array_equal(ids_t.cpu().numpy()[0], g_ids)
+    np.testing.assert_array_equal(vals_t.cpu().numpy()[0], vals[0].cpu().numpy())
+    ref = D.draft_block(cfg, wh, taps_h, tokens[0].cpu().tolist(), P, 0, mode="mirror")
+    Hn.assert_close(g_logits, ref["logits"], "logits")
+    comp, excl = Hn.topk_agrees_away_from_ties(ref["logits"], g_ids, 16, gpu_logits=g_logits)
+    print(f"top-16 ranks compared {comp}, excluded as near-ties {excl}", flush=True)
+    assert comp > 0
+
+
 def test_empty_and_oversized_calls_refused_before_any_launch(tiny_setup):
     """Host validation on a bound handle: a staging call of 0 rows or of more rows
     than the workspace holds, a draft of 0 or too many requests, a block length of
