@@ -122,12 +122,20 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
   }
 }
 
-// (128 + u_e, 128 + u_e+1) for the nibble pairs of one packed word (see above)
-DEV u32x4 int4_biased_bf16(uint32_t w) {
+// (128 + u_e, 128 + u_e+1) for the nibble pairs of one packed word (see above).
+// mask = 0x000F000F and bias = 0x43004300 come in registers (int4_unpack_consts):
+// gfx950's three-operand v_and_or_b32 cannot encode two literals, so with the
+// constants folded in the compiler spends an AND and an OR per pair.
+DEV u32x4 int4_biased_bf16(uint32_t w, uint32_t mask, uint32_t bias) {
   u32x4 r;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) r[t] = ((w >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+  for (int t = 0; t < 4; ++t) r[t] = ((w >> (4 * t)) & mask) | bias;
   return r;
+}
+// the two constants of int4_biased_bf16 as register values the compiler cannot fold
+DEV void int4_unpack_consts(uint32_t& mask, uint32_t& bias) {
+  asm("v_mov_b32 %0, 0x000F000F" : "=v"(mask));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
 }
 
 DEV float half_bits_to_float(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
@@ -253,6 +261,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  uint32_t q4_mask = 0, q4_bias = 0;
+  if constexpr (Q4) int4_unpack_consts(q4_mask, q4_bias);
   auto compute = [&](int c, int j) {
     if constexpr (Q4) {
 #pragma unroll
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         for (int mt = 0; mt < MT; ++mt) t[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 2 * gi; s < 2 * gi + 2; ++s) {
-          const bf16x8 b = as_bf16x8(int4_biased_bf16(wbuf[j][0][s]));
+          const bf16x8 b = as_bf16x8(int4_biased_bf16(wbuf[j][0][s], q4_mask, q4_bias));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) t[mt] = mfma16x16x32(as_bf16x8(xfrag(mt, 128 * c + 32 * s)), b, t[mt]);
         }
