@@ -78,8 +78,8 @@ __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) 
   for (int j = 0; j < D; ++j) issue(j, j);
   uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(K));
   NormRowsLoads<XP> L;
-  norm_rows_issue<128 * NP, XP>(a, gains, L);
-  norm_rows_store<128 * NP, XP>(a, gains, xs, ldl, L);
+  norm_rows_issue<128 * NP, XP>(a, 0, K, gains, L);
+  norm_rows_store<128 * NP, XP>(a, K, gains, xs, ldl, L);
 
   // stream: chunk c's slot is read as 4 MFMA B fragments, then refilled with
   // chunk c + D; a split's chain is added to the running sum when it ends
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) 
 
 size_t gateup_lds_bytes(int M, int K) {
   // rows, whole chunks, a full ring, and one producer sum of squares per thread
-  if (M < 1 || M > 16 || K / 128 < GU_DEPTH || !norm_rows_fit(K, 128 * GU_PAIRS, GU_XP)) return 0;
+  if (M < 1 || M > 16 || K / 128 < GU_DEPTH || !norm_rows_fit(K, K, 128 * GU_PAIRS, GU_XP)) return 0;
   const size_t b = gu_x_bytes(K) + (size_t)2 * GU_PAIRS * GU_DEPTH * 4096;
   return b <= GU_LDS_MAX ? b : 0;
 }

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 // logits are the same bit for bit.
 constexpr int LM_LDS_MAX_GROUPS = 8;
 constexpr int LM_LDS_DEPTH = 2;   // W chunks in flight per wave (measured in the probe: 2 as fast as 3 or 4)
-constexpr int LM_LDS_XP = 12;     // staged X pieces per thread
+constexpr int LM_LDS_XP = 10;     // staged X pieces per thread
 
 template <int D>
 DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited for
@@ -268,15 +268,17 @@ DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D>
+template <int D, int KPH>
 __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_groups, float* logits,
                                                             int transposed, float* gmax, int w_off) {
+  constexpr int kph = KPH;
   constexpr int GC = 128;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int K = a.K, nchunks = K / 128, ldl = K + 8;
+  const int K = a.K, kw = K / kph, npc = kw / 128, ldl = kw + 8;
   uint16_t* xs = (uint16_t*)smem;
+  uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(kw));
   char* wring = smem + w_off + (size_t)wave * D * 4096;
   const uint16_t* W = (const uint16_t*)a.w;
   auto issue = [&](int gg, int c, int slot) {
@@ -287,46 +289,55 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(wring + slot * 4096 + s * 1024), 16, 0, 2);
     }
   };
-  // the first group's first D chunks, then the normed rows' loads; one wait
-  // covers all of them
   const int g0 = blockIdx.x;
-  if (g0 < n_groups) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) issue(g0, j, j);
-  }
-  uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(K));
-  NormRowsLoads<LM_LDS_XP> L;
-  norm_rows_issue<512, LM_LDS_XP>(a, gains, L);
-  norm_rows_store<512, LM_LDS_XP>(a, gains, xs, ldl, L);
   f32x4 park[LM_LDS_MAX_GROUPS];
-  int slot = 0;
 #pragma unroll
-  for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) {
-    const int g = g0 + gi * (int)gridDim.x;
-    if (g < n_groups) {
-      const int gn = g + (int)gridDim.x;
-      const bool last = gn >= n_groups;   // no refills past its end: its last D - 1 chunks wait for every load
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int c = 0; c < nchunks; ++c) {
-        if (last && c > nchunks - D) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
-        else wait_w_chunk<D>();
-        const char* sl = wring + slot * 4096;
-        u32x4 f[4];
+  for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) park[gi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // K in kph phases of kw columns: each phase stages its columns of the normed
+  // rows and streams every group's chunks of those columns; a group's chain of
+  // MFMAs runs over the chunks in order across the phases
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const int b = 4 * s2 + lg;
-          f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
+  for (int ph = 0; ph < kph; ++ph) {
+    const int cb = ph * npc;   // first chunk of the phase
+    // the first group's first D chunks of the phase, then the rows' loads; one
+    // wait covers all of them (the previous phase ended with every load landed,
+    // and the staging's first barrier follows every wave's last read of xs)
+    if (g0 < n_groups) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) issue(g0, cb + j, j);
+    }
+    NormRowsLoads<LM_LDS_XP> L;
+    norm_rows_issue<512, LM_LDS_XP>(a, ph * kw, kw, gains, L);
+    norm_rows_store<512, LM_LDS_XP>(a, kw, gains, xs, ldl, L);
+    int slot = 0;
+#pragma unroll
+    for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) {
+      const int g = g0 + gi * (int)gridDim.x;
+      if (g < n_groups) {
+        const int gn = g + (int)gridDim.x;
+        const bool last = gn >= n_groups;   // no refills past its end: its last D - 1 chunks wait for every load
+        f32x4 acc = park[gi];
+        for (int c = 0; c < npc; ++c) {
+          if (last && c > npc - D) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+          else wait_w_chunk<D>();
+          const char* sl = wring + slot * 4096;
+          u32x4 f[4];
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const int b = 4 * s2 + lg;
+            f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            acc = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + lr * ldl + 128 * c + 32 * s2 + 8 * lg)),
+                               as_bf16x8(f[s2]), acc);
+          const int nc = c + D;
+          if (nc < npc) issue(g, cb + nc, slot);
+          else if (!last) issue(gn, cb + nc - npc, slot);
+          slot = slot + 1 == D ? 0 : slot + 1;
         }
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2)
-          acc = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + lr * ldl + 128 * c + 32 * s2 + 8 * lg)), as_bf16x8(f[s2]),
-                             acc);
-        const int nc = c + D;
-        if (nc < nchunks) issue(g, nc, slot);
-        else if (!last) issue(gn, nc - nchunks, slot);
-        slot = slot + 1 == D ? 0 : slot + 1;
+        park[gi] = acc;
       }
-      park[gi] = acc;
     }
   }
 #pragma unroll
@@ -627,15 +638,21 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   const size_t xbytes = (size_t)rows * (K + 8) * 2;            // the whole normed rows
   const size_t wbytes = (size_t)2 * rows * (4 * 128 + 8) * 2;  // two windows of 4 chunks
   p.XL = xbytes <= LM_XL_MAX_BYTES ? 1 : (K % 512 == 0 && wbytes <= LM_XL_MAX_BYTES ? 2 : 0);
-  // one row tile, staged whole with its gains, with room for the W slots: W through LDS (XL 3)
-  const size_t xoff = norm_rows_bytes(K) + norm_gain_bytes(K);
-  if (p.MT == 1 && norm_rows_fit(K, 512, LM_LDS_XP) && K / 128 >= LM_LDS_DEPTH && per <= LM_LDS_MAX_GROUPS &&
-      xoff + (size_t)8 * LM_LDS_DEPTH * 4096 <= LM_XL_MAX_BYTES) {
-    p.XL = 3;
-    p.defer_off = (int)xoff;   // the W slots
-    p.slots = 0;
-    p.lds = xoff + (size_t)8 * LM_LDS_DEPTH * 4096;
-    return p;
+  // one row tile, staged with its gains in 1 or 2 phases of K, with room for
+  // the W slots: W through LDS (XL 3)
+  for (int kph = 1; kph <= 2 && p.MT == 1 && per <= LM_LDS_MAX_GROUPS; kph *= 2) {
+    if (K % kph) break;
+    const int kw = K / kph;
+    const size_t xoff = norm_rows_bytes(kw) + norm_gain_bytes(kw);
+    if (norm_rows_fit(K, kw, 512, LM_LDS_XP) && kw / 128 >= LM_LDS_DEPTH &&
+        xoff + (size_t)8 * LM_LDS_DEPTH * 4096 <= LM_XL_MAX_BYTES) {
+      p.XL = 3;
+      p.kph = kph;
+      p.defer_off = (int)xoff;   // the W slots
+      p.slots = 0;
+      p.lds = xoff + (size_t)8 * LM_LDS_DEPTH * 4096;
+      return p;
+    }
   }
   p.lds = p.XL == 1 ? xbytes : (p.XL == 2 ? wbytes : 0);
   // LDS left over holds the deferred accumulator fragments (8 waves x MT x 1 KB per group)
@@ -657,11 +674,18 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
                             hipStream_t st) {
   if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
   if (p.XL == 3) {
-    if (p.MT != 1 || !norm_rows_fit(a.K, 512, LM_LDS_XP) || a.K / 128 < LM_LDS_DEPTH || a.M > 16 ||
-        a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX || (long long)p.P * LM_LDS_MAX_GROUPS < p.groups)
+    if (p.MT != 1 || p.kph < 1 || a.K % p.kph || !norm_rows_fit(a.K, a.K / p.kph, 512, LM_LDS_XP) ||
+        a.K / p.kph / 128 < LM_LDS_DEPTH || a.M > 16 || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX ||
+        (long long)p.P * LM_LDS_MAX_GROUPS < p.groups)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
-                       transposed, gmax, p.defer_off);
+    if (p.kph == 1)
+      hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, 1>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
+                         transposed, gmax, p.defer_off);
+    else if (p.kph == 2)
+      hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, 2>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
+                         transposed, gmax, p.defer_off);
+    else
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   hipError_t e;
