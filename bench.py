@@ -26,7 +26,7 @@ COPY_BYTES = 512 << 20   # calibration copy read (and written) once before warm-
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the LM-head kernel at the default workload
 LM_PROFILE = os.path.join(ROOT, "profiles", "lm_logits_qwen3-4b_b16_ctx4k.md")
 LM_SOURCES = [os.path.join(ROOT, "block_diffusion_drafter_tap_amd", "csrc", f)
-              for f in ("lmhead.hip", "device.h", "kernels.h")]
+              for f in ("lmhead.hip", "norm_stage.h", "device.h", "kernels.h")]
 
 
 def lm_sources_sha256() -> str:
@@ -80,17 +80,29 @@ WORKLOADS = {
 
 
 def lm_kernel_label(hidden: int, vocab: int, rows: int) -> str:
-    """Name of the LM-head logits kernel the library launches for this shape: the
-    variant that streams the weights through LDS needs one 16-row tile of normed
-    rows staged whole beside its ring of 16 weight slots (8 waves x 2 chunks x
-    4 KB) within 159 KB of LDS, a hidden size in whole 128-column chunks, and at
-    most 8 column groups of 128 per workgroup."""
+    """Name of the LM-head logits kernel the library launches for this shape, as
+    its planner picks it on 256 compute units: up to 16 rows, the normed rows
+    staged in LDS in 1 or 2 phases of K beside a ring of 16 weight slots (8 waves
+    x 2 chunks x 4 KB); 17..64 rows, bf16 normed rows and weights both loaded
+    straight into LDS in phases of whole 128-column chunks; otherwise the
+    windowed kernel. Either LDS kernel takes at most 8 (16 rows) or 5 (more
+    rows) column groups of 128 per workgroup."""
     groups = (vocab + 127) // 128
-    x = (16 * (hidden + 8) * 2 + 15) & ~15
-    fits = (rows <= 16 and hidden % 128 == 0 and hidden // 128 >= 2 and x + 8 * 2 * 4096 <= 159 * 1024
-            and -(-groups // 256) <= 8)
-    if fits:
-        return "lm_logits_lds_kernel (shared LM head logits + 16-column maxima, weights streamed through LDS)"
+    per = -(-groups // 256)
+    nch = hidden // 128 if hidden % 128 == 0 else 0
+    if rows <= 16 and nch and per <= 8:
+        for kph in (1, 2):
+            kw = hidden // kph
+            if hidden % kph or kw % 128 or kw // 128 < 2 or kw // 8 > 10 * 32:
+                continue
+            lds = ((16 * (kw + 8) * 2 + 15) & ~15) + ((kw * 2 + 1023) & ~1023) + 8 * 2 * 4096 + 2048
+            if lds <= 160 * 1024:
+                return "lm_logits_lds_kernel (shared LM head logits + 16-column maxima, weights streamed through LDS)"
+    if 16 < rows <= 64 and nch and per <= 5:
+        npcs = (2,) if rows > 32 else (5, 4)
+        if any(nch % n == 0 for n in npcs):
+            return ("lm_logits_dma_kernel (shared LM head logits + 16-column maxima, normed rows and weights "
+                    "loaded straight into LDS)")
     return "lm_logits_kernel (shared LM head logits + 16-column maxima)"
 
 

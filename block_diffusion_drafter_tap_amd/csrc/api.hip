@@ -1011,9 +1011,10 @@ int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st,
     a.lm_first_row = first_row;
     a.topk = k;
     LmPlan p = plan_lmhead(M, B, g.vocab, H, ctx->n_cu);
-    if (p.XL == 0 || p.XL == 2) {
-      // more rows than LDS holds: the final RMSNorm once into bf16 rows, which
-      // the head streams through LDS windows (or reads from L2)
+    if (p.XL == 0 || p.XL == 2 || p.XL == 4) {
+      // more than one row tile: the final RMSNorm once into bf16 rows, which the
+      // head loads straight into LDS (or streams through LDS windows, or reads
+      // from L2)
       uint16_t* z = at<uint16_t>(ws, wl.z);
       e = launch_lm_norm_rows(a, z, st);
       if (e != hipSuccess) return hip_fail(e, "final norm");

@@ -34,7 +34,7 @@ namespace {
 constexpr int GU_PAIRS = 3;   // gate/up wave pairs per workgroup
 constexpr int GU_DEPTH = 2;   // ring slots per wave
 constexpr int GU_XP = 16;     // staged X pieces per thread
-constexpr size_t GU_LDS_MAX = 159 * 1024;
+constexpr size_t GU_LDS_TOTAL = 160 * 1024;   // a workgroup's LDS, dynamic and static
 
 template <int D>
 DEV void wait_chunk_ring() {   // vmcnt <= 4 (D - 1): the oldest chunk has landed
@@ -77,12 +77,13 @@ __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) 
 #pragma unroll
   for (int j = 0; j < D; ++j) issue(j, j);
   uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(K));
-  NormRowsLoads<XP> L;
+  NormRowsLoads<XP, norm_sqp<128 * NP, 16>()> L;
   norm_rows_issue<128 * NP, XP>(a, 0, K, gains, L);
   norm_rows_store<128 * NP, XP>(a, K, gains, xs, ldl, L);
 
-  // stream: chunk c's slot is read as 4 MFMA B fragments, then refilled with
-  // chunk c + D; a split's chain is added to the running sum when it ends
+  // stream: chunk c's slot is read as 4 MFMA B fragments and refilled with
+  // chunk c + D before they are used; a split's chain is added to the running
+  // sum when it ends
   f32x4 tot = {0.f, 0.f, 0.f, 0.f}, acc = {0.f, 0.f, 0.f, 0.f};
   int slot = 0;
   for (int c = 0; c < nchunks; ++c) {
@@ -95,12 +96,14 @@ __global__ __launch_bounds__(128 * NP) void gateup_lds_kernel(const GemmArgs a) 
       const int b = 4 * s2 + lg;
       f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
     }
+    // the slot's fragments are in registers: refill it before the MFMAs
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    if (c + D < nchunks) issue(c + D, slot);
+    slot = slot + 1 == D ? 0 : slot + 1;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
       acc = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + lr * ldl + 128 * c + 32 * s2 + 8 * lg)), as_bf16x8(f[s2]),
                          acc);
-    if (c + D < nchunks) issue(c + D, slot);
-    slot = slot + 1 == D ? 0 : slot + 1;
     if ((c + 1) % split_chunks == 0 || c + 1 == nchunks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) tot[i] = tot[i] + acc[i];
@@ -137,7 +140,7 @@ size_t gateup_lds_bytes(int M, int K) {
   // rows, whole chunks, a full ring, and one producer sum of squares per thread
   if (M < 1 || M > 16 || K / 128 < GU_DEPTH || !norm_rows_fit(K, K, 128 * GU_PAIRS, GU_XP)) return 0;
   const size_t b = gu_x_bytes(K) + (size_t)2 * GU_PAIRS * GU_DEPTH * 4096;
-  return b <= GU_LDS_MAX ? b : 0;
+  return b + norm_sq_bytes(128 * GU_PAIRS, 16) <= GU_LDS_TOTAL ? b : 0;
 }
 
 hipError_t launch_gateup_lds(const GemmArgs& a, int ks, hipStream_t st) {

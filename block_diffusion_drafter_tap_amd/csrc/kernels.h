@@ -109,7 +109,7 @@ struct LmPlan {
   int slots, defer_off;    // groups per workgroup whose epilogue waits for the last load; their LDS
                            // offset (XL 3: the offset of the W slots)
   size_t lds;
-  int kph = 1;             // XL 3: phases of K, each staging K / kph columns of the rows
+  int kph = 1;             // XL 3: phases of K, each staging K / kph columns of the 16 MT rows
 };
 LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu);
 // the final-normed rows as bf16 z[M][K] (for plans with XL = 0), from the same

@@ -24,6 +24,7 @@ namespace {
 // stage the normed rows in LDS up to this size (one persistent workgroup per
 // CU, so nearly all of the 160 KB of a gfx950 CU)
 constexpr size_t LM_XL_MAX_BYTES = 159 * 1024;
+constexpr size_t LM_LDS_TOTAL = 160 * 1024;   // a workgroup's LDS, dynamic and static
 
 // The final-normed rows as bf16 for the path that does not stage them in LDS,
 // with the staging's arithmetic (sums of squares added in column-group order,
@@ -239,7 +240,9 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
   }
 }
 
-// W through LDS (16 rows, the normed rows staged whole): every weight load is a
+// W through LDS (one tile of 16 rows, the normed rows staged in LDS whole or a
+// phase of K columns at a time; the code takes MT tiles, but more rows go to
+// lm_logits_dma_kernel, whose rows need no register staging): every weight load is a
 // direct-to-LDS, nontemporal 16-byte load, and one load instruction covers 4
 // whole W rows x 256 bytes, so the 128-byte lines of the stream are each read
 // by one instruction. (The MFMA operand pattern, 16 rows x 64 bytes per
@@ -254,11 +257,13 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 // the wait for a slot is an explicit vmcnt: the only vector memory operations
 // in the streaming loop are these loads (4 per chunk), with D chunks in flight
 // (after the last group's last refill, a wait is for every load).
-// Each wave's accumulators of its (at most LM_LDS_MAX_GROUPS) groups stay in
+// Each wave's accumulators of its (at most lm_lds_max_groups) groups stay in
 // registers until the last load is out, so no store interleaves with the
 // stream. The MFMA inputs and their order equal lm_logits_kernel's, so the
 // logits are the same bit for bit.
 constexpr int LM_LDS_MAX_GROUPS = 8;
+// groups per workgroup the LDS kernel parks in registers: fewer with more row tiles
+constexpr int lm_lds_max_groups(int MT) { return MT == 1 ? LM_LDS_MAX_GROUPS : 5; }
 constexpr int LM_LDS_DEPTH = 2;   // W chunks in flight per wave (measured in the probe: 2 as fast as 3 or 4)
 constexpr int LM_LDS_XP = 10;     // staged X pieces per thread
 
@@ -268,17 +273,16 @@ DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int KPH>
+template <int D, int KPH, int MT>
 __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_groups, float* logits,
                                                             int transposed, float* gmax, int w_off) {
-  constexpr int kph = KPH;
-  constexpr int GC = 128;
+  constexpr int GC = 128, ROWS = 16 * MT, kph = KPH, MAXG = lm_lds_max_groups(MT);
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = a.K, kw = K / kph, npc = kw / 128, ldl = kw + 8;
   uint16_t* xs = (uint16_t*)smem;
-  uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(kw));
+  uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(kw, ROWS));
   char* wring = smem + w_off + (size_t)wave * D * 4096;
   const uint16_t* W = (const uint16_t*)a.w;
   auto issue = [&](int gg, int c, int slot) {
@@ -290,12 +294,15 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
     }
   };
   const int g0 = blockIdx.x;
-  f32x4 park[LM_LDS_MAX_GROUPS];
+  f32x4 park[MAXG][MT];
 #pragma unroll
-  for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) park[gi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < MAXG; ++gi)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) park[gi][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // K in kph phases of kw columns: each phase stages its columns of the normed
   // rows and streams every group's chunks of those columns; a group's chain of
-  // MFMAs runs over the chunks in order across the phases
+  // MFMAs runs over the chunks in order across the phases, and a row's chain does
+  // not depend on the other row tiles, so its logits are the same bits for any MT
 #pragma unroll
   for (int ph = 0; ph < kph; ++ph) {
     const int cb = ph * npc;   // first chunk of the phase
@@ -306,17 +313,19 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
 #pragma unroll
       for (int j = 0; j < D; ++j) issue(g0, cb + j, j);
     }
-    NormRowsLoads<LM_LDS_XP> L;
-    norm_rows_issue<512, LM_LDS_XP>(a, ph * kw, kw, gains, L);
-    norm_rows_store<512, LM_LDS_XP>(a, kw, gains, xs, ldl, L);
+    NormRowsLoads<LM_LDS_XP, norm_sqp<512, ROWS>()> L;
+    norm_rows_issue<512, LM_LDS_XP, ROWS>(a, ph * kw, kw, gains, L);
+    norm_rows_store<512, LM_LDS_XP, ROWS>(a, kw, gains, xs, ldl, L);
     int slot = 0;
 #pragma unroll
-    for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) {
+    for (int gi = 0; gi < MAXG; ++gi) {
       const int g = g0 + gi * (int)gridDim.x;
       if (g < n_groups) {
         const int gn = g + (int)gridDim.x;
         const bool last = gn >= n_groups;   // no refills past its end: its last D - 1 chunks wait for every load
-        f32x4 acc = park[gi];
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = park[gi][mt];
         for (int c = 0; c < npc; ++c) {
           if (last && c > npc - D) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
           else wait_w_chunk<D>();
@@ -327,26 +336,153 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
             const int b = 4 * s2 + lg;
             f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
           }
-#pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2)
-            acc = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + lr * ldl + 128 * c + 32 * s2 + 8 * lg)),
-                               as_bf16x8(f[s2]), acc);
+          // the slot's fragments are in registers: refill it before the MFMAs, so
+          // a slot turns over in one load latency, not that plus the chunk's math
+          __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
           const int nc = c + D;
           if (nc < npc) issue(g, cb + nc, slot);
           else if (!last) issue(gn, cb + nc - npc, slot);
           slot = slot + 1 == D ? 0 : slot + 1;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt] = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + (mt * 16 + lr) * ldl + 128 * c + 32 * s2 + 8 * lg)),
+                                     as_bf16x8(f[s2]), acc[mt]);
         }
-        park[gi] = acc;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) park[gi][mt] = acc[mt];
       }
     }
   }
 #pragma unroll
-  for (int gi = 0; gi < LM_LDS_MAX_GROUPS; ++gi) {
+  for (int gi = 0; gi < MAXG; ++gi) {
     const int g = g0 + gi * (int)gridDim.x;
-    if (g < n_groups) {
-      const f32x4 ac[1] = {park[gi]};
-      lm_epilogue<1>(a, g, ac, logits, transposed, gmax);
+    if (g < n_groups) lm_epilogue<MT>(a, g, park[gi], logits, transposed, gmax);
+  }
+}
+
+template <int n>
+DEV void wait_vm() {   // vmcnt <= n (n < 64); expcnt and lgkmcnt not waited for
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// A workgroup barrier without the fence of __syncthreads, whose release waits
+// for every direct-to-LDS load in flight (here: the W ring's next chunks). The
+// caller has waited for the loads whose LDS data the other waves read after it,
+// and its own LDS reads before it have completed (their values were used). The
+// memory clobber keeps the compiler from moving memory accesses across it.
+DEV void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// W through LDS as above, for 17..64 rows (MT = 2 or 4 row tiles). The rows are
+// the final-normed bf16 rows z (written beforehand by lm_norm_rows_kernel, whose
+// bits equal the staging's), and go from L2 straight into LDS as well, in MFMA
+// operand order: K is taken in phases of NPC chunks, and a phase's rows are 4 MT
+// NPC fragments of 1 KB, fragment (c * 4 + s2) * MT + mt holding rows mt * 16 +
+// (0..15) x columns 32 s2 + (0..31) of chunk c with lane L's 16 bytes at 16 L
+// (row L % 16, columns 8 (L / 16) + (0..7)), so an A-operand read is one linear
+// 1 KB read per wave. Two phase buffers: the next phase's rows are loaded while
+// this phase streams, and each wave's W ring runs on across the phase
+// boundaries, where the workgroup only meets at a barrier. Every wave's
+// sequence of W chunks runs over (phase, group, chunk); the rows of phase p + 1
+// are issued at the first chunk of phase p, just before that chunk's refill,
+// so the wait of the next chunk allows for them. A row's chain of MFMAs runs
+// over the chunks in order, with the same inputs as the 16-row kernels, so its
+// logits are the same bits for any number of rows.
+template <int MT, int NPC>
+__global__ __launch_bounds__(512) void lm_logits_dma_kernel(const GemmArgs a, int n_groups, float* logits,
+                                                            int transposed, float* gmax) {
+  constexpr int D = 2, GC = 128, NF = 4 * MT * NPC, NXW = NF / 8, MAXG = lm_lds_max_groups(MT);
+  static_assert(NF % 8 == 0 && NPC >= D, "whole fragments per wave; a group spans at least D chunks per phase");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = a.K, nph = K / (128 * NPC);
+  char* wring = smem + 2 * NF * 1024 + (size_t)wave * D * 4096;
+  const uint16_t* W = (const uint16_t*)a.w;
+  auto issue_w = [&](int gg, int c, int slot) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int row = 4 * s + lg, kb = (lane - row) & 15;
+      const uint16_t* src = W + (size_t)min(gg * GC + wave * 16 + row, a.N - 1) * K + c * 128 + kb * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(wring + slot * 4096 + s * 1024), 16, 0, 2);
     }
+  };
+  auto issue_x = [&](int ph, int b) {   // this wave's NXW fragments of phase ph into buffer b
+#pragma unroll
+    for (int j = 0; j < NXW; ++j) {
+      const int f = wave * NXW + j;
+      const int mt = f % MT, s2 = (f / MT) % 4, cl = f / (4 * MT);
+      const uint16_t* src = a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + 128 * (ph * NPC + cl) + 32 * s2 + 8 * lg;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(smem + ((size_t)b * NF + f) * 1024), 16, 0, 0);
+    }
+  };
+  const int g0 = blockIdx.x, P = gridDim.x;
+  f32x4 park[MAXG][MT];
+#pragma unroll
+  for (int gi = 0; gi < MAXG; ++gi)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) park[gi][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // phase 0's rows, then the first D chunks; the rows land first
+  issue_x(0, 0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue_w(g0, j, j);
+  wait_vm<4 * D>();
+  barrier_no_fence();
+  int slot = 0;
+  for (int ph = 0; ph < nph; ++ph) {
+    const bool more = ph + 1 < nph;
+    const char* xb = smem + (size_t)(ph & 1) * NF * 1024;
+#pragma unroll
+    for (int gi = 0; gi < MAXG; ++gi) {
+      const int g = g0 + gi * P;
+      if (g < n_groups) {
+        const bool gnext = g + P < n_groups;
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = park[gi][mt];
+#pragma unroll
+        for (int c = 0; c < NPC; ++c) {
+          // this chunk's loads were followed by the next chunk's (if any) and,
+          // at the second chunk of a phase, by the next phase's rows
+          if (!more && !gnext && c == NPC - 1) wait_vm<0>();
+          else if (more && gi == 0 && c == 1) wait_vm<4 + NXW>();
+          else wait_vm<4>();
+          const char* sl = wring + slot * 4096;
+          u32x4 f[4];
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const int b = 4 * s2 + lg;
+            f[s2] = *(const u32x4*)(sl + ((lr >> 2) * 64 + (lr & 3) * 16 + ((b + lr) & 15)) * 16);
+          }
+          __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): the slot is free
+          if (more && gi == 0 && c == 0) issue_x(ph + 1, (ph + 1) & 1);
+          // the chunk D steps on: this group's, the next group's, or the next phase's first group's
+          if (c + D < NPC) issue_w(g, ph * NPC + c + D, slot);
+          else if (gnext) issue_w(g + P, ph * NPC + c + D - NPC, slot);
+          else if (more) issue_w(g0, (ph + 1) * NPC + c + D - NPC, slot);
+          slot ^= 1;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt] = mfma16x16x32(as_bf16x8(*(const u32x4*)(xb + (((c * 4 + s2) * MT + mt) * 64 + lane) * 16)),
+                                     as_bf16x8(f[s2]), acc[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) park[gi][mt] = acc[mt];
+      }
+    }
+    if (more) {
+      // the next phase's rows were followed by at least one refill (4 loads):
+      // they have landed; after the barrier no wave reads this phase's buffer
+      wait_vm<4>();
+      barrier_no_fence();
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < MAXG; ++gi) {
+    const int g = g0 + gi * P;
+    if (g < n_groups) lm_epilogue<MT>(a, g, park[gi], logits, transposed, gmax);
   }
 }
 
@@ -638,14 +774,28 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   const size_t xbytes = (size_t)rows * (K + 8) * 2;            // the whole normed rows
   const size_t wbytes = (size_t)2 * rows * (4 * 128 + 8) * 2;  // two windows of 4 chunks
   p.XL = xbytes <= LM_XL_MAX_BYTES ? 1 : (K % 512 == 0 && wbytes <= LM_XL_MAX_BYTES ? 2 : 0);
-  // one row tile, staged with its gains in 1 or 2 phases of K, with room for
-  // the W slots: W through LDS (XL 3)
-  for (int kph = 1; kph <= 2 && p.MT == 1 && per <= LM_LDS_MAX_GROUPS; kph *= 2) {
+  // 17..64 rows: normed bf16 rows and W both straight into LDS (XL 4), in phases
+  // of npc chunks (the largest that divides K / 128, at most 48 KB of rows each)
+  if (p.MT > 1 && K % 128 == 0 && per <= lm_lds_max_groups(p.MT)) {
+    const int nch = K / 128;
+    for (int npc = p.MT == 4 ? 2 : 5; npc >= (p.MT == 4 ? 2 : 4); --npc)
+      if (nch % npc == 0) {
+        p.XL = 4;
+        p.kph = nch / npc;
+        p.slots = 0;
+        p.defer_off = 0;
+        p.lds = (size_t)2 * 4 * p.MT * npc * 1024 + (size_t)8 * LM_LDS_DEPTH * 4096;
+        return p;
+      }
+  }
+  // one row tile staged with its gains in 1 or 2 phases of K, with room for the
+  // W slots: W through LDS (XL 3)
+  for (int kph = 1; p.MT == 1 && kph <= 2 && per <= lm_lds_max_groups(1); kph *= 2) {
     if (K % kph) break;
     const int kw = K / kph;
-    const size_t xoff = norm_rows_bytes(kw) + norm_gain_bytes(kw);
-    if (norm_rows_fit(K, kw, 512, LM_LDS_XP) && kw / 128 >= LM_LDS_DEPTH &&
-        xoff + (size_t)8 * LM_LDS_DEPTH * 4096 <= LM_XL_MAX_BYTES) {
+    const size_t xoff = norm_rows_bytes(kw, rows) + norm_gain_bytes(kw);
+    if (norm_rows_fit(K, kw, 512, LM_LDS_XP, rows) && kw / 128 >= LM_LDS_DEPTH &&
+        xoff + (size_t)8 * LM_LDS_DEPTH * 4096 + norm_sq_bytes(512, rows) <= LM_LDS_TOTAL) {
       p.XL = 3;
       p.kph = kph;
       p.defer_off = (int)xoff;   // the W slots
@@ -674,18 +824,33 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
                             hipStream_t st) {
   if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
   if (p.XL == 3) {
-    if (p.MT != 1 || p.kph < 1 || a.K % p.kph || !norm_rows_fit(a.K, a.K / p.kph, 512, LM_LDS_XP) ||
-        a.K / p.kph / 128 < LM_LDS_DEPTH || a.M > 16 || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX ||
-        (long long)p.P * LM_LDS_MAX_GROUPS < p.groups)
+    const int rows = 16 * p.MT;
+    if (p.kph < 1 || a.K % p.kph || !norm_rows_fit(a.K, a.K / p.kph, 512, LM_LDS_XP, rows) ||
+        a.K / p.kph / 128 < LM_LDS_DEPTH || a.M > rows || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX ||
+        (long long)p.P * lm_lds_max_groups(p.MT) < p.groups)
       return hipErrorInvalidValue;
-    if (p.kph == 1)
-      hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, 1>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
-                         transposed, gmax, p.defer_off);
-    else if (p.kph == 2)
-      hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, 2>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits,
-                         transposed, gmax, p.defer_off);
-    else
+#define LMLDS(KPH)                                                                                            \
+  hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, KPH, 1>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, \
+                     logits, transposed, gmax, p.defer_off)
+    if (p.MT == 1 && p.kph == 1) LMLDS(1);
+    else if (p.MT == 1 && p.kph == 2) LMLDS(2);
+    else return hipErrorInvalidValue;
+#undef LMLDS
+    return hipGetLastError();
+  }
+  if (p.XL == 4) {
+    const int nch = a.K / 128, npc = p.kph > 0 ? nch / p.kph : 0;
+    if (a.K % 128 || p.kph < 1 || nch % p.kph || a.M > 16 * p.MT || a.M < 1 || !a.x || a.ldx < a.K ||
+        (long long)p.P * lm_lds_max_groups(p.MT) < p.groups)
       return hipErrorInvalidValue;
+#define LMDMA(MT, NPC)                                                                                          \
+  hipLaunchKernelGGL((lm_logits_dma_kernel<MT, NPC>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, logits, \
+                     transposed, gmax)
+    if (p.MT == 4 && npc == 2) LMDMA(4, 2);
+    else if (p.MT == 2 && npc == 4) LMDMA(2, 4);
+    else if (p.MT == 2 && npc == 5) LMDMA(2, 5);
+    else return hipErrorInvalidValue;
+#undef LMDMA
     return hipGetLastError();
   }
   hipError_t e;

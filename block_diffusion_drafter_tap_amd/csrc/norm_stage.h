@@ -1,16 +1,15 @@
-// Staging of up to 16 RMS-normed rows, or columns [k0, k0 + kw) of them, in LDS
-// (bf16 [16][kw + 8]) by a workgroup of NT threads, for kernels that also stream
+// Staging of ROWS (16, 32 or 64) RMS-normed rows, or columns [k0, k0 + kw) of
+// them, in LDS (bf16 [ROWS][kw + 8]) by a workgroup of NT threads, for kernels that also stream
 // weights straight into LDS: the RMSNorm of the layer input before the gate/up
 // projection and the final norm before the LM head (x = h * rsqrt(ss / K + eps) * gain, ss the sum
 // over the producer's 128-column groups of h^2, added in group order).
 //
 // Two calls around the kernel's own weight prologue:
 //   norm_rows_issue  the gains of the columns (straight to LDS), then for this
-//                    thread's row (NT / 16 threads per row) one of the
-//                    producer's sums of squares (the whole row's, one group per
-//                    thread of the row) and this thread's X pieces (8 fp32
-//                    values each, pieces t % TPR + TPR u of the columns) into
-//                    registers;
+//                    thread's row (NT / ROWS threads per row) its share of the
+//                    producer's sums of squares (the whole row's) and its X
+//                    pieces (8 fp32 values each, pieces t % TPR + TPR u of the
+//                    columns) into registers;
 //   norm_rows_store  one wait covers every load issued so far; the row's sums
 //                    pass through LDS, each thread adds its row's in group order
 //                    to form 1/rms and stores its pieces, reading the gains of
@@ -29,25 +28,36 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int NORM_SSQ_MAX = 32;   // producer column groups per row: K / 128 <= 32
 
-// LDS bytes of kw staged columns of the 16 rows, then of their gains (whole KB)
-__host__ __device__ inline size_t norm_rows_bytes(int kw) { return ((size_t)16 * (kw + 8) * 2 + 15) & ~(size_t)15; }
+// LDS bytes of kw staged columns of `rows` rows, then of their gains (whole KB)
+__host__ __device__ inline size_t norm_rows_bytes(int kw, int rows = 16) {
+  return ((size_t)rows * (kw + 8) * 2 + 15) & ~(size_t)15;
+}
 __host__ __device__ inline size_t norm_gain_bytes(int kw) { return ((size_t)kw * 2 + 1023) & ~(size_t)1023; }
-// whether NT threads with XP pieces each cover kw columns of rows of K (and the
-// row's sums of squares, one per thread of the row, fit)
-__host__ __device__ inline bool norm_rows_fit(int K, int kw, int NT, int XP) {
-  return K % 128 == 0 && kw % 128 == 0 && kw <= K && K / 128 <= NORM_SSQ_MAX && K / 128 <= NT / 16 &&
-         kw / 8 <= XP * (NT / 16);
+// whether NT threads with XP pieces each cover kw columns of `rows` rows of K
+__host__ __device__ inline bool norm_rows_fit(int K, int kw, int NT, int XP, int rows = 16) {
+  return K % 128 == 0 && kw % 128 == 0 && kw <= K && K / 128 <= NORM_SSQ_MAX && kw / 8 <= XP * (NT / rows);
 }
 
-template <int XP>
+// static LDS of norm_rows_store: each row's sums of squares as its threads loaded them
+__host__ __device__ inline size_t norm_sq_bytes(int NT, int rows) {
+  const int tpr = NT / rows, sqp = (NORM_SSQ_MAX + tpr - 1) / tpr;
+  return (size_t)rows * tpr * sqp * 4;
+}
+
+// per thread: SQP of the row's sums of squares (groups t % TPR + TPR j) and XP
+// pieces of its columns
+template <int XP, int SQP>
 struct NormRowsLoads {
-  float sq;   // group t % (NT / 16) of the row's sums of squares
+  float sq[SQP];
   f32x4 h0[XP], h1[XP];
 };
+template <int NT, int ROWS>
+constexpr int norm_sqp() { return (NORM_SSQ_MAX + NT / ROWS - 1) / (NT / ROWS); }
 
-template <int NT, int XP>
-DEV void norm_rows_issue(const GemmArgs& a, int k0, int kw, uint16_t* gains, NormRowsLoads<XP>& L) {
-  constexpr int TPR = NT / 16;
+template <int NT, int XP, int ROWS = 16>
+DEV void norm_rows_issue(const GemmArgs& a, int k0, int kw, uint16_t* gains,
+                         NormRowsLoads<XP, norm_sqp<NT, ROWS>()>& L) {
+  constexpr int TPR = NT / ROWS, SQP = norm_sqp<NT, ROWS>();
   const int per_row = kw / 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = threadIdx.x / TPR, pc0 = threadIdx.x % TPR;
@@ -55,7 +65,8 @@ DEV void norm_rows_issue(const GemmArgs& a, int k0, int kw, uint16_t* gains, Nor
   for (int i = wave; i < (int)(norm_gain_bytes(kw) / 1024); i += NT / 64)   // 1 KB of gains per instruction
     __builtin_amdgcn_global_load_lds((const void*)(a.xgain + k0 + min(512 * i + 8 * lane, kw - 8)),
                                      (lds_void*)(gains + 512 * i), 16, 0, 0);
-  L.sq = a.ssq_in[(size_t)min(pc0, a.n_ssq - 1) * a.ssq_ld + m];
+#pragma unroll
+  for (int j = 0; j < SQP; ++j) L.sq[j] = a.ssq_in[(size_t)min(pc0 + TPR * j, a.n_ssq - 1) * a.ssq_ld + m];
   const float* hrow = a.xf + (size_t)m * a.ldx + k0;
 #pragma unroll
   for (int u = 0; u < XP; ++u) {
@@ -67,15 +78,17 @@ DEV void norm_rows_issue(const GemmArgs& a, int k0, int kw, uint16_t* gains, Nor
   }
 }
 
-template <int NT, int XP>
-DEV void norm_rows_store(const GemmArgs& a, int kw, const uint16_t* gains, uint16_t* xs, int ldl, NormRowsLoads<XP>& L) {
+template <int NT, int XP, int ROWS = 16>
+DEV void norm_rows_store(const GemmArgs& a, int kw, const uint16_t* gains, uint16_t* xs, int ldl,
+                         NormRowsLoads<XP, norm_sqp<NT, ROWS>()>& L) {
   static_assert(XP % 2 == 0, "gains are read for half the pieces at a time");
-  constexpr int TPR = NT / 16, GB = XP / 2;
+  constexpr int TPR = NT / ROWS, GB = XP / 2, SQP = norm_sqp<NT, ROWS>();
   __builtin_amdgcn_sched_barrier(0);
   const int K = a.K, per_row = kw / 8;
   const int row = threadIdx.x / TPR, pc0 = threadIdx.x % TPR;
-  __shared__ float s_sq[16][TPR];
-  s_sq[row][pc0] = L.sq;
+  __shared__ float s_sq[ROWS][TPR * SQP];
+#pragma unroll
+  for (int j = 0; j < SQP; ++j) s_sq[row][pc0 + TPR * j] = L.sq[j];
   __syncthreads();   // the gains and the sums of squares are in LDS
   float ss = 0.f;
   for (int b = 0; b < a.n_ssq; ++b) ss += s_sq[row][b];
