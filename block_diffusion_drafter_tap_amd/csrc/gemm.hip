@@ -236,10 +236,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     // bf16 values per 64-group (8 lanes hold the 8 pieces of one group: the
     // per-row count klen/8 is a multiple of 16, so groups never straddle rows
     // and all 8 lanes of a group are active together)
+    // Only the rows below M are loaded (an 8-row block would otherwise read its
+    // X twice); the tile's padding rows are zeros. The loop bound is a multiple
+    // of 16 pieces, so the 8 lanes of a group are active together.
     const int per_row = klen / 8;
-    for (int e = threadIdx.x; e < ROWS * per_row; e += blockDim.x) {
+    const int rows_x = min(ROWS, a.M - m0);
+    for (int e = threadIdx.x; e < (ROWS - rows_x) * per_row; e += blockDim.x) {
+      const int r = rows_x + e / per_row, c = e % per_row;
+      if (XL) *(u32x4*)(xs + r * ldl + 8 * c) = (u32x4){0u, 0u, 0u, 0u};
+      if (Q4 && (c & 7) == 0) xsum[(c >> 3) * ROWS + r] = 0.f;
+    }
+    for (int e = threadIdx.x; e < rows_x * per_row; e += blockDim.x) {
       const int r = e / per_row, c = e % per_row;
-      const u32x4 v = load_x<XK>(a, min(m0 + r, a.M - 1), kbeg + 8 * c, row_inv(r));
+      const u32x4 v = load_x<XK>(a, m0 + r, kbeg + 8 * c, row_inv(r));
       if (XL) *(u32x4*)(xs + r * ldl + 8 * c) = v;
       if constexpr (Q4) {
         float t = 0.f;

@@ -67,13 +67,18 @@ DEV void norm_rows_issue(const GemmArgs& a, int k0, int kw, uint16_t* gains,
                                      (lds_void*)(gains + 512 * i), 16, 0, 0);
 #pragma unroll
   for (int j = 0; j < SQP; ++j) L.sq[j] = a.ssq_in[(size_t)min(pc0 + TPR * j, a.n_ssq - 1) * a.ssq_ld + m];
+  // rows at or past M are the tile's padding: zeros, not a second copy of a row
   const float* hrow = a.xf + (size_t)m * a.ldx + k0;
+  const bool real = row < a.M;
 #pragma unroll
   for (int u = 0; u < XP; ++u) {
     const int pc = pc0 + TPR * u;
-    if (pc < per_row) {
+    if (pc < per_row && real) {
       L.h0[u] = *(const f32x4*)(hrow + 8 * pc);
       L.h1[u] = *(const f32x4*)(hrow + 8 * pc + 4);
+    } else {
+      L.h0[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      L.h1[u] = L.h0[u];
     }
   }
 }
