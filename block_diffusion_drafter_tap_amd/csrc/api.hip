@@ -963,6 +963,8 @@ int forward_block(dflash_ctx* ctx, char* ws, const WsLayout& wl, hipStream_t st,
       Timed tm(ctx, DFLASH_K_GATEUP, st);
       if (wf == WF_BF16 && gateup_lds_bytes(M, H)) {
         e = launch_gateup_lds(a, p.ks, st);   // same sums as the split plan p, one launch
+      } else if (wf == WF_INT4 && gateup_q4_bytes(M, H)) {
+        e = launch_gateup_q4(a, p.ks, st);
       } else if (p.S > 1) {
         e = launch_gemm(a, p, X_NORM, E_PARTP, wf, st);
         if (e == hipSuccess) e = launch_finish_silu(a.partials, p.S, M, g.ffn, act, g.ffn, st);

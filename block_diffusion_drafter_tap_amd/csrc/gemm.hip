@@ -122,23 +122,6 @@ DEV void epi_head(const GemmArgs& a, float (*tile)[GC + 1], int m0, int rows, in
   }
 }
 
-// (128 + u_e, 128 + u_e+1) for the nibble pairs of one packed word (see above).
-// mask = 0x000F000F and bias = 0x43004300 come in registers (int4_unpack_consts):
-// gfx950's three-operand v_and_or_b32 cannot encode two literals, so with the
-// constants folded in the compiler spends an AND and an OR per pair.
-DEV u32x4 int4_biased_bf16(uint32_t w, uint32_t mask, uint32_t bias) {
-  u32x4 r;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) r[t] = ((w >> (4 * t)) & mask) | bias;
-  return r;
-}
-// the two constants of int4_biased_bf16 as register values the compiler cannot fold
-DEV void int4_unpack_consts(uint32_t& mask, uint32_t& bias) {
-  asm("v_mov_b32 %0, 0x000F000F" : "=v"(mask));
-  asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
-}
-
-DEV float half_bits_to_float(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
 
 // Per-row sums over 64-wide K groups of the bf16 X values, [klen/64][ROWS] floats
 // after the X slice (or at the start of LDS when X is not staged).

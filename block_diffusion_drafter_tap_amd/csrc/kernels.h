@@ -94,6 +94,10 @@ size_t gemm_partial_floats(const GemmPlan& p, int M, int N, int pair);
 // gateup_lds_bytes: dynamic LDS of a launch, 0 when the shape does not fit.
 size_t gateup_lds_bytes(int M, int K);
 hipError_t launch_gateup_lds(const GemmArgs& a, int ks, hipStream_t st);
+// The same with INT4 weights (packed [2N][K/2] + fp16 scales [2N][K/64] in
+// wscale), matching the INT4 split-K GEMM and its finish bit for bit.
+size_t gateup_q4_bytes(int M, int K);
+hipError_t launch_gateup_q4(const GemmArgs& a, int ks, hipStream_t st);
 
 // LM head: persistent logits GEMM over the block rows (GemmArgs X_NORM fields
 // xf, xgain, ssq_*, w = W_lm, M = R*B, N = vocab, K, B, topk; when the plan does

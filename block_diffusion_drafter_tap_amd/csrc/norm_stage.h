@@ -83,11 +83,17 @@ DEV void norm_rows_issue(const GemmArgs& a, int k0, int kw, uint16_t* gains,
   }
 }
 
-template <int NT, int XP, int ROWS = 16>
+// With XSUM, also each row's sums over the 64-column groups of the staged bf16
+// values, xsum[g][ROWS] (the INT4 weights' correction term): each 8-value piece
+// summed in order, then the 8 pieces of a group in a butterfly over the 8
+// consecutive lanes that hold them (TPR is a multiple of 8, so a group never
+// straddles rows or lane groups).
+template <int NT, int XP, int ROWS = 16, bool XSUM = false>
 DEV void norm_rows_store(const GemmArgs& a, int kw, const uint16_t* gains, uint16_t* xs, int ldl,
-                         NormRowsLoads<XP, norm_sqp<NT, ROWS>()>& L) {
+                         NormRowsLoads<XP, norm_sqp<NT, ROWS>()>& L, float* xsum = nullptr) {
   static_assert(XP % 2 == 0, "gains are read for half the pieces at a time");
   constexpr int TPR = NT / ROWS, GB = XP / 2, SQP = norm_sqp<NT, ROWS>();
+  static_assert(!XSUM || TPR % 8 == 0, "a group's 8 pieces in 8 lanes of one row");
   __builtin_amdgcn_sched_barrier(0);
   const int K = a.K, per_row = kw / 8;
   const int row = threadIdx.x / TPR, pc0 = threadIdx.x % TPR;
@@ -106,7 +112,17 @@ DEV void norm_rows_store(const GemmArgs& a, int kw, const uint16_t* gains, uint1
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
       const int pc = pc0 + TPR * (u0 + j);
-      if (pc < per_row) *(u32x4*)(xs + row * ldl + 8 * pc) = norm8(L.h0[u0 + j], L.h1[u0 + j], g[j], inv);
+      const u32x4 v = norm8(L.h0[u0 + j], L.h1[u0 + j], g[j], inv);
+      if (pc < per_row) *(u32x4*)(xs + row * ldl + 8 * pc) = v;
+      if constexpr (XSUM) {   // every lane takes part; per_row is a multiple of 8
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t += __uint_as_float(v[i] << 16) + __uint_as_float(v[i] & 0xffff0000u);
+        t += __shfl_xor(t, 1, 64);
+        t += __shfl_xor(t, 2, 64);
+        t += __shfl_xor(t, 4, 64);
+        if (pc < per_row && (pc & 7) == 0) xsum[(pc >> 3) * ROWS + row] = t;
+      }
     }
   }
   __syncthreads();

@@ -131,3 +131,40 @@ def test_int4_qwen3_8b_prefill_and_rounds():
     torch.cuda.synchronize()
     assert dr6.check() == 0
     _check(cfg6, wq, hist, tok6[0].cpu().tolist(), pos, pos - W, logits6[0], ids6[0], "8b int4 block 6")
+
+
+def test_int4_batch_invariance_qwen3_8b():
+    """Qwen3-8B-shaped INT4 drafter, block 8: two requests drafted in one call
+    (16 rows: the split-K INT4 gate/up and its SiLU finish) equal each request
+    drafted alone (8 rows: the one-launch INT4 gate/up), logits and top-16 bit
+    for bit. The single-request path is the one the oracle test above covers."""
+    binding = _gpu()
+    W = 256
+    cfg = config.qwen3_8b_int4(block=8, window=W, max_requests=2, max_stage_rows=2 * W)
+    print("case: qwen3-8b-shaped INT4 B=8 W=256, 2 requests batched vs alone", flush=True)
+    w = synth.make_weights(cfg, seed=0, device="cuda")
+    R, B, V = 2, cfg.block, cfg.vocab
+    starts = [W + 29 * r for r in range(R)]
+    hist = [synth.make_taps(cfg, W, seed=11, device="cuda", stream=r) for r in range(R)]
+    tokens = synth.block_tokens(cfg, R, seed=12, device="cuda")
+
+    def run(dr, reqs):
+        # one stage call per request, so that both runs use the same GEMM plans
+        for i, r in enumerate(reqs):
+            dr.reset(i, starts[r] - W, starts[r])
+            ps = torch.arange(starts[r] - W, starts[r], dtype=torch.int32, device="cuda")
+            dr.tap_stage([hist[r][t] for t in range(cfg.n_taps)], W, req_of_row=torch.full_like(ps, i),
+                         pos_of_row=ps)
+        lg = torch.empty((len(reqs), B - 1, V), dtype=torch.float32, device="cuda")
+        ids = dr.draft_block(tokens[reqs].contiguous(), k=16, logits=lg)
+        torch.cuda.synchronize()
+        assert dr.check() == 0
+        return lg.cpu().numpy(), ids.cpu().numpy()
+
+    batched = run(binding.Drafter(cfg, w), [0, 1])
+    one = cfg.replace(max_requests=1)
+    for r in range(R):
+        single = run(binding.Drafter(one, w), [r])
+        np.testing.assert_array_equal(batched[0][r:r + 1], single[0], err_msg=f"request {r} logits")
+        np.testing.assert_array_equal(batched[1][r:r + 1], single[1], err_msg=f"request {r} top-16")
+    print("batched == alone for both requests", flush=True)
