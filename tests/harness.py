@@ -46,6 +46,33 @@ def topk_self_consistent(gpu_logits: np.ndarray, gpu_ids: np.ndarray):
         np.testing.assert_array_equal(ids[r], ref, err_msg=f"row {r}")
 
 
+def topk_valid_within_error(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k: int, gpu_logits: np.ndarray):
+    """Every rank of every GPU top-k list checked against the oracle, ties or not.
+
+    With eps_row = max |gpu - oracle| over the row, an exact top-k of the GPU
+    logits satisfies, for any rounding within eps_row: its ids are distinct and
+    in range; each id's oracle logit is at least the oracle's k-th largest value
+    minus 2 eps_row (the GPU's k-th largest is at least the oracle's minus eps_row);
+    and consecutive ranks keep their oracle order up to 2 eps_row. A wrong or
+    misplaced id fails one of these unless it lies within the error band. Returns
+    the number of ranks checked."""
+    L = np.asarray(oracle_logits, dtype=np.float64).reshape(-1, np.shape(oracle_logits)[-1])
+    G = np.asarray(gpu_logits, dtype=np.float64).reshape(L.shape)
+    ids = np.asarray(gpu_ids).reshape(-1, k)
+    n = 0
+    for r in range(L.shape[0]):
+        sel = ids[r].astype(np.int64)
+        assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < L.shape[1], f"row {r}: ids {sel}"
+        band = 2.0 * float(np.max(np.abs(G[r] - L[r]))) + 1e-9 * (1.0 + float(np.max(np.abs(L[r]))))
+        kth = np.partition(L[r], L.shape[1] - k)[L.shape[1] - k]
+        v = L[r][sel]
+        assert v.min() >= kth - band, f"row {r}: id {sel[np.argmin(v)]} oracle {v.min()} < k-th {kth} - {band}"
+        for j in range(k - 1):
+            assert v[j] >= v[j + 1] - band, f"row {r} ranks {j},{j + 1}: oracle {v[j]} < {v[j + 1]} - {band}"
+        n += k
+    return n
+
+
 def topk_agrees_away_from_ties(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k: int,
                                gpu_logits: np.ndarray = None):
     """Compare GPU ids with the oracle's at the ranks the numerics decide.
@@ -55,9 +82,12 @@ def topk_agrees_away_from_ties(oracle_logits: np.ndarray, gpu_ids: np.ndarray, k
     measured max |gpu - oracle| logit error of that row: if every GPU logit is
     within eps_row of the oracle's, two values more than 2 * eps_row apart keep
     their order, so a mismatch there is a selection bug, not rounding. Returns
-    (compared, excluded) counts."""
+    (compared, excluded) counts. Given the GPU logits, every rank is also checked
+    by topk_valid_within_error."""
     L = oracle_logits.reshape(-1, oracle_logits.shape[-1])
     G = None if gpu_logits is None else np.asarray(gpu_logits, dtype=np.float64).reshape(L.shape)
+    if G is not None:
+        topk_valid_within_error(L, gpu_ids, k, G)
     ids = gpu_ids.reshape(-1, k)
     compared = excluded = 0
     for r in range(L.shape[0]):
