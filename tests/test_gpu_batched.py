@@ -181,15 +181,18 @@ def test_ctx_norm_tiny():
     Hn.topk_self_consistent(logits[0].cpu().numpy(), ids[0].cpu().numpy())
 
 
-def test_batch_invariance_qwen3_hc():
+@pytest.mark.parametrize("W", [512, 1536])
+def test_batch_invariance_qwen3_hc(W):
     """qwen3-4b-shaped drafter with 4 hc streams, block 8, 8 requests with their
-    own 512-row contexts: a batched round, the stage of the verify rows and the
+    own W-row contexts: a batched round, the stage of the verify rows and the
     accept, then a second batched round, all equal to the same requests run
-    alone (bit for bit). Request 0's first round also matches the oracle."""
+    alone (bit for bit). Request 0's first round also matches the oracle. At
+    W = 1536 the batched attention has 448 (chunk, kv head) workgroups against
+    112 per request alone (query slots split in two), and the combine sums 7
+    chunk partials."""
     binding = _binding()
-    W = 512
     cfg = config.qwen3_4b_hc(block=8, window=W, max_requests=8, max_stage_rows=W * 8)
-    print("case: qwen3-4b hc=4 block 8, 8 requests, window 512", flush=True)
+    print(f"case: qwen3-4b hc=4 block 8, 8 requests, window {W}", flush=True)
     w = synth.make_weights(cfg, seed=0, device="cuda")
     R, B = 8, cfg.block
     starts = [W + 37 * r for r in range(R)]   # the oracle indexes taps by absolute position
