@@ -21,8 +21,9 @@
 //  2. wave w owns head_dim tile w: it accumulates O^T = V^T P^T over all the
 //     chunk's sub-tiles (MFMA, head_dim x queries) and writes its rows of the
 //     chunk partial straight from the accumulators.
-// All K/V loads of a wave are issued before its first MFMA, so a chunk's 128 KB
-// is in flight at once, and no wave holds more than one head_dim tile of O.
+// A wave's K loads are issued first and its V loads once its scores are formed
+// (K lands sooner without V competing for HBM; V streams in during the
+// softmax), and no wave holds more than one head_dim tile of O.
 // The ring keeps V transposed ([hd][C]) so that both MFMA operands are 16-byte
 // loads. Keys of the two 16-row S^T tiles are permuted so that after the first
 // MFMA each lane group already holds the 8 consecutive keys the second MFMA
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
   const uint16_t* rk = a.ring_k + (size_t)lrg * a.C * HD;
   const uint16_t* rv = a.ring_v + (size_t)lrg * HD * a.C;
 
-  // issue every K/V load of this wave first
+  // this wave's K loads first
   const int k0 = kb + 32 * wave;
   const bool live = k0 < kr.hi;
   u32x4 kf[2][QS];
@@ -106,17 +107,6 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
     const uint16_t* kp = rk + (size_t)(key % a.C) * HD + 8 * lg;
 #pragma unroll
     for (int s = 0; s < QS; ++s) kf[kt][s] = live ? ld16(kp + 32 * s) : (u32x4){0u, 0u, 0u, 0u};
-  }
-  u32x4 vf[ATT_WAVES][HTW];
-#pragma unroll
-  for (int sb = 0; sb < ATT_WAVES; ++sb) {
-    const int ks = kb + 32 * sb;
-    const int vslot = (ks + 8 * lg) % a.C;
-#pragma unroll
-    for (int tt = 0; tt < HTW; ++tt) {
-      const int t = wave * HTW + tt;
-      vf[sb][tt] = ks < kr.hi ? ld16(rv + (size_t)(16 * t + lr) * a.C + vslot) : (u32x4){0u, 0u, 0u, 0u};
-    }
   }
 
   // Q of this workgroup's query slots (slot = h_local * B + i); zero rows pad the last tile
@@ -170,6 +160,20 @@ __global__ __launch_bounds__(64 * NWA) void attn_kernel(const AttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lg == 0) s_mx[wave][qt * 16 + lr] = mx;
+  }
+  // V only now, once this wave's K has landed: every workgroup issues its K and V
+  // at the same moment, so K alone lands sooner and V streams in during the
+  // softmax
+  u32x4 vf[ATT_WAVES][HTW];
+#pragma unroll
+  for (int sb = 0; sb < ATT_WAVES; ++sb) {
+    const int ks = kb + 32 * sb;
+    const int vslot = (ks + 8 * lg) % a.C;
+#pragma unroll
+    for (int tt = 0; tt < HTW; ++tt) {
+      const int t = wave * HTW + tt;
+      vf[sb][tt] = ks < kr.hi ? ld16(rv + (size_t)(16 * t + lr) * a.C + vslot) : (u32x4){0u, 0u, 0u, 0u};
+    }
   }
   __syncthreads();
 #pragma unroll
