@@ -82,7 +82,8 @@ WORKLOADS = {
 def lm_kernel_label(hidden: int, vocab: int, rows: int) -> str:
     """Name of the LM-head logits kernel the library launches for this shape, as
     its planner picks it on 256 compute units: up to 16 rows, the normed rows
-    staged in LDS in 1 or 2 phases of K beside a ring of 16 weight slots (8 waves
+    (8 of them when there are at most 8) staged in LDS in 1 or 2 phases of K
+    beside a ring of 16 weight slots (8 waves
     x 2 chunks x 4 KB); 17..64 rows, bf16 normed rows and weights both loaded
     straight into LDS in phases of whole 128-column chunks; otherwise the
     windowed kernel. Either LDS kernel takes at most 8 (16 rows) or 5 (more
@@ -91,11 +92,12 @@ def lm_kernel_label(hidden: int, vocab: int, rows: int) -> str:
     per = -(-groups // 256)
     nch = hidden // 128 if hidden % 128 == 0 else 0
     if rows <= 16 and nch and per <= 8:
+        rx = 8 if rows <= 8 else 16   # rows staged
         for kph in (1, 2):
             kw = hidden // kph
-            if hidden % kph or kw % 128 or kw // 128 < 2 or kw // 8 > 10 * 32:
+            if hidden % kph or kw % 128 or kw // 128 < 2 or kw // 8 > 10 * (512 // rx):
                 continue
-            lds = ((16 * (kw + 8) * 2 + 15) & ~15) + ((kw * 2 + 1023) & ~1023) + 8 * 2 * 4096 + 2048
+            lds = ((rx * (kw + 8) * 2 + 15) & ~15) + ((kw * 2 + 1023) & ~1023) + 8 * 2 * 4096 + 2048
             if lds <= 160 * 1024:
                 return "lm_logits_lds_kernel (shared LM head logits + 16-column maxima, weights streamed through LDS)"
     if 16 < rows <= 64 and nch and per <= 5:

@@ -113,7 +113,8 @@ struct LmPlan {
   int slots, defer_off;    // groups per workgroup whose epilogue waits for the last load; their LDS
                            // offset (XL 3: the offset of the W slots)
   size_t lds;
-  int kph = 1;             // XL 3: phases of K, each staging K / kph columns of the 16 MT rows
+  int kph = 1;             // XL 3/4: phases of K (XL 3: each stages K / kph columns of the rows)
+  int rx = 16;             // XL 3: rows staged (8 when the call has at most 8)
 };
 LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu);
 // the final-normed rows as bf16 z[M][K] (for plans with XL = 0), from the same

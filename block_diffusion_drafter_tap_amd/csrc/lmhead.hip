@@ -240,9 +240,10 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
   }
 }
 
-// W through LDS (one tile of 16 rows, the normed rows staged in LDS whole or a
-// phase of K columns at a time; the code takes MT tiles, but more rows go to
-// lm_logits_dma_kernel, whose rows need no register staging): every weight load is a
+// W through LDS (one tile of up to 16 rows, the normed rows staged in LDS whole
+// or a phase of K columns at a time; 8 staged rows when the call has at most 8,
+// so that a wider hidden size still fits in one phase; more than 16 rows go to
+// lm_logits_dma_kernel): every weight load is a
 // direct-to-LDS, nontemporal 16-byte load, and one load instruction covers 4
 // whole W rows x 256 bytes, so the 128-byte lines of the stream are each read
 // by one instruction. (The MFMA operand pattern, 16 rows x 64 bytes per
@@ -273,10 +274,13 @@ DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int KPH, int MT>
+template <int D, int KPH, int RX>
 __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_groups, float* logits,
                                                             int transposed, float* gmax, int w_off) {
-  constexpr int GC = 128, ROWS = 16 * MT, kph = KPH, MAXG = lm_lds_max_groups(MT);
+  // one 16-row tile, of which RX rows (8 or 16) are staged: with 8, the A
+  // operand's rows 8..15 repeat rows 0..7 and their logits are never read
+  constexpr int MT = 1, GC = 128, ROWS = RX, kph = KPH, MAXG = lm_lds_max_groups(MT);
+  static_assert(RX == 8 || RX == 16, "8 or 16 staged rows");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
           for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              acc[mt] = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + (mt * 16 + lr) * ldl + 128 * c + 32 * s2 + 8 * lg)),
+              acc[mt] = mfma16x16x32(as_bf16x8(*(const u32x4*)(xs + (lr & (RX - 1)) * ldl + 128 * c + 32 * s2 + 8 * lg)),
                                      as_bf16x8(f[s2]), acc[mt]);
         }
 #pragma unroll
@@ -788,15 +792,17 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
         return p;
       }
   }
-  // one row tile staged with its gains in 1 or 2 phases of K, with room for the
-  // W slots: W through LDS (XL 3)
+  // one row tile (8 of its rows staged when the call has at most 8) with its
+  // gains in 1 or 2 phases of K, with room for the W slots: W through LDS (XL 3)
+  const int rx = M <= 8 ? 8 : 16;
   for (int kph = 1; p.MT == 1 && kph <= 2 && per <= lm_lds_max_groups(1); kph *= 2) {
     if (K % kph) break;
     const int kw = K / kph;
-    const size_t xoff = norm_rows_bytes(kw, rows) + norm_gain_bytes(kw);
-    if (norm_rows_fit(K, kw, 512, LM_LDS_XP, rows) && kw / 128 >= LM_LDS_DEPTH &&
-        xoff + (size_t)8 * LM_LDS_DEPTH * 4096 + norm_sq_bytes(512, rows) <= LM_LDS_TOTAL) {
+    const size_t xoff = norm_rows_bytes(kw, rx) + norm_gain_bytes(kw);
+    if (norm_rows_fit(K, kw, 512, LM_LDS_XP, rx) && kw / 128 >= LM_LDS_DEPTH &&
+        xoff + (size_t)8 * LM_LDS_DEPTH * 4096 + norm_sq_bytes(512, rx) <= LM_LDS_TOTAL) {
       p.XL = 3;
+      p.rx = rx;
       p.kph = kph;
       p.defer_off = (int)xoff;   // the W slots
       p.slots = 0;
@@ -824,16 +830,17 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
                             hipStream_t st) {
   if (a.lm_first_row < 0 || a.lm_first_row > 1 || a.B < a.lm_first_row + 1) return hipErrorInvalidValue;
   if (p.XL == 3) {
-    const int rows = 16 * p.MT;
-    if (p.kph < 1 || a.K % p.kph || !norm_rows_fit(a.K, a.K / p.kph, 512, LM_LDS_XP, rows) ||
-        a.K / p.kph / 128 < LM_LDS_DEPTH || a.M > rows || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX ||
-        (long long)p.P * lm_lds_max_groups(p.MT) < p.groups)
+    if (p.MT != 1 || (p.rx != 8 && p.rx != 16) || p.kph < 1 || a.K % p.kph ||
+        !norm_rows_fit(a.K, a.K / p.kph, 512, LM_LDS_XP, p.rx) || a.K / p.kph / 128 < LM_LDS_DEPTH ||
+        a.M > p.rx || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX || (long long)p.P * lm_lds_max_groups(1) < p.groups)
       return hipErrorInvalidValue;
-#define LMLDS(KPH)                                                                                            \
-  hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, KPH, 1>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, \
+#define LMLDS(KPH, RX)                                                                                          \
+  hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, KPH, RX>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, \
                      logits, transposed, gmax, p.defer_off)
-    if (p.MT == 1 && p.kph == 1) LMLDS(1);
-    else if (p.MT == 1 && p.kph == 2) LMLDS(2);
+    if (p.kph == 1 && p.rx == 16) LMLDS(1, 16);
+    else if (p.kph == 2 && p.rx == 16) LMLDS(2, 16);
+    else if (p.kph == 1 && p.rx == 8) LMLDS(1, 8);
+    else if (p.kph == 2 && p.rx == 8) LMLDS(2, 8);
     else return hipErrorInvalidValue;
 #undef LMLDS
     return hipGetLastError();
