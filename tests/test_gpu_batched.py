@@ -181,20 +181,23 @@ def test_ctx_norm_tiny():
     Hn.topk_self_consistent(logits[0].cpu().numpy(), ids[0].cpu().numpy())
 
 
-@pytest.mark.parametrize("W", [512, 1536])
-def test_batch_invariance_qwen3_hc(W):
-    """qwen3-4b-shaped drafter with 4 hc streams, block 8, 8 requests with their
+@pytest.mark.parametrize("W,R", [(512, 8), (1536, 8), (512, 3), (512, 5)])
+def test_batch_invariance_qwen3_hc(W, R):
+    """qwen3-4b-shaped drafter with 4 hc streams, block 8, R requests with their
     own W-row contexts: a batched round, the stage of the verify rows and the
     accept, then a second batched round, all equal to the same requests run
-    alone (bit for bit). Request 0's first round also matches the oracle. At
-    W = 1536 the batched attention has 448 (chunk, kv head) workgroups against
-    112 per request alone (query slots split in two), and the combine sums 7
-    chunk partials."""
+    alone (bit for bit). Request 0's first round also matches the oracle.
+    The batched LM head takes 64 rows (R = 8: four row tiles), 24 (R = 3: two
+    tiles, K in phases of 5 chunks) or 40 rows (R = 5: four tiles, the last
+    partly padding); each request alone takes the 8-row kernel. At W = 1536 the
+    batched attention has 448 (chunk, kv head) workgroups against 112 per
+    request alone (query slots split in two), and the combine sums 7 chunk
+    partials."""
     binding = _binding()
-    cfg = config.qwen3_4b_hc(block=8, window=W, max_requests=8, max_stage_rows=W * 8)
-    print(f"case: qwen3-4b hc=4 block 8, 8 requests, window {W}", flush=True)
+    cfg = config.qwen3_4b_hc(block=8, window=W, max_requests=R, max_stage_rows=W * R)
+    print(f"case: qwen3-4b hc=4 block 8, {R} requests, window {W}", flush=True)
     w = synth.make_weights(cfg, seed=0, device="cuda")
-    R, B = 8, cfg.block
+    B = cfg.block
     starts = [W + 37 * r for r in range(R)]   # the oracle indexes taps by absolute position
     hist = [synth.make_taps(cfg, W + 3 * B, seed=9, device="cuda", stream=r, outliers=False) for r in range(R)]
     tokens = synth.block_tokens(cfg, R, seed=10, device="cuda")
@@ -227,7 +230,7 @@ def test_batch_invariance_qwen3_hc(W):
 
     batched = run(binding.Drafter(cfg, w), list(range(R)))
     one = cfg.replace(max_requests=1)
-    for r in (0, 3, 7):
+    for r in sorted({0, R // 2, R - 1}):
         single = run(binding.Drafter(one, w), [r])
         for a, b, what in zip(batched, single, ("logits 1", "ids 1", "logits 2", "ids 2", "n_emit")):
             np.testing.assert_array_equal(a[r:r + 1], b, err_msg=f"request {r} {what}")
