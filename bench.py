@@ -419,7 +419,10 @@ def main():
 
     # prefill: each request stages the trailing W rows of a 16384-row tap buffer;
     # request 0's staging is timed (HIP events on the launch stream) after a warm-up
-    # staging of the same rows
+    # staging of the same rows. A spin kernel of about 2 ms runs before the first
+    # event, so the host has enqueued the whole staging by the time the GPU gets
+    # to it: the events bracket the device's time, not the host's submission
+    # latency from an idle GPU (about 0.23 ms of Python, binding and launches)
     total_rows = 16384
     start = [total_rows + 37 * r for r in range(R)]
     hist = []
@@ -434,6 +437,7 @@ def main():
         for rep in range(2 if r == 0 else 1):
             if r == 0 and rep == 1:
                 torch.cuda.synchronize()
+                torch.cuda._sleep(4_000_000)
                 pre_ev[0].record()
             dr.tap_stage([t[total_rows - W:] for t in taps], W, req_of_row=req, pos_of_row=rows)
             if r == 0 and rep == 1:

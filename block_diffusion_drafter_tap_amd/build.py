@@ -22,10 +22,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
 SOURCES = ["api.hip", "gemm.hip", "gateup.hip", "finish.hip", "lmhead.hip", "attention.hip", "small.hip",
-           "prefill.hip", "tree.hip", "sampling.hip"]
+           "prefill.hip", "tree.hip", "sampling.hip", "blaslt.hip"]
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# hipBLASLt (the staging stage's plain fc product), found at run time next to the HIP runtime
+ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+LINK_FLAGS = ["-lhipblaslt", "-Wl,-rpath," + ROCM_LIB]
 
 
 def hipcc() -> str:
@@ -55,7 +58,7 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK_FLAGS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
@@ -108,7 +111,7 @@ def build_host_sanitized(verbose: bool = False) -> str:
     objs = [obj] + [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.hip"]
     lib = os.path.join(out_dir, "libdflash.so")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-shared-libsan", *HOST_SANITIZE,
-           *objs, "-o", lib]
+           *objs, *LINK_FLAGS, "-o", lib]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link of the sanitized library failed:\n{r.stderr}")

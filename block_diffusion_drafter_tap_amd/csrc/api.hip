@@ -315,7 +315,10 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     if (e == hipSuccess) {
       TileArgs ta{xg, TW, ctx->fc, n_rows, H, TW,
                   g.ctx_norm ? (void*)at<float>(ctx->ws, ctx->wl.c32) : (void*)c_bf, H, ctx->fc_s};
-      e = launch_gemm_tile(ta, tile_bn(n_rows, H, ctx->n_cu), !g.ctx_norm, st);
+      // bf16 weights: a plain product, through hipBLASLt when it has a kernel for the shape
+      e = ctx->fc_s ? hipErrorNotSupported
+                    : blaslt_gemm_nt(xg, TW, (const uint16_t*)ctx->fc, n_rows, H, TW, ta.out, H, g.ctx_norm, st);
+      if (e == hipErrorNotSupported) e = launch_gemm_tile(ta, tile_bn(n_rows, H, ctx->n_cu), !g.ctx_norm, st);
     }
   }
   if (e != hipSuccess) return hip_fail(e, "prefill fc");
