@@ -459,6 +459,10 @@ int dflash_bind(dflash_ctx* ctx, void* state, void* workspace, void* stream) {
   hipError_t e = launch_fill_zero(state, ctx->sl.total, st);
   if (e == hipSuccess) e = launch_fill_zero(workspace, ctx->wl.total, st);
   if (e != hipSuccess) return hip_fail(e, "bind fill");
+  // staging calls that take the prefill path run a bf16 fc through hipBLASLt:
+  // its handle for this device is created here, not in a stream call (without
+  // one, staging runs the tile kernel)
+  if (!ctx->target && ctx->cfg.wfmt == DFLASH_W_BF16 && prefill_enabled(ctx->cfg)) blaslt_prepare();
   return DFLASH_OK;
 }
 

@@ -7,11 +7,12 @@
 //
 // In hipBLASLt's column-major terms Y^T (N x M, ld ldo) = op(A) op(B) with A the
 // weights as a K x N matrix (ld K, transposed) and B the rows as a K x M matrix
-// (ld ldx). One handle per device (created on first use), and the descriptors,
-// layouts and the heuristic's first algorithm are kept per shape. No workspace
-// is offered, so the algorithms chosen need none and allocate nothing. When the
-// library offers no algorithm for a shape, or cannot start, the call returns
-// hipErrorNotSupported and the caller runs its own kernel instead.
+// (ld ldx). One handle per device, created by blaslt_prepare (from the handle
+// binding call, never from a stream call), and the descriptors, layouts and the
+// heuristic's first algorithm are kept per shape. No workspace is offered, so the
+// algorithms chosen need none. When there is no handle for the device, or the
+// library offers no algorithm for a shape, the call returns hipErrorNotSupported
+// and the caller runs its own kernel instead.
 #include <hipblaslt/hipblaslt.h>
 
 #include <mutex>
@@ -76,20 +77,27 @@ void plan(LtPlan& p, hipblasLtHandle_t h) {
 
 }  // namespace
 
+hipError_t blaslt_prepare() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= LT_MAX_DEV) return hipErrorNotSupported;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_handle[dev]) return hipSuccess;
+  if (g_handle_failed[dev]) return hipErrorNotSupported;
+  if (hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
+    g_handle[dev] = nullptr;
+    g_handle_failed[dev] = true;
+    return hipErrorNotSupported;
+  }
+  return hipSuccess;
+}
+
 hipError_t blaslt_gemm_nt(const uint16_t* x, long long ldx, const uint16_t* w, int M, int N, int K, void* out,
                           long long ldo, int out_f32, hipStream_t st) {
   if (!x || !w || !out || M < 1 || N < 1 || K < 1 || ldx < K || ldo < N) return hipErrorInvalidValue;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= LT_MAX_DEV) return hipErrorNotSupported;
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_handle[dev]) {
-    if (g_handle_failed[dev]) return hipErrorNotSupported;
-    if (hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
-      g_handle[dev] = nullptr;
-      g_handle_failed[dev] = true;
-      return hipErrorNotSupported;
-    }
-  }
+  if (!g_handle[dev]) return hipErrorNotSupported;
   LtPlan* p = nullptr;
   for (auto& q : g_plans)
     if (q.used && q.dev == dev && q.M == M && q.N == N && q.K == K && q.ldx == ldx && q.ldo == ldo &&

@@ -184,8 +184,10 @@ hipError_t launch_tap_gather(const TapGather& g, int M, hipStream_t st);
 int tile_bn(int M, int N, int n_cu);   // 0: N fits neither tile
 hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t st);
 // Y[M][N] = X[M][K] . W[N][K]^T through hipBLASLt (bf16 in, fp32 accumulation,
-// bf16 or fp32 out); hipErrorNotSupported when the library offers no algorithm
-// that needs no workspace (the caller then runs launch_gemm_tile).
+// bf16 or fp32 out); hipErrorNotSupported when the current device has no handle
+// (blaslt_prepare creates it: once per process and device) or the library offers
+// no algorithm that needs no workspace (the caller then runs launch_gemm_tile).
+hipError_t blaslt_prepare();
 hipError_t blaslt_gemm_nt(const uint16_t* x, long long ldx, const uint16_t* w, int M, int N, int K, void* out,
                           long long ldo, int out_f32, hipStream_t st);
 // Context K/V projection (N = 2 * nkv * hd, 128-column tiles of whole heads)
