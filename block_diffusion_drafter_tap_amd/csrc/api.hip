@@ -340,7 +340,7 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     b.req_of_row = req_of_row;
     b.pos_of_row = pos_of_row;
     b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
-    e = launch_gemm_tile_heads(ta, b, st);
+    e = launch_gemm_tile_heads(ta, b, ctx->n_cu, st);
     if (e != hipSuccess) return hip_fail(e, "prefill kv");
   }
   return DFLASH_OK;

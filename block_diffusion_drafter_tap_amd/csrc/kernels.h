@@ -192,7 +192,9 @@ hipError_t blaslt_gemm_nt(const uint16_t* x, long long ldx, const uint16_t* w, i
                           long long ldo, int out_f32, hipStream_t st);
 // Context K/V projection (N = 2 * nkv * hd, 128-column tiles of whole heads)
 // straight into the rings: GemmArgs head fields as for the head finish.
-hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStream_t st);
+// (n_cu: the device's compute units, which decide the row tile: 256 rows when
+// every CU gets at least one such tile, else 128)
+hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, int n_cu, hipStream_t st);
 
 // Verify pass of a causal target: copy the residual rows h [M][H] of a tapped
 // layer to a tap buffer with row pitch ld; add n_emit to the positions.

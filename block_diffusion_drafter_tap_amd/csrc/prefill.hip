@@ -49,24 +49,31 @@ enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_HEADS = 2 };
 // staging also leaves each row's sum of the stage's bf16 values. The stage's
 // MFMAs accumulate t = sum x * (u + 128) from zero and the stage adds
 // s * (t - 136 * sum x) = s * sum x * q.
-template <int BN, int OUT, int Q4>
-__global__ __launch_bounds__(256, Q4 ? 1 : 2)   // INT4 holds per-group accumulators too: one workgroup per CU
+// BM rows x BN columns per workgroup of BM / 32 waves (a 2-column grid of 64-row
+// x BN/2-column wave tiles). 128-row tiles run two workgroups per CU; a 256-row
+// tile (bf16 only) takes a CU alone and loads a quarter fewer operand bytes per
+// flop, which is what bounds these tiles (operand reads from L2 at the CU's
+// load rate). Every output's MFMA chain over the K stages is the same for both.
+template <int BM, int BN, int OUT, int Q4>
+__global__ __launch_bounds__(BM * 2, Q4 || BM > 128 ? 1 : 2)   // INT4 holds per-group accumulators too
 void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
+  constexpr int NTH = BM * 2, NWV = NTH / 64, RB = BM / 64;
+  static_assert(!Q4 || BM == 128, "INT4 tiles are 128 rows");
   constexpr int WN = BN / 2;        // columns per wave
   constexpr int NJ = WN / 16;       // 16-column MFMA tiles per wave
-  constexpr int XP = PF_BM * PF_BK / 8 / 256;   // 16-byte X pieces per thread per stage
-  constexpr int WP = Q4 ? 1 : BN * PF_BK / 8 / 256;   // W pieces (bf16)
+  constexpr int XP = BM * PF_BK / 8 / NTH;   // 16-byte X pieces per thread per stage
+  constexpr int WP = Q4 ? 1 : BN * PF_BK / 8 / NTH;   // W pieces (bf16)
   constexpr int TPR = 256 / BN;     // INT4: threads per W row, each with 4 / TPR of its word pairs
   constexpr int JPT = 4 / TPR;
-  constexpr int XS_BYTES = 2 * PF_BM * PF_LDK * 2, WS_BYTES = 2 * BN * PF_LDK * 2;
-  constexpr int TILE_BYTES = OUT == OUT_HEADS ? PF_BM * (BN + 1) * 4 : 0;
+  constexpr int XS_BYTES = 2 * BM * PF_LDK * 2, WS_BYTES = 2 * BN * PF_LDK * 2;
+  constexpr int TILE_BYTES = OUT == OUT_HEADS ? BM * (BN + 1) * 4 : 0;
   constexpr int SMEM = XS_BYTES + WS_BYTES > TILE_BYTES ? XS_BYTES + WS_BYTES : TILE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  auto xs = (uint16_t(*)[PF_BM][PF_LDK])smem;
+  auto xs = (uint16_t(*)[BM][PF_LDK])smem;
   auto ws = (uint16_t(*)[BN][PF_LDK])(smem + XS_BYTES);
   __shared__ float s_xsum[Q4 ? 2 : 1][Q4 ? PF_BM : 1], s_sc[Q4 ? 2 : 1][Q4 ? BN : 1];
 
-  const int mt = (a.M + PF_BM - 1) / PF_BM, nt = a.N / BN, tiles = mt * nt;
+  const int mt = (a.M + BM - 1) / BM, nt = a.N / BN, tiles = mt * nt;
   const int per_xcd = (tiles + 7) / 8;
   const int seq = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (seq >= tiles) return;
@@ -76,7 +83,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
   const int grp = seq / (PF_GM * nt), first = grp * PF_GM;
   const int gm = min(PF_GM, mt - first);
   const int r = seq - grp * PF_GM * nt;
-  const int m0 = (first + r % gm) * PF_BM, n0 = (r / gm) * BN;
+  const int m0 = (first + r % gm) * BM, n0 = (r / gm) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -93,7 +100,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
     const int k0 = s * PF_BK;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int p = tid + i * 256, row = p / 8, seg = p % 8;
+      const int p = tid + i * NTH, row = p / 8, seg = p % 8;
       xr[q][i] = ld16(a.x + (size_t)min(m0 + row, a.M - 1) * a.ldx + k0 + 8 * seg);
     }
     if constexpr (Q4) {
@@ -106,7 +113,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
     } else {
 #pragma unroll
       for (int i = 0; i < WP; ++i) {
-        const int p = tid + i * 256, row = p / 8, seg = p % 8;
+        const int p = tid + i * NTH, row = p / 8, seg = p % 8;
         wr[q][i] = ld16((const uint16_t*)a.w + (size_t)(n0 + row) * a.K + k0 + 8 * seg);
       }
     }
@@ -114,7 +121,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
   auto store = [&](int b, int q) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int p = tid + i * 256;
+      const int p = tid + i * NTH;
       *(u32x4*)&xs[b][p / 8][8 * (p % 8)] = xr[q][i];
       if constexpr (Q4) {
         // the row's 8 pieces sit on 8 consecutive lanes
@@ -142,7 +149,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
     } else {
 #pragma unroll
       for (int i = 0; i < WP; ++i) {
-        const int p = tid + i * 256;
+        const int p = tid + i * NTH;
         *(u32x4*)&ws[b][p / 8][8 * (p % 8)] = wr[q][i];
       }
     }
@@ -224,7 +231,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
       }
   } else {
     // the stage buffers are free after the loop's last barrier
-    __shared__ int s_req[PF_BM], s_pos[PF_BM];
+    __shared__ int s_req[BM], s_pos[BM];
     auto tile = (float(*)[BN + 1])smem;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -232,8 +239,8 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) tile[wm * 64 + 16 * i + 4 * lg + r][wn * WN + 16 * j + lr] = acc[i][j][r];
-    const int rows = min(PF_BM, a.M - m0);
-    for (int r = tid; r < rows; r += 256) {
+    const int rows = min(BM, a.M - m0);
+    for (int r = tid; r < rows; r += NTH) {
       int req;
       long long p, rp;
       const unsigned bad = ring_row(h, m0 + r, &req, &p, &rp);
@@ -248,7 +255,7 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
       const bool on = lane < half;
       const float g1 = on ? bfbits2f(h.k_gain[lane]) : 0.f, g2 = on ? bfbits2f(h.k_gain[lane + half]) : 0.f;
       const double freq = rope_freq(on ? lane : 0, hd, h.log2_theta);
-      for (int it = wave; it < rows * nh; it += 4) {
+      for (int it = wave; it < rows * nh; it += NWV) {
         const int r = it / nh, hh = it % nh;
         const int p = s_pos[r];
         if (p < 0) continue;
@@ -265,9 +272,9 @@ void gemm_tile_kernel(const TileArgs a, const GemmArgs h) {
         o[lane + half] = f2bfbits(y2 * c + y1 * sn);
       }
     } else {
-      // V heads: one wave per (dimension, 64-row half); lane = row
-      for (int it = wave; it < nh * hd * 2; it += 4) {
-        const int hh = it / (2 * hd), d = (it / 2) % hd, r = (it & 1) * 64 + lane;
+      // V heads: one wave per (dimension, 64-row block); lane = row
+      for (int it = wave; it < nh * hd * RB; it += NWV) {
+        const int hh = it / (RB * hd), d = (it / RB) % hd, r = (it % RB) * 64 + lane;
         if (r >= rows) continue;
         const int p = s_pos[r];
         if (p < 0) continue;
@@ -282,9 +289,9 @@ template <int BN, int Q4>
 hipError_t launch_tile_q(const TileArgs& a, const GemmArgs& h, int out, hipStream_t st) {
   const int tiles = ((a.M + PF_BM - 1) / PF_BM) * (a.N / BN);
   const dim3 grid(8 * ((tiles + 7) / 8));
-  if (out == OUT_BF16) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_BF16, Q4>), grid, dim3(256), 0, st, a, h);
-  else if (out == OUT_F32) hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_F32, Q4>), grid, dim3(256), 0, st, a, h);
-  else hipLaunchKernelGGL((gemm_tile_kernel<BN, OUT_HEADS, Q4>), grid, dim3(256), 0, st, a, h);
+  if (out == OUT_BF16) hipLaunchKernelGGL((gemm_tile_kernel<PF_BM, BN, OUT_BF16, Q4>), grid, dim3(256), 0, st, a, h);
+  else if (out == OUT_F32) hipLaunchKernelGGL((gemm_tile_kernel<PF_BM, BN, OUT_F32, Q4>), grid, dim3(256), 0, st, a, h);
+  else hipLaunchKernelGGL((gemm_tile_kernel<PF_BM, BN, OUT_HEADS, Q4>), grid, dim3(256), 0, st, a, h);
   return hipGetLastError();
 }
 
@@ -324,10 +331,16 @@ hipError_t launch_gemm_tile(const TileArgs& a, int bn, int out_bf16, hipStream_t
   return bn == 128 ? launch_tile<128>(a, none, out, st) : launch_tile<64>(a, none, out, st);
 }
 
-hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, hipStream_t st) {
+hipError_t launch_gemm_tile_heads(const TileArgs& a, const GemmArgs& h, int n_cu, hipStream_t st) {
   // whole heads per tile: 128 columns (1 head of 128 or 2 of 64)
   if (a.M < 1 || a.K % (2 * PF_BK) || h.hd < 2 || h.hd > 128 || h.hd % 2 || 128 % h.hd || a.N != 2 * h.nkv * h.hd ||
       (h.nkv * h.hd) % 128)
     return hipErrorInvalidValue;
+  // bf16 weights with at least one 256-row tile per CU: the larger tile
+  if (!a.wscale && n_cu > 0 && (long long)(a.M / 256) * (a.N / 128) >= n_cu) {
+    const int tiles = ((a.M + 255) / 256) * (a.N / 128);
+    hipLaunchKernelGGL((gemm_tile_kernel<256, 128, OUT_HEADS, 0>), dim3(8 * ((tiles + 7) / 8)), dim3(512), 0, st, a, h);
+    return hipGetLastError();
+  }
   return launch_tile<128>(a, h, OUT_HEADS, st);
 }
