@@ -86,12 +86,14 @@ def lm_kernel_label(hidden: int, vocab: int, rows: int) -> str:
     beside a ring of 16 weight slots (8 waves
     x 2 chunks x 4 KB); 17..64 rows, bf16 normed rows and weights both loaded
     straight into LDS in phases of whole 128-column chunks; otherwise the
-    windowed kernel. Either LDS kernel takes at most 8 (16 rows) or 5 (more
-    rows) column groups of 128 per workgroup."""
+    windowed kernel. The 16-row kernel deals out 16-row weight tiles, at most 8
+    per wave; the 17..64-row kernel takes at most 5 column groups of 128 per
+    workgroup."""
     groups = (vocab + 127) // 128
     per = -(-groups // 256)
+    tiles = (vocab + 15) // 16
     nch = hidden // 128 if hidden % 128 == 0 else 0
-    if rows <= 16 and nch and per <= 8:
+    if rows <= 16 and nch and tiles <= 8 * min(256, tiles) * 8:
         rx = 8 if rows <= 8 else 16   # rows staged
         for kph in (1, 2):
             kw = hidden // kph

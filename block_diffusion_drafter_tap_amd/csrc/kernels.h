@@ -109,12 +109,13 @@ hipError_t launch_gateup_q4(const GemmArgs& a, int ks, hipStream_t st);
 // [R*(B-1)][topk] (topk <= 16).
 struct LmPlan {
   int MT, XL, groups, P;   // XL: 1 rows staged in LDS, 2 LDS windows of bf16 rows, 0 rows from L2,
-                           // 3 rows staged and W through LDS (direct loads)
+                           // 3 rows staged and W through LDS (direct loads); P workgroups
   int slots, defer_off;    // groups per workgroup whose epilogue waits for the last load; their LDS
                            // offset (XL 3: the offset of the W slots)
   size_t lds;
   int kph = 1;             // XL 3/4: phases of K (XL 3: each stages K / kph columns of the rows)
   int rx = 16;             // XL 3: rows staged (8 when the call has at most 8)
+  int contig = 0;          // XL 3: W's 16-row tiles in contiguous ranges per workgroup, not by groups
 };
 LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu);
 // the final-normed rows as bf16 z[M][K] (for plans with XL = 0), from the same

@@ -53,12 +53,13 @@ __global__ __launch_bounds__(256) void lm_norm_rows_kernel(const GemmArgs a, uin
 // their row's max over the wave's 16 columns (one entry per 16-column group, for
 // the top-k filter).
 template <int MT>
-DEV void lm_epilogue(const GemmArgs& a, int gg, const f32x4 (&ac)[MT], float* logits, int transposed, float* gmax) {
-  constexpr int GC = 128, ROWS = MT * 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+DEV void lm_epilogue(const GemmArgs& a, int grp16, const f32x4 (&ac)[MT], float* logits, int transposed,
+                     float* gmax) {
+  constexpr int ROWS = MT * 16;
+  const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n = gg * GC + wave * 16 + lr;
-  const int ng = (a.N + 15) / 16, grp16 = gg * (GC / 16) + wave;
+  const int n = grp16 * 16 + lr;   // this wave's 16 columns are grp16's
+  const int ng = (a.N + 15) / 16;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (transposed && n < a.N) *(f32x4*)(logits + (size_t)n * ROWS + mt * 16 + 4 * lg) = ac[mt];
@@ -187,7 +188,9 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
     return ld16(a.x + (size_t)min(mt * 16 + lr, a.M - 1) * a.ldx + kk + 8 * lg);
   };
 
-  auto epilogue = [&](int gg, const f32x4 (&ac)[MT]) { lm_epilogue<MT>(a, gg, ac, logits, transposed, gmax); };
+  auto epilogue = [&](int gg, const f32x4 (&ac)[MT]) {
+    lm_epilogue<MT>(a, gg * (GC / 16) + wave, ac, logits, transposed, gmax);
+  };
 
   for (; g < n_groups; g += gridDim.x) {
     const int gnext = g + gridDim.x;
@@ -258,9 +261,20 @@ __global__ __launch_bounds__(512) void lm_logits_kernel(const GemmArgs a, int n_
 // the wait for a slot is an explicit vmcnt: the only vector memory operations
 // in the streaming loop are these loads (4 per chunk), with D chunks in flight
 // (after the last group's last refill, a wait is for every load).
-// Each wave's accumulators of its (at most lm_lds_max_groups) groups stay in
+// Work is dealt out in 16-row tiles of W (T of them), wave w of workgroup b (of
+// P) taking tiles base + i * stride below an end, so the 8 waves of a workgroup
+// are always on 128 adjacent rows:
+//   by 128-row groups  base 8 b + w, stride 8 P, end T: groups b, b + P, ...,
+//                      every wave of a workgroup the same count of tiles;
+//   contiguous         base b T / P + w, stride 8, end (b + 1) T / P: one
+//                      workgroup per CU, each CU 37 or 38 tiles of the qwen3
+//                      vocabulary where groups give 238 CUs 40 and the rest none.
+// Measured on the qwen3 vocabulary: with 5 KB rows (hidden 2560) groups are
+// faster (127.5 against 129.7 us; the waves' unequal counts leave a tail), with
+// 8 KB rows (hidden 4096) the contiguous ranges (214.8 -> 206.6 us).
+// Each wave's accumulators of its (at most lm_lds_max_groups) tiles stay in
 // registers until the last load is out, so no store interleaves with the
-// stream. The MFMA inputs and their order equal lm_logits_kernel's, so the
+// stream. A tile's MFMA inputs and their order equal lm_logits_kernel's, so the
 // logits are the same bit for bit.
 constexpr int LM_LDS_MAX_GROUPS = 8;
 // groups per workgroup the LDS kernel parks in registers: fewer with more row tiles
@@ -275,11 +289,11 @@ DEV void wait_w_chunk() {   // vmcnt <= 4 (D - 1); expcnt and lgkmcnt not waited
 }
 
 template <int D, int KPH, int RX>
-__global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_groups, float* logits,
-                                                            int transposed, float* gmax, int w_off) {
+__global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, int n_tiles, int contig,
+                                                            float* logits, int transposed, float* gmax, int w_off) {
   // one 16-row tile, of which RX rows (8 or 16) are staged: with 8, the A
   // operand's rows 8..15 repeat rows 0..7 and their logits are never read
-  constexpr int MT = 1, GC = 128, ROWS = RX, kph = KPH, MAXG = lm_lds_max_groups(MT);
+  constexpr int MT = 1, ROWS = RX, kph = KPH, MAXG = lm_lds_max_groups(MT);
   static_assert(RX == 8 || RX == 16, "8 or 16 staged rows");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -289,15 +303,19 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
   uint16_t* gains = (uint16_t*)(smem + norm_rows_bytes(kw, ROWS));
   char* wring = smem + w_off + (size_t)wave * D * 4096;
   const uint16_t* W = (const uint16_t*)a.w;
-  auto issue = [&](int gg, int c, int slot) {
+  auto issue = [&](int t, int c, int slot) {   // chunk c of tile t (W rows 16 t .. 16 t + 15)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int row = 4 * s + lg, kb = (lane - row) & 15;
-      const uint16_t* src = W + (size_t)min(gg * GC + wave * 16 + row, a.N - 1) * K + c * 128 + kb * 8;
+      const uint16_t* src = W + (size_t)min(t * 16 + row, a.N - 1) * K + c * 128 + kb * 8;
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(wring + slot * 4096 + s * 1024), 16, 0, 2);
     }
   };
-  const int g0 = blockIdx.x;
+  // this wave's tiles: t0, t0 + step, ... below t_end
+  const int P = gridDim.x, b = blockIdx.x;
+  const int step = contig ? 8 : 8 * P;
+  const int t0 = (contig ? (int)((long long)b * n_tiles / P) : 8 * b) + wave;
+  const int t_end = contig ? (int)((long long)(b + 1) * n_tiles / P) : n_tiles;
   f32x4 park[MAXG][MT];
 #pragma unroll
   for (int gi = 0; gi < MAXG; ++gi)
@@ -313,9 +331,9 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
     // the first group's first D chunks of the phase, then the rows' loads; one
     // wait covers all of them (the previous phase ended with every load landed,
     // and the staging's first barrier follows every wave's last read of xs)
-    if (g0 < n_groups) {
+    if (t0 < t_end) {
 #pragma unroll
-      for (int j = 0; j < D; ++j) issue(g0, cb + j, j);
+      for (int j = 0; j < D; ++j) issue(t0, cb + j, j);
     }
     NormRowsLoads<LM_LDS_XP, norm_sqp<512, ROWS>()> L;
     norm_rows_issue<512, LM_LDS_XP, ROWS>(a, ph * kw, kw, gains, L);
@@ -323,10 +341,10 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
     int slot = 0;
 #pragma unroll
     for (int gi = 0; gi < MAXG; ++gi) {
-      const int g = g0 + gi * (int)gridDim.x;
-      if (g < n_groups) {
-        const int gn = g + (int)gridDim.x;
-        const bool last = gn >= n_groups;   // no refills past its end: its last D - 1 chunks wait for every load
+      const int g = t0 + gi * step;
+      if (g < t_end) {
+        const int gn = g + step;
+        const bool last = gn >= t_end;   // no refills past its end: its last D - 1 chunks wait for every load
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = park[gi][mt];
@@ -361,8 +379,8 @@ __global__ __launch_bounds__(512) void lm_logits_lds_kernel(const GemmArgs a, in
   }
 #pragma unroll
   for (int gi = 0; gi < MAXG; ++gi) {
-    const int g = g0 + gi * (int)gridDim.x;
-    if (g < n_groups) lm_epilogue<MT>(a, g, park[gi], logits, transposed, gmax);
+    const int g = t0 + gi * step;
+    if (g < t_end) lm_epilogue<MT>(a, g, park[gi], logits, transposed, gmax);
   }
 }
 
@@ -486,7 +504,7 @@ __global__ __launch_bounds__(512) void lm_logits_dma_kernel(const GemmArgs a, in
 #pragma unroll
   for (int gi = 0; gi < MAXG; ++gi) {
     const int g = g0 + gi * P;
-    if (g < n_groups) lm_epilogue<MT>(a, g, park[gi], logits, transposed, gmax);
+    if (g < n_groups) lm_epilogue<MT>(a, g * (GC / 16) + wave, park[gi], logits, transposed, gmax);
   }
 }
 
@@ -795,13 +813,19 @@ LmPlan plan_lmhead(int M, int B, int V, int K, int n_cu) {
   // one row tile (8 of its rows staged when the call has at most 8) with its
   // gains in 1 or 2 phases of K, with room for the W slots: W through LDS (XL 3)
   const int rx = M <= 8 ? 8 : 16;
-  for (int kph = 1; p.MT == 1 && kph <= 2 && per <= lm_lds_max_groups(1); kph *= 2) {
+  // 16-row W tiles dealt by 128-row groups (P as above), or as contiguous ranges
+  // of one workgroup per CU when W rows are 8 KB or longer (measured)
+  const int tiles = (V + 15) / 16, contig = K >= 4096 ? 1 : 0;
+  const int pt = contig ? std::min(n_cu, tiles) : p.P;
+  for (int kph = 1; p.MT == 1 && kph <= 2 && tiles <= 8 * pt * lm_lds_max_groups(1); kph *= 2) {
     if (K % kph) break;
     const int kw = K / kph;
     const size_t xoff = norm_rows_bytes(kw, rx) + norm_gain_bytes(kw);
     if (norm_rows_fit(K, kw, 512, LM_LDS_XP, rx) && kw / 128 >= LM_LDS_DEPTH &&
         xoff + (size_t)8 * LM_LDS_DEPTH * 4096 + norm_sq_bytes(512, rx) <= LM_LDS_TOTAL) {
       p.XL = 3;
+      p.P = pt;
+      p.contig = contig;
       p.rx = rx;
       p.kph = kph;
       p.defer_off = (int)xoff;   // the W slots
@@ -832,11 +856,12 @@ hipError_t launch_lm_logits(const GemmArgs& a, const LmPlan& p, float* logits, i
   if (p.XL == 3) {
     if (p.MT != 1 || (p.rx != 8 && p.rx != 16) || p.kph < 1 || a.K % p.kph ||
         !norm_rows_fit(a.K, a.K / p.kph, 512, LM_LDS_XP, p.rx) || a.K / p.kph / 128 < LM_LDS_DEPTH ||
-        a.M > p.rx || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX || (long long)p.P * lm_lds_max_groups(1) < p.groups)
+        a.M > p.rx || a.n_ssq < 1 || a.n_ssq > NORM_SSQ_MAX || p.P < 1 ||
+        (long long)8 * p.P * lm_lds_max_groups(1) < (a.N + 15) / 16)
       return hipErrorInvalidValue;
-#define LMLDS(KPH, RX)                                                                                          \
-  hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, KPH, RX>), dim3(p.P), dim3(512), p.lds, st, a, p.groups, \
-                     logits, transposed, gmax, p.defer_off)
+#define LMLDS(KPH, RX)                                                                                      \
+  hipLaunchKernelGGL((lm_logits_lds_kernel<LM_LDS_DEPTH, KPH, RX>), dim3(p.P), dim3(512), p.lds, st, a, \
+                     (a.N + 15) / 16, p.contig, logits, transposed, gmax, p.defer_off)
     if (p.kph == 1 && p.rx == 16) LMLDS(1, 16);
     else if (p.kph == 2 && p.rx == 16) LMLDS(2, 16);
     else if (p.kph == 1 && p.rx == 8) LMLDS(1, 8);
