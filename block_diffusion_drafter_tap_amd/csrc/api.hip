@@ -327,11 +327,17 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     if (e != hipSuccess) return hip_fail(e, "prefill ctx norm");
   }
   const size_t rl = ring_layer_elems(g);
+  // bf16 weights: each layer's K/V product through hipBLASLt as fp32 rows into the
+  // gathered tap rows' buffer (dead once the fc has read it), then the head finish
+  // (k RMSNorm, RoPE, K rows and V^T columns into the rings); otherwise, or when
+  // hipBLASLt has no kernel for the shape, the tile GEMM with that epilogue fused
+  float* kv32 = at<float>(ctx->ws, ctx->wl.xg);
+  const bool kv_lt = hd == 128 && (size_t)n_rows * nkv_w * 4 <= (size_t)g.max_stage_rows * TW * 2;
   for (int l = 0; l < g.n_layers; ++l) {
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
     const size_t kv_row0 = (size_t)g.n_q_heads * hd;   // the K and V rows of the fused QKV matrix
-    TileArgs ta{c_bf, H, w_rows(g, ctx->wqkv[l], kv_row0, H), n_rows, nkv_w, H, nullptr, 0,
-                s_rows(dflash_ctx::sc(ctx->wqkv_s, l), kv_row0, H)};
+    const uint16_t* wscale = s_rows(dflash_ctx::sc(ctx->wqkv_s, l), kv_row0, H);
+    TileArgs ta{c_bf, H, w_rows(g, ctx->wqkv[l], kv_row0, H), n_rows, nkv_w, H, nullptr, 0, wscale};
     GemmArgs b = base_args(ctx);
     b.M = n_rows;
     b.k_gain = ctx->k_norm[l];
@@ -340,7 +346,16 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
     b.req_of_row = req_of_row;
     b.pos_of_row = pos_of_row;
     b.rows_per_req = rows_per_req < 1 ? 1 : rows_per_req;
-    e = launch_gemm_tile_heads(ta, b, ctx->n_cu, st);
+    e = hipErrorNotSupported;
+    if (!wscale && kv_lt) {
+      e = blaslt_gemm_nt(c_bf, H, (const uint16_t*)ta.w, n_rows, nkv_w, H, kv32, nkv_w, 1, st);
+      if (e == hipSuccess) {
+        b.head_base = g.n_q_heads;
+        b.q_gain = ctx->q_norm[l];
+        e = launch_finish_kv_rows(b, kv32, nkv_w, st);
+      }
+    }
+    if (e == hipErrorNotSupported) e = launch_gemm_tile_heads(ta, b, ctx->n_cu, st);
     if (e != hipSuccess) return hip_fail(e, "prefill kv");
   }
   return DFLASH_OK;

@@ -1,9 +1,10 @@
 // Plain bf16 GEMMs through hipBLASLt: Y[M][N] = X[M][K] . W[N][K]^T with X and W
 // bf16 row-major (leading dimensions ldx and K), Y bf16 or fp32 row-major
 // (leading dimension ldo), fp32 accumulation. Used for the staging stage's fc
-// projection of a whole context window (4096 rows at the qwen3-4b shape), a
-// dense MFMA-bound product with no epilogue of its own, where the library's
-// tuned kernels run faster than the tile GEMM of prefill.hip.
+// projection of a whole context window (4096 rows at the qwen3-4b shape) and for
+// its context K/V projections (fp32 rows, whose head epilogue then runs as a
+// kernel of its own): dense MFMA-bound products where the library's tuned
+// kernels run faster than the tile GEMM of prefill.hip.
 //
 // In hipBLASLt's column-major terms Y^T (N x M, ld ldo) = op(A) op(B) with A the
 // weights as a K x N matrix (ld K, transposed) and B the rows as a K x M matrix

@@ -131,7 +131,87 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
   }
 }
 
+// Head finish of many staged rows from one fp32 product P[M][ld] holding the K
+// and V heads of the rows (head_dim 128): a workgroup takes 64 rows of one head.
+// Every load goes out at once (each thread 8 pieces of the 64 x 128 block, the
+// first 64 threads one row's slot), the block lands in LDS, and then:
+//   K heads  a wave per row, lane d owning the rotation pair (d, d + 64), with
+//            finish_head_kernel's arithmetic; each row is 256 contiguous bytes;
+//   V heads  each store instruction writes one dimension of the 64 rows, which
+//            sit at consecutive ring slots when their positions do (128
+//            contiguous bytes of V^T).
+constexpr int KV_ROWS = 64;
+__global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, const float* __restrict__ P, int ld) {
+  __shared__ float tile[KV_ROWS][129];
+  __shared__ long long s_off[KV_ROWS];   // the row's K or V^T offset in its ring, or -1
+  __shared__ long long s_rp[KV_ROWS];    // its RoPE position
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * KV_ROWS, hl = blockIdx.y;
+  const int rows = min(KV_ROWS, a.M - m0);
+  const int head = a.head_base + hl;
+  const bool is_k = head < a.nq + a.nkv;
+  f32x4 v[8];   // piece e = threadIdx.x + 256 u: row e / 32, columns 4 (e % 32) .. + 3
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = (int)threadIdx.x + 256 * u, r = min(e / 32, rows - 1);
+    v[u] = *(const f32x4*)(P + (size_t)(m0 + r) * ld + (size_t)hl * 128 + 4 * (e % 32));
+  }
+  if (threadIdx.x < KV_ROWS) {
+    long long off = -1, rpos = 0;
+    if ((int)threadIdx.x < rows) {
+      int req;
+      long long p, rp;
+      const unsigned bad = ring_row(a, m0 + (int)threadIdx.x, &req, &p, &rp);
+      if (bad) {
+        set_error(a.err, bad);
+      } else if (is_k) {
+        off = (((long long)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * 128;
+        rpos = rp;
+      } else {
+        off = (((long long)req * a.nkv + (head - a.nq - a.nkv)) * 128) * a.C + p % a.C;
+      }
+    }
+    s_off[threadIdx.x] = off;
+    s_rp[threadIdx.x] = rpos;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = (int)threadIdx.x + 256 * u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[e / 32][4 * (e % 32) + i] = v[u][i];
+  }
+  __syncthreads();
+  if (is_k) {
+    const float g1 = bfbits2f(a.k_gain[lane]), g2 = bfbits2f(a.k_gain[lane + 64]);
+    const double freq = rope_freq(lane, 128, a.log2_theta);   // once per lane, not per row
+    for (int r = wave; r < rows; r += 4) {
+      const long long off = s_off[r];
+      if (off < 0) continue;
+      const float x1 = tile[r][lane], x2 = tile[r][lane + 64];
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float inv = 1.0f / sqrtf(ss / 128.0f + a.eps);
+      const float y1 = x1 * inv * g1;
+      const float y2 = x2 * inv * g2;
+      float c, s;
+      rope_cs(s_rp[r], freq, &c, &s);
+      a.ring_k[off + lane] = f2bfbits(y1 * c - y2 * s);
+      a.ring_k[off + lane + 64] = f2bfbits(y2 * c + y1 * s);
+    }
+    return;
+  }
+  const long long off = s_off[lane];
+  if (off >= 0)
+    for (int d = wave; d < 128; d += 4) a.ring_v[off + (long long)d * a.C] = f2bfbits(tile[lane][d]);
+}
+
 }  // namespace
+
+hipError_t launch_finish_kv_rows(const GemmArgs& a, const float* P, int ld, hipStream_t st) {
+  if (a.hd != 128 || a.nb > 0 || a.M < 1 || a.head_base != a.nq || ld < 2 * a.nkv * 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(finish_kv_rows_kernel, dim3((a.M + KV_ROWS - 1) / KV_ROWS, 2 * a.nkv), dim3(256), 0, st, a, P,
+                     ld);
+  return hipGetLastError();
+}
 
 hipError_t launch_finish_resid(const float* P, int S, int M, int N, float* h, int ldh, float* ssq_out, int ssq_ld,
                                hipStream_t st) {

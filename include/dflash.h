@@ -29,10 +29,10 @@
  *     outputs belong to the caller (e.g. PyTorch tensors) and must outlive the
  *     handle. The handle stores the config and borrowed pointers only.
  *     One exception: a staging call of at least 256 rows with bf16 weights runs
- *     its fc product through hipBLASLt. dflash_bind of such a drafter creates the
- *     device's hipBLASLt handle (once per process and device: the library's own
- *     internal buffers), and hipBLASLt loads its kernel the first time a staging
- *     shape runs. Nothing in a draft round (draft, accept, reset, check, staging of
+ *     its fc and context K/V products through hipBLASLt. dflash_bind of such a
+ *     drafter creates the device's hipBLASLt handle (once per process and device:
+ *     the library's own internal buffers), and hipBLASLt loads its kernels the
+ *     first time a staging shape runs. Nothing in a draft round (draft, accept, reset, check, staging of
  *     fewer than 256 rows) allocates.
  *   - One handle = one state + one workspace; calls on one handle must be ordered
  *     (one stream, or events between streams). Two handles never share a workspace.
