@@ -132,15 +132,18 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
 }
 
 // Head finish of many staged rows from one fp32 product P[M][ld] holding the K
-// and V heads of the rows (head_dim 128): a workgroup takes 64 rows of one head.
-// Every load goes out at once (each thread 8 pieces of the 64 x 128 block, the
-// first 64 threads one row's slot), the block lands in LDS, and then:
+// and V heads of the rows (head_dim 128): a workgroup takes 32 rows of one head.
+// Every load goes out at once (each thread 4 pieces of the 32 x 128 block, the
+// first 32 threads one row's slot), the block lands in LDS, and then:
 //   K heads  a wave per row, lane d owning the rotation pair (d, d + 64), with
 //            finish_head_kernel's arithmetic; each row is 256 contiguous bytes;
-//   V heads  each store instruction writes one dimension of the 64 rows, which
-//            sit at consecutive ring slots when their positions do (128
-//            contiguous bytes of V^T).
-constexpr int KV_ROWS = 64;
+//   V heads  each store instruction writes two dimensions of the 32 rows, which
+//            sit at consecutive ring slots when their positions do (64
+//            contiguous bytes of V^T each).
+// Measured for 4096 rows x 16 heads: 64-row blocks took the staging 0.607 ms, 32-row
+// blocks 0.589-0.597, 16-row blocks 0.591 (the waves' chains of rows are shorter).
+constexpr int KV_ROWS = 32;
+constexpr int KV_NP = KV_ROWS * 32 / 256;   // 16-byte pieces of the block per thread
 __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, const float* __restrict__ P, int ld) {
   __shared__ float tile[KV_ROWS][129];
   __shared__ long long s_off[KV_ROWS];   // the row's K or V^T offset in its ring, or -1
@@ -150,9 +153,9 @@ __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, c
   const int rows = min(KV_ROWS, a.M - m0);
   const int head = a.head_base + hl;
   const bool is_k = head < a.nq + a.nkv;
-  f32x4 v[8];   // piece e = threadIdx.x + 256 u: row e / 32, columns 4 (e % 32) .. + 3
+  f32x4 v[KV_NP];   // piece e = threadIdx.x + 256 u: row e / 32, columns 4 (e % 32) .. + 3
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < KV_NP; ++u) {
     const int e = (int)threadIdx.x + 256 * u, r = min(e / 32, rows - 1);
     v[u] = *(const f32x4*)(P + (size_t)(m0 + r) * ld + (size_t)hl * 128 + 4 * (e % 32));
   }
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, c
     s_rp[threadIdx.x] = rpos;
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < KV_NP; ++u) {
     const int e = (int)threadIdx.x + 256 * u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) tile[e / 32][4 * (e % 32) + i] = v[u][i];
@@ -199,9 +202,12 @@ __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, c
     }
     return;
   }
-  const long long off = s_off[lane];
+  // V^T: thread t stores row t % KV_ROWS of dimensions t / KV_ROWS + 256 / KV_ROWS * j
+  const int vr = threadIdx.x % KV_ROWS;
+  const long long off = s_off[vr];
   if (off >= 0)
-    for (int d = wave; d < 128; d += 4) a.ring_v[off + (long long)d * a.C] = f2bfbits(tile[lane][d]);
+    for (int d = threadIdx.x / KV_ROWS; d < 128; d += 256 / KV_ROWS)
+      a.ring_v[off + (long long)d * a.C] = f2bfbits(tile[vr][d]);
 }
 
 }  // namespace
