@@ -419,6 +419,20 @@ static int create_impl(const dflash_config* cfg, const dflash_weights* w, dflash
         if (!sarr[i][l]) return fail(DFLASH_E_ARG, "INT4 scale array %d[%d] is NULL", i, l);
     }
   }
+  // every kernel reads weights, gains and scales in 16-byte pieces
+  auto misaligned = [](const void* p) { return ((uintptr_t)p & 15) != 0; };
+  if (misaligned(w->embed) || misaligned(w->lm_head) || misaligned(w->fc) || misaligned(w->final_norm) ||
+      misaligned(w->ctx_norm) || misaligned(w->fc_scales))
+    return fail(DFLASH_E_ARG, "embed, lm_head, fc, final_norm, ctx_norm and fc_scales must be 16-byte aligned");
+  for (int i = 0; i < 8; ++i)
+    for (int l = 0; l < c.n_layers; ++l)
+      if (misaligned(arrays[i][l])) return fail(DFLASH_E_ARG, "%s[%d] must be 16-byte aligned", names[i], l);
+  if (q4) {
+    const void* const* sarr[] = {w->wqkv_scales, w->wo_scales, w->wgu_scales, w->wd_scales};
+    for (int i = 0; i < 4; ++i)
+      for (int l = 0; l < c.n_layers; ++l)
+        if (misaligned(sarr[i][l])) return fail(DFLASH_E_ARG, "INT4 scale array %d[%d] must be 16-byte aligned", i, l);
+  }
   dflash_ctx* x = new dflash_ctx;
   x->cfg = c;
   x->embed = (const uint16_t*)w->embed;

@@ -133,6 +133,8 @@ typedef struct {
  *   (e odd). The weight is q * scale.
  *   ln_in[l], ln_post[l]: bf16 [hidden]; q_norm[l], k_norm[l]: bf16 [head_dim];
  *   final_norm: bf16 [hidden]; ctx_norm: bf16 [hidden] (read only if cfg.ctx_norm).
+ *   Every pointer is 16-byte aligned (the kernels read in 16-byte pieces;
+ *   dflash_create refuses others with DFLASH_E_ARG).
  */
 typedef struct {
   const void* embed;

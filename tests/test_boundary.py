@@ -102,6 +102,26 @@ def test_missing_weights_rejected_before_any_buffer():
     assert rc == -1 and "ctx_norm" in msg
 
 
+def test_misaligned_weights_rejected():
+    """Every kernel reads weights in 16-byte pieces: create() refuses a weight,
+    gain or per-layer pointer that is not 16-byte aligned."""
+    cfg = config.tiny()
+    w = _fake_weights(cfg)
+    w.embed = 0x1002
+    rc, msg = _create(cfg, w)
+    assert rc == -1 and "16-byte aligned" in msg
+    w = _fake_weights(cfg)
+    arr = (ctypes.c_void_p * cfg.n_layers)(*([0x1000] * (cfg.n_layers - 1) + [0x1008]))
+    _keep.append(arr)
+    w.k_norm = ctypes.cast(arr, Bd.PP)
+    rc, msg = _create(cfg, w)
+    assert rc == -1 and f"k_norm[{cfg.n_layers - 1}]" in msg and "aligned" in msg
+    w = _fake_weights(cfg)
+    w.lm_head = 0x1010   # 16-byte aligned: accepted
+    rc, msg = _create(cfg, w)
+    assert rc == 0, msg
+
+
 def test_unbound_handle_refuses_calls():
     lib = Bd.load()
     cfg = config.tiny()
