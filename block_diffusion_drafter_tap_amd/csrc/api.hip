@@ -332,7 +332,7 @@ int stage_prefill(dflash_ctx* ctx, hipStream_t st, const float* const* taps, lon
   // (k RMSNorm, RoPE, K rows and V^T columns into the rings); otherwise, or when
   // hipBLASLt has no kernel for the shape, the tile GEMM with that epilogue fused
   float* kv32 = at<float>(ctx->ws, ctx->wl.xg);
-  const bool kv_lt = hd == 128 && (size_t)n_rows * nkv_w * 4 <= (size_t)g.max_stage_rows * TW * 2;
+  const bool kv_lt = (hd == 64 || hd == 128) && (size_t)n_rows * nkv_w * 4 <= (size_t)g.max_stage_rows * TW * 2;
   for (int l = 0; l < g.n_layers; ++l) {
     Timed tm(ctx, DFLASH_K_STAGE_KV, st);
     const size_t kv_row0 = (size_t)g.n_q_heads * hd;   // the K and V rows of the fused QKV matrix

@@ -132,18 +132,21 @@ __global__ __launch_bounds__(256) void finish_head_kernel(const GemmArgs a, cons
 }
 
 // Head finish of many staged rows from one fp32 product P[M][ld] holding the K
-// and V heads of the rows (head_dim 128): a workgroup takes 32 rows of one head.
-// Every load goes out at once (each thread 4 pieces of the 32 x 128 block, the
-// first 32 threads one row's slot), the block lands in LDS, and then:
-//   K heads  a wave per row, lane d owning the rotation pair (d, d + 64), with
-//            finish_head_kernel's arithmetic; each row is 256 contiguous bytes;
+// and V heads of the rows (head_dim HD, 64 or 128): a workgroup takes 32 rows
+// of one head. Every load goes out at once (each thread up to 4
+// 16-byte pieces of the 32 x hd block, the first 32 threads one row's slot),
+// the block lands in LDS, and then:
+//   K heads  a wave per row, lane d < hd/2 owning the rotation pair (d, d + hd/2),
+//            with finish_head_kernel's arithmetic; each row is contiguous;
 //   V heads  each store instruction writes two dimensions of the 32 rows, which
 //            sit at consecutive ring slots when their positions do (64
 //            contiguous bytes of V^T each).
-// Measured for 4096 rows x 16 heads: 64-row blocks took the staging 0.607 ms, 32-row
-// blocks 0.589-0.597, 16-row blocks 0.591 (the waves' chains of rows are shorter).
+// Measured for 4096 rows x 16 heads of 128: 64-row blocks took the staging
+// 0.607 ms, 32-row blocks 0.589-0.597, 16-row blocks 0.591 (the waves' chains
+// of rows are shorter).
 constexpr int KV_ROWS = 32;
-constexpr int KV_NP = KV_ROWS * 32 / 256;   // 16-byte pieces of the block per thread
+constexpr int KV_NP = KV_ROWS * 32 / 256;   // 16-byte pieces of a 32 x 128 block per thread
+template <int HD>
 __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, const float* __restrict__ P, int ld) {
   __shared__ float tile[KV_ROWS][129];
   __shared__ long long s_off[KV_ROWS];   // the row's K or V^T offset in its ring, or -1
@@ -151,13 +154,14 @@ __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, c
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * KV_ROWS, hl = blockIdx.y;
   const int rows = min(KV_ROWS, a.M - m0);
+  constexpr int hd = HD, half = HD / 2, pr = HD / 4;   // pr: pieces per row
   const int head = a.head_base + hl;
   const bool is_k = head < a.nq + a.nkv;
-  f32x4 v[KV_NP];   // piece e = threadIdx.x + 256 u: row e / 32, columns 4 (e % 32) .. + 3
+  f32x4 v[KV_NP];   // piece e = threadIdx.x + 256 u: row e / pr, columns 4 (e % pr) .. + 3
 #pragma unroll
   for (int u = 0; u < KV_NP; ++u) {
-    const int e = (int)threadIdx.x + 256 * u, r = min(e / 32, rows - 1);
-    v[u] = *(const f32x4*)(P + (size_t)(m0 + r) * ld + (size_t)hl * 128 + 4 * (e % 32));
+    const int e = min((int)threadIdx.x + 256 * u, rows * pr - 1);
+    v[u] = *(const f32x4*)(P + (size_t)(m0 + e / pr) * ld + (size_t)hl * hd + 4 * (e % pr));
   }
   if (threadIdx.x < KV_ROWS) {
     long long off = -1, rpos = 0;
@@ -168,10 +172,10 @@ __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, c
       if (bad) {
         set_error(a.err, bad);
       } else if (is_k) {
-        off = (((long long)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * 128;
+        off = (((long long)req * a.nkv + (head - a.nq)) * a.C + p % a.C) * hd;
         rpos = rp;
       } else {
-        off = (((long long)req * a.nkv + (head - a.nq - a.nkv)) * 128) * a.C + p % a.C;
+        off = (((long long)req * a.nkv + (head - a.nq - a.nkv)) * hd) * a.C + p % a.C;
       }
     }
     s_off[threadIdx.x] = off;
@@ -180,42 +184,48 @@ __global__ __launch_bounds__(256) void finish_kv_rows_kernel(const GemmArgs a, c
 #pragma unroll
   for (int u = 0; u < KV_NP; ++u) {
     const int e = (int)threadIdx.x + 256 * u;
+    if (e < rows * pr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tile[e / 32][4 * (e % 32) + i] = v[u][i];
+      for (int i = 0; i < 4; ++i) tile[e / pr][4 * (e % pr) + i] = v[u][i];
+    }
   }
   __syncthreads();
   if (is_k) {
-    const float g1 = bfbits2f(a.k_gain[lane]), g2 = bfbits2f(a.k_gain[lane + 64]);
-    const double freq = rope_freq(lane, 128, a.log2_theta);   // once per lane, not per row
+    const bool on = lane < half;
+    const float g1 = on ? bfbits2f(a.k_gain[lane]) : 0.f, g2 = on ? bfbits2f(a.k_gain[lane + half]) : 0.f;
+    const double freq = rope_freq(on ? lane : 0, hd, a.log2_theta);   // once per lane, not per row
     for (int r = wave; r < rows; r += 4) {
       const long long off = s_off[r];
       if (off < 0) continue;
-      const float x1 = tile[r][lane], x2 = tile[r][lane + 64];
+      const float x1 = on ? tile[r][lane] : 0.f, x2 = on ? tile[r][lane + half] : 0.f;
       const float ss = wave_sum(x1 * x1 + x2 * x2);
-      const float inv = 1.0f / sqrtf(ss / 128.0f + a.eps);
+      const float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
+      if (!on) continue;
       const float y1 = x1 * inv * g1;
       const float y2 = x2 * inv * g2;
       float c, s;
       rope_cs(s_rp[r], freq, &c, &s);
       a.ring_k[off + lane] = f2bfbits(y1 * c - y2 * s);
-      a.ring_k[off + lane + 64] = f2bfbits(y2 * c + y1 * s);
+      a.ring_k[off + lane + half] = f2bfbits(y2 * c + y1 * s);
     }
     return;
   }
   // V^T: thread t stores row t % KV_ROWS of dimensions t / KV_ROWS + 256 / KV_ROWS * j
   const int vr = threadIdx.x % KV_ROWS;
   const long long off = s_off[vr];
-  if (off >= 0)
-    for (int d = threadIdx.x / KV_ROWS; d < 128; d += 256 / KV_ROWS)
+  if (off >= 0 && vr < rows)
+    for (int d = threadIdx.x / KV_ROWS; d < hd; d += 256 / KV_ROWS)
       a.ring_v[off + (long long)d * a.C] = f2bfbits(tile[vr][d]);
 }
 
 }  // namespace
 
 hipError_t launch_finish_kv_rows(const GemmArgs& a, const float* P, int ld, hipStream_t st) {
-  if (a.hd != 128 || a.nb > 0 || a.M < 1 || a.head_base != a.nq || ld < 2 * a.nkv * 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(finish_kv_rows_kernel, dim3((a.M + KV_ROWS - 1) / KV_ROWS, 2 * a.nkv), dim3(256), 0, st, a, P,
-                     ld);
+  if ((a.hd != 64 && a.hd != 128) || a.nb > 0 || a.M < 1 || a.head_base != a.nq || ld < 2 * a.nkv * a.hd || ld % 4)
+    return hipErrorInvalidValue;
+  const dim3 grid((a.M + KV_ROWS - 1) / KV_ROWS, 2 * a.nkv);
+  if (a.hd == 128) hipLaunchKernelGGL(finish_kv_rows_kernel<128>, grid, dim3(256), 0, st, a, P, ld);
+  else hipLaunchKernelGGL(finish_kv_rows_kernel<64>, grid, dim3(256), 0, st, a, P, ld);
   return hipGetLastError();
 }
 

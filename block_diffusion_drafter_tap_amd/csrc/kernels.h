@@ -160,8 +160,8 @@ hipError_t launch_finish_resid(const float* P, int S, int M, int N, float* h, in
                                hipStream_t st);
 hipError_t launch_finish_silu(const float* P, int S, int M, int N, uint16_t* act, int ldo, hipStream_t st);
 hipError_t launch_finish_head(const GemmArgs& a, const float* P, int S, int ld, int n_heads, hipStream_t st);
-// the K and V heads of many staged rows (head_dim 128) from one fp32 product
-// P[M][ld] (K heads then V heads): 64 rows of one head per workgroup
+// the K and V heads of many staged rows (head_dim 64 or 128) from one
+// fp32 product P[M][ld] (K heads then V heads): 32 rows of one head per workgroup
 hipError_t launch_finish_kv_rows(const GemmArgs& a, const float* P, int ld, hipStream_t st);
 hipError_t launch_finish_store(const float* P, int S, int M, int N, void* out, int ldo, int bf16, hipStream_t st);
 
