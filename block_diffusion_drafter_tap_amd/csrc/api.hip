@@ -33,7 +33,7 @@ enum Proj { P_QKV, P_O, P_GATEUP, P_DOWN, P_FC, P_STAGE_KV };
 constexpr int CPS_BF16[] = {2, 3, 4, 3, 4, 2};
 // INT4 chunks carry a quarter of the bytes; measured best at the qwen3-8b
 // shape with 8 rows (hidden 4096, ffn 12288)
-constexpr int CPS_INT4[] = {6, 2, 8, 4, 4, 2};
+constexpr int CPS_INT4[] = {6, 4, 8, 4, 4, 2};
 constexpr int GC_DEFAULT = 128;
 
 int wf_of(const dflash_config& c) { return c.wfmt == DFLASH_W_INT4_G64 ? WF_INT4 : WF_BF16; }
